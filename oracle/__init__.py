@@ -1,0 +1,202 @@
+"""fp64 CPU oracle for the KDA core -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  It shares no code with the HIP
+library: its arithmetic lives in ``kda_oracle.c`` (plain C, double precision,
+token by token) and in the numpy modules ``bruteforce`` and ``chunked``, which
+pin the C code from independent derivations.
+
+Every function here accepts the *stored* input tensors (bf16 bit patterns or
+float32, as produced by ``kda_inputs``) and widens them exactly to float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+from kda_inputs import BF16, FP32, Problem, as_f64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+FLAG_SKIP_CONV = 1
+FLAG_SKIP_L2NORM = 2
+FLAG_RAW_GATE = 4
+FLAG_RAW_BETA = 8
+FLAG_BETA_X2 = 16
+
+DEFAULT_LOWER_BOUND = -5.0   # safe gate (Ling-3.0-flash-VL page, section "KDA 层的安全门")
+DEFAULT_EPS = 1e-6           # L2-norm epsilon (not stated on the pages; a reading)
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall",
+                               "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_forward.restype = ctypes.c_int
+        lib.kda_oracle_forward.argtypes = [
+            ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_uint,
+            dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_int]
+        lib.kda_oracle_preprocess_head.restype = None
+        lib.kda_oracle_preprocess_head.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_uint,
+            dp, dp, dp, dp, dp]
+        lib.kda_oracle_recurrence.restype = None
+        lib.kda_oracle_recurrence.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, ctypes.c_long]
+        _lib = lib
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a, io):
+    return None if a is None else np.ascontiguousarray(as_f64(a, io))
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def forward(p: Problem, *, scale: float = 1.0, lower_bound: float = DEFAULT_LOWER_BOUND,
+            eps: float = DEFAULT_EPS, flags: int = 0, initial_state=None, conv_state=None,
+            items: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+            with_conv_out: bool = True):
+    """Run the oracle over a packed problem.
+
+    Returns (o [total_T, H, dv], S [N, H, dk, dv], conv_out [N, 3, Ctot] or None,
+    threads_used), all float64.  ``initial_state``/``conv_state`` default to the
+    problem's own; pass arrays to override (used by continuation tests).
+    ``items`` restricts the work to the listed (seq*H + head) pairs; rows of
+    the other pairs are left as NaN.
+    """
+    lib = _load()
+    io = p.io
+    H, dk, dv = p.H, p.dk, p.dv
+    N = len(p.seqlens)
+    cu = np.ascontiguousarray(p.cu_seqlens, dtype=np.int64)
+    q, k, v = _f64(p.q, io), _f64(p.k, io), _f64(p.v, io)
+    alpha, b = _f64(p.alpha, io), _f64(p.b, io)
+    w_q, w_k, w_v = _f64(p.w_q, io), _f64(p.w_k, io), _f64(p.w_v, io)
+    A_log = np.ascontiguousarray(p.A_log, dtype=np.float64)
+    dt_bias = np.ascontiguousarray(p.dt_bias, dtype=np.float64)
+    S0 = initial_state if initial_state is not None else p.initial_state
+    S0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+    cs = conv_state if conv_state is not None else p.conv_state
+    if cs is not None and cs.dtype == np.uint16:
+        cs = as_f64(cs, BF16)
+    cs = None if cs is None else np.ascontiguousarray(np.asarray(cs, dtype=np.float64))
+    total = p.total_T
+    o = np.full((total, H, dv), np.nan)
+    S = np.full((N, H, dk, dv), np.nan)
+    cout = np.zeros((N, 3, p.ctot)) if with_conv_out else None
+    it = None
+    n_it = 0
+    if items is not None:
+        it = np.ascontiguousarray(np.asarray(items, dtype=np.int32))
+        n_it = int(it.size)
+    nt = nthreads if nthreads is not None else default_threads()
+    used = lib.kda_oracle_forward(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        _p(q), _p(k), _p(v), _p(alpha), _p(b), _p(w_q), _p(w_k), _p(w_v), _p(A_log), _p(dt_bias),
+        float(scale), float(lower_bound), float(eps), int(flags),
+        _p(S0), _p(cs), _p(o), _p(S), _p(cout),
+        None if it is None else it.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_it, int(nt))
+    return o, S, cout, used
+
+
+def preprocess_head(p: Problem, seq: int, h: int, *, scale: float = 1.0,
+                    lower_bound: float = DEFAULT_LOWER_BOUND, eps: float = DEFAULT_EPS,
+                    flags: int = 0, conv_state=None):
+    """Post-preprocess tensors of one (sequence, head): q, k [L, dk], v [L, dv],
+    g [L, dk], beta [L] (float64)."""
+    lib = _load()
+    io = p.io
+    H, dk, dv = p.H, p.dk, p.dv
+    cu = p.cu_seqlens
+    t0, t1 = int(cu[seq]), int(cu[seq + 1])
+    L = t1 - t0
+    q = np.ascontiguousarray(_f64(p.q, io)[t0:t1])
+    k = np.ascontiguousarray(_f64(p.k, io)[t0:t1])
+    v = np.ascontiguousarray(_f64(p.v, io)[t0:t1])
+    alpha = np.ascontiguousarray(_f64(p.alpha, io)[t0:t1])
+    b = np.ascontiguousarray(_f64(p.b, io)[t0:t1])
+    w_q, w_k, w_v = _f64(p.w_q, io), _f64(p.w_k, io), _f64(p.w_v, io)
+    A_log = np.ascontiguousarray(p.A_log, dtype=np.float64)
+    dt_bias = np.ascontiguousarray(p.dt_bias, dtype=np.float64)
+    cs = conv_state if conv_state is not None else p.conv_state
+    if cs is not None:
+        cs = as_f64(cs, BF16) if cs.dtype == np.uint16 else np.asarray(cs, dtype=np.float64)
+        cs = np.ascontiguousarray(cs[seq])
+    qh = np.zeros((L, dk)); kh = np.zeros((L, dk)); vh = np.zeros((L, dv))
+    g = np.zeros((L, dk)); beta = np.zeros((L,))
+    lib.kda_oracle_preprocess_head(L, H, dk, dv, h, _p(q), _p(k), _p(v), _p(alpha), _p(b),
+                                   _p(w_q), _p(w_k), _p(w_v), _p(A_log), _p(dt_bias), _p(cs),
+                                   float(scale), float(lower_bound), float(eps), int(flags),
+                                   _p(qh), _p(kh), _p(vh), _p(g), _p(beta))
+    return qh, kh, vh, g, beta
+
+
+def recurrence(q, k, v, g, beta, S0=None):
+    """The token recurrence alone on post-preprocess inputs of one head.
+    q, k, g [L, dk]; v [L, dv]; beta [L]; S0 [dk, dv] or None.
+    Returns (o [L, dv], S [dk, dv])."""
+    lib = _load()
+    q, k, v, g = (np.ascontiguousarray(np.asarray(a, dtype=np.float64)) for a in (q, k, v, g))
+    beta = np.ascontiguousarray(np.asarray(beta, dtype=np.float64))
+    L, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, copy=True, order="C")
+    o = np.zeros((L, dv))
+    lib.kda_oracle_recurrence(L, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(o), dv)
+    return o, S
+
+
+def decode_reference(S, conv_state, tokens, params, H, dk, dv, io, *, scale=1.0,
+                     lower_bound=DEFAULT_LOWER_BOUND, eps=DEFAULT_EPS, flags=0,
+                     items: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+    """One decode step for N sequences (one token each): a length-1 forward per
+    sequence with the given state and conv history.
+
+    S [N, H, dk, dv] fp32/fp64; conv_state [N, 3, Ctot] stored dtype;
+    tokens = (q, k, v, alpha, b) for N tokens; params = (w_q, w_k, w_v, A_log, dt_bias).
+    Returns (o [N, H, dv], S_new, conv_new) in float64."""
+    q, k, v, alpha, b = tokens
+    w_q, w_k, w_v, A_log, dt_bias = params
+    N = q.shape[0]
+    prob = Problem([1] * N, H, dk, dv, io, q, k, v, alpha, b, w_q, w_k, w_v, A_log, dt_bias,
+                   np.asarray(S, dtype=np.float64), conv_state)
+    o, S_new, cout, _ = forward(prob, scale=scale, lower_bound=lower_bound, eps=eps, flags=flags,
+                               items=items, nthreads=nthreads)
+    return o, S_new, cout
