@@ -1,0 +1,244 @@
+"""Python binding of the MI355X KDA library (``libkda.so``, C ABI in include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the stream.
+The library must have been built (``python gated_delta_rule_03_amd/build.py``);
+importing the binding without it raises ImportError -- there is no fallback.
+
+Entry points (same names as the C ABI):
+  kda_prefill(cfg, q, k, v, alpha, b, ...)          B equal-length sequences
+  kda_varlen_prefill(cfg, cu_seqlens, q, ...)       packed sequences
+  kda_decode_step(cfg, q, k, v, alpha, b, state, conv_state, o=None)
+  kda_prefill_workspace_bytes / kda_varlen_workspace_bytes
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE_TOO_SMALL = 3
+KDA_ERR_HIP = 4
+
+KDA_BF16 = 0
+KDA_FP32 = 1
+
+FLAG_SKIP_CONV = 1 << 0
+FLAG_SKIP_L2NORM = 1 << 1
+FLAG_RAW_GATE = 1 << 2
+FLAG_RAW_BETA = 1 << 3
+FLAG_BETA_X2 = 1 << 4
+
+EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
+            "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, name: str):
+        super().__init__(f"{name} returned {status_string(status)} ({status})")
+        self.status = status
+
+
+class KdaConfigC(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_k_dim", ctypes.c_int32),
+        ("head_v_dim", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("gate_lower_bound", ctypes.c_float),
+        ("l2norm_eps", ctypes.c_float),
+        ("chunk_size", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("conv_w_q", ctypes.c_void_p),
+        ("conv_w_k", ctypes.c_void_p),
+        ("conv_w_v", ctypes.c_void_p),
+    ]
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"KDA HIP library not built: {LIB_PATH} is missing "
+                          "(run `python gated_delta_rule_03_amd/build.py`)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(KdaConfigC)
+    lib.kda_version.restype = i32
+    lib.kda_version.argtypes = []
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_prefill_workspace_bytes.restype = sz
+    lib.kda_prefill_workspace_bytes.argtypes = [cfgp, i32, i32]
+    lib.kda_varlen_workspace_bytes.restype = sz
+    lib.kda_varlen_workspace_bytes.argtypes = [cfgp, i32, i32]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_varlen_prefill.restype = ctypes.c_int
+    lib.kda_varlen_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    return lib
+
+
+_lib = _load_library()
+
+
+def library():
+    """The loaded ctypes library handle."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.kda_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_lib.kda_version())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_FP32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Config:
+    """Per-layer parameters and numerics of the KDA core (device tensors)."""
+    A_log: torch.Tensor          # [H] fp32
+    dt_bias: torch.Tensor        # [H*dk] fp32
+    conv_w_q: torch.Tensor       # [H*dk, 4] io dtype
+    conv_w_k: torch.Tensor       # [H*dk, 4]
+    conv_w_v: torch.Tensor       # [H*dv, 4]
+    num_heads: int
+    head_k_dim: int
+    head_v_dim: int
+    io_dtype: torch.dtype = torch.bfloat16
+    out_dtype: torch.dtype = torch.bfloat16
+    scale: float = 1.0
+    gate_lower_bound: float = -5.0
+    l2norm_eps: float = 1e-6
+    chunk_size: int = 64
+    flags: int = 0
+    _c: Optional[KdaConfigC] = field(default=None, repr=False)
+
+    def c_struct(self) -> KdaConfigC:
+        c = KdaConfigC()
+        c.num_heads = self.num_heads
+        c.head_k_dim = self.head_k_dim
+        c.head_v_dim = self.head_v_dim
+        c.io_dtype = _dtype_code(self.io_dtype)
+        c.out_dtype = _dtype_code(self.out_dtype)
+        c.scale = self.scale
+        c.gate_lower_bound = self.gate_lower_bound
+        c.l2norm_eps = self.l2norm_eps
+        c.chunk_size = self.chunk_size
+        c.flags = self.flags
+        for name in ("A_log", "dt_bias", "conv_w_q", "conv_w_k", "conv_w_v"):
+            t = getattr(self, name)
+            setattr(c, name, None if t is None else t.data_ptr())
+        self._c = c   # keep alive
+        return c
+
+    @property
+    def ctot(self) -> int:
+        return self.num_heads * (2 * self.head_k_dim + self.head_v_dim)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, name: str):
+    if status != KDA_OK:
+        raise KdaError(status, name)
+
+
+def kda_prefill_workspace_bytes(cfg: Config, B: int, T: int) -> int:
+    return int(_lib.kda_prefill_workspace_bytes(ctypes.byref(cfg.c_struct()), B, T))
+
+
+def kda_varlen_workspace_bytes(cfg: Config, N: int, total_T: int) -> int:
+    return int(_lib.kda_varlen_workspace_bytes(ctypes.byref(cfg.c_struct()), N, total_T))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def kda_prefill(cfg: Config, q, k, v, alpha, b, initial_state=None, conv_state_in=None, *,
+                o=None, final_state=None, conv_state_out=None, workspace=None, stream=None):
+    """q, k [B, T, H*dk]; v [B, T, H*dv]; alpha [B, T, H, dk]; b [B, T, H].
+    Returns (o [B, T, H, dv], final_state or None, conv_state_out or None)."""
+    B, T = q.shape[0], q.shape[1]
+    H, dv = cfg.num_heads, cfg.head_v_dim
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=cfg.out_dtype, device=q.device)
+    nbytes = kda_prefill_workspace_bytes(cfg, B, T)
+    ws = _workspace(nbytes, q.device, workspace)
+    st = _lib.kda_prefill(ctypes.byref(cfg.c_struct()), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                          _ptr(initial_state), _ptr(conv_state_in), _ptr(o), _ptr(final_state),
+                          _ptr(conv_state_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kda_prefill")
+    return o, final_state, conv_state_out
+
+
+def kda_varlen_prefill(cfg: Config, cu_seqlens, q, k, v, alpha, b, initial_state=None, conv_state_in=None, *,
+                       o=None, final_state=None, conv_state_out=None, workspace=None, stream=None):
+    """cu_seqlens int32 [N+1] on the device; q, k [total_T, H*dk]; v [total_T, H*dv];
+    alpha [total_T, H, dk]; b [total_T, H].  Returns (o, final_state, conv_state_out)."""
+    N = cu_seqlens.numel() - 1
+    total = q.shape[0]
+    H, dv = cfg.num_heads, cfg.head_v_dim
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if o is None:
+        o = torch.empty((total, H, dv), dtype=cfg.out_dtype, device=q.device)
+    nbytes = kda_varlen_workspace_bytes(cfg, N, total)
+    ws = _workspace(nbytes, q.device, workspace)
+    st = _lib.kda_varlen_prefill(ctypes.byref(cfg.c_struct()), N, total, _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(alpha), _ptr(b), _ptr(initial_state), _ptr(conv_state_in),
+                                 _ptr(o), _ptr(final_state), _ptr(conv_state_out), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kda_varlen_prefill")
+    return o, final_state, conv_state_out
+
+
+def kda_decode_step(cfg: Config, q, k, v, alpha, b, state, conv_state, *, o=None, stream=None):
+    """One token for each of N sequences: q, k [N, H*dk]; v [N, H*dv];
+    alpha [N, H, dk]; b [N, H]; state [N, H, dk, dv] fp32 and conv_state
+    [N, 3, Ctot] are updated in place.  Returns o [N, H, dv]."""
+    N = q.shape[0]
+    if o is None:
+        o = torch.empty((N, cfg.num_heads, cfg.head_v_dim), dtype=cfg.out_dtype, device=q.device)
+    st = _lib.kda_decode_step(ctypes.byref(cfg.c_struct()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                              _ptr(state), _ptr(conv_state), _ptr(o), _stream(stream))
+    _check(st, "kda_decode_step")
+    return o

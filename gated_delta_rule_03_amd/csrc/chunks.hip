@@ -1,0 +1,108 @@
+// Packed-batch bookkeeping for the chunked prefill.
+//
+// build_chunks_kernel turns sequence offsets (device cu_seqlens, or B equal
+// lengths) into a chunk table without any host synchronisation: chunk0[s] is
+// the first 64-token chunk of sequence s (an exclusive scan of ceil(len/64)),
+// chunk0[N] the number of chunks, and chunk_seq[c] the sequence owning chunk c.
+// Chunks never straddle two sequences; the last chunk of a sequence may be
+// partial.  Grids of the chunk kernels are sized by a host upper bound and
+// blocks past chunk0[N] exit.
+//
+// conv_state_out_kernel writes each sequence's conv history for continuation:
+// its last three raw inputs per channel (reaching into the incoming history
+// when the sequence is shorter than three tokens), oldest first.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+__global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __restrict__ cu_in, int32_t N,
+                                                            int32_t T_uniform, int32_t* __restrict__ cu_ws,
+                                                            int32_t* __restrict__ chunk0) {
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x;
+  for (int s = tid; s <= N; s += 1024) cu_ws[s] = cu_in ? cu_in[s] : s * T_uniform;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int s = base + tid;
+    int nc = 0;
+    if (s < N) {
+      const int len = cu_in ? (cu_in[s + 1] - cu_in[s]) : T_uniform;
+      nc = (len + kChunk - 1) / kChunk;
+    }
+    scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int carry = carry_s;
+    if (s < N) chunk0[s] = carry + scan[tid] - nc;
+    __syncthreads();
+    if (tid == 0) carry_s = carry + scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) chunk0[N] = carry_s;
+}
+
+// chunk_seq[c] = the last sequence whose first chunk is <= c (empty sequences
+// share their successor's first chunk and are skipped this way).  A separate
+// launch, so that every chunk0 entry written above is visible.
+__global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __restrict__ chunk0, int32_t N,
+                                                             int32_t* __restrict__ chunk_seq, int32_t max_chunks) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= max_chunks || c >= chunk0[N]) return;
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk0[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  chunk_seq[c] = lo;
+}
+
+hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws, int32_t* chunk0,
+                               int32_t* chunk_seq, int32_t max_chunks, hipStream_t st) {
+  build_chunks_kernel<<<1, 1024, 0, st>>>(cu_in, N, T_uniform, cu_ws, chunk0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || max_chunks <= 0) return e;
+  fill_chunk_seq_kernel<<<(max_chunks + 255) / 256, 256, 0, st>>>(chunk0, N, chunk_seq, max_chunks);
+  return hipGetLastError();
+}
+
+template <bool IO_BF16>
+__global__ __launch_bounds__(256) void conv_state_out_kernel(ChunkTable t, PrefillIO io, int H, int D) {
+  const int s = blockIdx.y;
+  const size_t Ctot = static_cast<size_t>(3) * H * D;
+  const size_t c = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= Ctot) return;
+  const int64_t t0 = t.cu[s];
+  const int L = t.cu[s + 1] - t.cu[s];
+  const int grp = static_cast<int>(c / (static_cast<size_t>(H) * D));
+  const size_t cc = c - static_cast<size_t>(grp) * H * D;
+  const void* x = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
+  float val[3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const int tt = L - 3 + m;
+    if (tt >= 0) val[m] = ld<IO_BF16>(x, static_cast<size_t>(t0 + tt) * H * D + cc);
+    else if (io.conv_in) val[m] = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(s) * 3 + (3 + tt)) * Ctot + c);
+    else val[m] = 0.0f;
+  }
+#pragma unroll
+  for (int m = 0; m < 3; ++m) st<IO_BF16>(io.conv_out, (static_cast<size_t>(s) * 3 + m) * Ctot + c, val[m]);
+}
+
+hipError_t launch_conv_state_out(const Params& p, const ChunkTable& t, const PrefillIO& io, bool io_bf16,
+                                 hipStream_t st) {
+  const size_t Ctot = static_cast<size_t>(3) * p.H * p.D;
+  const dim3 grid(static_cast<unsigned>((Ctot + 255) / 256), static_cast<unsigned>(t.N));
+  if (io_bf16) conv_state_out_kernel<true><<<grid, 256, 0, st>>>(t, io, p.H, p.D);
+  else conv_state_out_kernel<false><<<grid, 256, 0, st>>>(t, io, p.H, p.D);
+  return hipGetLastError();
+}
+
+}  // namespace kda

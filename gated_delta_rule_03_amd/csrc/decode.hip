@@ -1,0 +1,174 @@
+// Single-token KDA decode step (the fused recurrent form): one workgroup per
+// (sequence, head).  The step is HBM-bound: the fp32 dk x dv state is streamed
+// in once and out once, in place.
+//
+// Per (sequence n, head h), following the delta-rule loop of the AliceAI page
+// (section 二) with the conv history of section 四/五:
+//   conv over [3 history inputs, new input] -> SiLU -> L2 norm (q, k)
+//   g = max(-exp(A_log) softplus(alpha + dt_bias), lb),  beta = sigmoid(b)
+//   S~ = Diag(e^g) S;  p = k^T S~;  r = q^T S~;  delta = beta (v - p)
+//   o = r + (q.k) delta          (= q^T (S~ + k delta^T), the updated state)
+//   S <- S~ + k delta^T;  history <- [h1, h2, x]
+// A wave covers two full state rows per load (512 B contiguous each), every
+// lane moves 16 B per access, and the k^T S~ / q^T S~ column sums are reduced
+// across row groups through LDS.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int D, bool IO_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_kernel(Params p, DecodeIO io) {
+  constexpr int NT = 256;
+  constexpr int C4 = D / 4;                  // float4 columns per state row
+  constexpr int RPP = NT / C4;               // state rows covered by one pass of the block
+  constexpr int RPT = (D + RPP - 1) / RPP;   // passes (rows per thread)
+  __shared__ float u_s[3 * D];               // q | k | v after conv + SiLU
+  __shared__ float e_s[D];                   // exp(g)
+  __shared__ float red[2][RPP][D];           // per-row-group partial k^T S~, q^T S~
+  __shared__ float d_s[D];                   // delta
+  __shared__ float scal[4];                  // q scale * inv|q|, inv|k|, beta, q.k
+
+  const int tid = threadIdx.x;
+  const int H = p.H;
+  const int n = blockIdx.x / H, h = blockIdx.x % H;
+  const size_t Ctot = static_cast<size_t>(3) * H * D;
+  const uint32_t flags = p.flags;
+
+  // ---- preprocess: conv + SiLU for the 3D channels of this head; shift history
+  for (int c = tid; c < 3 * D; c += NT) {
+    const int grp = c / D, i = c % D;
+    const size_t ch = static_cast<size_t>(grp) * H * D + static_cast<size_t>(h) * D + i;
+    const void* x = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
+    const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
+    const float xt = ld<IO_BF16>(x, static_cast<size_t>(n) * H * D + static_cast<size_t>(h) * D + i);
+    const size_t cb = static_cast<size_t>(n) * 3 * Ctot + ch;
+    const float h0 = ld<IO_BF16>(io.conv_state, cb);
+    const float h1 = ld<IO_BF16>(io.conv_state, cb + Ctot);
+    const float h2 = ld<IO_BF16>(io.conv_state, cb + 2 * Ctot);
+    float u;
+    if (flags & KDA_FLAG_SKIP_CONV) {
+      u = xt;
+    } else {
+      const size_t wi = (static_cast<size_t>(h) * D + i) * 4;
+      const float y = ld<IO_BF16>(w, wi) * h0 + ld<IO_BF16>(w, wi + 1) * h1 + ld<IO_BF16>(w, wi + 2) * h2 +
+                      ld<IO_BF16>(w, wi + 3) * xt;
+      u = siluf_(y);
+    }
+    st<IO_BF16>(io.conv_state, cb, h1);
+    st<IO_BF16>(io.conv_state, cb + Ctot, h2);
+    st<IO_BF16>(io.conv_state, cb + 2 * Ctot, xt);
+    u_s[c] = u;
+  }
+  const float a_exp = expf(p.A_log[h]);
+  for (int i = tid; i < D; i += NT) {
+    const float al = ld<IO_BF16>(io.alpha, (static_cast<size_t>(n) * H + h) * D + i);
+    const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, p.dt_bias[h * D + i], a_exp, p.lower_bound);
+    e_s[i] = expf(g);
+  }
+  if (tid == 0) {
+    const float bb = ld<IO_BF16>(io.b, static_cast<size_t>(n) * H + h);
+    float be = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
+    if (flags & KDA_FLAG_BETA_X2) be *= 2.0f;
+    scal[2] = be;
+  }
+  __syncthreads();
+
+  // ---- norms and q.k (waves 0, 1, 2)
+  {
+    const int wv = tid / kWave, lane = tid % kWave;
+    if (wv < 3) {
+      float s = 0.0f;
+      for (int i = lane; i < D; i += kWave) {
+        const float a = u_s[(wv == 1 ? D : 0) + i];
+        const float b2 = u_s[(wv == 0 ? 0 : D) + i];
+        s += a * b2;
+      }
+      s = group_sum<kWave>(s);
+      if (lane == 0) scal[wv == 2 ? 3 : wv] = s;   // wave 2 stores raw u_q . u_k in slot 3
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
+    const float iq = norm ? 1.0f / sqrtf(scal[0] + p.eps) : 1.0f;
+    const float ik = norm ? 1.0f / sqrtf(scal[1] + p.eps) : 1.0f;
+    scal[3] = scal[3] * iq * ik * p.scale;
+    scal[0] = iq * p.scale;
+    scal[1] = ik;
+  }
+  __syncthreads();
+  const float qs = scal[0], ks = scal[1], beta = scal[2], qk = scal[3];
+
+  // ---- one pass over the state
+  const int col4 = tid % C4, rg = tid / C4;
+  const size_t base = (static_cast<size_t>(n) * H + h) * D * D;
+  float4* Sp = reinterpret_cast<float4*>(io.state + base);
+  float4 Sv[RPT];
+  float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = rg + rr * RPP;
+    if (r < D) Sv[rr] = Sp[static_cast<size_t>(r) * C4 + col4];
+  }
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = rg + rr * RPP;
+    if (r < D) {
+      const float e = e_s[r];
+      Sv[rr].x *= e; Sv[rr].y *= e; Sv[rr].z *= e; Sv[rr].w *= e;
+      const float kr = u_s[D + r] * ks, qr = u_s[r] * qs;
+      pk[0] += kr * Sv[rr].x; pk[1] += kr * Sv[rr].y; pk[2] += kr * Sv[rr].z; pk[3] += kr * Sv[rr].w;
+      pq[0] += qr * Sv[rr].x; pq[1] += qr * Sv[rr].y; pq[2] += qr * Sv[rr].z; pq[3] += qr * Sv[rr].w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    red[0][rg][col4 * 4 + j] = pk[j];
+    red[1][rg][col4 * 4 + j] = pq[j];
+  }
+  __syncthreads();
+  for (int j = tid; j < D; j += NT) {
+    float pp = 0.f, rq = 0.f;
+#pragma unroll 8
+    for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][j]; rq += red[1][g2][j]; }
+    const float delta = beta * (u_s[2 * D + j] - pp);
+    d_s[j] = delta;
+    st<OUT_BF16>(io.o, (static_cast<size_t>(n) * H + h) * D + j, rq + qk * delta);
+  }
+  __syncthreads();
+  const float d0 = d_s[col4 * 4], d1 = d_s[col4 * 4 + 1], d2 = d_s[col4 * 4 + 2], d3 = d_s[col4 * 4 + 3];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = rg + rr * RPP;
+    if (r < D) {
+      const float kr = u_s[D + r] * ks;
+      float4 s = Sv[rr];
+      s.x += kr * d0; s.y += kr * d1; s.z += kr * d2; s.w += kr * d3;
+      Sp[static_cast<size_t>(r) * C4 + col4] = s;
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_decode_d(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16,
+                                  hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(N) * p.H), block(256);
+  if (io_bf16 && out_bf16) decode_kernel<D, true, true><<<grid, block, 0, st>>>(p, io);
+  else if (io_bf16) decode_kernel<D, true, false><<<grid, block, 0, st>>>(p, io);
+  else if (out_bf16) decode_kernel<D, false, true><<<grid, block, 0, st>>>(p, io);
+  else decode_kernel<D, false, false><<<grid, block, 0, st>>>(p, io);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16, hipStream_t st) {
+  switch (p.D) {
+    case 16: return launch_decode_d<16>(p, io, N, io_bf16, out_bf16, st);
+    case 32: return launch_decode_d<32>(p, io, N, io_bf16, out_bf16, st);
+    case 64: return launch_decode_d<64>(p, io, N, io_bf16, out_bf16, st);
+    case 128: return launch_decode_d<128>(p, io, N, io_bf16, out_bf16, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

@@ -1,0 +1,224 @@
+// Host side of the KDA C ABI: validation, workspace layout and launch
+// sequencing on the caller's stream.  No allocation, no synchronisation, no
+// host reads of device memory.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "kda_internal.h"
+
+namespace {
+
+using kda::ChunkBuffers;
+using kda::ChunkTable;
+using kda::Params;
+using kda::PrefillIO;
+
+constexpr size_t kAlign = 256;
+constexpr uint32_t kKnownFlags = KDA_FLAG_SKIP_CONV | KDA_FLAG_SKIP_L2NORM | KDA_FLAG_RAW_GATE |
+                                 KDA_FLAG_RAW_BETA | KDA_FLAG_BETA_X2;
+// Sub-block decay factors e^{-P} of 16 tokens stay finite in fp32 when every
+// log decay is >= -5.4 (16 * 5.4 = 86.4 < ln FLT_MAX).
+constexpr float kChunkedGateFloor = -5.4f;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+kda_status_t check_config(const kda_config_t* cfg, bool chunked) {
+  if (!cfg) return KDA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_heads < 1 || cfg->head_k_dim < 1 || cfg->head_v_dim < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_heads > 65535) return KDA_ERR_UNSUPPORTED;
+  if (cfg->head_k_dim != cfg->head_v_dim) return KDA_ERR_UNSUPPORTED;
+  const int d = cfg->head_k_dim;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+  if ((cfg->io_dtype != KDA_BF16 && cfg->io_dtype != KDA_FP32) ||
+      (cfg->out_dtype != KDA_BF16 && cfg->out_dtype != KDA_FP32))
+    return KDA_ERR_UNSUPPORTED;
+  if (cfg->flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+  if (chunked && cfg->chunk_size != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if (std::isnan(cfg->gate_lower_bound) || std::isnan(cfg->l2norm_eps) || std::isnan(cfg->scale))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (chunked && !(cfg->flags & KDA_FLAG_RAW_GATE) && !(cfg->gate_lower_bound >= kChunkedGateFloor))
+    return KDA_ERR_UNSUPPORTED;
+  if (!cfg->A_log || !cfg->dt_bias) return KDA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->flags & KDA_FLAG_SKIP_CONV) && (!cfg->conv_w_q || !cfg->conv_w_k || !cfg->conv_w_v))
+    return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
+
+Params make_params(const kda_config_t* cfg) {
+  Params p;
+  p.H = cfg->num_heads;
+  p.D = cfg->head_k_dim;
+  p.scale = cfg->scale;
+  p.lower_bound = cfg->gate_lower_bound;
+  p.eps = cfg->l2norm_eps;
+  p.flags = cfg->flags;
+  p.A_log = cfg->A_log;
+  p.dt_bias = cfg->dt_bias;
+  p.wq = cfg->conv_w_q;
+  p.wk = cfg->conv_w_k;
+  p.wv = cfg->conv_w_v;
+  return p;
+}
+
+struct Layout {
+  size_t cu, chunk0, chunk_seq, qh, kh, vh, g, beta, W, U, Qp, Kt, eGC, Aqk, Sst, total;
+};
+
+Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t ch = static_cast<size_t>(max_chunks) * H;     // chunk-heads
+  const size_t tileb = ch * kda::kChunk * D * sizeof(float);
+  L.cu = take((N + 1) * sizeof(int32_t));
+  L.chunk0 = take((N + 1) * sizeof(int32_t));
+  L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
+  L.qh = take(tileb);
+  L.kh = take(tileb);
+  L.vh = take(tileb);
+  L.g = take(tileb);
+  L.beta = take(ch * kda::kChunk * sizeof(float));
+  L.W = take(tileb);
+  L.U = take(tileb);
+  L.Qp = take(tileb);
+  L.Kt = take(tileb);
+  L.eGC = take(ch * D * sizeof(float));
+  L.Aqk = take(ch * kda::kChunk * kda::kChunk * sizeof(float));
+  L.Sst = take(ch * D * D * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+int64_t chunks_uniform(int64_t B, int64_t T) { return B * ((T + kda::kChunk - 1) / kda::kChunk); }
+int64_t chunks_varlen(int64_t N, int64_t total_T) { return (total_T + kda::kChunk - 1) / kda::kChunk + N; }
+
+kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// The shared prefill pipeline over a packed batch.
+kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, int64_t max_chunks,
+                         const int32_t* cu_in, int32_t T_uniform, const PrefillIO& io, void* workspace,
+                         hipStream_t st) {
+  const Params p = make_params(cfg);
+  const Layout L = make_layout(N, max_chunks, p.H, p.D);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* cu_ws = reinterpret_cast<int32_t*>(ws + L.cu);
+  int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
+  int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
+  ChunkTable t{cu_ws, chunk0, chunk_seq, N};
+  ChunkBuffers b;
+  b.qh = reinterpret_cast<float*>(ws + L.qh);
+  b.kh = reinterpret_cast<float*>(ws + L.kh);
+  b.vh = reinterpret_cast<float*>(ws + L.vh);
+  b.g = reinterpret_cast<float*>(ws + L.g);
+  b.beta = reinterpret_cast<float*>(ws + L.beta);
+  b.W = reinterpret_cast<float*>(ws + L.W);
+  b.U = reinterpret_cast<float*>(ws + L.U);
+  b.Qp = reinterpret_cast<float*>(ws + L.Qp);
+  b.Kt = reinterpret_cast<float*>(ws + L.Kt);
+  b.eGC = reinterpret_cast<float*>(ws + L.eGC);
+  b.Aqk = reinterpret_cast<float*>(ws + L.Aqk);
+  b.Sst = reinterpret_cast<float*>(ws + L.Sst);
+  const bool io_bf16 = cfg->io_dtype == KDA_BF16;
+  const bool out_bf16 = cfg->out_dtype == KDA_BF16;
+  const int mc = static_cast<int>(max_chunks);
+
+  kda_status_t s = hip_status(kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, mc, st));
+  if (s != KDA_OK) return s;
+  if (total_T > 0 && mc > 0) {
+    if ((s = hip_status(kda::launch_preprocess(p, t, io, b, mc, io_bf16, st))) != KDA_OK) return s;
+    if ((s = hip_status(kda::launch_chunk_intra(p, t, b, mc, st))) != KDA_OK) return s;
+  }
+  if ((s = hip_status(kda::launch_chunk_state(p, t, io, b, st))) != KDA_OK) return s;
+  if (total_T > 0 && mc > 0) {
+    if ((s = hip_status(kda::launch_chunk_output(p, t, io, b, mc, out_bf16, st))) != KDA_OK) return s;
+  }
+  if (io.conv_out) {
+    if ((s = hip_status(kda::launch_conv_state_out(p, t, io, io_bf16, st))) != KDA_OK) return s;
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_version(void) { return 100; }
+
+const char* kda_status_string(kda_status_t status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    default: return "KDA_ERR_UNKNOWN";
+  }
+}
+
+size_t kda_prefill_workspace_bytes(const kda_config_t* cfg, int32_t B, int32_t T) {
+  if (check_config(cfg, true) != KDA_OK || B < 0 || T < 0) return 0;
+  const int64_t mc = chunks_uniform(B, T);
+  if (static_cast<int64_t>(B) * T > INT32_MAX || mc > INT32_MAX) return 0;
+  return make_layout(B, mc, cfg->num_heads, cfg->head_k_dim).total;
+}
+
+size_t kda_varlen_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t total_T) {
+  if (check_config(cfg, true) != KDA_OK || N < 0 || total_T < 0) return 0;
+  return make_layout(N, chunks_varlen(N, total_T), cfg->num_heads, cfg->head_k_dim).total;
+}
+
+kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const void* q, const void* k, const void* v,
+                         const void* alpha, const void* b, const float* initial_state, const void* conv_state_in,
+                         void* o, float* final_state, void* conv_state_out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  kda_status_t s = check_config(cfg, true);
+  if (s != KDA_OK) return s;
+  if (B < 0 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(B) * T > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (T > 0 && (!q || !k || !v || !alpha || !b || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t mc = chunks_uniform(B, T);
+  const size_t need = make_layout(B, mc, cfg->num_heads, cfg->head_k_dim).total;
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};
+  return run_prefill(cfg, B, static_cast<int64_t>(B) * T, mc, nullptr, T, io, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+kda_status_t kda_varlen_prefill(const kda_config_t* cfg, int32_t N, int32_t total_T, const int32_t* cu_seqlens,
+                                const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                                const float* initial_state, const void* conv_state_in, void* o, float* final_state,
+                                void* conv_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status_t s = check_config(cfg, true);
+  if (s != KDA_OK) return s;
+  if (N < 0 || total_T < 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (N == 0) return KDA_OK;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+  if (total_T > 0 && (!q || !k || !v || !alpha || !b || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t mc = chunks_varlen(N, total_T);
+  if (mc > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const size_t need = make_layout(N, mc, cfg->num_heads, cfg->head_k_dim).total;
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};
+  return run_prefill(cfg, N, total_T, mc, cu_seqlens, 0, io, workspace, static_cast<hipStream_t>(stream));
+}
+
+kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, const void* k, const void* v,
+                             const void* alpha, const void* b, float* state, void* conv_state, void* o,
+                             void* stream) {
+  kda_status_t s = check_config(cfg, false);
+  if (s != KDA_OK) return s;
+  if (N < 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(N) * cfg->num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !alpha || !b || !state || !conv_state || !o) return KDA_ERR_INVALID_ARGUMENT;
+  const Params p = make_params(cfg);
+  kda::DecodeIO io{q, k, v, alpha, b, state, conv_state, o};
+  return hip_status(kda::launch_decode(p, io, N, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

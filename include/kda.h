@@ -1,0 +1,171 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) core.
+ *
+ * What the library computes.  For every sequence and head, with raw per-token
+ * projections q, k (dk channels per head), v (dv channels per head), a
+ * per-channel decay input alpha and a per-head write-strength input b:
+ *
+ *   1. each q, k, v channel passes a depthwise causal conv1d of kernel 4,
+ *      padding 3, no bias, then SiLU;  q and k are L2-normalised per head
+ *      (AliceAI-Foundation-80B-A3B page, section 二);
+ *   2. g = max(-exp(A_log[h]) * softplus(alpha + dt_bias[h]), lower_bound)
+ *      (same page, section 二, gate formula; the -5.0 lower bound is the safe
+ *      gate of the Ling-3.0-flash-VL page, section "KDA 层的安全门");
+ *      beta = sigmoid(b) (AliceAI page, section 二: beta is not doubled);
+ *   3. per token, with the dk x dv state S (rows = key channels):
+ *        S <- Diag(exp(g)) S;  delta = beta (v - k^T S);  S <- S + k delta^T;
+ *        o = q^T S   (the read uses the updated state)
+ *      (AliceAI page, section 二, the delta-rule loop; state shape
+ *      (batch, v_heads, k_dim, v_dim)).
+ *
+ * Prefill and decode share the state interface: a prefill's final state and
+ * conv history are a decode step's input (AliceAI page, section 五).  The
+ * conv history of a sequence is its last 3 raw (pre-conv) inputs per channel
+ * (AliceAI page, section 四: kernel-1 = 3 history elements), stored oldest
+ * first with channels ordered q | k | v:  Ctot = H * (2*dk + dv).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, contiguous, row-major in the
+ *    layout given, 16-byte aligned.  The caller owns every buffer; the library
+ *    allocates no device memory and keeps no mutable global state, so calls on
+ *    different streams are independent.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is asynchronous: the library never synchronises and never reads
+ *    device data on the host.
+ *  - Host-side validation runs before any launch.  On failure the call
+ *    returns a nonzero kda_status_t, launches nothing and leaves every output
+ *    untouched.  A launch failure returns KDA_ERR_HIP.  Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - NaN/Inf inputs propagate; they are not trapped.
+ *  - T == 0 or N == 0 is a valid no-op returning KDA_OK.
+ *  - Supported geometry: dk == dv, dk in {16, 32, 64, 128}; chunk_size 64.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,    /* null required pointer, negative size, bad cu_seqlens length */
+    KDA_ERR_UNSUPPORTED = 2,         /* geometry / dtype / flag combination not built */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the size query's answer */
+    KDA_ERR_HIP = 4                  /* a HIP launch reported an error */
+} kda_status_t;
+
+typedef enum kda_dtype {
+    KDA_BF16 = 0,
+    KDA_FP32 = 1
+} kda_dtype_t;
+
+/* Test hooks; 0 for the method as described. */
+#define KDA_FLAG_SKIP_CONV   (1u << 0) /* q, k, v are already conv + SiLU outputs           */
+#define KDA_FLAG_SKIP_L2NORM (1u << 1) /* q, k are used without L2 normalisation           */
+#define KDA_FLAG_RAW_GATE    (1u << 2) /* alpha holds g itself (no softplus, no clamp)      */
+#define KDA_FLAG_RAW_BETA    (1u << 3) /* b holds beta itself (no sigmoid)                  */
+#define KDA_FLAG_BETA_X2     (1u << 4) /* beta = 2 sigmoid(b): negative eigenvalues allowed */
+
+typedef struct kda_config {
+    int32_t num_heads;        /* H                                                      */
+    int32_t head_k_dim;       /* dk                                                     */
+    int32_t head_v_dim;       /* dv (must equal dk)                                     */
+    int32_t io_dtype;         /* kda_dtype_t of q, k, v, alpha, b, conv weights, conv history */
+    int32_t out_dtype;        /* kda_dtype_t of o                                       */
+    float scale;              /* multiplies the normalised q; 1.0 as on the pages       */
+    float gate_lower_bound;   /* -5.0 (safe gate); -INFINITY disables the clamp         */
+    float l2norm_eps;         /* q / sqrt(|q|^2 + eps); 1e-6                            */
+    int32_t chunk_size;       /* 64                                                     */
+    uint32_t flags;           /* KDA_FLAG_* test hooks, normally 0                      */
+    const float *A_log;       /* [H] fp32, device                                       */
+    const float *dt_bias;     /* [H*dk] fp32, device                                    */
+    const void *conv_w_q;     /* [H*dk][4] io_dtype, device; tap 3 multiplies the current token */
+    const void *conv_w_k;     /* [H*dk][4]                                              */
+    const void *conv_w_v;     /* [H*dv][4]                                              */
+} kda_config_t;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t kda_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Workspace size in bytes for kda_prefill over B sequences of T tokens.
+ * Returns 0 for an invalid or unsupported configuration.
+ */
+size_t kda_prefill_workspace_bytes(const kda_config_t *cfg, int32_t B, int32_t T);
+
+/*
+ * Chunked prefill of B equal-length sequences of T tokens.
+ *   q, k           [B][T][H*dk]  io_dtype, raw projections (pre-conv)
+ *   v              [B][T][H*dv]  io_dtype
+ *   alpha          [B][T][H][dk] io_dtype, decay input
+ *   b              [B][T][H]     io_dtype, pre-sigmoid write strength
+ *   initial_state  [B][H][dk][dv] fp32, or NULL for zeros
+ *   conv_state_in  [B][3][Ctot] io_dtype, oldest first, or NULL for zeros
+ *   o              [B][T][H][dv] out_dtype (required)
+ *   final_state    [B][H][dk][dv] fp32, or NULL; may alias initial_state
+ *   conv_state_out [B][3][Ctot] io_dtype, or NULL; may alias conv_state_in
+ *   workspace      device scratch of at least kda_prefill_workspace_bytes()
+ * No other aliasing is allowed.
+ */
+kda_status_t kda_prefill(const kda_config_t *cfg, int32_t B, int32_t T,
+                         const void *q, const void *k, const void *v,
+                         const void *alpha, const void *b,
+                         const float *initial_state, const void *conv_state_in,
+                         void *o, float *final_state, void *conv_state_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace size in bytes for kda_varlen_prefill over N packed sequences
+ * holding total_T tokens.  Returns 0 for an invalid configuration.
+ */
+size_t kda_varlen_workspace_bytes(const kda_config_t *cfg, int32_t N, int32_t total_T);
+
+/*
+ * Chunked prefill of N sequences packed back to back (varlen).
+ *   cu_seqlens     [N+1] int32, DEVICE; cu[0] = 0, cu[N] = total_T,
+ *                  nondecreasing (zero-length sequences allowed).  The
+ *                  library does not read it on the host; a malformed array
+ *                  is undefined behaviour.
+ *   q, k           [total_T][H*dk];  v [total_T][H*dv]
+ *   alpha          [total_T][H][dk]; b [total_T][H]
+ *   initial_state  [N][H][dk][dv] fp32 or NULL;  conv_state_in [N][3][Ctot] or NULL
+ *   o              [total_T][H][dv]
+ *   final_state    [N][H][dk][dv] or NULL;  conv_state_out [N][3][Ctot] or NULL
+ * State and conv history restart at each sequence; chunks never straddle two
+ * sequences.  Aliasing rules as for kda_prefill.
+ */
+kda_status_t kda_varlen_prefill(const kda_config_t *cfg, int32_t N, int32_t total_T,
+                                const int32_t *cu_seqlens,
+                                const void *q, const void *k, const void *v,
+                                const void *alpha, const void *b,
+                                const float *initial_state, const void *conv_state_in,
+                                void *o, float *final_state, void *conv_state_out,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: one new token for each of N independent sequences
+ * (the fused recurrent form; AliceAI page, section 五).
+ *   q, k           [N][H*dk] io_dtype;  v [N][H*dv]
+ *   alpha          [N][H][dk];          b [N][H]
+ *   state          [N][H][dk][dv] fp32, read and updated in place (required)
+ *   conv_state     [N][3][Ctot] io_dtype, read and shifted in place (required)
+ *   o              [N][H][dv] out_dtype
+ * Needs no workspace.
+ */
+kda_status_t kda_decode_step(const kda_config_t *cfg, int32_t N,
+                             const void *q, const void *k, const void *v,
+                             const void *alpha, const void *b,
+                             float *state, void *conv_state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

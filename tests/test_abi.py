@@ -1,0 +1,171 @@
+"""The C ABI: header, exported symbols and host-side validation (CPU only).
+
+Every call here fails validation (or is a no-op) before any launch, so no GPU
+is needed; outputs passed in are host canaries that must stay untouched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def kda():
+    lib_path = os.path.join(ROOT, "gated_delta_rule_03_amd", "libkda.so")
+    if not os.path.exists(lib_path):
+        pytest.fail("libkda.so is not built (run __graft_entry__.build())")
+    import gated_delta_rule_03_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        subprocess.check_call(["gcc", "-fsyntax-only", "-Wall", "-Werror", std, "-x", lang, HEADER])
+
+
+def test_every_declared_symbol_is_exported(kda):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTED)
+    for n in names:
+        assert hasattr(kda.library(), n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), f"{n} not exported as a text symbol"
+
+
+def test_version_and_status_strings(kda):
+    assert kda.version() == 100
+    for code, name in ((0, "KDA_OK"), (1, "KDA_ERR_INVALID_ARGUMENT"), (2, "KDA_ERR_UNSUPPORTED"),
+                       (3, "KDA_ERR_WORKSPACE_TOO_SMALL"), (4, "KDA_ERR_HIP")):
+        assert kda.status_string(code) == name
+
+
+def test_struct_layout_matches_header(kda):
+    # kda_config_t: 10 four-byte fields, then 5 pointers
+    assert ctypes.sizeof(kda.KdaConfigC) == 10 * 4 + 5 * 8
+    assert kda.KdaConfigC.A_log.offset == 40
+
+
+class Canary:
+    def __init__(self, n=64):
+        self.a = np.full(n, 12345.0, dtype=np.float32)
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.a.ctypes.data)
+
+    def untouched(self):
+        return bool(np.all(self.a == 12345.0))
+
+
+def make_cfg(kda, H=2, dk=16, dv=16, **kw):
+    keep = [Canary() for _ in range(5)]
+    c = kda.KdaConfigC()
+    c.num_heads, c.head_k_dim, c.head_v_dim = H, dk, dv
+    c.io_dtype, c.out_dtype = kda.KDA_BF16, kda.KDA_FP32
+    c.scale, c.gate_lower_bound, c.l2norm_eps, c.chunk_size, c.flags = 1.0, -5.0, 1e-6, 64, 0
+    c.A_log, c.dt_bias, c.conv_w_q, c.conv_w_k, c.conv_w_v = (k.a.ctypes.data for k in keep)
+    for name, val in kw.items():
+        setattr(c, name, val)
+    return c, keep
+
+
+def call_prefill(kda, cfg, B=1, T=8, null=(), ws_bytes=None):
+    bufs = {n: Canary(1 << 12) for n in ("q", "k", "v", "alpha", "b", "S0", "cin", "o", "Sout", "cout", "ws")}
+    ptr = {n: (None if n in null else b.ptr) for n, b in bufs.items()}
+    need = kda.library().kda_prefill_workspace_bytes(ctypes.byref(cfg), B, T)
+    st = kda.library().kda_prefill(ctypes.byref(cfg), B, T, ptr["q"], ptr["k"], ptr["v"], ptr["alpha"], ptr["b"],
+                                   ptr["S0"], ptr["cin"], ptr["o"], ptr["Sout"], ptr["cout"], ptr["ws"],
+                                   need if ws_bytes is None else ws_bytes, None)
+    return st, bufs
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "alpha", "b", "o", "ws"])
+def test_null_required_pointer(kda, missing):
+    cfg, _ = make_cfg(kda)
+    st, bufs = call_prefill(kda, cfg, null=(missing,))
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
+    assert all(b.untouched() for b in bufs.values())
+
+
+@pytest.mark.parametrize("field,val", [("head_k_dim", 48), ("head_v_dim", 32), ("io_dtype", 7),
+                                       ("out_dtype", 3), ("chunk_size", 32), ("flags", 1 << 9),
+                                       ("gate_lower_bound", float("-inf")), ("num_heads", 70000)])
+def test_unsupported_configuration(kda, field, val):
+    cfg, _ = make_cfg(kda, **{field: val})
+    st, bufs = call_prefill(kda, cfg)
+    assert st == kda.KDA_ERR_UNSUPPORTED
+    assert all(b.untouched() for b in bufs.values())
+    assert kda.library().kda_prefill_workspace_bytes(ctypes.byref(cfg), 1, 8) == 0
+
+
+def test_invalid_sizes_and_parameters(kda):
+    cfg, _ = make_cfg(kda)
+    assert call_prefill(kda, cfg, B=-1)[0] == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_prefill(kda, cfg, T=-5)[0] == kda.KDA_ERR_INVALID_ARGUMENT
+    cfg2, _ = make_cfg(kda, A_log=None)
+    assert call_prefill(kda, cfg2)[0] == kda.KDA_ERR_INVALID_ARGUMENT
+    cfg3, _ = make_cfg(kda, conv_w_v=None)
+    assert call_prefill(kda, cfg3)[0] == kda.KDA_ERR_INVALID_ARGUMENT
+    cfg4, _ = make_cfg(kda, conv_w_v=None, flags=kda.FLAG_SKIP_CONV)
+    assert call_prefill(kda, cfg4, null=("ws",))[0] == kda.KDA_ERR_INVALID_ARGUMENT   # only ws missing now
+    cfg5, _ = make_cfg(kda, gate_lower_bound=float("nan"))
+    assert call_prefill(kda, cfg5)[0] == kda.KDA_ERR_INVALID_ARGUMENT
+    assert kda.library().kda_prefill(None, 1, 8, *([None] * 11), 0, None) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_too_small(kda):
+    cfg, _ = make_cfg(kda)
+    st, bufs = call_prefill(kda, cfg, ws_bytes=100)
+    assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert all(b.untouched() for b in bufs.values())
+
+
+def test_workspace_query_grows_with_size(kda):
+    cfg, _ = make_cfg(kda, H=32, dk=128, dv=128)
+    lib = kda.library()
+    a = lib.kda_prefill_workspace_bytes(ctypes.byref(cfg), 1, 64)
+    b = lib.kda_prefill_workspace_bytes(ctypes.byref(cfg), 1, 128)
+    c = lib.kda_varlen_workspace_bytes(ctypes.byref(cfg), 2, 128)
+    assert 0 < a < b <= c
+    assert a % 256 == 0
+
+
+def test_empty_batches_are_noops(kda):
+    cfg, _ = make_cfg(kda)
+    lib = kda.library()
+    st, bufs = call_prefill(kda, cfg, B=0, null=("q", "k", "v", "alpha", "b", "o", "ws"))
+    assert st == kda.KDA_OK and all(b.untouched() for b in bufs.values())
+    assert lib.kda_varlen_prefill(ctypes.byref(cfg), 0, 0, None, *([None] * 10), None, 0, None) == kda.KDA_OK
+    assert lib.kda_decode_step(ctypes.byref(cfg), 0, *([None] * 8), None) == kda.KDA_OK
+
+
+def test_varlen_and_decode_validation(kda):
+    cfg, _ = make_cfg(kda)
+    lib = kda.library()
+    c = Canary()
+    p = c.ptr
+    # varlen: missing cu_seqlens
+    assert lib.kda_varlen_prefill(ctypes.byref(cfg), 2, 16, None, p, p, p, p, p, None, None, p, None, None,
+                                  p, 1 << 30, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_varlen_prefill(ctypes.byref(cfg), -1, 16, p, p, p, p, p, p, None, None, p, None, None,
+                                  p, 1 << 30, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_varlen_prefill(ctypes.byref(cfg), 2, 16, p, p, p, p, p, p, None, None, p, None, None,
+                                  p, 10, None) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    # decode: state and conv history are required
+    assert lib.kda_decode_step(ctypes.byref(cfg), 4, p, p, p, p, p, None, p, p, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_decode_step(ctypes.byref(cfg), 4, p, p, p, p, p, p, None, p, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_decode_step(ctypes.byref(cfg), -2, p, p, p, p, p, p, p, p, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert c.untouched()
