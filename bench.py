@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X KDA core.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Headline: chunked prefill of B=4 sequences x T=32768 tokens, H=32 heads,
+dk=dv=128, bf16 inputs, fp32 state with a random initial state (the
+long-context prefill workload).  A step is one kda_prefill call over the whole
+batch; inputs are resident in HBM before the timed region.  The same run also
+times the single-token decode step (256 sequences, 128 steps) and the varlen
+packed prefill (8 sequences, 262144 tokens), reported as sub-objects.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+H, D = 32, 128
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix
+CHUNK = 64
+
+# Algorithmic work per unit (token-head, chunk-head or (sequence, head) step),
+# d = 128, C = 64.  FLOPs of the chunked form per chunk-head, by stage:
+#   intra   (A_kk, A_qk, W, U, solve): C * (2C(3dk + dv) + 2C^2/3)
+#   state   (W S, K~^T Delta):          C * 4 dk dv
+#   output  (Q+ S, Aqk Delta):          C * (2 dk dv + 2 C dv)
+FLOPS_PER_CHUNK_HEAD = {
+    "intra": CHUNK * (2 * CHUNK * (3 * D + D) + 2 * CHUNK * CHUNK / 3.0),
+    "state": CHUNK * 4.0 * D * D,
+    "output": CHUNK * (2.0 * D * D + 2.0 * CHUNK * D),
+}
+# Bytes per token-head of the preprocess stage's own interface: raw bf16
+# q, k, v, alpha (4 x 2d) and b (2) in; fp32 q, k, v, g (4 x 4d) and beta (4) out.
+PREPROCESS_BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 2 + 4 * 4 * D + 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream_ptr):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream_ptr)) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        return float(out.value) if rc == 0 else float("nan")
+
+    def stage_array(self, stages):
+        """A (2*NUM_STAGES) array of events with entries only for `stages`."""
+        import gated_delta_rule_03_amd as kda
+        arr = (ctypes.c_void_p * (2 * kda.NUM_STAGES))()
+        for s in stages:
+            arr[2 * s] = self.create()
+            arr[2 * s + 1] = self.create()
+        return arr
+
+
+def stage_means(ev, arrays, stages):
+    out = {}
+    for s in stages:
+        vals = [ev.ms(a[2 * s], a[2 * s + 1]) for a in arrays]
+        out[s] = sum(vals) / len(vals)
+    return out
+
+
+def bench_prefill(kda, torch, ev, steps, warmup):
+    from kda_inputs import BF16
+    from kda_inputs.device_gen import DeviceProblem
+    dev = torch.device("cuda:0")
+    B, T = 4, 32768
+    t0 = time.time()
+    dp = DeviceProblem(3, [T] * B, H, D, D, BF16, dev, state_seqs=list(range(B)))
+    log(f"[bench] prefill inputs generated on device in {time.time() - t0:.1f}s")
+    cfg = dp.config(out_dtype=torch.bfloat16)
+    tz = dp.tensors
+    q, k, v = (tz[n].view(B, T, -1) for n in ("q", "k", "v"))
+    alpha, b = tz["alpha"].view(B, T, H, D), tz["b"].view(B, T, H)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    cs_out = torch.empty((B, 3, dp.ctot), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
+    log(f"[bench] prefill workspace {ws.numel() / 2**30:.2f} GiB")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_prefill(cfg, q, k, v, alpha, b, tz["initial_state"], tz["conv_state"], o=o, final_state=S_out,
+                        conv_state_out=cs_out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stages = list(range(6))
+    arrays = [ev.stage_array(stages) for _ in range(steps)]
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev.record(e0, stream.cuda_stream)
+    for i in range(steps):
+        cfg.stage_events = arrays[i]
+        step()
+    ev.record(e1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    cfg.stage_events = None
+    gpu_ms = ev.ms(e0, e1)
+    per_stage = stage_means(ev, arrays, stages)
+    log(f"[bench] prefill: {steps} steps, wall {wall * 1e3:.1f} ms, events {gpu_ms:.1f} ms; stage ms " +
+        ", ".join(f"{kda.STAGES[s]}={per_stage[s]:.3f}" for s in stages))
+    return dp, wall, gpu_ms, per_stage
+
+
+def roofline_for(kda, per_stage, B, T):
+    """Roofline object for the stage with the largest mean duration."""
+    chunk_heads = B * ((T + CHUNK - 1) // CHUNK) * H
+    token_heads = B * T * H
+    name_of = {i: n for i, n in enumerate(kda.STAGES)}
+    s_dom = max(per_stage, key=per_stage.get)
+    name = name_of[s_dom]
+    ms = per_stage[s_dom]
+    if name in FLOPS_PER_CHUNK_HEAD:
+        work = FLOPS_PER_CHUNK_HEAD[name] * chunk_heads
+        achieved = work / (ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(ms, 4), "work_per_launch": work}
+    work = PREPROCESS_BYTES_PER_TOKEN_HEAD * token_heads
+    achieved = work / (ms * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "avg_ms": round(ms, 4),
+            "work_per_launch": work}
+
+
+def bench_decode(kda, torch, ev, n_steps=128, warmup=3):
+    from kda_inputs import BF16, make_params
+    from kda_inputs.device_gen import device_tokens
+    from kda_inputs.torch_io import make_config
+    dev = torch.device("cuda:0")
+    N, wid = 256, 4
+
+    class P:  # parameter holder for make_config
+        pass
+    p = P()
+    p.H, p.dk, p.dv, p.io = H, D, D, BF16
+    p.w_q, p.w_k, p.w_v, p.A_log, p.dt_bias = make_params(wid, H, D, D, BF16)
+    cfg = make_config(p, dev, torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4_000_017)
+    S = (torch.randn((N, H, D, D), generator=g, device=dev) * 0.02).contiguous()
+    cs = torch.randn((N, 3, H * 3 * D), generator=g, device=dev).to(torch.bfloat16)
+    toks = [device_tokens(wid, N, H, D, D, BF16, dev, step=s + 1) for s in range(n_steps)]
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        kda.kda_decode_step(cfg, *toks[i], S, cs, o=o, stream=stream)
+    torch.cuda.synchronize()
+    st = kda.STAGES.index("decode")
+    arrays = [ev.stage_array([st]) for _ in range(n_steps)]
+    w0 = time.perf_counter()
+    for i in range(n_steps):
+        cfg.stage_events = arrays[i]
+        kda.kda_decode_step(cfg, *toks[i], S, cs, o=o, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    cfg.stage_events = None
+    us = [1e3 * ev.ms(a[2 * st], a[2 * st + 1]) for a in arrays]
+    mean_us = sum(us) / len(us)
+    ctot = H * 3 * D
+    bytes_step = (2 * N * H * D * D * 4          # state in + out (fp32)
+                  + 2 * N * 3 * ctot * 2         # conv history in + out (bf16)
+                  + N * (ctot + H * D + H) * 2   # q, k, v, alpha, b (bf16)
+                  + N * H * D * 2)               # o (bf16)
+    gbs = bytes_step / (mean_us * 1e-6) / 1e9
+    log(f"[bench] decode: mean {mean_us:.1f} us/step, p50 {statistics.median(us):.1f} us, {gbs:.0f} GB/s")
+    return {"workload": "kda decode step, 256 sequences x 1 token, H=32, dk=dv=128, bf16 in, fp32 state, 128 steps",
+            "us_per_step": round(mean_us, 2), "us_per_step_p50": round(statistics.median(us), 2),
+            "wall_us_per_step": round(wall / n_steps * 1e6, 2),
+            "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": bytes_step}}
+
+
+def bench_varlen(kda, torch, ev, steps=3, warmup=1):
+    from kda_inputs import BF16, VARLEN_LENGTHS
+    from kda_inputs.device_gen import DeviceProblem
+    dev = torch.device("cuda:0")
+    dp = DeviceProblem(5, VARLEN_LENGTHS, H, D, D, BF16, dev, state_seqs=[1, 3, 5, 7])
+    cfg = dp.config(out_dtype=torch.bfloat16)
+    tz = dp.tensors
+    total = sum(VARLEN_LENGTHS)
+    N = len(VARLEN_LENGTHS)
+    o = torch.empty((total, H, D), dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.kda_varlen_workspace_bytes(cfg, N, total), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_varlen_prefill(cfg, tz["cu_seqlens"], tz["q"], tz["k"], tz["v"], tz["alpha"], tz["b"],
+                               tz["initial_state"], None, o=o, final_state=S_out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, stream.cuda_stream)
+    for _ in range(steps):
+        step()
+    ev.record(e1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / steps
+    log(f"[bench] varlen: {ms:.2f} ms/step, {total / ms * 1e3 / 1e6:.2f} M tokens/s")
+    del ws
+    return {"workload": "kda varlen prefill, 8 packed sequences (1024..132096, 262144 tokens), H=32, dk=dv=128, bf16",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(total / ms * 1e3, 1)}
+
+
+def cpu_baseline(dp, seqs=2):
+    """The fp64 oracle on the first `seqs` sequences of the prefill workload
+    (all heads, full length), on all host cores."""
+    import numpy as np
+    import torch
+    import oracle
+    from kda_inputs import Problem
+    T = dp.seqlens[0]
+    n_tok = T * seqs
+
+    def host(x):
+        x = x[:n_tok].contiguous()
+        return x.view(torch.int16).cpu().numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.cpu().numpy()
+    tz = dp.tensors
+    p = Problem([T] * seqs, dp.H, dp.dk, dp.dv, dp.io, host(tz["q"]), host(tz["k"]), host(tz["v"]), host(tz["alpha"]),
+                host(tz["b"]), dp.w_q, dp.w_k, dp.w_v, dp.A_log, dp.dt_bias, dp.initial_state[:seqs], None)
+    oracle.build()
+    t0 = time.perf_counter()
+    _, _, _, threads = oracle.forward(p, with_conv_out=False)
+    dt = time.perf_counter() - t0
+    log(f"[bench] cpu oracle: {n_tok} tokens x {dp.H} heads in {dt:.1f}s on {threads} threads")
+    return {"value": round(n_tok / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 token-by-token oracle on {seqs} of the 4 sequences (all {dp.H} heads, all {T} tokens "
+                      f"each, {n_tok} tokens), wall {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the KDA core has no cross-GPU path here (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_03_amd as kda
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ev = HipEvents()
+    B, T = 4, 32768
+    dp, wall, gpu_ms, per_stage = bench_prefill(kda, torch, ev, args.steps, args.warmup)
+    ms_step = wall / args.steps * 1e3
+    value = B * T / (wall / args.steps)
+    roof = roofline_for(kda, per_stage, B, T)
+    result = {
+        "metric": "KDA prefill tokens/s (H=32,d=128,T=32K) + decode step us; % of roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "kda chunked prefill B=4 T=32768 H=32 dk=dv=128, bf16 q/k/v/alpha/b, fp32 state "
+                               "(initial state ~N(0,0.02)), bf16 o, chunk 64",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "stage_ms": {kda.STAGES[s]: round(v, 4) for s, v in per_stage.items()},
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+        "roofline": roof,
+    }
+    if not args.no_extras:
+        result["decode"] = bench_decode(kda, torch, ev)
+        result["varlen"] = bench_varlen(kda, torch, ev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -39,6 +39,9 @@ FLAG_RAW_GATE = 1 << 2
 FLAG_RAW_BETA = 1 << 3
 FLAG_BETA_X2 = 1 << 4
 
+STAGES = ("chunk_table", "preprocess", "intra", "state", "output", "conv_state", "decode")
+NUM_STAGES = len(STAGES)
+
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
             "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step")
 
@@ -66,6 +69,7 @@ class KdaConfigC(ctypes.Structure):
         ("conv_w_q", ctypes.c_void_p),
         ("conv_w_k", ctypes.c_void_p),
         ("conv_w_v", ctypes.c_void_p),
+        ("stage_events", ctypes.c_void_p),
     ]
 
 
@@ -143,6 +147,7 @@ class Config:
     l2norm_eps: float = 1e-6
     chunk_size: int = 64
     flags: int = 0
+    stage_events: Optional[object] = None   # ctypes array of 2*NUM_STAGES hipEvent_t, or None
     _c: Optional[KdaConfigC] = field(default=None, repr=False)
 
     def c_struct(self) -> KdaConfigC:
@@ -160,6 +165,7 @@ class Config:
         for name in ("A_log", "dt_bias", "conv_w_q", "conv_w_k", "conv_w_v"):
             t = getattr(self, name)
             setattr(c, name, None if t is None else t.data_ptr())
+        c.stage_events = None if self.stage_events is None else ctypes.cast(self.stage_events, ctypes.c_void_p)
         self._c = c   # keep alive
         return c
 

@@ -95,6 +95,22 @@ int64_t chunks_varlen(int64_t N, int64_t total_T) { return (total_T + kda::kChun
 
 kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// Records the caller's timing event `which` (0 = before, 1 = after) of a stage.
+void mark(const kda_config_t* cfg, int stage, int which, hipStream_t st) {
+  if (!cfg->stage_events) return;
+  void* ev = cfg->stage_events[2 * stage + which];
+  if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev), st);
+}
+
+// Runs one stage's launcher between its two timing marks.
+template <class F>
+kda_status_t stage(const kda_config_t* cfg, int s, hipStream_t st, F&& launch) {
+  mark(cfg, s, 0, st);
+  const hipError_t e = launch();
+  mark(cfg, s, 1, st);
+  return hip_status(e);
+}
+
 // The shared prefill pipeline over a packed batch.
 kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, int64_t max_chunks,
                          const int32_t* cu_in, int32_t T_uniform, const PrefillIO& io, void* workspace,
@@ -123,18 +139,26 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   const bool out_bf16 = cfg->out_dtype == KDA_BF16;
   const int mc = static_cast<int>(max_chunks);
 
-  kda_status_t s = hip_status(kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, mc, st));
+  kda_status_t s = stage(cfg, KDA_STAGE_CHUNK_TABLE, st, [&] {
+    return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, mc, st);
+  });
   if (s != KDA_OK) return s;
-  if (total_T > 0 && mc > 0) {
-    if ((s = hip_status(kda::launch_preprocess(p, t, io, b, mc, io_bf16, st))) != KDA_OK) return s;
-    if ((s = hip_status(kda::launch_chunk_intra(p, t, b, mc, st))) != KDA_OK) return s;
+  const bool any = total_T > 0 && mc > 0;
+  if (any) {
+    s = stage(cfg, KDA_STAGE_PREPROCESS, st, [&] { return kda::launch_preprocess(p, t, io, b, mc, io_bf16, st); });
+    if (s != KDA_OK) return s;
+    s = stage(cfg, KDA_STAGE_INTRA, st, [&] { return kda::launch_chunk_intra(p, t, b, mc, st); });
+    if (s != KDA_OK) return s;
   }
-  if ((s = hip_status(kda::launch_chunk_state(p, t, io, b, st))) != KDA_OK) return s;
-  if (total_T > 0 && mc > 0) {
-    if ((s = hip_status(kda::launch_chunk_output(p, t, io, b, mc, out_bf16, st))) != KDA_OK) return s;
+  s = stage(cfg, KDA_STAGE_STATE, st, [&] { return kda::launch_chunk_state(p, t, io, b, st); });
+  if (s != KDA_OK) return s;
+  if (any) {
+    s = stage(cfg, KDA_STAGE_OUTPUT, st, [&] { return kda::launch_chunk_output(p, t, io, b, mc, out_bf16, st); });
+    if (s != KDA_OK) return s;
   }
   if (io.conv_out) {
-    if ((s = hip_status(kda::launch_conv_state_out(p, t, io, io_bf16, st))) != KDA_OK) return s;
+    s = stage(cfg, KDA_STAGE_CONV_STATE, st, [&] { return kda::launch_conv_state_out(p, t, io, io_bf16, st); });
+    if (s != KDA_OK) return s;
   }
   return KDA_OK;
 }
@@ -217,8 +241,10 @@ kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, 
   if (!q || !k || !v || !alpha || !b || !state || !conv_state || !o) return KDA_ERR_INVALID_ARGUMENT;
   const Params p = make_params(cfg);
   kda::DecodeIO io{q, k, v, alpha, b, state, conv_state, o};
-  return hip_status(kda::launch_decode(p, io, N, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16,
-                                       static_cast<hipStream_t>(stream)));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return stage(cfg, KDA_STAGE_DECODE, st, [&] {
+    return kda::launch_decode(p, io, N, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16, st);
+  });
 }
 
 }  // extern "C"

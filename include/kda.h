@@ -70,6 +70,18 @@ typedef enum kda_dtype {
 #define KDA_FLAG_RAW_BETA    (1u << 3) /* b holds beta itself (no sigmoid)                  */
 #define KDA_FLAG_BETA_X2     (1u << 4) /* beta = 2 sigmoid(b): negative eigenvalues allowed */
 
+/* Stages of a call, for the optional per-stage timing hook below. */
+typedef enum kda_stage {
+    KDA_STAGE_CHUNK_TABLE = 0,  /* packed-batch chunk table (device cu_seqlens scan)   */
+    KDA_STAGE_PREPROCESS = 1,   /* conv + SiLU + L2 norm + gate + beta                 */
+    KDA_STAGE_INTRA = 2,        /* intra-chunk A, forward substitution -> W, U         */
+    KDA_STAGE_STATE = 3,        /* inter-chunk state propagation                       */
+    KDA_STAGE_OUTPUT = 4,       /* chunk output                                        */
+    KDA_STAGE_CONV_STATE = 5,   /* conv history out                                    */
+    KDA_STAGE_DECODE = 6,       /* the decode step kernel                              */
+    KDA_NUM_STAGES = 7
+} kda_stage_t;
+
 typedef struct kda_config {
     int32_t num_heads;        /* H                                                      */
     int32_t head_k_dim;       /* dk                                                     */
@@ -86,6 +98,11 @@ typedef struct kda_config {
     const void *conv_w_q;     /* [H*dk][4] io_dtype, device; tap 3 multiplies the current token */
     const void *conv_w_k;     /* [H*dk][4]                                              */
     const void *conv_w_v;     /* [H*dv][4]                                              */
+    /* Optional timing hook, NULL for none: an array of 2*KDA_NUM_STAGES
+     * hipEvent_t handles owned by the caller.  Entries 2*s and 2*s+1 (when
+     * non-NULL) are recorded on the call's stream right before and right
+     * after the launches of stage s. */
+    void **stage_events;
 } kda_config_t;
 
 /* Library version, major*10000 + minor*100 + patch. */

@@ -53,8 +53,8 @@ def test_version_and_status_strings(kda):
 
 
 def test_struct_layout_matches_header(kda):
-    # kda_config_t: 10 four-byte fields, then 5 pointers
-    assert ctypes.sizeof(kda.KdaConfigC) == 10 * 4 + 5 * 8
+    # kda_config_t: 10 four-byte fields, then 6 pointers
+    assert ctypes.sizeof(kda.KdaConfigC) == 10 * 4 + 6 * 8
     assert kda.KdaConfigC.A_log.offset == 40
 
 
