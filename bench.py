@@ -31,19 +31,23 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix
 CHUNK = 64
 
-# Algorithmic work per unit (token-head, chunk-head or (sequence, head) step),
-# d = 128, C = 64.  FLOPs of the chunked form per chunk-head, by stage:
-#   intra   (A_kk, A_qk, W, U, solve): C * (2C(3dk + dv) + 2C^2/3)
-#   state   (W S, K~^T Delta):          C * 4 dk dv
-#   output  (Q+ S, Aqk Delta):          C * (2 dk dv + 2 C dv)
+# Algorithmic work per chunk-head (C = 64 tokens of one head), d = 128, from
+# the chunked form's operation count (per token-head: 2C(3dk + 2dv) + 6 dk dv
+# + 2C^2/3 FLOPs in total):
+#   chunk_prep  A, Aqk, W, U and the solve:      C * (2C(3dk + dv) + 2C^2/3)
+#   chunk_scan  W S, K~^T Delta, Q+ S, Aqk Delta: C * (6 dk dv + 2 C dv)
+# and the bytes each stage must move at least: prep reads the raw bf16 q, k,
+# v, alpha (4 x 2d per token-head) and b, and writes its per-chunk record;
+# scan reads the record and writes o (bf16).
 FLOPS_PER_CHUNK_HEAD = {
-    "intra": CHUNK * (2 * CHUNK * (3 * D + D) + 2 * CHUNK * CHUNK / 3.0),
-    "state": CHUNK * 4.0 * D * D,
-    "output": CHUNK * (2.0 * D * D + 2.0 * CHUNK * D),
+    "chunk_prep": CHUNK * (2 * CHUNK * (3 * D + D) + 2 * CHUNK * CHUNK / 3.0),
+    "chunk_scan": CHUNK * (6.0 * D * D + 2.0 * CHUNK * D),
 }
-# Bytes per token-head of the preprocess stage's own interface: raw bf16
-# q, k, v, alpha (4 x 2d) and b (2) in; fp32 q, k, v, g (4 x 4d) and beta (4) out.
-PREPROCESS_BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 2 + 4 * 4 * D + 4
+RECORD_BYTES = 4 * 64 * D * 4 + 64 * 64 * 4 + D * 4          # one per chunk-head (fp32)
+BYTES_PER_CHUNK_HEAD = {
+    "chunk_prep": CHUNK * (4 * 2 * D + 2) + RECORD_BYTES,
+    "chunk_scan": RECORD_BYTES + CHUNK * 2 * D,
+}
 
 
 def log(*a):
@@ -118,7 +122,7 @@ def bench_prefill(kda, torch, ev, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    stages = list(range(6))
+    stages = [kda.STAGES.index(n) for n in ("chunk_table", "chunk_prep", "chunk_scan", "conv_state")]
     arrays = [ev.stage_array(stages) for _ in range(steps)]
     e0, e1 = ev.create(), ev.create()
     torch.cuda.synchronize()
@@ -139,24 +143,29 @@ def bench_prefill(kda, torch, ev, steps, warmup):
 
 
 def roofline_for(kda, per_stage, B, T):
-    """Roofline object for the stage with the largest mean duration."""
+    """Roofline object for the stage with the largest mean duration: the
+    matrix-core fraction (algorithmic FLOPs against the dense bf16 peak) and
+    the HBM fraction (the stage's minimum bytes against 8 TB/s); the larger
+    one names the bound."""
     chunk_heads = B * ((T + CHUNK - 1) // CHUNK) * H
-    token_heads = B * T * H
     name_of = {i: n for i, n in enumerate(kda.STAGES)}
     s_dom = max(per_stage, key=per_stage.get)
     name = name_of[s_dom]
     ms = per_stage[s_dom]
-    if name in FLOPS_PER_CHUNK_HEAD:
-        work = FLOPS_PER_CHUNK_HEAD[name] * chunk_heads
-        achieved = work / (ms * 1e-3) / 1e12
-        return {"kernel": name, "bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_ms": round(ms, 4), "work_per_launch": work}
-    work = PREPROCESS_BYTES_PER_TOKEN_HEAD * token_heads
-    achieved = work / (ms * 1e-3) / 1e9
-    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "avg_ms": round(ms, 4),
-            "work_per_launch": work}
+    flops = FLOPS_PER_CHUNK_HEAD.get(name, 0.0) * chunk_heads
+    nbytes = BYTES_PER_CHUNK_HEAD.get(name, 0.0) * chunk_heads
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    mfma_frac, hbm_frac = tf / BF16_MFMA_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
+    if mfma_frac >= hbm_frac:
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(tf, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(mfma_frac, 4), "traffic": None}
+    else:
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": None}
+    roof.update({"avg_ms": round(ms, 4), "flops_per_launch": flops, "bytes_per_launch": nbytes,
+                 "mfma_frac": round(mfma_frac, 4), "hbm_frac": round(hbm_frac, 4)})
+    return roof
 
 
 def bench_decode(kda, torch, ev, n_steps=128, warmup=3):
@@ -292,17 +301,19 @@ def main():
     ms_step = wall / args.steps * 1e3
     value = B * T / (wall / args.steps)
     roof = roofline_for(kda, per_stage, B, T)
+    path_gbs = B * T * H * (4 * 2 * D + 2 + 2 * D) / (ms_step * 1e-3) / 1e9
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128,T=32K) + decode step us; % of roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32", "data": "synthetic",
+        "dtype": "bf16x3/fp32", "data": "synthetic",
         "config": {"workload": "kda chunked prefill B=4 T=32768 H=32 dk=dv=128, bf16 q/k/v/alpha/b, fp32 state "
                                "(initial state ~N(0,0.02)), bf16 o, chunk 64",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "stage_ms": {kda.STAGES[s]: round(v, 4) for s, v in per_stage.items()},
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
         "roofline": roof,
+        "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
     }
     if not args.no_extras:
         result["decode"] = bench_decode(kda, torch, ev)

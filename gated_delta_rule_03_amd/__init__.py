@@ -39,7 +39,7 @@ FLAG_RAW_GATE = 1 << 2
 FLAG_RAW_BETA = 1 << 3
 FLAG_BETA_X2 = 1 << 4
 
-STAGES = ("chunk_table", "preprocess", "intra", "state", "output", "conv_state", "decode")
+STAGES = ("chunk_table", "chunk_prep", "chunk_scan", "conv_state", "decode")
 NUM_STAGES = len(STAGES)
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",

@@ -53,6 +53,7 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
+    shutil.rmtree(BUILD, ignore_errors=True)
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))

@@ -1,0 +1,259 @@
+// Sequential scan of the chunked KDA prefill: inter-chunk state propagation
+// fused with the chunk output, on the matrix cores (NP bf16 pieces per fp32
+// operand, fp32 accumulate; see mfma.h).
+//
+// One workgroup of four waves per (sequence, head, tile of DVT value
+// columns); the columns of the dk x dv state evolve independently.  For each
+// chunk of the sequence, in order, with the chunk's Record from chunk prep:
+//   Delta = U - W S                       (the corrected values)
+//   O     = Q+ S + Aqk Delta              (cross-chunk read + intra-chunk part)
+//   S     = Diag(e^{G_C}) S + K~^T Delta  (the state at the next chunk start)
+// The output reads the state updated by the current token, as in the pages'
+// loop (AliceAI page, section 二), which is why Aqk keeps its diagonal.
+//
+// Wave w owns token rows 16w..16w+15 of Delta and O and the state rows
+// (key channels) 16(w + 4i)..+15; its A operands come straight from the
+// record and are split into pieces in registers.  The state stays in fp32
+// accumulators for the whole sequence; its transpose is published once per
+// chunk to LDS as NP bf16 planes, the B operand of W S and Q+ S, and Delta
+// likewise for Aqk Delta and K~^T Delta.
+// Workgroups of the same (sequence, head) sit on the same XCD, so the
+// record's second reader finds it in that XCD's L2.
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "mfma.h"
+
+namespace kda {
+
+template <int D, int DVT, int NP, bool OUT_BF16>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t, PrefillIO io, const uint8_t* records,
+                                                         int n_sh) {
+  constexpr int NTILE = D / DVT;
+  constexpr int KP = D < 32 ? 32 : D;     // channel extent in whole 32-wide steps
+  constexpr int KS = KP / 32;             // k steps over channels
+  constexpr int CJ = DVT / 16;            // 16-column blocks of the tile
+  constexpr int CB = D / 16;              // 16-row blocks of the state
+  constexpr int CBW = (CB + 3) / 4;       // state row blocks per wave
+  constexpr int LST = KP + 8;             // row stride of S^T in LDS (bf16)
+  constexpr int LDT = kChunk + 8;         // row stride of Delta^T in LDS (bf16)
+  constexpr Record REC = record_layout(D);
+  __shared__ __align__(16) __bf16 sST[NP][DVT * LST];
+  __shared__ __align__(16) __bf16 sDT[NP][DVT * LDT];
+
+  const int H = p.H;
+  // XCD-aware order: blockIdx = ((sh / 8) * NTILE + tile) * 8 + sh % 8
+  const int bx = blockIdx.x;
+  const int tile = (bx / 8) % NTILE;
+  const int sh = (bx / 8 / NTILE) * 8 + bx % 8;
+  if (sh >= n_sh) return;
+  const int s = sh / H, h = sh % H;
+  const int j0 = tile * DVT;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
+  const size_t sbase = (static_cast<size_t>(s) * H + h) * D * D;
+
+  // ---- initial state into the accumulators and S^T into LDS
+  f32x4 Sacc[CBW][CJ];
+#pragma unroll
+  for (int i = 0; i < CBW; ++i) {
+    const int cb = wave + 4 * i;
+#pragma unroll
+    for (int cj = 0; cj < CJ; ++cj) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = 0.f;
+        if (cb < CB && io.S0) v = io.S0[sbase + static_cast<size_t>(16 * cb + 4 * q4 + j) * D + j0 + 16 * cj + ln];
+        Sacc[i][cj][j] = v;
+      }
+    }
+  }
+  for (int e = tid; e < DVT * (KP - D); e += 256) {   // zero channel padding (dk = 16 only)
+    const int col = e / (KP - D), ch = D + e % (KP - D);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) sST[k][col * LST + ch] = static_cast<__bf16>(0.f);
+  }
+  auto publish_state = [&]() {
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+      const int cb = wave + 4 * i;
+      if (cb >= CB) continue;
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          __bf16 pc[NP];
+          split_pieces<NP>(Sacc[i][cj][j], pc);
+          const int idx = (16 * cj + ln) * LST + 16 * cb + 4 * q4 + j;
+#pragma unroll
+          for (int k = 0; k < NP; ++k) sST[k][idx] = pc[k];
+        }
+      }
+    }
+  };
+  publish_state();
+  __syncthreads();
+
+  const int c_first = t.chunk0[s], c_end = t.chunk0[s + 1];
+  const int64_t seq0 = t.cu[s];
+  const int seq_len = t.cu[s + 1] - t.cu[s];
+  const int r0 = 16 * wave;                         // this wave's token rows
+  const int nks_a = wave >= 2 ? 2 : 1;              // k steps of Aqk Delta (causal)
+  for (int c = c_first; c < c_end; ++c) {
+    const uint8_t* rec = records + (static_cast<size_t>(c) * H + h) * REC.bytes;
+    const float* Wr = reinterpret_cast<const float*>(rec + REC.W);
+    const float* Qr = reinterpret_cast<const float*>(rec + REC.Qp);
+    const float* KTr = reinterpret_cast<const float*>(rec + REC.KT);
+    const float* Ar = reinterpret_cast<const float*>(rec + REC.Aqk);
+    const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
+    const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
+    const int tau = (c - c_first) * kChunk;
+    const int len = min(kChunk, seq_len - tau);
+
+    // ---- W S and Q+ S for this wave's 16 token rows
+    f32x4 accW[CJ], accQ[CJ];
+#pragma unroll
+    for (int cj = 0; cj < CJ; ++cj) { accW[cj] = zero4(); accQ[cj] = zero4(); }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * q4;
+      SplitN<NP> aW, aQ;
+      if (ch0 < D) {
+        const size_t off = static_cast<size_t>(r0 + ln) * D + ch0;
+        aW = load_split<NP>(Wr + off);
+        aQ = load_split<NP>(Qr + off);
+      } else {
+        aW = aQ = zero_split<NP>();
+      }
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) {
+        SplitN<NP> bS;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) bS.v[k] = load_bf16x8(&sST[k][(16 * cj + ln) * LST + ch0]);
+        accW[cj] = mfmaN<NP>(aW, bS, accW[cj]);
+        accQ[cj] = mfmaN<NP>(aQ, bS, accQ[cj]);
+      }
+    }
+    // Delta = U - W S, published transposed for the B operands below
+#pragma unroll
+    for (int cj = 0; cj < CJ; ++cj) {
+      const float4 u = *reinterpret_cast<const float4*>(UT + static_cast<size_t>(j0 + 16 * cj + ln) * kChunk + r0 + 4 * q4);
+      const float dl[4] = {u.x - accW[cj][0], u.y - accW[cj][1], u.z - accW[cj][2], u.w - accW[cj][3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __bf16 pc[NP];
+        split_pieces<NP>(dl[j], pc);
+        const int idx = (16 * cj + ln) * LDT + r0 + 4 * q4 + j;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) sDT[k][idx] = pc[k];
+      }
+    }
+    __syncthreads();
+
+    // ---- O = Q+ S + Aqk Delta;  S = e^{G_C} S + K~^T Delta
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+      const int cb = wave + 4 * i;
+      if (cb >= CB) continue;
+      const float4 e4 = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) {
+        Sacc[i][cj][0] *= e4.x; Sacc[i][cj][1] *= e4.y; Sacc[i][cj][2] *= e4.z; Sacc[i][cj][3] *= e4.w;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int t0 = 32 * ks + 8 * q4;
+      SplitN<NP> aA, aK[CBW];
+      if (ks < nks_a) aA = load_split<NP>(Ar + static_cast<size_t>(r0 + ln) * kChunk + t0);
+#pragma unroll
+      for (int i = 0; i < CBW; ++i) {
+        const int cb = wave + 4 * i;
+        if (cb < CB) aK[i] = load_split<NP>(KTr + static_cast<size_t>(16 * cb + ln) * kChunk + t0);
+      }
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) {
+        SplitN<NP> bD;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) bD.v[k] = load_bf16x8(&sDT[k][(16 * cj + ln) * LDT + t0]);
+        if (ks < nks_a) accQ[cj] = mfmaN<NP>(aA, bD, accQ[cj]);
+#pragma unroll
+        for (int i = 0; i < CBW; ++i)
+          if (wave + 4 * i < CB) Sacc[i][cj] = mfmaN<NP>(aK[i], bD, Sacc[i][cj]);
+      }
+    }
+    // store this wave's output rows
+#pragma unroll
+    for (int cj = 0; cj < CJ; ++cj) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + 4 * q4 + j;
+        if (r < len)
+          st<OUT_BF16>(io.o, (static_cast<size_t>(seq0 + tau + r) * H + h) * D + j0 + 16 * cj + ln, accQ[cj][j]);
+      }
+    }
+    // every wave is past its reads of S^T (barrier above): publish the new state
+    publish_state();
+    __syncthreads();
+  }
+
+  if (io.S_out) {
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+      const int cb = wave + 4 * i;
+      if (cb >= CB) continue;
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          io.S_out[sbase + static_cast<size_t>(16 * cb + 4 * q4 + j) * D + j0 + 16 * cj + ln] = Sacc[i][cj][j];
+    }
+  }
+}
+
+// Value-tile width: the widest tile that still gives every CU a workgroup.
+static int pick_dvt(int D, int n_sh) {
+  for (int dvt : {64, 32, 16})
+    if (dvt <= D && static_cast<long>(n_sh) * (D / dvt) >= 256) return dvt;
+  return 16;
+}
+
+template <int D, int DVT>
+static hipError_t launch_scan_dt(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
+                                 bool io_bf16, bool out_bf16, hipStream_t st) {
+  const int n_sh = t.N * p.H;
+  const int groups = (n_sh + 7) / 8;
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / DVT)));
+  if (io_bf16) {
+    if (out_bf16) chunk_scan_kernel<D, DVT, 2, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
+    else chunk_scan_kernel<D, DVT, 2, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
+  } else {
+    if (out_bf16) chunk_scan_kernel<D, DVT, 3, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
+    else chunk_scan_kernel<D, DVT, 3, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_scan_d(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
+                                bool io_bf16, bool out_bf16, hipStream_t st) {
+  const int dvt = pick_dvt(D, t.N * p.H);
+  if constexpr (D >= 64) {
+    if (dvt == 64) return launch_scan_dt<D, 64>(p, t, io, records, io_bf16, out_bf16, st);
+  }
+  if constexpr (D >= 32) {
+    if (dvt == 32) return launch_scan_dt<D, 32>(p, t, io, records, io_bf16, out_bf16, st);
+  }
+  return launch_scan_dt<D, 16>(p, t, io, records, io_bf16, out_bf16, st);
+}
+
+hipError_t launch_chunk_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
+                             bool io_bf16, bool out_bf16, hipStream_t st) {
+  switch (p.D) {
+    case 16: return launch_scan_d<16>(p, t, io, records, io_bf16, out_bf16, st);
+    case 32: return launch_scan_d<32>(p, t, io, records, io_bf16, out_bf16, st);
+    case 64: return launch_scan_d<64>(p, t, io, records, io_bf16, out_bf16, st);
+    case 128: return launch_scan_d<128>(p, t, io, records, io_bf16, out_bf16, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

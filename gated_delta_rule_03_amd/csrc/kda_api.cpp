@@ -9,7 +9,6 @@
 
 namespace {
 
-using kda::ChunkBuffers;
 using kda::ChunkTable;
 using kda::Params;
 using kda::PrefillIO;
@@ -62,30 +61,17 @@ Params make_params(const kda_config_t* cfg) {
 }
 
 struct Layout {
-  size_t cu, chunk0, chunk_seq, qh, kh, vh, g, beta, W, U, Qp, Kt, eGC, Aqk, Sst, total;
+  size_t cu, chunk0, chunk_seq, records, total;
 };
 
 Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
-  const size_t ch = static_cast<size_t>(max_chunks) * H;     // chunk-heads
-  const size_t tileb = ch * kda::kChunk * D * sizeof(float);
   L.cu = take((N + 1) * sizeof(int32_t));
   L.chunk0 = take((N + 1) * sizeof(int32_t));
   L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
-  L.qh = take(tileb);
-  L.kh = take(tileb);
-  L.vh = take(tileb);
-  L.g = take(tileb);
-  L.beta = take(ch * kda::kChunk * sizeof(float));
-  L.W = take(tileb);
-  L.U = take(tileb);
-  L.Qp = take(tileb);
-  L.Kt = take(tileb);
-  L.eGC = take(ch * D * sizeof(float));
-  L.Aqk = take(ch * kda::kChunk * kda::kChunk * sizeof(float));
-  L.Sst = take(ch * D * D * sizeof(float));
+  L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D)).bytes);
   L.total = off;
   return L;
 }
@@ -122,19 +108,7 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
   int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
   ChunkTable t{cu_ws, chunk0, chunk_seq, N};
-  ChunkBuffers b;
-  b.qh = reinterpret_cast<float*>(ws + L.qh);
-  b.kh = reinterpret_cast<float*>(ws + L.kh);
-  b.vh = reinterpret_cast<float*>(ws + L.vh);
-  b.g = reinterpret_cast<float*>(ws + L.g);
-  b.beta = reinterpret_cast<float*>(ws + L.beta);
-  b.W = reinterpret_cast<float*>(ws + L.W);
-  b.U = reinterpret_cast<float*>(ws + L.U);
-  b.Qp = reinterpret_cast<float*>(ws + L.Qp);
-  b.Kt = reinterpret_cast<float*>(ws + L.Kt);
-  b.eGC = reinterpret_cast<float*>(ws + L.eGC);
-  b.Aqk = reinterpret_cast<float*>(ws + L.Aqk);
-  b.Sst = reinterpret_cast<float*>(ws + L.Sst);
+  uint8_t* records = reinterpret_cast<uint8_t*>(ws + L.records);
   const bool io_bf16 = cfg->io_dtype == KDA_BF16;
   const bool out_bf16 = cfg->out_dtype == KDA_BF16;
   const int mc = static_cast<int>(max_chunks);
@@ -143,19 +117,12 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
     return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, mc, st);
   });
   if (s != KDA_OK) return s;
-  const bool any = total_T > 0 && mc > 0;
-  if (any) {
-    s = stage(cfg, KDA_STAGE_PREPROCESS, st, [&] { return kda::launch_preprocess(p, t, io, b, mc, io_bf16, st); });
-    if (s != KDA_OK) return s;
-    s = stage(cfg, KDA_STAGE_INTRA, st, [&] { return kda::launch_chunk_intra(p, t, b, mc, st); });
+  if (total_T > 0 && mc > 0) {
+    s = stage(cfg, KDA_STAGE_CHUNK_PREP, st, [&] { return kda::launch_chunk_prep(p, t, io, records, mc, io_bf16, st); });
     if (s != KDA_OK) return s;
   }
-  s = stage(cfg, KDA_STAGE_STATE, st, [&] { return kda::launch_chunk_state(p, t, io, b, st); });
+  s = stage(cfg, KDA_STAGE_CHUNK_SCAN, st, [&] { return kda::launch_chunk_scan(p, t, io, records, io_bf16, out_bf16, st); });
   if (s != KDA_OK) return s;
-  if (any) {
-    s = stage(cfg, KDA_STAGE_OUTPUT, st, [&] { return kda::launch_chunk_output(p, t, io, b, mc, out_bf16, st); });
-    if (s != KDA_OK) return s;
-  }
   if (io.conv_out) {
     s = stage(cfg, KDA_STAGE_CONV_STATE, st, [&] { return kda::launch_conv_state_out(p, t, io, io_bf16, st); });
     if (s != KDA_OK) return s;

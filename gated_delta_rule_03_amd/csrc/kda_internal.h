@@ -12,6 +12,32 @@ namespace kda {
 constexpr int kChunk = 64;   // tokens per chunk of the chunked form
 constexpr int kSub = 16;     // tokens per decay sub-block inside a chunk
 
+// Per (chunk, head) record written by the chunk-prep kernel and read by the
+// chunk-scan kernel: the operands of the state recurrence, fp32, in the
+// layouts the matrix-core operand loads read.  Byte offsets:
+//   W   [64][D]  W = (I + A)^-1 Diag(beta) (K * e^G), token-major
+//   Qp  [64][D]  Q+ = Q * e^G, token-major
+//   KT  [D][64]  K~^T = (K * e^{G_C - G})^T, channel-major
+//   Aqk [64][64] the masked intra-chunk attention, token-major
+//   UT  [D][64]  U^T = ((I + A)^-1 Diag(beta) V)^T
+//   eGC [D]      e^{G_C}, the whole-chunk decay
+struct Record {
+  size_t W, Qp, KT, Aqk, UT, eGC, bytes;
+};
+
+__host__ __device__ constexpr Record record_layout(int D) {
+  const size_t tile = static_cast<size_t>(64) * D * 4;
+  Record r{};
+  r.W = 0;
+  r.Qp = r.W + tile;
+  r.KT = r.Qp + tile;
+  r.Aqk = r.KT + tile;
+  r.UT = r.Aqk + static_cast<size_t>(64) * 64 * 4;
+  r.eGC = r.UT + tile;
+  r.bytes = (r.eGC + static_cast<size_t>(D) * 4 + 255) / 256 * 256;
+  return r;
+}
+
 // Parameters every kernel that touches raw inputs needs.
 struct Params {
   int H;
@@ -35,22 +61,6 @@ struct ChunkTable {
   int32_t N;
 };
 
-// Per-chunk fp32 intermediates, chunk-major: [chunk][H][64][D] unless noted.
-struct ChunkBuffers {
-  float* qh;     // normalised, scaled q
-  float* kh;     // normalised k
-  float* vh;     // v after conv + SiLU
-  float* g;      // per-channel log decay
-  float* beta;   // [chunk][H][64]
-  float* W;      // T (beta * k * e^G)
-  float* U;      // T (beta * v); overwritten by Delta = U - W S
-  float* Qp;     // q * e^G
-  float* Kt;     // k * e^{G_C - G}
-  float* eGC;    // [chunk][H][D] e^{G_C}
-  float* Aqk;    // [chunk][H][64][64] masked intra-chunk attention
-  float* Sst;    // [chunk][H][D][D] state at chunk start
-};
-
 struct PrefillIO {
   const void* q;
   const void* k;
@@ -66,14 +76,10 @@ struct PrefillIO {
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws,
                                int32_t* chunk0, int32_t* chunk_seq, int32_t max_chunks, hipStream_t st);
-hipError_t launch_preprocess(const Params& p, const ChunkTable& t, const PrefillIO& io, const ChunkBuffers& b,
+hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                              int max_chunks, bool io_bf16, hipStream_t st);
-hipError_t launch_chunk_intra(const Params& p, const ChunkTable& t, const ChunkBuffers& b, int max_chunks,
-                              hipStream_t st);
-hipError_t launch_chunk_state(const Params& p, const ChunkTable& t, const PrefillIO& io, const ChunkBuffers& b,
-                              hipStream_t st);
-hipError_t launch_chunk_output(const Params& p, const ChunkTable& t, const PrefillIO& io, const ChunkBuffers& b,
-                               int max_chunks, bool out_bf16, hipStream_t st);
+hipError_t launch_chunk_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
+                             bool io_bf16, bool out_bf16, hipStream_t st);
 hipError_t launch_conv_state_out(const Params& p, const ChunkTable& t, const PrefillIO& io, bool io_bf16,
                                  hipStream_t st);
 

@@ -1,0 +1,91 @@
+// bf16 matrix-core helpers for gfx950 (wave64, v_mfma_f32_16x16x32_bf16).
+//
+// Operand layouts of one 16x16x32 step (verified on MI355X):
+//   A (16 x 32, M x K): lane l holds A[l % 16][8 * (l / 16) + i], i < 8
+//   B (32 x 16, K x N): lane l holds B[8 * (l / 16) + i][l % 16], i < 8
+//   C (16 x 16):        lane l holds C[4 * (l / 16) + i][l % 16], i < 4
+//
+// Compensated products.  Plain bf16 operands (8 significant bits) are far too
+// coarse for the chunked form of the delta rule, so every fp32 operand x is
+// split into NP bf16 pieces, x ~ p0 + p1 (+ p2), each piece the bf16 rounding
+// of what the earlier pieces left, and a product accumulates in fp32 all
+// piece pairs (i, j) with i + j < NP, smallest terms first.  NP = 2 gives 16
+// significant bits with 3 matrix-core passes (dropping only p1*p1, ~2^-16
+// relative): the path for bf16 inputs.  NP = 3 gives fp32's 24 bits with 6
+// passes: the all-fp32 path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NP>
+struct SplitN {
+  bf16x8 v[NP];
+};
+
+// c += a * b over all piece pairs i + j < NP, smallest terms first.
+template <int NP>
+__device__ __forceinline__ f32x4 mfmaN(const SplitN<NP>& a, const SplitN<NP>& b, f32x4 c) {
+#pragma unroll
+  for (int sum = NP - 1; sum >= 0; --sum)
+#pragma unroll
+    for (int i = 0; i <= sum; ++i) c = mfma(a.v[i], b.v[sum - i], c);
+  return c;
+}
+
+// The NP bf16 pieces of one fp32 value.
+template <int NP>
+__device__ __forceinline__ void split_pieces(float x, __bf16 (&pc)[NP]) {
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    pc[k] = static_cast<__bf16>(x);
+    x -= static_cast<float>(pc[k]);
+  }
+}
+
+template <int NP>
+__device__ __forceinline__ SplitN<NP> splitN(const float (&x)[8]) {
+  SplitN<NP> s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __bf16 pc[NP];
+    split_pieces<NP>(x[i], pc);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) s.v[k][i] = pc[k];
+  }
+  return s;
+}
+
+// Eight consecutive fp32 values (16-byte aligned) split into pieces.
+template <int NP>
+__device__ __forceinline__ SplitN<NP> load_split(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return splitN<NP>(x);
+}
+
+template <int NP>
+__device__ __forceinline__ SplitN<NP> zero_split() {
+  SplitN<NP> s;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) s.v[k] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+  return s;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace kda

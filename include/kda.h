@@ -37,7 +37,8 @@
  *    untouched.  A launch failure returns KDA_ERR_HIP.  Faults inside kernels
  *    surface at the caller's next synchronisation.
  *  - NaN/Inf inputs propagate; they are not trapped.
- *  - T == 0 or N == 0 is a valid no-op returning KDA_OK.
+ *  - B == 0 or N == 0 is a valid no-op returning KDA_OK.  A sequence of
+ *    length 0 passes its initial state and conv history through unchanged.
  *  - Supported geometry: dk == dv, dk in {16, 32, 64, 128}; chunk_size 64.
  */
 #ifndef KDA_H
@@ -72,14 +73,12 @@ typedef enum kda_dtype {
 
 /* Stages of a call, for the optional per-stage timing hook below. */
 typedef enum kda_stage {
-    KDA_STAGE_CHUNK_TABLE = 0,  /* packed-batch chunk table (device cu_seqlens scan)   */
-    KDA_STAGE_PREPROCESS = 1,   /* conv + SiLU + L2 norm + gate + beta                 */
-    KDA_STAGE_INTRA = 2,        /* intra-chunk A, forward substitution -> W, U         */
-    KDA_STAGE_STATE = 3,        /* inter-chunk state propagation                       */
-    KDA_STAGE_OUTPUT = 4,       /* chunk output                                        */
-    KDA_STAGE_CONV_STATE = 5,   /* conv history out                                    */
-    KDA_STAGE_DECODE = 6,       /* the decode step kernel                              */
-    KDA_NUM_STAGES = 7
+    KDA_STAGE_CHUNK_TABLE = 0,  /* packed-batch chunk table (device cu_seqlens scan)          */
+    KDA_STAGE_CHUNK_PREP = 1,   /* preprocess + intra-chunk solve, parallel over chunks       */
+    KDA_STAGE_CHUNK_SCAN = 2,   /* inter-chunk state propagation + chunk output, sequential   */
+    KDA_STAGE_CONV_STATE = 3,   /* conv history out                                           */
+    KDA_STAGE_DECODE = 4,       /* the decode step kernel                                     */
+    KDA_NUM_STAGES = 5
 } kda_stage_t;
 
 typedef struct kda_config {
@@ -89,7 +88,9 @@ typedef struct kda_config {
     int32_t io_dtype;         /* kda_dtype_t of q, k, v, alpha, b, conv weights, conv history */
     int32_t out_dtype;        /* kda_dtype_t of o                                       */
     float scale;              /* multiplies the normalised q; 1.0 as on the pages       */
-    float gate_lower_bound;   /* -5.0 (safe gate); -INFINITY disables the clamp         */
+    float gate_lower_bound;   /* -5.0 (safe gate).  The chunked prefill needs >= -5.4
+                                 (KDA_ERR_UNSUPPORTED otherwise); the decode step takes
+                                 any value, -INFINITY disabling the clamp              */
     float l2norm_eps;         /* q / sqrt(|q|^2 + eps); 1e-6                            */
     int32_t chunk_size;       /* 64                                                     */
     uint32_t flags;           /* KDA_FLAG_* test hooks, normally 0                      */
