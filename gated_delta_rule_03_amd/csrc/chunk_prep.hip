@@ -44,17 +44,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
   constexpr int NT = 256;
   constexpr int LDR = D + 4;                       // LDS row stride of the fp32 tiles
   constexpr int KP = D < 32 ? 32 : D;              // channel extent in whole 32-wide steps
-  constexpr int VSZ = (64 * LDR > 2 * 64 * 65) ? 64 * LDR : 2 * 64 * 65;
+  constexpr int LA = 68;                           // row stride of A / Aqk in LDS (16-byte rows)
+  constexpr int VSZ = (64 * LDR > 2 * 64 * LA) ? 64 * LDR : 2 * 64 * LA;
   constexpr Record REC = record_layout(D);
   constexpr int NP = IO_BF16 ? 2 : 3;              // bf16 pieces per operand
-  __shared__ float sQ[64 * LDR];                   // q, then q e^{P}
-  __shared__ float sK[64 * LDR];                   // k, then k e^{P}
-  __shared__ float sG[64 * LDR];                   // g, then k e^{-P}
-  __shared__ float sV[VSZ];                        // v, then A (I + A solve) and Aqk
-  __shared__ float sE[6][D];                       // e^{sum of block totals between I and R}
+  __shared__ __align__(16) float sQ[64 * LDR];    // q, then q e^{P}
+  __shared__ __align__(16) float sK[64 * LDR];    // k, then k e^{P}
+  __shared__ __align__(16) float sG[64 * LDR];    // g, then k e^{-P}
+  __shared__ __align__(16) float sV[VSZ];          // v, then A (I + A solve) and Aqk
+  __shared__ __align__(16) float sE[6][D];         // e^{sum of block totals between I and R}
   __shared__ float sBeta[64];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  // head-fastest order: the resident workgroups cover every head of a few
+  // chunks, so each raw token row is read whole while it is open in DRAM
+  const int h = blockIdx.x, c = blockIdx.y;
   if (c >= t.chunk0[t.N]) return;
   const int H = p.H;
   const int s = t.chunk_seq[c];
@@ -86,27 +89,28 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
         else if (io.conv_in) hm[m] = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(s) * 3 + (3 + tau)) * Ctot + grp * HD + col);
         else hm[m] = 0.f;
       }
+      float xr[kChunk];   // all loads of the channel in flight at once
+#pragma unroll
+      for (int r = 0; r < kChunk; ++r)   // rows past the chunk's end re-read its last row (no branch)
+        xr[r] = ld<IO_BF16>(x, static_cast<size_t>(tok0 + min(r, len - 1)) * HD + col);
       float h3 = hm[0], h2 = hm[1], h1 = hm[2];
-#pragma unroll 8
+#pragma unroll
       for (int r = 0; r < kChunk; ++r) {
-        float u = 0.f;
-        if (r < len) {
-          const float xt = ld<IO_BF16>(x, static_cast<size_t>(tok0 + r) * HD + col);
-          u = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h3 + w1 * h2 + w2 * h1 + w3 * xt);
-          h3 = h2; h2 = h1; h1 = xt;
-        }
+        const float xt = xr[r];
+        float u = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h3 + w1 * h2 + w2 * h1 + w3 * xt);
+        u = r < len ? u : 0.f;
+        h3 = h2; h2 = h1; h1 = xt;
         dst[r * LDR + ch] = u;
       }
     } else {
       const float dtb = p.dt_bias[col];
-#pragma unroll 8
+      float ar[kChunk];
+#pragma unroll
+      for (int r = 0; r < kChunk; ++r) ar[r] = ld<IO_BF16>(io.alpha, static_cast<size_t>(tok0 + min(r, len - 1)) * HD + col);
+#pragma unroll
       for (int r = 0; r < kChunk; ++r) {
-        float g = 0.f;
-        if (r < len) {
-          const float al = ld<IO_BF16>(io.alpha, static_cast<size_t>(tok0 + r) * HD + col);
-          g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound);
-        }
-        sG[r * LDR + ch] = g;
+        float g = (flags & KDA_FLAG_RAW_GATE) ? ar[r] : gate_value(ar[r], dtb, a_exp, p.lower_bound);
+        sG[r * LDR + ch] = r < len ? g : 0.f;
       }
     }
   }
@@ -161,7 +165,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
       Bt[J] = sum;
     }
     float* Qp = reinterpret_cast<float*>(rec + REC.Qp);
-    float before = 0.f;
+    // e^{G_r} = e^{P_r} * e^{sum of earlier block totals}: products of factors
+    // that each carry one rounding, never exponentials of long sums
+    float eBt[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) eBt[J] = expf(Bt[J]);
+    float eBefore = 1.f;
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       float P = 0.f;
@@ -173,12 +182,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
         const float qv = sQ[r * LDR + ch];
         sK[r * LDR + ch] = kc[r] * eP;
         sQ[r * LDR + ch] = qv * eP;
-        sG[r * LDR + ch] = kc[r] * expf(-P);
-        const float eG = expf(before + P);
+        sG[r * LDR + ch] = kc[r] / eP;
+        const float eG = eP * eBefore;
         Qp[r * D + ch] = qv * eG;
         x[r] = sBeta[r] * kc[r] * eG;
       }
-      before += Bt[J];
+      eBefore *= eBt[J];
     }
     // K~^T row of this channel: k e^{Q_r + later block totals}, Q_r = in-block
     // sum of g after token r; built backwards, 4 tokens per 16-byte store
@@ -196,13 +205,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
         if (r % 4 == 0) KT[r / 4] = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
       }
     }
-    reinterpret_cast<float*>(rec + REC.eGC)[ch] = expf(Bt[0] + Bt[1] + Bt[2] + Bt[3]);
-    sE[0][ch] = expf(Bt[0]);
-    sE[1][ch] = expf(Bt[0] + Bt[1]);
-    sE[2][ch] = expf(Bt[0] + Bt[1] + Bt[2]);
-    sE[3][ch] = expf(Bt[1]);
-    sE[4][ch] = expf(Bt[1] + Bt[2]);
-    sE[5][ch] = expf(Bt[2]);
+    reinterpret_cast<float*>(rec + REC.eGC)[ch] = eBefore;
+    sE[0][ch] = eBt[0];
+    sE[1][ch] = eBt[0] * eBt[1];
+    sE[2][ch] = eBt[0] * eBt[1] * eBt[2];
+    sE[3][ch] = eBt[1];
+    sE[4][ch] = eBt[1] * eBt[2];
+    sE[5][ch] = eBt[2];
   } else if (tid >= 128 && tid < 128 + D) {
     const int ch = tid - 128;
 #pragma unroll
@@ -211,8 +220,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
   __syncthreads();
 
   // ---- 2b. A and Aqk, one 16x16 sub-block per task on the matrix cores
-  float* sA = sV;                 // [64][65]  A (strictly lower, rows scaled by beta)
-  float* sAqk = sV + 64 * 65;     // [64][65]  Aqk (lower, with diagonal)
+  float* sA = sV;                 // [64][LA]  A (strictly lower, rows scaled by beta)
+  float* sAqk = sV + 64 * LA;     // [64][LA]  Aqk (lower, with diagonal)
   {
     const int wave = tid / kWave, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
     for (int task = wave; task < 32; task += NT / kWave) {
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
       float* dst = mat == 0 ? sA : sAqk;
       if (I > R) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[(16 * R + 4 * q4 + j) * 65 + 16 * I + ln] = 0.f;
+        for (int j = 0; j < 4; ++j) dst[(16 * R + 4 * q4 + j) * LA + 16 * I + ln] = 0.f;
         continue;
       }
       const float* rows = mat == 0 ? sK : sQ;
@@ -229,22 +238,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
 #pragma unroll
       for (int ks = 0; ks < KP / 32; ++ks) {
         const int ch0 = 32 * ks + 8 * q4;
-        float a[8], b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int ch = ch0 + i;
-          const bool in = ch < D;
-          const float e = (E && in) ? E[ch] : 1.0f;
-          a[i] = in ? rows[(16 * R + ln) * LDR + ch] * e : 0.f;
-          b[i] = in ? sG[(16 * I + ln) * LDR + ch] : 0.f;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (ch0 < D) {   // eight whole channels (dk >= 16 is a multiple of 8)
+          const float4* ra = reinterpret_cast<const float4*>(&rows[(16 * R + ln) * LDR + ch0]);
+          const float4* cb = reinterpret_cast<const float4*>(&sG[(16 * I + ln) * LDR + ch0]);
+          const float4 a0 = ra[0], a1 = ra[1], b0 = cb[0], b1 = cb[1];
+          a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+          b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+          if (E) {
+            const float4 e0 = *reinterpret_cast<const float4*>(&E[ch0]);
+            const float4 e1 = *reinterpret_cast<const float4*>(&E[ch0 + 4]);
+            a[0] *= e0.x; a[1] *= e0.y; a[2] *= e0.z; a[3] *= e0.w;
+            a[4] *= e1.x; a[5] *= e1.y; a[6] *= e1.z; a[7] *= e1.w;
+          }
         }
         acc = mfmaN<NP>(splitN<NP>(a), splitN<NP>(b), acc);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * R + 4 * q4 + j, i = 16 * I + ln;
-        if (mat == 0) dst[r * 65 + i] = (i < r) ? sBeta[r] * acc[j] : 0.f;
-        else dst[r * 65 + i] = (i <= r) ? acc[j] : 0.f;
+        if (mat == 0) dst[r * LA + i] = (i < r) ? sBeta[r] * acc[j] : 0.f;
+        else dst[r * LA + i] = (i <= r) ? acc[j] : 0.f;
       }
     }
   }
@@ -254,10 +268,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
   if (tid < D || (tid >= 128 && tid < 128 + D)) {
 #pragma unroll
     for (int r = 1; r < kChunk; ++r) {
-      float acc = x[r];
+      // four independent partial sums over i (rows of A read 4 at a time)
+      float a4[4] = {x[r], 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= sA[r * 65 + i] * x[i];
-      x[r] = acc;
+      for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+        const float4 av = *reinterpret_cast<const float4*>(&sA[r * LA + 4 * i4]);
+        const float aa[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * i4 + j < r) a4[j] -= aa[j] * x[4 * i4 + j];
+      }
+      x[r] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
     }
     if (tid < D) {
       float* W = reinterpret_cast<float*>(rec + REC.W);
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
     float4* Aq = reinterpret_cast<float4*>(rec + REC.Aqk);
     for (int e = tid; e < kChunk * kChunk / 4; e += NT) {
       const int r = (4 * e) / kChunk, i = (4 * e) % kChunk;
-      Aq[e] = make_float4(sAqk[r * 65 + i], sAqk[r * 65 + i + 1], sAqk[r * 65 + i + 2], sAqk[r * 65 + i + 3]);
+      Aq[e] = *reinterpret_cast<const float4*>(&sAqk[r * LA + i]);
     }
   }
 }
@@ -281,7 +302,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
 template <int D>
 static hipError_t launch_prep_d(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                                 int max_chunks, bool io_bf16, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(max_chunks), static_cast<unsigned>(p.H));
+  const dim3 grid(static_cast<unsigned>(p.H), static_cast<unsigned>(max_chunks));
   if (io_bf16) chunk_prep_kernel<D, true><<<grid, 256, 0, st>>>(p, t, io, records);
   else chunk_prep_kernel<D, false><<<grid, 256, 0, st>>>(p, t, io, records);
   return hipGetLastError();

@@ -25,6 +25,74 @@
 
 namespace kda {
 
+// One wave's record operands for one chunk, raw fp32, so that the next
+// chunk's loads are in flight while the current chunk computes.
+template <int D, int DVT>
+struct WaveOps {
+  static constexpr int KS = (D < 32 ? 32 : D) / 32;
+  static constexpr int CJ = DVT / 16;
+  static constexpr int CBW = (D / 16 + 3) / 4;
+  float4 w[KS][2], q[KS][2];     // W, Q+ rows of this wave's tokens
+  float4 u[CJ];                  // U^T, four tokens of one value column
+  float4 a[2][2];                // Aqk rows (two 32-token steps)
+  float4 kt[CBW][2][2];          // K~^T rows of this wave's state rows
+  float4 e[CBW];                 // e^{G_C} of this lane's four state rows
+};
+
+template <int D, int DVT>
+__device__ __forceinline__ void load_ops(WaveOps<D, DVT>& o, const uint8_t* rec, int wave, int ln, int q4, int j0,
+                                         int nks_a) {
+  constexpr Record REC = record_layout(D);
+  constexpr int KS = WaveOps<D, DVT>::KS, CJ = WaveOps<D, DVT>::CJ, CBW = WaveOps<D, DVT>::CBW, CB = D / 16;
+  const float* Wr = reinterpret_cast<const float*>(rec + REC.W);
+  const float* Qr = reinterpret_cast<const float*>(rec + REC.Qp);
+  const float* KTr = reinterpret_cast<const float*>(rec + REC.KT);
+  const float* Ar = reinterpret_cast<const float*>(rec + REC.Aqk);
+  const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
+  const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
+  const int r0 = 16 * wave;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int ch0 = 32 * ks + 8 * q4;
+    if (ch0 < D) {
+      const float4* pw = reinterpret_cast<const float4*>(Wr + static_cast<size_t>(r0 + ln) * D + ch0);
+      const float4* pq = reinterpret_cast<const float4*>(Qr + static_cast<size_t>(r0 + ln) * D + ch0);
+      o.w[ks][0] = pw[0]; o.w[ks][1] = pw[1];
+      o.q[ks][0] = pq[0]; o.q[ks][1] = pq[1];
+    } else {
+      o.w[ks][0] = o.w[ks][1] = o.q[ks][0] = o.q[ks][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+#pragma unroll
+  for (int cj = 0; cj < CJ; ++cj)
+    o.u[cj] = *reinterpret_cast<const float4*>(UT + static_cast<size_t>(j0 + 16 * cj + ln) * kChunk + r0 + 4 * q4);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks < nks_a) {
+      const float4* pa = reinterpret_cast<const float4*>(Ar + static_cast<size_t>(r0 + ln) * kChunk + 32 * ks + 8 * q4);
+      o.a[ks][0] = pa[0]; o.a[ks][1] = pa[1];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CBW; ++i) {
+    const int cb = wave + 4 * i;
+    if (cb < CB) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const float4* pk = reinterpret_cast<const float4*>(KTr + static_cast<size_t>(16 * cb + ln) * kChunk + 32 * ks + 8 * q4);
+        o.kt[i][ks][0] = pk[0]; o.kt[i][ks][1] = pk[1];
+      }
+      o.e[i] = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
+    }
+  }
+}
+
+template <int NP>
+__device__ __forceinline__ SplitN<NP> split_pair(const float4& a, const float4& b) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return splitN<NP>(x);
+}
+
 template <int D, int DVT, int NP, bool OUT_BF16>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t, PrefillIO io, const uint8_t* records,
                                                          int n_sh) {
@@ -66,10 +134,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
       }
     }
   }
-  for (int e = tid; e < DVT * (KP - D); e += 256) {   // zero channel padding (dk = 16 only)
-    const int col = e / (KP - D), ch = D + e % (KP - D);
+  if constexpr (KP > D) {   // zero channel padding (dk = 16 only)
+    for (int e = tid; e < DVT * (KP - D); e += 256) {
+      const int col = e / (KP - D), ch = D + e % (KP - D);
 #pragma unroll
-    for (int k = 0; k < NP; ++k) sST[k][col * LST + ch] = static_cast<__bf16>(0.f);
+      for (int k = 0; k < NP; ++k) sST[k][col * LST + ch] = static_cast<__bf16>(0.f);
+    }
   }
   auto publish_state = [&]() {
 #pragma unroll
@@ -97,14 +167,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   const int seq_len = t.cu[s + 1] - t.cu[s];
   const int r0 = 16 * wave;                         // this wave's token rows
   const int nks_a = wave >= 2 ? 2 : 1;              // k steps of Aqk Delta (causal)
+  WaveOps<D, DVT> cur, nxt;
+  if (c_first < c_end)
+    load_ops<D, DVT>(cur, records + (static_cast<size_t>(c_first) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
   for (int c = c_first; c < c_end; ++c) {
-    const uint8_t* rec = records + (static_cast<size_t>(c) * H + h) * REC.bytes;
-    const float* Wr = reinterpret_cast<const float*>(rec + REC.W);
-    const float* Qr = reinterpret_cast<const float*>(rec + REC.Qp);
-    const float* KTr = reinterpret_cast<const float*>(rec + REC.KT);
-    const float* Ar = reinterpret_cast<const float*>(rec + REC.Aqk);
-    const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
-    const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
+    if (c + 1 < c_end)
+      load_ops<D, DVT>(nxt, records + (static_cast<size_t>(c + 1) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
     const int tau = (c - c_first) * kChunk;
     const int len = min(kChunk, seq_len - tau);
 
@@ -115,14 +183,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * q4;
-      SplitN<NP> aW, aQ;
-      if (ch0 < D) {
-        const size_t off = static_cast<size_t>(r0 + ln) * D + ch0;
-        aW = load_split<NP>(Wr + off);
-        aQ = load_split<NP>(Qr + off);
-      } else {
-        aW = aQ = zero_split<NP>();
-      }
+      const SplitN<NP> aW = split_pair<NP>(cur.w[ks][0], cur.w[ks][1]);
+      const SplitN<NP> aQ = split_pair<NP>(cur.q[ks][0], cur.q[ks][1]);
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         SplitN<NP> bS;
@@ -135,7 +197,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
     // Delta = U - W S, published transposed for the B operands below
 #pragma unroll
     for (int cj = 0; cj < CJ; ++cj) {
-      const float4 u = *reinterpret_cast<const float4*>(UT + static_cast<size_t>(j0 + 16 * cj + ln) * kChunk + r0 + 4 * q4);
+      const float4 u = cur.u[cj];
       const float dl[4] = {u.x - accW[cj][0], u.y - accW[cj][1], u.z - accW[cj][2], u.w - accW[cj][3]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -151,9 +213,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
     // ---- O = Q+ S + Aqk Delta;  S = e^{G_C} S + K~^T Delta
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
-      const int cb = wave + 4 * i;
-      if (cb >= CB) continue;
-      const float4 e4 = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
+      if (wave + 4 * i >= CB) continue;
+      const float4 e4 = cur.e[i];
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         Sacc[i][cj][0] *= e4.x; Sacc[i][cj][1] *= e4.y; Sacc[i][cj][2] *= e4.z; Sacc[i][cj][3] *= e4.w;
@@ -163,12 +224,10 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
     for (int ks = 0; ks < 2; ++ks) {
       const int t0 = 32 * ks + 8 * q4;
       SplitN<NP> aA, aK[CBW];
-      if (ks < nks_a) aA = load_split<NP>(Ar + static_cast<size_t>(r0 + ln) * kChunk + t0);
+      if (ks < nks_a) aA = split_pair<NP>(cur.a[ks][0], cur.a[ks][1]);
 #pragma unroll
-      for (int i = 0; i < CBW; ++i) {
-        const int cb = wave + 4 * i;
-        if (cb < CB) aK[i] = load_split<NP>(KTr + static_cast<size_t>(16 * cb + ln) * kChunk + t0);
-      }
+      for (int i = 0; i < CBW; ++i)
+        if (wave + 4 * i < CB) aK[i] = split_pair<NP>(cur.kt[i][ks][0], cur.kt[i][ks][1]);
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         SplitN<NP> bD;
@@ -193,6 +252,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
     // every wave is past its reads of S^T (barrier above): publish the new state
     publish_state();
     __syncthreads();
+    cur = nxt;
   }
 
   if (io.S_out) {
