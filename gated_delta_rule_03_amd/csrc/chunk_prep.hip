@@ -3,12 +3,13 @@
 // workgroup, fully parallel over the batch.
 //
 // 1. Preprocess (AliceAI page, section 二; safe gate from the Ling-3.0-flash-VL
-//    page, section "KDA 层的安全门"): each lane owns a channel and slides the
-//    4-tap causal conv window down the chunk (the three earlier inputs come
-//    from the same sequence or from the incoming conv history), then SiLU;
-//    q and k are L2-normalised per token; g = max(-e^{A_log} softplus(alpha +
-//    dt_bias), lb); beta = sigmoid(b).  Rows past a partial chunk's end are
-//    zero with g = beta = 0, an exact identity step of the recurrence.
+//    page, section "KDA 层的安全门"): a lane owns one channel of one input
+//    (q, k, v or alpha) and slides the 4-tap causal conv window down the
+//    chunk (the three earlier inputs come from the same sequence or from the
+//    incoming conv history), then SiLU; q and k are L2-normalised per token;
+//    g = max(-e^{A_log} softplus(alpha + dt_bias), lb); beta = sigmoid(b).
+//    Rows past a partial chunk's end are zero with g = beta = 0, an exact
+//    identity step of the recurrence.
 // 2. Chunked form (derived by unrolling the pages' token loop over the chunk;
 //    G_r = sum_{i<=r} g_i per key channel):
 //      A[r,i]   = beta_r sum_c k_r k_i e^{G_r - G_i}   (i < r)
@@ -16,14 +17,19 @@
 //      W = (I + A)^-1 Diag(beta)(K * e^G),  U = (I + A)^-1 Diag(beta) V
 //      Q+ = Q * e^G,  K~ = K * e^{G_C - G},  e^{G_C}
 //    A and Aqk are 16x16 sub-block products on the matrix cores (bf16 pieces,
-//    see mfma.h: two for bf16 inputs, three for fp32 inputs).
-//    A sub-block pair (rows in block R, columns in block I <= R) uses the
-//    reference point "end of block I-1": row factor e^{G_r - ref} <= 1 and
-//    column factor e^{ref - G_i} = e^{-P_i} <= e^{80} (P = in-block prefix
-//    sum, each g >= -5), both finite in fp32; every exponent is a short sum.
-//    W and U come from fp32 forward substitution: a lane owns one column of
-//    [beta K+ | beta V] in registers and eliminates row by row against A.
+//    see mfma.h: two for bf16 inputs, three for fp32 inputs).  A sub-block
+//    pair (rows in block R, columns in block I <= R) uses the reference point
+//    "end of block I-1": row factor e^{G_r - ref} <= 1 and column factor
+//    e^{ref - G_i} = e^{-P_i} <= e^{80} (P = in-block prefix sum, each
+//    g >= -5), both finite in fp32; every exponent is a short sum.
+//    W and U solve (I + A) X = [beta K+ | beta V] block-row by block-row on
+//    the matrix cores: X_R = T_R (B_R - A_{R,<R} X_{<R}) with T_R the inverse
+//    of the unit lower-triangular 16x16 diagonal block (I + A_RR), found by a
+//    short fp32 substitution.
 // The results are written as one Record per (chunk, head).
+//
+// Eight waves: lane t has role t / D (q, k, v, alpha) and channel t % D, so
+// every conv task is one lane's, and each SIMD interleaves two waves.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "mfma.h"
@@ -31,6 +37,8 @@
 namespace kda {
 
 namespace {
+
+constexpr int kPrepThreads = 512;
 
 __device__ __forceinline__ int pair_index(int I, int R) {
   // (I, R) with I < R: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
@@ -40,18 +48,24 @@ __device__ __forceinline__ int pair_index(int I, int R) {
 }  // namespace
 
 template <int D, bool IO_BF16>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t, PrefillIO io, uint8_t* records) {
-  constexpr int NT = 256;
+__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, ChunkTable t, PrefillIO io,
+                                                                  uint8_t* records) {
+  constexpr int NT = kPrepThreads;
   constexpr int LDR = D + 4;                       // LDS row stride of the fp32 tiles
   constexpr int KP = D < 32 ? 32 : D;              // channel extent in whole 32-wide steps
-  constexpr int LA = 68;                           // row stride of A / Aqk in LDS (16-byte rows)
-  constexpr int VSZ = (64 * LDR > 2 * 64 * LA) ? 64 * LDR : 2 * 64 * LA;
+  constexpr int LA = 68;                           // row stride of A in LDS (16-byte rows)
+  constexpr int GSZ = (64 * LDR > 64 * LA) ? 64 * LDR : 64 * LA;
   constexpr Record REC = record_layout(D);
   constexpr int NP = IO_BF16 ? 2 : 3;              // bf16 pieces per operand
-  __shared__ __align__(16) float sQ[64 * LDR];    // q, then q e^{P}
-  __shared__ __align__(16) float sK[64 * LDR];    // k, then k e^{P}
-  __shared__ __align__(16) float sG[64 * LDR];    // g, then k e^{-P}
-  __shared__ __align__(16) float sV[VSZ];          // v, then A (I + A solve) and Aqk
+  constexpr int LX = kChunk + 4;                   // row stride of X^T in LDS
+  static_assert(2 * D * LX <= 3 * 64 * LDR, "X^T must fit where q, k and k e^{-P} were");
+  __shared__ __align__(16) float sBig[3 * 64 * LDR];
+  float* sQ = sBig;                                // q, then q e^{P}        (A row operand)
+  float* sK = sBig + 64 * LDR;                     // k, then k e^{P}        (A row operand)
+  float* sC = sBig + 2 * 64 * LDR;                 // k e^{-P}               (A column operand)
+  float* sX = sBig;                                // then X^T [2D][LX], the solve's columns
+  __shared__ __align__(16) float sG[GSZ];          // g, then A
+  __shared__ __align__(16) float sT[4][16][20];    // inverses of the diagonal blocks of I + A
   __shared__ __align__(16) float sE[6][D];         // e^{sum of block totals between I and R}
   __shared__ float sBeta[64];
 
@@ -65,53 +79,61 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
   const int64_t tok0 = static_cast<int64_t>(t.cu[s]) + tau0;
   const int len = min(kChunk, t.cu[s + 1] - static_cast<int>(tok0));
   const int tid = threadIdx.x;
+  const int role = tid / D, ch = tid % D;          // role 0 q, 1 k, 2 v, 3 alpha (4+ idle)
   const size_t HD = static_cast<size_t>(H) * D;
   const size_t Ctot = 3 * HD;
+  const size_t col = static_cast<size_t>(h) * D + ch;
   const uint32_t flags = p.flags;
   uint8_t* rec = records + (static_cast<size_t>(c) * H + h) * REC.bytes;
 
-  // ---- 1. conv + SiLU (q, k, v) and gate, one channel per task
-  const float a_exp = expf(p.A_log[h]);
-  for (int task = tid; task < 4 * D; task += NT) {
-    const int grp = task / D, ch = task % D;
-    const size_t col = static_cast<size_t>(h) * D + ch;
-    if (grp < 3) {
-      const void* x = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
-      const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
-      float* dst = grp == 0 ? sQ : (grp == 1 ? sK : sV);
-      const float w0 = ld<IO_BF16>(w, col * 4), w1 = ld<IO_BF16>(w, col * 4 + 1);
-      const float w2 = ld<IO_BF16>(w, col * 4 + 2), w3 = ld<IO_BF16>(w, col * 4 + 3);
-      float hm[3];
+  // ---- 1. conv + SiLU (q, k, v) or gate (alpha): one channel per lane
+  float x[kChunk];   // v lanes: v, then beta v;  k lanes: beta K+  (columns of the solve)
+  if (role < 3) {
+    const void* xin = role == 0 ? io.q : (role == 1 ? io.k : io.v);
+    const void* w = role == 0 ? p.wq : (role == 1 ? p.wk : p.wv);
+    const float w0 = ld<IO_BF16>(w, col * 4), w1 = ld<IO_BF16>(w, col * 4 + 1);
+    const float w2 = ld<IO_BF16>(w, col * 4 + 2), w3 = ld<IO_BF16>(w, col * 4 + 3);
+    float hm[3];
 #pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int tau = tau0 - 3 + m;
-        if (tau >= 0) hm[m] = ld<IO_BF16>(x, static_cast<size_t>(t.cu[s] + tau) * HD + col);
-        else if (io.conv_in) hm[m] = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(s) * 3 + (3 + tau)) * Ctot + grp * HD + col);
-        else hm[m] = 0.f;
-      }
-      float xr[kChunk];   // all loads of the channel in flight at once
+    for (int m = 0; m < 3; ++m) {
+      const int tau = tau0 - 3 + m;
+      if (tau >= 0) hm[m] = ld<IO_BF16>(xin, static_cast<size_t>(t.cu[s] + tau) * HD + col);
+      else if (io.conv_in) hm[m] = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(s) * 3 + (3 + tau)) * Ctot + role * HD + col);
+      else hm[m] = 0.f;
+    }
 #pragma unroll
-      for (int r = 0; r < kChunk; ++r)   // rows past the chunk's end re-read its last row (no branch)
-        xr[r] = ld<IO_BF16>(x, static_cast<size_t>(tok0 + min(r, len - 1)) * HD + col);
-      float h3 = hm[0], h2 = hm[1], h1 = hm[2];
+    for (int r = 0; r < kChunk; ++r)   // rows past the chunk's end re-read its last row (no branch)
+      x[r] = ld<IO_BF16>(xin, static_cast<size_t>(tok0 + min(r, len - 1)) * HD + col);
+    // the conv of every row is independent once its inputs are loaded; no
+    // branch inside the row loops, so rows overlap in the pipeline
+    const bool raw = flags & KDA_FLAG_SKIP_CONV;
+    auto conv_row = [&](int r) {
+      const float xm3 = r >= 3 ? x[r - 3] : hm[r], xm2 = r >= 2 ? x[r - 2] : hm[r + 1];
+      const float xm1 = r >= 1 ? x[r - 1] : hm[2], xt = x[r];
+      const float u = raw ? xt : siluf_(w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xt);
+      return r < len ? u : 0.f;
+    };
+    if (role < 2) {
+      float* dst = role == 0 ? sQ : sK;
 #pragma unroll
-      for (int r = 0; r < kChunk; ++r) {
-        const float xt = xr[r];
-        float u = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h3 + w1 * h2 + w2 * h1 + w3 * xt);
-        u = r < len ? u : 0.f;
-        h3 = h2; h2 = h1; h1 = xt;
-        dst[r * LDR + ch] = u;
-      }
+      for (int r = 0; r < kChunk; ++r) dst[r * LDR + ch] = conv_row(r);
     } else {
-      const float dtb = p.dt_bias[col];
-      float ar[kChunk];
+      float u[kChunk];
 #pragma unroll
-      for (int r = 0; r < kChunk; ++r) ar[r] = ld<IO_BF16>(io.alpha, static_cast<size_t>(tok0 + min(r, len - 1)) * HD + col);
+      for (int r = 0; r < kChunk; ++r) u[r] = conv_row(r);
 #pragma unroll
-      for (int r = 0; r < kChunk; ++r) {
-        float g = (flags & KDA_FLAG_RAW_GATE) ? ar[r] : gate_value(ar[r], dtb, a_exp, p.lower_bound);
-        sG[r * LDR + ch] = r < len ? g : 0.f;
-      }
+      for (int r = 0; r < kChunk; ++r) x[r] = u[r];
+    }
+  } else if (role == 3) {
+    const float a_exp = expf(p.A_log[h]);
+    const float dtb = p.dt_bias[col];
+    float ar[kChunk];
+#pragma unroll
+    for (int r = 0; r < kChunk; ++r) ar[r] = ld<IO_BF16>(io.alpha, static_cast<size_t>(tok0 + min(r, len - 1)) * HD + col);
+#pragma unroll
+    for (int r = 0; r < kChunk; ++r) {
+      const float g = (flags & KDA_FLAG_RAW_GATE) ? ar[r] : gate_value(ar[r], dtb, a_exp, p.lower_bound);
+      sG[r * LDR + ch] = r < len ? g : 0.f;
     }
   }
   if (tid < kChunk) {
@@ -125,10 +147,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
   }
   __syncthreads();
 
-  // ---- L2 norms of q and k: four lanes per token
+  // ---- L2 norms of q and k: eight lanes per token
   {
-    constexpr int CPP = D / 4;
-    const int r = tid >> 2, part = tid & 3;
+    constexpr int CPP = D / 8;
+    const int r = tid >> 3, part = tid & 7;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int i = 0; i < CPP; ++i) {
@@ -136,8 +158,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
       sq += a * a;
       sk += b * b;
     }
-    sq = group_sum<4>(sq);
-    sk = group_sum<4>(sk);
+    sq = group_sum<8>(sq);
+    sk = group_sum<8>(sk);
     const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
     const float iq = (norm ? 1.0f / sqrtf(sq + p.eps) : 1.0f) * p.scale;
     const float ik = norm ? 1.0f / sqrtf(sk + p.eps) : 1.0f;
@@ -149,87 +171,101 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
   }
   __syncthreads();
 
-  // ---- 2a. per-channel decays (channel owners) and right-hand sides
-  float x[kChunk];   // this lane's column of [beta K+ | beta V]
-  if (tid < D) {
-    const int ch = tid;
-    float gc[kChunk], kc[kChunk];
+  // ---- 2a. per-channel decays: q lanes and k lanes each rebuild the
+  //      in-block prefix sums P of their channel from g; e^{G_r} is formed as
+  //      e^{P_r} times the earlier block factors (one rounding per factor)
+  if (role < 2) {
+    float gc[kChunk];
 #pragma unroll
-    for (int r = 0; r < kChunk; ++r) { gc[r] = sG[r * LDR + ch]; kc[r] = sK[r * LDR + ch]; }
-    float Bt[4];
+    for (int r = 0; r < kChunk; ++r) gc[r] = sG[r * LDR + ch];
+    float Bt[4], eBt[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       float sum = 0.f;
 #pragma unroll
       for (int m = 0; m < kSub; ++m) sum += gc[J * kSub + m];
       Bt[J] = sum;
+      eBt[J] = exp_precise(sum);
     }
-    float* Qp = reinterpret_cast<float*>(rec + REC.Qp);
-    // e^{G_r} = e^{P_r} * e^{sum of earlier block totals}: products of factors
-    // that each carry one rounding, never exponentials of long sums
-    float eBt[4];
+    if (role == 0) {
+      float* Qp = reinterpret_cast<float*>(rec + REC.Qp);
+      float eBefore = 1.f;
 #pragma unroll
-    for (int J = 0; J < 4; ++J) eBt[J] = expf(Bt[J]);
-    float eBefore = 1.f;
+      for (int J = 0; J < 4; ++J) {
+        float P = 0.f;
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      float P = 0.f;
-#pragma unroll
-      for (int m = 0; m < kSub; ++m) {
-        const int r = J * kSub + m;
-        P += gc[r];
-        const float eP = expf(P);
-        const float qv = sQ[r * LDR + ch];
-        sK[r * LDR + ch] = kc[r] * eP;
-        sQ[r * LDR + ch] = qv * eP;
-        sG[r * LDR + ch] = kc[r] / eP;
-        const float eG = eP * eBefore;
-        Qp[r * D + ch] = qv * eG;
-        x[r] = sBeta[r] * kc[r] * eG;
-      }
-      eBefore *= eBt[J];
-    }
-    // K~^T row of this channel: k e^{Q_r + later block totals}, Q_r = in-block
-    // sum of g after token r; built backwards, 4 tokens per 16-byte store
-    float4* KT = reinterpret_cast<float4*>(rec + REC.KT) + ch * (kChunk / 4);
-    {
-      float after = 0.f, Qs = 0.f, tmp[4];
-#pragma unroll
-      for (int r = kChunk - 1; r >= 0; --r) {
-        if (r % kSub == kSub - 1) {
-          Qs = 0.f;
-          if (r < kChunk - 1) after += Bt[(r + 1) / kSub];
+        for (int m = 0; m < kSub; ++m) {
+          const int r = J * kSub + m;
+          P += gc[r];
+          const float eP = exp_precise(P);
+          const float qv = sQ[r * LDR + ch];
+          sQ[r * LDR + ch] = qv * eP;
+          Qp[r * D + ch] = qv * (eP * eBefore);
         }
-        tmp[r % 4] = kc[r] * expf(Qs + after);
-        Qs += gc[r];
-        if (r % 4 == 0) KT[r / 4] = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        eBefore *= eBt[J];
       }
-    }
-    reinterpret_cast<float*>(rec + REC.eGC)[ch] = eBefore;
-    sE[0][ch] = eBt[0];
-    sE[1][ch] = eBt[0] * eBt[1];
-    sE[2][ch] = eBt[0] * eBt[1] * eBt[2];
-    sE[3][ch] = eBt[1];
-    sE[4][ch] = eBt[1] * eBt[2];
-    sE[5][ch] = eBt[2];
-  } else if (tid >= 128 && tid < 128 + D) {
-    const int ch = tid - 128;
+    } else {
+      // K~^T row of this channel first, from the still unscaled k:
+      // k e^{Q_r + later block totals}, Q_r = in-block sum of g after token r;
+      // built backwards, 4 tokens per 16-byte store
+      float4* KT = reinterpret_cast<float4*>(rec + REC.KT) + ch * (kChunk / 4);
+      {
+        float after = 0.f, Qs = 0.f, tmp[4];
 #pragma unroll
-    for (int r = 0; r < kChunk; ++r) x[r] = sBeta[r] * sV[r * LDR + ch];
+        for (int r = kChunk - 1; r >= 0; --r) {
+          if (r % kSub == kSub - 1) {
+            Qs = 0.f;
+            if (r < kChunk - 1) after += Bt[(r + 1) / kSub];
+          }
+          tmp[r % 4] = sK[r * LDR + ch] * exp_precise(Qs + after);
+          Qs += gc[r];
+          if (r % 4 == 0) KT[r / 4] = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        }
+      }
+      float eBefore = 1.f;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        float P = 0.f;
+#pragma unroll
+        for (int m = 0; m < kSub; ++m) {
+          const int r = J * kSub + m;
+          P += gc[r];
+          const float eP = exp_precise(P);
+          const float kv = sK[r * LDR + ch];
+          sK[r * LDR + ch] = kv * eP;
+          sC[r * LDR + ch] = kv * rcp_fast(eP);
+          x[r] = sBeta[r] * kv * (eP * eBefore);
+        }
+        eBefore *= eBt[J];
+      }
+      reinterpret_cast<float*>(rec + REC.eGC)[ch] = eBefore;
+      sE[0][ch] = eBt[0];
+      sE[1][ch] = eBt[0] * eBt[1];
+      sE[2][ch] = eBt[0] * eBt[1] * eBt[2];
+      sE[3][ch] = eBt[1];
+      sE[4][ch] = eBt[1] * eBt[2];
+      sE[5][ch] = eBt[2];
+    }
+  } else if (role == 2) {
+#pragma unroll
+    for (int r = 0; r < kChunk; ++r) x[r] = sBeta[r] * x[r];
   }
   __syncthreads();
 
   // ---- 2b. A and Aqk, one 16x16 sub-block per task on the matrix cores
-  float* sA = sV;                 // [64][LA]  A (strictly lower, rows scaled by beta)
-  float* sAqk = sV + 64 * LA;     // [64][LA]  Aqk (lower, with diagonal)
+  float* sA = sG;    // [64][LA]  A (strictly lower, rows scaled by beta); g is consumed
   {
     const int wave = tid / kWave, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
+    float* Aq = reinterpret_cast<float*>(rec + REC.Aqk);
     for (int task = wave; task < 32; task += NT / kWave) {
       const int mat = task >> 4, R = (task >> 2) & 3, I = task & 3;
-      float* dst = mat == 0 ? sA : sAqk;
       if (I > R) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[(16 * R + 4 * q4 + j) * LA + 16 * I + ln] = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * R + 4 * q4 + j, i = 16 * I + ln;
+          if (mat == 0) sA[r * LA + i] = 0.f;
+          else Aq[r * kChunk + i] = 0.f;
+        }
         continue;
       }
       const float* rows = mat == 0 ? sK : sQ;
@@ -241,7 +277,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
         float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (ch0 < D) {   // eight whole channels (dk >= 16 is a multiple of 8)
           const float4* ra = reinterpret_cast<const float4*>(&rows[(16 * R + ln) * LDR + ch0]);
-          const float4* cb = reinterpret_cast<const float4*>(&sG[(16 * I + ln) * LDR + ch0]);
+          const float4* cb = reinterpret_cast<const float4*>(&sC[(16 * I + ln) * LDR + ch0]);
           const float4 a0 = ra[0], a1 = ra[1], b0 = cb[0], b1 = cb[1];
           a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
           b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
@@ -257,44 +293,112 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(Params p, ChunkTable t,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * R + 4 * q4 + j, i = 16 * I + ln;
-        if (mat == 0) dst[r * LA + i] = (i < r) ? sBeta[r] * acc[j] : 0.f;
-        else dst[r * LA + i] = (i <= r) ? acc[j] : 0.f;
+        if (mat == 0) sA[r * LA + i] = (i < r) ? sBeta[r] * acc[j] : 0.f;
+        else Aq[r * kChunk + i] = (i <= r) ? acc[j] : 0.f;
       }
     }
   }
   __syncthreads();
 
-  // ---- 2c. forward substitution: x_r -= sum_{i<r} A[r,i] x_i
-  if (tid < D || (tid >= 128 && tid < 128 + D)) {
+  // ---- 2c. solve (I + A) X = B = [beta K+ | beta V] by 16-row blocks.
+  //      The column owners publish B^T; wave 0 inverts the four unit
+  //      lower-triangular diagonal blocks (fp32 substitution, lane = column).
+  if (role == 1 || role == 2) {
+    float4* xr = reinterpret_cast<float4*>(&sX[((role == 1 ? 0 : D) + ch) * LX]);
 #pragma unroll
-    for (int r = 1; r < kChunk; ++r) {
-      // four independent partial sums over i (rows of A read 4 at a time)
-      float a4[4] = {x[r], 0.f, 0.f, 0.f};
+    for (int v4 = 0; v4 < kChunk / 4; ++v4) xr[v4] = make_float4(x[4 * v4], x[4 * v4 + 1], x[4 * v4 + 2], x[4 * v4 + 3]);
+  }
+  if (tid < 64) {
+    const int R = tid >> 4, j = tid & 15;
+    float tcol[16];
 #pragma unroll
-      for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-        const float4 av = *reinterpret_cast<const float4*>(&sA[r * LA + 4 * i4]);
-        const float aa[4] = {av.x, av.y, av.z, av.w};
+    for (int i = 0; i < 16; ++i) {
+      float v = (i == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (4 * i4 + j < r) a4[j] -= aa[j] * x[4 * i4 + j];
-      }
-      x[r] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+      for (int m = 0; m < i; ++m) v -= sA[(16 * R + i) * LA + 16 * R + m] * tcol[m];
+      tcol[i] = (i < j) ? 0.f : v;
     }
-    if (tid < D) {
-      float* W = reinterpret_cast<float*>(rec + REC.W);
 #pragma unroll
-      for (int r = 0; r < kChunk; ++r) W[r * D + tid] = x[r];
-    } else {
-      float4* UT = reinterpret_cast<float4*>(rec + REC.UT) + (tid - 128) * (kChunk / 4);
+    for (int i = 0; i < 16; ++i) sT[R][i][j] = tcol[i];
+  }
+  __syncthreads();
+  {
+    // wave w owns 16-column blocks w, w + 8 of X (2D columns in all); every
+    // barrier below is outside the per-wave loops
+    constexpr int NCB = 2 * D / 16;
+    constexpr int CBPW = (NCB + NT / kWave - 1) / (NT / kWave);
+    const int wave = tid / kWave, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
 #pragma unroll
-      for (int v4 = 0; v4 < kChunk / 4; ++v4) UT[v4] = make_float4(x[4 * v4], x[4 * v4 + 1], x[4 * v4 + 2], x[4 * v4 + 3]);
+    for (int R = 0; R < 4; ++R) {
+      // Y = B_R - A_{R,<R} X_{<R}, written back over B_R
+#pragma unroll
+      for (int bi = 0; bi < CBPW; ++bi) {
+        const int cb = wave + bi * (NT / kWave);
+        if (cb >= NCB) continue;
+        float* xc = &sX[(16 * cb + ln) * LX];
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < (R + 1) / 2; ++ks) {
+          const int i0 = 32 * ks + 8 * q4;
+          const float4 a0 = *reinterpret_cast<const float4*>(&sA[(16 * R + ln) * LA + i0]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&sA[(16 * R + ln) * LA + i0 + 4]);
+          const float4 b0 = *reinterpret_cast<const float4*>(&xc[i0]);
+          const float4 b1 = *reinterpret_cast<const float4*>(&xc[i0 + 4]);
+          const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          float a[8], xb[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const bool in = i0 + i < 16 * R;          // only the finished blocks I < R
+            a[i] = in ? av[i] : 0.f;
+            xb[i] = in ? bv[i] : 0.f;
+          }
+          acc = mfmaN<NP>(splitN<NP>(a), splitN<NP>(xb), acc);
+        }
+        float4* yr = reinterpret_cast<float4*>(&xc[16 * R + 4 * q4]);
+        const float4 bR = *yr;
+        *yr = make_float4(bR.x - acc[0], bR.y - acc[1], bR.z - acc[2], bR.w - acc[3]);
+      }
+      __syncthreads();
+      // X_R = T_R Y  (K = 16: lanes of the upper half-wave contribute zeros)
+      f32x4 xr[CBPW];
+#pragma unroll
+      for (int bi = 0; bi < CBPW; ++bi) {
+        const int cb = wave + bi * (NT / kWave);
+        if (cb >= NCB) continue;
+        const float* xc = &sX[(16 * cb + ln) * LX];
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, yb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (q4 < 2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            a[i] = sT[R][ln][8 * q4 + i];
+            yb[i] = xc[16 * R + 8 * q4 + i];
+          }
+        }
+        xr[bi] = mfmaN<NP>(splitN<NP>(a), splitN<NP>(yb), zero4());
+      }
+      __syncthreads();
+#pragma unroll
+      for (int bi = 0; bi < CBPW; ++bi) {
+        const int cb = wave + bi * (NT / kWave);
+        if (cb >= NCB) continue;
+        *reinterpret_cast<float4*>(&sX[(16 * cb + ln) * LX + 16 * R + 4 * q4]) =
+            make_float4(xr[bi][0], xr[bi][1], xr[bi][2], xr[bi][3]);
+      }
+      __syncthreads();
     }
   }
+  // W token-major and U^T channel-major from X^T
   {
-    float4* Aq = reinterpret_cast<float4*>(rec + REC.Aqk);
-    for (int e = tid; e < kChunk * kChunk / 4; e += NT) {
-      const int r = (4 * e) / kChunk, i = (4 * e) % kChunk;
-      Aq[e] = *reinterpret_cast<const float4*>(&sAqk[r * LA + i]);
+    float* W = reinterpret_cast<float*>(rec + REC.W);
+    for (int e = tid; e < kChunk * D; e += NT) {
+      const int r = e / D, cc = e % D;
+      W[e] = sX[cc * LX + r];
+    }
+    float4* UT = reinterpret_cast<float4*>(rec + REC.UT);
+    for (int e = tid; e < D * kChunk / 4; e += NT) {
+      const int cc = e / (kChunk / 4), v4 = e % (kChunk / 4);
+      UT[e] = *reinterpret_cast<const float4*>(&sX[(D + cc) * LX + 4 * v4]);
     }
   }
 }
@@ -303,8 +407,8 @@ template <int D>
 static hipError_t launch_prep_d(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                                 int max_chunks, bool io_bf16, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.H), static_cast<unsigned>(max_chunks));
-  if (io_bf16) chunk_prep_kernel<D, true><<<grid, 256, 0, st>>>(p, t, io, records);
-  else chunk_prep_kernel<D, false><<<grid, 256, 0, st>>>(p, t, io, records);
+  if (io_bf16) chunk_prep_kernel<D, true><<<grid, kPrepThreads, 0, st>>>(p, t, io, records);
+  else chunk_prep_kernel<D, false><<<grid, kPrepThreads, 0, st>>>(p, t, io, records);
   return hipGetLastError();
 }
 

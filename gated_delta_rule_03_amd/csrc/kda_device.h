@@ -54,12 +54,37 @@ __device__ __forceinline__ void st2(void* p, size_t i, float2 x) {
   }
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// e^x through the hardware base-2 exponential (v_exp_f32): a few ulp, no
+// range-reduction sequence.  Underflows to 0 below about -87.
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-// log(1 + e^x) without overflow: max(x, 0) + log1p(e^-|x|).
-__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))); }
+// e^x to about 2 ulp over the whole fp32 range: the rounding residual of
+// x * log2(e) is carried to first order instead of being lost (it reaches
+// ~5e-6 relative for |x| ~ 80, the span of a 16-token decay sub-block).
+__device__ __forceinline__ float exp_precise(float x) {
+  constexpr float kLog2e = 1.4426950408889634f;           // fp32 rounding of log2(e)
+  constexpr float kLog2eLo = 1.925963033500011e-08f;      // log2(e) - kLog2e
+  const float t = x * kLog2e;
+  const float r = fmaf(x, kLog2e, -t) + x * kLog2eLo;
+  return __builtin_amdgcn_exp2f(t) * fmaf(r, 0.6931471805599453f, 1.0f);
+}
 
-__device__ __forceinline__ float siluf_(float y) { return y / (1.0f + expf(-y)); }
+// 1/x through the hardware reciprocal (v_rcp_f32, 1 ulp).
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return rcp_fast(1.0f + exp_fast(-x)); }
+
+// log(1 + e^x) without overflow: max(x, 0) + log(1 + e^-|x|), the second
+// term through the hardware base-2 logarithm (v_log_f32).  Its absolute
+// error is ~1e-7, which is all that matters here: the result enters the gate
+// additively.
+__device__ __forceinline__ float softplusf_(float x) {
+  return fmaxf(x, 0.0f) + __builtin_amdgcn_logf(1.0f + exp_fast(-fabsf(x))) * 0.6931471805599453f;
+}
+
+// y * sigmoid(y); for y below about -87 the exponential overflows and the
+// reciprocal gives 0, the correct limit.
+__device__ __forceinline__ float siluf_(float y) { return y * rcp_fast(1.0f + exp_fast(-y)); }
 
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
