@@ -284,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (to scale HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA core has no cross-GPU path here (asked for --gpus {args.gpus})",
@@ -296,6 +298,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ev = HipEvents()
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     B, T = 4, 32768
     dp, wall, gpu_ms, per_stage = bench_prefill(kda, torch, ev, args.steps, args.warmup)
     ms_step = wall / args.steps * 1e3

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
   constexpr int KP = D < 32 ? 32 : D;              // channel extent in whole 32-wide steps
   constexpr int LA = 68;                           // row stride of A in LDS (16-byte rows)
   constexpr int GSZ = (64 * LDR > 64 * LA) ? 64 * LDR : 64 * LA;
-  constexpr Record REC = record_layout(D);
   constexpr int NP = IO_BF16 ? 2 : 3;              // bf16 pieces per operand
+  constexpr Record REC = record_layout(D, NP);
   constexpr int LX = kChunk + 4;                   // row stride of X^T in LDS
   static_assert(2 * D * LX <= 3 * 64 * LDR, "X^T must fit where q, k and k e^{-P} were");
   __shared__ __align__(16) float sBig[3 * 64 * LDR];
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
       eBt[J] = exp_precise(sum);
     }
     if (role == 0) {
-      float* Qp = reinterpret_cast<float*>(rec + REC.Qp);
+      __bf16* Qp = reinterpret_cast<__bf16*>(rec + REC.Qp);
       float eBefore = 1.f;
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
@@ -200,26 +200,34 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
           const float eP = exp_precise(P);
           const float qv = sQ[r * LDR + ch];
           sQ[r * LDR + ch] = qv * eP;
-          Qp[r * D + ch] = qv * (eP * eBefore);
+          __bf16 pc[NP];
+          split_pieces<NP>(qv * (eP * eBefore), pc);
+#pragma unroll
+          for (int k = 0; k < NP; ++k) Qp[k * (REC.tile_plane / 2) + r * D + ch] = pc[k];
         }
         eBefore *= eBt[J];
       }
     } else {
       // K~^T row of this channel first, from the still unscaled k:
       // k e^{Q_r + later block totals}, Q_r = in-block sum of g after token r;
-      // built backwards, 4 tokens per 16-byte store
-      float4* KT = reinterpret_cast<float4*>(rec + REC.KT) + ch * (kChunk / 4);
+      // built backwards
+      // (8 tokens per 16-byte store of each piece plane)
+      bf16x8* KT = reinterpret_cast<bf16x8*>(rec + REC.KT) + ch * (kChunk / 8);
       {
-        float after = 0.f, Qs = 0.f, tmp[4];
+        float after = 0.f, Qs = 0.f, tmp[8];
 #pragma unroll
         for (int r = kChunk - 1; r >= 0; --r) {
           if (r % kSub == kSub - 1) {
             Qs = 0.f;
             if (r < kChunk - 1) after += Bt[(r + 1) / kSub];
           }
-          tmp[r % 4] = sK[r * LDR + ch] * exp_precise(Qs + after);
+          tmp[r % 8] = sK[r * LDR + ch] * exp_precise(Qs + after);
           Qs += gc[r];
-          if (r % 4 == 0) KT[r / 4] = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+          if (r % 8 == 0) {
+            const SplitN<NP> sp = splitN<NP>(tmp);
+#pragma unroll
+            for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 16) + r / 8] = sp.v[k];
+          }
         }
       }
       float eBefore = 1.f;
@@ -256,15 +264,19 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
   float* sA = sG;    // [64][LA]  A (strictly lower, rows scaled by beta); g is consumed
   {
     const int wave = tid / kWave, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
-    float* Aq = reinterpret_cast<float*>(rec + REC.Aqk);
+    __bf16* Aq = reinterpret_cast<__bf16*>(rec + REC.Aqk);
     for (int task = wave; task < 32; task += NT / kWave) {
       const int mat = task >> 4, R = (task >> 2) & 3, I = task & 3;
       if (I > R) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * R + 4 * q4 + j, i = 16 * I + ln;
-          if (mat == 0) sA[r * LA + i] = 0.f;
-          else Aq[r * kChunk + i] = 0.f;
+          if (mat == 0) {
+            sA[r * LA + i] = 0.f;
+          } else {
+#pragma unroll
+            for (int k = 0; k < NP; ++k) Aq[k * (REC.aqk_plane / 2) + r * kChunk + i] = static_cast<__bf16>(0.f);
+          }
         }
         continue;
       }
@@ -293,8 +305,14 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * R + 4 * q4 + j, i = 16 * I + ln;
-        if (mat == 0) sA[r * LA + i] = (i < r) ? sBeta[r] * acc[j] : 0.f;
-        else Aq[r * kChunk + i] = (i <= r) ? acc[j] : 0.f;
+        if (mat == 0) {
+          sA[r * LA + i] = (i < r) ? sBeta[r] * acc[j] : 0.f;
+        } else {
+          __bf16 pc[NP];
+          split_pieces<NP>((i <= r) ? acc[j] : 0.f, pc);
+#pragma unroll
+          for (int k = 0; k < NP; ++k) Aq[k * (REC.aqk_plane / 2) + r * kChunk + i] = pc[k];
+        }
       }
     }
   }
@@ -390,10 +408,13 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
   }
   // W token-major and U^T channel-major from X^T
   {
-    float* W = reinterpret_cast<float*>(rec + REC.W);
+    __bf16* W = reinterpret_cast<__bf16*>(rec + REC.W);
     for (int e = tid; e < kChunk * D; e += NT) {
       const int r = e / D, cc = e % D;
-      W[e] = sX[cc * LX + r];
+      __bf16 pc[NP];
+      split_pieces<NP>(sX[cc * LX + r], pc);
+#pragma unroll
+      for (int k = 0; k < NP; ++k) W[k * (REC.tile_plane / 2) + e] = pc[k];
     }
     float4* UT = reinterpret_cast<float4*>(rec + REC.UT);
     for (int e = tid; e < D * kChunk / 4; e += NT) {

@@ -25,29 +25,34 @@
 
 namespace kda {
 
-// One wave's record operands for one chunk, raw fp32, so that the next
-// chunk's loads are in flight while the current chunk computes.
-template <int D, int DVT>
+// One wave's record operands for one chunk, already split into bf16 pieces,
+// so that the next chunk's loads are in flight while the current computes.
+template <int D, int DVT, int NP>
 struct WaveOps {
   static constexpr int KS = (D < 32 ? 32 : D) / 32;
   static constexpr int CJ = DVT / 16;
   static constexpr int CBW = (D / 16 + 3) / 4;
-  float4 w[KS][2], q[KS][2];     // W, Q+ rows of this wave's tokens
+  SplitN<NP> w[KS], q[KS];       // W, Q+ rows of this wave's tokens
   float4 u[CJ];                  // U^T, four tokens of one value column
-  float4 a[2][2];                // Aqk rows (two 32-token steps)
-  float4 kt[CBW][2][2];          // K~^T rows of this wave's state rows
+  SplitN<NP> a[2];               // Aqk rows (two 32-token steps)
+  SplitN<NP> kt[CBW][2];         // K~^T rows of this wave's state rows
   float4 e[CBW];                 // e^{G_C} of this lane's four state rows
 };
 
-template <int D, int DVT>
-__device__ __forceinline__ void load_ops(WaveOps<D, DVT>& o, const uint8_t* rec, int wave, int ln, int q4, int j0,
+template <int NP>
+__device__ __forceinline__ SplitN<NP> load_planes(const uint8_t* base, size_t plane_bytes, size_t elem) {
+  SplitN<NP> s;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) s.v[k] = load_bf16x8(base + k * plane_bytes + elem * 2);
+  return s;
+}
+
+template <int D, int DVT, int NP>
+__device__ __forceinline__ void load_ops(WaveOps<D, DVT, NP>& o, const uint8_t* rec, int wave, int ln, int q4, int j0,
                                          int nks_a) {
-  constexpr Record REC = record_layout(D);
-  constexpr int KS = WaveOps<D, DVT>::KS, CJ = WaveOps<D, DVT>::CJ, CBW = WaveOps<D, DVT>::CBW, CB = D / 16;
-  const float* Wr = reinterpret_cast<const float*>(rec + REC.W);
-  const float* Qr = reinterpret_cast<const float*>(rec + REC.Qp);
-  const float* KTr = reinterpret_cast<const float*>(rec + REC.KT);
-  const float* Ar = reinterpret_cast<const float*>(rec + REC.Aqk);
+  constexpr Record REC = record_layout(D, NP);
+  using Ops = WaveOps<D, DVT, NP>;
+  constexpr int KS = Ops::KS, CJ = Ops::CJ, CBW = Ops::CBW, CB = D / 16;
   const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
   const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
   const int r0 = 16 * wave;
@@ -55,42 +60,31 @@ __device__ __forceinline__ void load_ops(WaveOps<D, DVT>& o, const uint8_t* rec,
   for (int ks = 0; ks < KS; ++ks) {
     const int ch0 = 32 * ks + 8 * q4;
     if (ch0 < D) {
-      const float4* pw = reinterpret_cast<const float4*>(Wr + static_cast<size_t>(r0 + ln) * D + ch0);
-      const float4* pq = reinterpret_cast<const float4*>(Qr + static_cast<size_t>(r0 + ln) * D + ch0);
-      o.w[ks][0] = pw[0]; o.w[ks][1] = pw[1];
-      o.q[ks][0] = pq[0]; o.q[ks][1] = pq[1];
+      const size_t el = static_cast<size_t>(r0 + ln) * D + ch0;
+      o.w[ks] = load_planes<NP>(rec + REC.W, REC.tile_plane, el);
+      o.q[ks] = load_planes<NP>(rec + REC.Qp, REC.tile_plane, el);
     } else {
-      o.w[ks][0] = o.w[ks][1] = o.q[ks][0] = o.q[ks][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      o.w[ks] = o.q[ks] = zero_split<NP>();
     }
   }
 #pragma unroll
   for (int cj = 0; cj < CJ; ++cj)
     o.u[cj] = *reinterpret_cast<const float4*>(UT + static_cast<size_t>(j0 + 16 * cj + ln) * kChunk + r0 + 4 * q4);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if (ks < nks_a) {
-      const float4* pa = reinterpret_cast<const float4*>(Ar + static_cast<size_t>(r0 + ln) * kChunk + 32 * ks + 8 * q4);
-      o.a[ks][0] = pa[0]; o.a[ks][1] = pa[1];
-    }
-  }
+  for (int ks = 0; ks < 2; ++ks)
+    if (ks < nks_a)
+      o.a[ks] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, static_cast<size_t>(r0 + ln) * kChunk + 32 * ks + 8 * q4);
 #pragma unroll
   for (int i = 0; i < CBW; ++i) {
     const int cb = wave + 4 * i;
     if (cb < CB) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const float4* pk = reinterpret_cast<const float4*>(KTr + static_cast<size_t>(16 * cb + ln) * kChunk + 32 * ks + 8 * q4);
-        o.kt[i][ks][0] = pk[0]; o.kt[i][ks][1] = pk[1];
-      }
+      for (int ks = 0; ks < 2; ++ks)
+        o.kt[i][ks] = load_planes<NP>(rec + REC.KT, REC.tile_plane,
+                                      static_cast<size_t>(16 * cb + ln) * kChunk + 32 * ks + 8 * q4);
       o.e[i] = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
     }
   }
-}
-
-template <int NP>
-__device__ __forceinline__ SplitN<NP> split_pair(const float4& a, const float4& b) {
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  return splitN<NP>(x);
 }
 
 template <int D, int DVT, int NP, bool OUT_BF16>
@@ -104,7 +98,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   constexpr int CBW = (CB + 3) / 4;       // state row blocks per wave
   constexpr int LST = KP + 8;             // row stride of S^T in LDS (bf16)
   constexpr int LDT = kChunk + 8;         // row stride of Delta^T in LDS (bf16)
-  constexpr Record REC = record_layout(D);
+  constexpr Record REC = record_layout(D, NP);
   __shared__ __align__(16) __bf16 sST[NP][DVT * LST];
   __shared__ __align__(16) __bf16 sDT[NP][DVT * LDT];
 
@@ -148,14 +142,17 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
       if (cb >= CB) continue;
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
+        bf16x4 pk[NP];   // the lane's four consecutive state rows, one 8-byte store per plane
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           __bf16 pc[NP];
           split_pieces<NP>(Sacc[i][cj][j], pc);
-          const int idx = (16 * cj + ln) * LST + 16 * cb + 4 * q4 + j;
 #pragma unroll
-          for (int k = 0; k < NP; ++k) sST[k][idx] = pc[k];
+          for (int k = 0; k < NP; ++k) pk[k][j] = pc[k];
         }
+        const int idx = (16 * cj + ln) * LST + 16 * cb + 4 * q4;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4*>(&sST[k][idx]) = pk[k];
       }
     }
   };
@@ -167,12 +164,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   const int seq_len = t.cu[s + 1] - t.cu[s];
   const int r0 = 16 * wave;                         // this wave's token rows
   const int nks_a = wave >= 2 ? 2 : 1;              // k steps of Aqk Delta (causal)
-  WaveOps<D, DVT> cur, nxt;
+  WaveOps<D, DVT, NP> cur, nxt;
   if (c_first < c_end)
-    load_ops<D, DVT>(cur, records + (static_cast<size_t>(c_first) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
+    load_ops<D, DVT, NP>(cur, records + (static_cast<size_t>(c_first) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
   for (int c = c_first; c < c_end; ++c) {
     if (c + 1 < c_end)
-      load_ops<D, DVT>(nxt, records + (static_cast<size_t>(c + 1) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
+      load_ops<D, DVT, NP>(nxt, records + (static_cast<size_t>(c + 1) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
     const int tau = (c - c_first) * kChunk;
     const int len = min(kChunk, seq_len - tau);
 
@@ -183,8 +180,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * q4;
-      const SplitN<NP> aW = split_pair<NP>(cur.w[ks][0], cur.w[ks][1]);
-      const SplitN<NP> aQ = split_pair<NP>(cur.q[ks][0], cur.q[ks][1]);
+      const SplitN<NP>& aW = cur.w[ks];
+      const SplitN<NP>& aQ = cur.q[ks];
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         SplitN<NP> bS;
@@ -199,14 +196,17 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
     for (int cj = 0; cj < CJ; ++cj) {
       const float4 u = cur.u[cj];
       const float dl[4] = {u.x - accW[cj][0], u.y - accW[cj][1], u.z - accW[cj][2], u.w - accW[cj][3]};
+      bf16x4 pk[NP];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         __bf16 pc[NP];
         split_pieces<NP>(dl[j], pc);
-        const int idx = (16 * cj + ln) * LDT + r0 + 4 * q4 + j;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) sDT[k][idx] = pc[k];
+        for (int k = 0; k < NP; ++k) pk[k][j] = pc[k];
       }
+      const int idx = (16 * cj + ln) * LDT + r0 + 4 * q4;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4*>(&sDT[k][idx]) = pk[k];
     }
     __syncthreads();
 
@@ -223,11 +223,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int t0 = 32 * ks + 8 * q4;
-      SplitN<NP> aA, aK[CBW];
-      if (ks < nks_a) aA = split_pair<NP>(cur.a[ks][0], cur.a[ks][1]);
-#pragma unroll
-      for (int i = 0; i < CBW; ++i)
-        if (wave + 4 * i < CB) aK[i] = split_pair<NP>(cur.kt[i][ks][0], cur.kt[i][ks][1]);
+      const SplitN<NP>& aA = cur.a[ks];
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         SplitN<NP> bD;
@@ -236,7 +232,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
         if (ks < nks_a) accQ[cj] = mfmaN<NP>(aA, bD, accQ[cj]);
 #pragma unroll
         for (int i = 0; i < CBW; ++i)
-          if (wave + 4 * i < CB) Sacc[i][cj] = mfmaN<NP>(aK[i], bD, Sacc[i][cj]);
+          if (wave + 4 * i < CB) Sacc[i][cj] = mfmaN<NP>(cur.kt[i][ks], bD, Sacc[i][cj]);
       }
     }
     // store this wave's output rows
@@ -270,6 +266,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 }
 
 // Value-tile width: the widest tile that still gives every CU a workgroup.
+// (Narrower tiles do not buy a second resident workgroup per CU: the
+// prefetched operands keep a wave near the register-file limit.)
 static int pick_dvt(int D, int n_sh) {
   for (int dvt : {64, 32, 16})
     if (dvt <= D && static_cast<long>(n_sh) * (D / dvt) >= 256) return dvt;

@@ -60,18 +60,21 @@ Params make_params(const kda_config_t* cfg) {
   return p;
 }
 
+// bf16 pieces per matrix operand: 2 for bf16 inputs, 3 for the all-fp32 path.
+int pieces(const kda_config_t* cfg) { return cfg->io_dtype == KDA_BF16 ? 2 : 3; }
+
 struct Layout {
   size_t cu, chunk0, chunk_seq, records, total;
 };
 
-Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D) {
+Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D, int NP) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   L.cu = take((N + 1) * sizeof(int32_t));
   L.chunk0 = take((N + 1) * sizeof(int32_t));
   L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
-  L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D)).bytes);
+  L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D), NP).bytes);
   L.total = off;
   return L;
 }
@@ -102,7 +105,7 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
                          const int32_t* cu_in, int32_t T_uniform, const PrefillIO& io, void* workspace,
                          hipStream_t st) {
   const Params p = make_params(cfg);
-  const Layout L = make_layout(N, max_chunks, p.H, p.D);
+  const Layout L = make_layout(N, max_chunks, p.H, p.D, pieces(cfg));
   char* ws = static_cast<char*>(workspace);
   int32_t* cu_ws = reinterpret_cast<int32_t*>(ws + L.cu);
   int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
@@ -151,12 +154,12 @@ size_t kda_prefill_workspace_bytes(const kda_config_t* cfg, int32_t B, int32_t T
   if (check_config(cfg, true) != KDA_OK || B < 0 || T < 0) return 0;
   const int64_t mc = chunks_uniform(B, T);
   if (static_cast<int64_t>(B) * T > INT32_MAX || mc > INT32_MAX) return 0;
-  return make_layout(B, mc, cfg->num_heads, cfg->head_k_dim).total;
+  return make_layout(B, mc, cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
 }
 
 size_t kda_varlen_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t total_T) {
   if (check_config(cfg, true) != KDA_OK || N < 0 || total_T < 0) return 0;
-  return make_layout(N, chunks_varlen(N, total_T), cfg->num_heads, cfg->head_k_dim).total;
+  return make_layout(N, chunks_varlen(N, total_T), cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
 }
 
 kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const void* q, const void* k, const void* v,
@@ -170,7 +173,7 @@ kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const vo
   if (B == 0) return KDA_OK;
   if (T > 0 && (!q || !k || !v || !alpha || !b || !o)) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t mc = chunks_uniform(B, T);
-  const size_t need = make_layout(B, mc, cfg->num_heads, cfg->head_k_dim).total;
+  const size_t need = make_layout(B, mc, cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};
@@ -190,7 +193,7 @@ kda_status_t kda_varlen_prefill(const kda_config_t* cfg, int32_t N, int32_t tota
   if (total_T > 0 && (!q || !k || !v || !alpha || !b || !o)) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t mc = chunks_varlen(N, total_T);
   if (mc > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  const size_t need = make_layout(N, mc, cfg->num_heads, cfg->head_k_dim).total;
+  const size_t need = make_layout(N, mc, cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};

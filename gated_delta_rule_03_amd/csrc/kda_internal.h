@@ -13,27 +13,33 @@ constexpr int kChunk = 64;   // tokens per chunk of the chunked form
 constexpr int kSub = 16;     // tokens per decay sub-block inside a chunk
 
 // Per (chunk, head) record written by the chunk-prep kernel and read by the
-// chunk-scan kernel: the operands of the state recurrence, fp32, in the
-// layouts the matrix-core operand loads read.  Byte offsets:
-//   W   [64][D]  W = (I + A)^-1 Diag(beta) (K * e^G), token-major
-//   Qp  [64][D]  Q+ = Q * e^G, token-major
-//   KT  [D][64]  K~^T = (K * e^{G_C - G})^T, channel-major
-//   Aqk [64][64] the masked intra-chunk attention, token-major
-//   UT  [D][64]  U^T = ((I + A)^-1 Diag(beta) V)^T
-//   eGC [D]      e^{G_C}, the whole-chunk decay
+// chunk-scan kernel: the operands of the state recurrence in the layouts the
+// matrix-core operand loads read.  The four matrix operands are stored as NP
+// bf16 piece planes (x ~ p0 + p1 (+ p2), see mfma.h), so the sequential scan
+// loads them ready for the matrix cores; U and e^{G_C} stay fp32.
+//   W   [NP][64][D]   W = (I + A)^-1 Diag(beta) (K * e^G), token-major
+//   Qp  [NP][64][D]   Q+ = Q * e^G, token-major
+//   KT  [NP][D][64]   K~^T = (K * e^{G_C - G})^T, channel-major
+//   Aqk [NP][64][64]  the masked intra-chunk attention, token-major
+//   UT  [D][64]       U^T = ((I + A)^-1 Diag(beta) V)^T, fp32
+//   eGC [D]           e^{G_C}, the whole-chunk decay, fp32
 struct Record {
   size_t W, Qp, KT, Aqk, UT, eGC, bytes;
+  size_t tile_plane, aqk_plane;   // bytes of one piece plane of a [64][D] tile / of Aqk
 };
 
-__host__ __device__ constexpr Record record_layout(int D) {
-  const size_t tile = static_cast<size_t>(64) * D * 4;
+__host__ __device__ constexpr Record record_layout(int D, int NP) {
+  const size_t tp = static_cast<size_t>(64) * D * 2;
+  const size_t ap = static_cast<size_t>(64) * 64 * 2;
   Record r{};
+  r.tile_plane = tp;
+  r.aqk_plane = ap;
   r.W = 0;
-  r.Qp = r.W + tile;
-  r.KT = r.Qp + tile;
-  r.Aqk = r.KT + tile;
-  r.UT = r.Aqk + static_cast<size_t>(64) * 64 * 4;
-  r.eGC = r.UT + tile;
+  r.Qp = r.W + NP * tp;
+  r.KT = r.Qp + NP * tp;
+  r.Aqk = r.KT + NP * tp;
+  r.UT = r.Aqk + NP * ap;
+  r.eGC = r.UT + static_cast<size_t>(64) * D * 4;
   r.bytes = (r.eGC + static_cast<size_t>(D) * 4 + 255) / 256 * 256;
   return r;
 }
