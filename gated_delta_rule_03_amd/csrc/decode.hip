@@ -9,17 +9,25 @@
 //   S~ = Diag(e^g) S;  p = k^T S~;  r = q^T S~;  delta = beta (v - p)
 //   o = r + (q.k) delta          (= q^T (S~ + k delta^T), the updated state)
 //   S <- S~ + k delta^T;  history <- [h1, h2, x]
-// A wave covers two full state rows per load (512 B contiguous each), every
-// lane moves 16 B per access, and the k^T S~ / q^T S~ column sums are reduced
-// across row groups through LDS.
+// The state loads are issued before anything else so that their latency
+// overlaps the preprocess; a wave covers two full state rows per load (512 B
+// contiguous each), every lane moves 16 B per access (streamed, non-temporal),
+// and the k^T S~ / q^T S~ column sums are reduced across row groups through
+// LDS.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Eight waves per (sequence, head): a 64 KB in-place tile streams measurably
+// faster with 512 threads than with 256 (more bytes in flight per workgroup).
+constexpr int kDecodeThreads = 512;
+
 template <int D, bool IO_BF16, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_kernel(Params p, DecodeIO io) {
-  constexpr int NT = 256;
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, DecodeIO io) {
+  constexpr int NT = kDecodeThreads;
   constexpr int C4 = D / 4;                  // float4 columns per state row
   constexpr int RPP = NT / C4;               // state rows covered by one pass of the block
   constexpr int RPT = (D + RPP - 1) / RPP;   // passes (rows per thread)
@@ -34,6 +42,17 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, DecodeIO io) {
   const int n = blockIdx.x / H, h = blockIdx.x % H;
   const size_t Ctot = static_cast<size_t>(3) * H * D;
   const uint32_t flags = p.flags;
+
+  // ---- the state tile is requested first: its latency overlaps the preprocess
+  const int col4 = tid % C4, rg = tid / C4;
+  const size_t base = (static_cast<size_t>(n) * H + h) * D * D;
+  f32x4v* Sp = reinterpret_cast<f32x4v*>(io.state + base);
+  f32x4v Sv[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = rg + rr * RPP;
+    if (r < D) Sv[rr] = __builtin_nontemporal_load(&Sp[static_cast<size_t>(r) * C4 + col4]);
+  }
 
   // ---- preprocess: conv + SiLU for the 3D channels of this head; shift history
   for (int c = tid; c < 3 * D; c += NT) {
@@ -101,16 +120,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, DecodeIO io) {
   const float qs = scal[0], ks = scal[1], beta = scal[2], qk = scal[3];
 
   // ---- one pass over the state
-  const int col4 = tid % C4, rg = tid / C4;
-  const size_t base = (static_cast<size_t>(n) * H + h) * D * D;
-  float4* Sp = reinterpret_cast<float4*>(io.state + base);
-  float4 Sv[RPT];
   float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) {
-    const int r = rg + rr * RPP;
-    if (r < D) Sv[rr] = Sp[static_cast<size_t>(r) * C4 + col4];
-  }
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) {
     const int r = rg + rr * RPP;
@@ -143,9 +153,9 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, DecodeIO io) {
     const int r = rg + rr * RPP;
     if (r < D) {
       const float kr = u_s[D + r] * ks;
-      float4 s = Sv[rr];
+      f32x4v s = Sv[rr];
       s.x += kr * d0; s.y += kr * d1; s.z += kr * d2; s.w += kr * d3;
-      Sp[static_cast<size_t>(r) * C4 + col4] = s;
+      __builtin_nontemporal_store(s, &Sp[static_cast<size_t>(r) * C4 + col4]);
     }
   }
 }
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, DecodeIO io) {
 template <int D>
 static hipError_t launch_decode_d(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16,
                                   hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(N) * p.H), block(256);
+  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
   if (io_bf16 && out_bf16) decode_kernel<D, true, true><<<grid, block, 0, st>>>(p, io);
   else if (io_bf16) decode_kernel<D, true, false><<<grid, block, 0, st>>>(p, io);
   else if (out_bf16) decode_kernel<D, false, true><<<grid, block, 0, st>>>(p, io);
