@@ -435,6 +435,7 @@ static hipError_t launch_prep_d(const Params& p, const ChunkTable& t, const Pref
 
 hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                              int max_chunks, bool io_bf16, hipStream_t st) {
+  if (chunk_prep_rows_supported(p, io, io_bf16)) return launch_chunk_prep_rows(p, t, io, records, max_chunks, st);
   switch (p.D) {
     case 16: return launch_prep_d<16>(p, t, io, records, max_chunks, io_bf16, st);
     case 32: return launch_prep_d<32>(p, t, io, records, max_chunks, io_bf16, st);

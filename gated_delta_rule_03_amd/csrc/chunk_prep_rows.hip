@@ -1,0 +1,742 @@
+// Chunk preparation, row-block form: the same Record as chunk_prep.hip (see
+// there and kda_internal.h for what it holds and why), computed with a
+// different division of labour for the common case of bf16 inputs and
+// dk = dv in {64, 128}.
+//
+// Differences from the general kernel:
+//  * Persistent workgroups with a fixed head.  Workgroup (h, grp) walks the
+//    chunks grp, grp + G, ... of head h; the raw q/k/v rows (with the three
+//    conv rows before the chunk), alpha and b of the NEXT chunk are loaded
+//    into registers during the last phases of the current one, so the input
+//    latency is hidden.  The conv weights and dt_bias of the head stay in LDS.
+//  * Wave (R, half) owns token rows 16R..16R+15 and key channels
+//    64 half .. 64 half + 63.  A lane holds one token row r and 16 channels
+//    (two groups of 8 at 32-channel spacing), which is exactly the A operand
+//    of a 16x16x32 matrix-core step, so the row operands of A = beta K K^T
+//    and Aqk = Q K^T (with their decays) never leave registers.  The token
+//    prefix sums of g inside a 16-row block are DPP scans across the 16
+//    lanes of a row, and e^{P} is formed once per element for both q and k.
+//  * The two channel halves of A and Aqk meet in LDS: the upper half stores
+//    its partial sums and the lower half adds its own on top, in that order.
+//  * The solve of (I + A) X = [beta K+ | beta V] runs per wave on the wave's
+//    own 16-column blocks of X with A and the inverted diagonal blocks split
+//    into bf16 pieces once, in LDS; no workgroup barrier inside it.
+// Row R of a wave is chosen so that the two waves sharing a SIMD (w, w + 4)
+// own row blocks R and 3 - R: the triangular A work is then even per SIMD.
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "mfma.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kRawRows = kChunk + 3;   // the chunk's rows and the three conv rows before it
+constexpr int kRowsNP = 2;             // bf16 pieces per operand (bf16 inputs)
+
+// Lane i of each 16-lane row reads lane i - N (row_shr) or i + N (row_shl)
+// of the same row; lanes shifted in from outside the row read 0.
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float dpp_row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, true));
+}
+
+// Sum over lanes 0..i of the lane's 16-lane row (inclusive prefix).
+__device__ __forceinline__ float row_prefix(float x) {
+  x += dpp_row_shr<1>(x);
+  x += dpp_row_shr<2>(x);
+  x += dpp_row_shr<4>(x);
+  x += dpp_row_shr<8>(x);
+  return x;
+}
+
+// Sum over lanes i+1..15 of the lane's 16-lane row (exclusive suffix).
+__device__ __forceinline__ float row_suffix_excl(float x) {
+  x = dpp_row_shl<1>(x);
+  x += dpp_row_shl<1>(x);
+  x += dpp_row_shl<2>(x);
+  x += dpp_row_shl<4>(x);
+  x += dpp_row_shl<8>(x);
+  return x;
+}
+
+// Keeps the compiler from moving memory accesses across this point: the LDS
+// hand-offs inside a wave rely on program order (a wave's LDS operations
+// execute in order), and it bounds how far loads are hoisted in unrolled
+// loops, which keeps the register count in check.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Pins computed values where they stand: the compiler may otherwise sink
+// arithmetic past a barrier to its first use and keep all of its inputs
+// alive instead (here, hundreds of registers of raw inputs and conv taps).
+template <int N>
+__device__ __forceinline__ void pin(float (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(a[i]));
+}
+
+// Position of one chunk in the packed batch.
+struct ChunkPos {
+  int s, tau0, len;
+  int64_t tok0;
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(const ChunkTable& t, int c) {
+  ChunkPos cp;
+  cp.s = t.chunk_seq[c];
+  cp.tau0 = (c - t.chunk0[cp.s]) * kChunk;
+  cp.tok0 = static_cast<int64_t>(t.cu[cp.s]) + cp.tau0;
+  cp.len = min(kChunk, t.cu[cp.s + 1] - static_cast<int>(cp.tok0));
+  return cp;
+}
+
+// The raw inputs of one chunk for one head, as this thread loads them.  The
+// q | k | v staging rows are 3D/8 pieces of 16 bytes wide; thread t stages
+// piece column t % (3D/8) of rows t / (3D/8) + SR j (SR staging rows per pass
+// of the block), so that its tensor and channels stay fixed.
+template <int D, int NT>
+struct RawChunk {
+  static constexpr int kCols = 3 * D / 8;
+  static constexpr int kSR = NT / kCols;                       // rows per pass
+  static constexpr int kPer = (kRawRows + kSR - 1) / kSR;      // passes
+  uint4 x[kPer];      // staging rows, then written to LDS
+  uint4 a[2];         // alpha of this lane's row and 16 channels
+  uint16_t b;         // b of this lane's row
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(Params p, ChunkTable t, PrefillIO io,
+                                                                               uint8_t* records) {
+  constexpr int HF = D / 64;            // channel halves
+  constexpr int NW = 4 * HF;            // waves
+  constexpr int NT = 64 * NW;
+  constexpr int NP = kRowsNP;
+  constexpr Record REC = record_layout(D, NP);
+  constexpr int RAWS = 3 * D + 8;       // staging row stride (bf16)
+  constexpr int KCS = D + 8;            // row stride of the k e^{-P} pieces (bf16)
+  constexpr int LX = D == 64 ? kChunk + 8 : kChunk + 4;   // row stride of X^T (fp32)
+  constexpr int LA = kChunk + 4;        // row stride of A, Aqk (fp32)
+  constexpr int LAP = kChunk + 8;       // row stride of the A pieces (bf16)
+  constexpr int LTP = 24;               // row stride of the T pieces (bf16)
+  constexpr int NCB = 2 * D / 16;       // 16-column blocks of X
+  constexpr int CBPW = NCB / NW;        // ... per wave
+  constexpr size_t kRawBytes = static_cast<size_t>(kRawRows) * RAWS * 2;
+  constexpr size_t kKcBytes = static_cast<size_t>(NP) * 64 * KCS * 2;
+  constexpr size_t kXBytes = static_cast<size_t>(2 * D) * LX * 4;
+  constexpr size_t kUBytes = kRawBytes > kKcBytes ? (kRawBytes > kXBytes ? kRawBytes : kXBytes)
+                                                  : (kKcBytes > kXBytes ? kKcBytes : kXBytes);
+  using Raw = RawChunk<D, NT>;
+  static_assert(CBPW * NW == NCB, "column blocks must divide evenly over the waves");
+  static_assert(kKcBytes <= static_cast<size_t>(D) * LX * 4, "the beta V^T rows of X^T must start past the k e^{-P} pieces");
+
+  // sU holds, in turn: the raw staging rows; the k e^{-P} pieces beside the
+  // beta V^T rows of X^T (which start past them); X^T
+  __shared__ __align__(16) unsigned char sU[kUBytes];
+  __shared__ __align__(16) float sA[64 * LA];            // A (rows scaled by beta)
+  __shared__ __align__(16) float sAqk[64 * LA];
+  __shared__ __align__(16) __bf16 sAp[NP][64 * LAP];     // A pieces, blocks below the diagonal only
+  __shared__ __align__(16) __bf16 sTp[NP][4][16 * LTP];  // (I + A_RR)^-1 pieces
+  __shared__ __align__(16) float sW[3][D][4];            // conv taps of this head (q, k, v)
+  __shared__ __align__(16) float sDtb[D];
+  __shared__ __align__(16) float sBt[4][D];              // in-block totals of g
+  __shared__ __align__(16) float sEBt[4][D];             // their exponentials
+  __shared__ float sNorm[HF][64][2];                     // partial sums of q^2, k^2
+  __shared__ float sBeta[64];
+  __bf16* sRaw = reinterpret_cast<__bf16*>(sU);
+  __bf16* sKc = reinterpret_cast<__bf16*>(sU);
+  float* sX = reinterpret_cast<float*>(sU);
+
+  const int H = p.H;
+  const int h = blockIdx.x % H, grp = blockIdx.x / H, G = gridDim.x / H;
+  const int total = t.chunk0[t.N];
+  // Lane coordinates.  Inside the chunk loop they are re-derived from a copy
+  // of the thread index the compiler cannot see through, so that it does not
+  // hoist per-lane addresses out of the loop and keep them in registers for
+  // its whole length (that alone would cost about 150 registers).
+  struct LaneCoords {
+    int tid, w, lane, ln, q4, R, hf, r;
+  };
+  auto coords = [](int t) {
+    LaneCoords L;
+    L.tid = t;
+    L.w = t / kWave;
+    L.lane = t % kWave;
+    L.ln = L.lane & 15;
+    L.q4 = L.lane >> 4;
+    L.R = L.w < 4 ? L.w : 7 - L.w;   // row block
+    L.hf = L.w / 4;                  // channel half
+    L.r = 16 * L.R + L.ln;           // this lane's token row
+    return L;
+  };
+  const int tid = threadIdx.x;
+  const size_t HD = static_cast<size_t>(H) * D;
+  const size_t Ctot = 3 * HD;
+  const uint32_t flags = p.flags;
+  const bool raw_conv = flags & KDA_FLAG_SKIP_CONV;
+  const bool l2 = !(flags & KDA_FLAG_SKIP_L2NORM);
+  const float a_exp = expf(p.A_log[h]);
+
+  // ---- the head's conv taps and dt_bias, once
+  {
+    for (int e = tid; e < 3 * D * 4; e += NT) {
+      const int tens = e / (4 * D), rem = e % (4 * D);
+      const void* wsrc = tens == 0 ? p.wq : (tens == 1 ? p.wk : p.wv);
+      sW[tens][rem / 4][rem % 4] = bf16_to_f32(static_cast<const uint16_t*>(wsrc)[static_cast<size_t>(h) * D * 4 + rem]);
+    }
+    for (int e = tid; e < D; e += NT) sDtb[e] = p.dt_bias[static_cast<size_t>(h) * D + e];
+  }
+
+  // Every piece is loaded from a valid address and zeroed where the history
+  // has no row (sequence start without a conv history) or past the staging rows.
+  auto load_raw = [&](Raw& nx, const ChunkPos& cp, const LaneCoords& L) {
+    const int st_col = L.tid % Raw::kCols, st_row0 = L.tid / Raw::kCols;
+    const bool stager = L.tid < Raw::kSR * Raw::kCols;
+    const int st_tens = st_col / (D / 8), st_ch = 8 * (st_col % (D / 8));
+    const uint16_t* st_x = static_cast<const uint16_t*>(st_tens == 0 ? io.q : (st_tens == 1 ? io.k : io.v)) +
+                           static_cast<size_t>(h) * D + st_ch;
+    const bool have_hist = io.conv_in != nullptr;
+    const uint16_t* st_h = static_cast<const uint16_t*>(have_hist ? io.conv_in : io.q) +
+                           (have_hist ? static_cast<size_t>(cp.s) * 3 * Ctot + st_tens * HD + static_cast<size_t>(h) * D + st_ch
+                                      : 0);
+#pragma unroll
+    for (int j = 0; j < Raw::kPer; ++j) {
+      const int sr = st_row0 + Raw::kSR * j;
+      const int tau = cp.tau0 + sr - 3;
+      const bool hist = tau < 0;
+      const int64_t tok = cp.tok0 + (hist ? 0 : min(sr - 3, cp.len - 1));   // any valid row for a history slot
+      const uint16_t* px = hist && have_hist ? st_h + static_cast<size_t>(3 + tau) * Ctot : st_x + tok * HD;
+      const uint4 v = *reinterpret_cast<const uint4*>(px);
+      const bool zero = !stager || sr >= kRawRows || (hist && !have_hist);
+      nx.x[j] = zero ? make_uint4(0u, 0u, 0u, 0u) : v;
+    }
+    const int64_t tok = cp.tok0 + min(L.r, cp.len - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      nx.a[ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(io.alpha) + tok * HD +
+                                                 static_cast<size_t>(h) * D + 64 * L.hf + 32 * ks + 8 * L.q4);
+    nx.b = static_cast<const uint16_t*>(io.b)[tok * H + h];
+  };
+
+  Raw nxt;
+  ChunkPos nxt_pos{};
+  if (grp < total) {
+    nxt_pos = chunk_pos(t, grp);
+    load_raw(nxt, nxt_pos, coords(tid));
+  }
+
+  for (int c = grp; c < total; c += G) {
+    const ChunkPos cp = nxt_pos;
+    int tid_opaque = tid;
+    asm volatile("" : "+v"(tid_opaque));
+    const LaneCoords L = coords(tid_opaque);
+    const int w = L.w, lane = L.lane, ln = L.ln, q4 = L.q4, R = L.R, hf = L.hf, r = L.r;
+    const int st_col = L.tid % Raw::kCols, st_row0 = L.tid / Raw::kCols;
+    const bool stager = L.tid < Raw::kSR * Raw::kCols;
+    __syncthreads();   // the previous chunk is done with sU, sA, sAqk
+    // ---- staging rows into LDS; the next chunk's loads go out
+#pragma unroll
+    for (int j = 0; j < Raw::kPer; ++j) {
+      const int sr = st_row0 + Raw::kSR * j;
+      if (stager && sr < kRawRows) *reinterpret_cast<uint4*>(&sRaw[sr * RAWS + 8 * st_col]) = nxt.x[j];
+    }
+    const uint4 a_cur[2] = {nxt.a[0], nxt.a[1]};
+    const uint16_t b_cur = nxt.b;
+    __syncthreads();
+
+    uint8_t* rec = records + (static_cast<size_t>(c) * H + h) * REC.bytes;
+    const bool live = r < cp.len;
+    // The conv taps and dt_bias never change inside this loop; reading them
+    // through an offset the compiler cannot see through keeps it from
+    // hoisting 200 registers' worth of LDS loads out of the loop.
+    int inv = 0;
+    asm volatile("" : "+v"(inv));
+    const float* tapw = &sW[0][0][0] + inv;
+    const float* dtb = sDtb + inv;
+
+    // ---- 1. conv + SiLU of this lane's row (q, k, v), gate, beta
+    float qv[16], kv[16], vv[16], gv[16];
+#pragma unroll
+    for (int tens = 0; tens < 3; ++tens) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+        uint4 xm[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xm[m] = *reinterpret_cast<const uint4*>(&sRaw[(r + m) * RAWS + tens * D + c0]);
+        float uo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 wt = *reinterpret_cast<const float4*>(&tapw[(tens * D + c0 + i) * 4]);
+          float xs[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t wd = (i >> 1) == 0 ? xm[m].x : ((i >> 1) == 1 ? xm[m].y : ((i >> 1) == 2 ? xm[m].z : xm[m].w));
+            xs[m] = (i & 1) ? __uint_as_float(wd & 0xffff0000u) : __uint_as_float(wd << 16);
+          }
+          const float y = wt.x * xs[0] + wt.y * xs[1] + wt.z * xs[2] + wt.w * xs[3];
+          uo[i] = live ? (raw_conv ? xs[3] : siluf_(y)) : 0.f;
+        }
+        pin(uo);   // this group is computed before the next group's loads
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (tens == 0) qv[8 * ks + i] = uo[i];
+          else if (tens == 1) kv[8 * ks + i] = uo[i];
+          else vv[8 * ks + i] = uo[i];
+        }
+        compiler_fence();
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      const uint32_t aw[4] = {a_cur[ks].x, a_cur[ks].y, a_cur[ks].z, a_cur[ks].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float al = (i & 1) ? __uint_as_float(aw[i / 2] & 0xffff0000u) : __uint_as_float(aw[i / 2] << 16);
+        const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb[c0 + i], a_exp, p.lower_bound);
+        gv[8 * ks + i] = live ? g : 0.f;
+      }
+    }
+    pin(qv);
+    pin(kv);
+    pin(vv);
+    pin(gv);
+    float beta = 0.f;
+    if (live) {
+      const float bb = bf16_to_f32(b_cur);
+      beta = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
+      if (flags & KDA_FLAG_BETA_X2) beta *= 2.0f;
+    }
+    if (hf == 0 && q4 == 0) sBeta[r] = beta;
+    {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        sq += qv[j] * qv[j];
+        sk += kv[j] * kv[j];
+      }
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 32);
+      if (q4 == 0) {
+        sNorm[hf][r][0] = sq;
+        sNorm[hf][r][1] = sk;
+      }
+    }
+    // in-block decay sums: P_r (through token r) and Q_r (after token r)
+    float P[16], Qs[16], eP[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      P[j] = row_prefix(gv[j]);
+      Qs[j] = row_suffix_excl(gv[j]);
+      eP[j] = exp_precise(P[j]);
+    }
+    pin(Qs);
+    pin(eP);
+    if (ln == 15) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+        *reinterpret_cast<float4*>(&sBt[R][c0]) = make_float4(P[8 * ks], P[8 * ks + 1], P[8 * ks + 2], P[8 * ks + 3]);
+        *reinterpret_cast<float4*>(&sBt[R][c0 + 4]) =
+            make_float4(P[8 * ks + 4], P[8 * ks + 5], P[8 * ks + 6], P[8 * ks + 7]);
+        *reinterpret_cast<float4*>(&sEBt[R][c0]) =
+            make_float4(eP[8 * ks], eP[8 * ks + 1], eP[8 * ks + 2], eP[8 * ks + 3]);
+        *reinterpret_cast<float4*>(&sEBt[R][c0 + 4]) =
+            make_float4(eP[8 * ks + 4], eP[8 * ks + 5], eP[8 * ks + 6], eP[8 * ks + 7]);
+      }
+    }
+    __syncthreads();
+
+    // ---- 2. norms, decays and the elementwise outputs of this lane's row
+    float iq, ik;
+    {
+      float nq = sNorm[0][r][0], nk = sNorm[0][r][1];
+      if constexpr (HF == 2) {
+        nq += sNorm[1][r][0];
+        nk += sNorm[1][r][1];
+      }
+      iq = (l2 ? 1.0f / sqrtf(nq + p.eps) : 1.0f) * p.scale;
+      ik = l2 ? 1.0f / sqrtf(nk + p.eps) : 1.0f;
+    }
+    float qP[16], kP[16];
+    SplitN<NP> kcp[2];   // k e^{-P} pieces: the B operand of this lane's diagonal block
+    // e^{G before block R} and the sum of the later block totals, per channel
+    auto before_after = [&](int c0, float (&eb)[8], float (&after)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        eb[i] = 1.f;
+        after[i] = 0.f;
+      }
+#pragma unroll 1
+      for (int J = 0; J < R; ++J) {
+        const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[J][c0]);
+        const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[J][c0 + 4]);
+        eb[0] *= e0.x; eb[1] *= e0.y; eb[2] *= e0.z; eb[3] *= e0.w;
+        eb[4] *= e1.x; eb[5] *= e1.y; eb[6] *= e1.z; eb[7] *= e1.w;
+      }
+#pragma unroll 1
+      for (int J = 3; J > R; --J) {
+        const float4 b0 = *reinterpret_cast<const float4*>(&sBt[J][c0]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&sBt[J][c0 + 4]);
+        after[0] += b0.x; after[1] += b0.y; after[2] += b0.z; after[3] += b0.w;
+        after[4] += b1.x; after[5] += b1.y; after[6] += b1.z; after[7] += b1.w;
+      }
+    };
+    {
+      // beta V^T straight to its rows of X^T, which lie past the k e^{-P}
+      // pieces in the shared region (beta K+ follows in phase 4)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sX[(D + c0 + i) * LX + r] = beta * vv[8 * ks + i];
+      }
+      compiler_fence();
+      // key side: k e^{P}, k e^{-P} pieces, K~^T, e^{G_C}
+      __bf16* KT = reinterpret_cast<__bf16*>(rec + REC.KT);
+      float* eGC = reinterpret_cast<float*>(rec + REC.eGC);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+        float eb[8], after[8];
+        before_after(c0, eb, after);
+        float kc[8], kt[8], pk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = 8 * ks + i;
+          const float kk = kv[j] * ik;
+          pk[i] = kk * eP[j];                            // row operand of the A sub-blocks
+          kc[i] = kk * rcp_fast(eP[j]);                  // column operand k e^{-P}
+          kt[i] = kk * exp_precise(Qs[j] + after[i]);    // K~ = k e^{G_C - G_r}
+        }
+        pin(pk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kP[8 * ks + i] = pk[i];
+        kcp[ks] = splitN<NP>(kc);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x8*>(&sKc[k * 64 * KCS + r * KCS + c0]) = kcp[ks].v[k];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __bf16 pc[NP];
+          split_pieces<NP>(kt[i], pc);
+#pragma unroll
+          for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 2) + (c0 + i) * kChunk + r] = pc[k];
+        }
+        if (R == 3 && ln == 15) {   // e^{G_C} = e^{G before block 3} e^{P_63}
+          float eg[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) eg[i] = eP[8 * ks + i] * eb[i];
+          *reinterpret_cast<float4*>(eGC + c0) = make_float4(eg[0], eg[1], eg[2], eg[3]);
+          *reinterpret_cast<float4*>(eGC + c0 + 4) = make_float4(eg[4], eg[5], eg[6], eg[7]);
+        }
+        compiler_fence();
+      }
+      // query side: Q+ = q e^{G_r} out, q e^{P} kept
+      __bf16* Qp = reinterpret_cast<__bf16*>(rec + REC.Qp);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+        float eb[8], after[8];
+        before_after(c0, eb, after);
+        float qo[8], pq[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = 8 * ks + i;
+          const float qq = qv[j] * iq;
+          qo[i] = qq * (eP[j] * eb[i]);
+          pq[i] = qq * eP[j];
+        }
+        pin(pq);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qP[8 * ks + i] = pq[i];
+        const SplitN<NP> qs = splitN<NP>(qo);
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+          *reinterpret_cast<bf16x8*>(Qp + k * (REC.tile_plane / 2) + r * D + c0) = qs.v[k];
+        compiler_fence();
+      }
+    }
+    pin(qP);
+    pin(kP);
+    __syncthreads();
+
+    // ---- 3. this wave's channel half of A and Aqk, sub-blocks (R, I <= R).
+    //      The upper half stores its partial sums, then the lower half adds its
+    //      own (held in registers) on top: lower + upper, the same every time.
+    {
+      f32x4 keepA[4], keepQ[4];
+      float E[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) E[j] = 1.f;
+#pragma unroll
+      for (int I = 3; I >= 0; --I) {
+        keepA[I] = keepQ[I] = zero4();
+        if (I > R) continue;
+        if (I < R) {   // E = e^{sum of the block totals of blocks I .. R-1}
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int c0 = 64 * hf + 32 * ks + 8 * q4;
+            const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[I][c0]);
+            const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[I][c0 + 4]);
+            const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) E[8 * ks + i] *= ev[i];
+          }
+        }
+        f32x4 accA = zero4(), accQ = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c0 = 64 * hf + 32 * ks + 8 * q4;
+          SplitN<NP> bk;
+          if (I == R) {
+            bk = kcp[ks];
+          } else {
+#pragma unroll
+            for (int k = 0; k < NP; ++k)
+              bk.v[k] = *reinterpret_cast<const bf16x8*>(&sKc[k * 64 * KCS + (16 * I + ln) * KCS + c0]);
+          }
+          float ra[8], rq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ra[i] = kP[8 * ks + i] * E[8 * ks + i];
+            rq[i] = qP[8 * ks + i] * E[8 * ks + i];
+          }
+          accA = mfmaN<NP>(splitN<NP>(ra), bk, accA);
+          accQ = mfmaN<NP>(splitN<NP>(rq), bk, accQ);
+        }
+        if (HF == 1 || hf == 1) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
+            sA[row * LA + col] = sBeta[row] * accA[j];
+            sAqk[row * LA + col] = accQ[j];
+          }
+        } else {
+          keepA[I] = accA;
+          keepQ[I] = accQ;
+        }
+        compiler_fence();
+      }
+      if constexpr (HF == 2) {
+        __syncthreads();
+        if (hf == 0) {
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            if (I > R) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
+              sA[row * LA + col] = sBeta[row] * keepA[I][j] + sA[row * LA + col];
+              sAqk[row * LA + col] = keepQ[I][j] + sAqk[row * LA + col];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- the next chunk's raw inputs go out now: phases 4 and 5 hold few
+    //      registers, and they hide the loads' latency
+    if (c + G < total) {
+      nxt_pos = chunk_pos(t, c + G);
+      load_raw(nxt, nxt_pos, L);
+    }
+
+    // ---- 4. Aqk pieces out; A pieces and the diagonal-block inverses to LDS; beta K+ to X^T
+    {
+      __bf16* Aq = reinterpret_cast<__bf16*>(rec + REC.Aqk);
+      for (int e = L.tid; e < 64 * 8; e += NT) {
+        const int rw = e >> 3, i0 = 8 * (e & 7);
+        const float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);
+        const float4 a0 = *reinterpret_cast<const float4*>(&sA[rw * LA + i0]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&sA[rw * LA + i0 + 4]);
+        const float qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const float aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        float qm[8], am[8];
+        const bool below = (i0 / 16) < (rw / 16);   // whole sub-block left of the diagonal block
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          qm[i] = (i0 + i <= rw) ? qa[i] : 0.f;
+          am[i] = below ? aa[i] : 0.f;
+        }
+        const SplitN<NP> qs = splitN<NP>(qm), as = splitN<NP>(am);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          *reinterpret_cast<bf16x8*>(Aq + k * (REC.aqk_plane / 2) + rw * kChunk + i0) = qs.v[k];
+          *reinterpret_cast<bf16x8*>(&sAp[k][rw * LAP + i0]) = as.v[k];
+        }
+      }
+      if (w == 0) {   // lane = (block, column) of the unit lower-triangular inverses
+        const int Rb = lane >> 4, j = lane & 15;
+        float tcol[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = (i == j) ? 1.f : 0.f;
+#pragma unroll
+          for (int m = 0; m < i; ++m) v -= sA[(16 * Rb + i) * LA + 16 * Rb + m] * tcol[m];
+          tcol[i] = (i < j) ? 0.f : v;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __bf16 pc[NP];
+          split_pieces<NP>(tcol[i], pc);
+#pragma unroll
+          for (int k = 0; k < NP; ++k) sTp[k][Rb][i * LTP + j] = pc[k];
+        }
+      }
+      // beta K+ = beta (k e^{P}) e^{G before the block}, over the k e^{-P} pieces
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+        float eb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) eb[i] = 1.f;
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+          if (J < R) {
+            const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[J][c0]);
+            const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[J][c0 + 4]);
+            const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) eb[i] *= ev[i];
+          }
+        }
+        const float beta = sBeta[r];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sX[(c0 + i) * LX + r] = (beta * kP[8 * ks + i]) * eb[i];
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. per wave: X = (I + A)^-1 B on its own column blocks, then W and U^T out
+    {
+#pragma unroll
+      for (int Rs = 0; Rs < 4; ++Rs) {
+        // Y = B_R - A_{R,<R} X_{<R}, over B_R in place
+#pragma unroll
+        for (int bi = 0; bi < CBPW; ++bi) {
+          const int cb = w + bi * NW;
+          float* xc = &sX[(16 * cb + ln) * LX];
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < (Rs + 1) / 2; ++ks) {
+            SplitN<NP> a;
+#pragma unroll
+            for (int k = 0; k < NP; ++k)
+              a.v[k] = *reinterpret_cast<const bf16x8*>(&sAp[k][(16 * Rs + ln) * LAP + 32 * ks + 8 * q4]);
+            const float4 b0 = *reinterpret_cast<const float4*>(&xc[32 * ks + 8 * q4]);
+            const float4 b1 = *reinterpret_cast<const float4*>(&xc[32 * ks + 8 * q4 + 4]);
+            const float xb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            acc = mfmaN<NP>(a, splitN<NP>(xb), acc);
+          }
+          if (Rs > 0) {
+            float4* yr = reinterpret_cast<float4*>(&xc[16 * Rs + 4 * q4]);
+            const float4 bR = *yr;
+            *yr = make_float4(bR.x - acc[0], bR.y - acc[1], bR.z - acc[2], bR.w - acc[3]);
+          }
+        }
+        compiler_fence();
+        // X_R = T_R Y (K = 16: the upper half-wave contributes zeros)
+        f32x4 xr[CBPW];
+#pragma unroll
+        for (int bi = 0; bi < CBPW; ++bi) {
+          const int cb = w + bi * NW;
+          const float* xc = &sX[(16 * cb + ln) * LX];
+          SplitN<NP> ta, yb;
+          if (q4 < 2) {
+#pragma unroll
+            for (int k = 0; k < NP; ++k) ta.v[k] = *reinterpret_cast<const bf16x8*>(&sTp[k][Rs][ln * LTP + 8 * q4]);
+            const float4 y0 = *reinterpret_cast<const float4*>(&xc[16 * Rs + 8 * q4]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&xc[16 * Rs + 8 * q4 + 4]);
+            const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            yb = splitN<NP>(yv);
+          } else {
+            ta = zero_split<NP>();
+            yb = zero_split<NP>();
+          }
+          xr[bi] = mfmaN<NP>(ta, yb, zero4());
+        }
+        compiler_fence();
+#pragma unroll
+        for (int bi = 0; bi < CBPW; ++bi) {
+          const int cb = w + bi * NW;
+          *reinterpret_cast<float4*>(&sX[(16 * cb + ln) * LX + 16 * Rs + 4 * q4]) =
+              make_float4(xr[bi][0], xr[bi][1], xr[bi][2], xr[bi][3]);
+        }
+        compiler_fence();
+      }
+      __bf16* W = reinterpret_cast<__bf16*>(rec + REC.W);
+      float* UT = reinterpret_cast<float*>(rec + REC.UT);
+#pragma unroll
+      for (int bi = 0; bi < CBPW; ++bi) {
+        const int cb = w + bi * NW;
+        if (cb < D / 16) {   // W, token-major: 8 channels of one token per lane and step
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int u = lane + 64 * k2, tok = u >> 1, c8 = 16 * cb + 8 * (u & 1);
+            float xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] = sX[(c8 + i) * LX + tok];
+            const SplitN<NP> ws = splitN<NP>(xv);
+#pragma unroll
+            for (int k = 0; k < NP; ++k)
+              *reinterpret_cast<bf16x8*>(W + k * (REC.tile_plane / 2) + tok * D + c8) = ws.v[k];
+          }
+        } else {             // U^T, channel-major fp32
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) {
+            const int u = lane + 64 * k2, m = u >> 4, t4 = u & 15;
+            const int cu = 16 * cb - D + m;
+            *reinterpret_cast<float4*>(UT + cu * kChunk + 4 * t4) =
+                *reinterpret_cast<const float4*>(&sX[(16 * cb + m) * LX + 4 * t4]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_rows_d(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
+                                int max_chunks, hipStream_t st) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  int& ncu = cus[dev & 63];
+  if (ncu == 0) {
+    const hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  // one resident workgroup per compute unit; each walks the chunks of one head
+  int groups = (ncu + p.H - 1) / p.H;
+  groups = groups < 1 ? 1 : (groups > max_chunks ? max_chunks : groups);
+  const dim3 grid(static_cast<unsigned>(p.H) * static_cast<unsigned>(groups));
+  chunk_prep_rows_kernel<D><<<grid, 64 * 4 * (D / 64), 0, st>>>(p, t, io, records);
+  return hipGetLastError();
+}
+
+bool chunk_prep_rows_supported(const Params& p, const PrefillIO& io, bool io_bf16) {
+  if (!io_bf16 || (p.D != 64 && p.D != 128)) return false;
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  return a16(io.q) && a16(io.k) && a16(io.v) && a16(io.alpha) && (io.conv_in == nullptr || a16(io.conv_in));
+}
+
+hipError_t launch_chunk_prep_rows(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
+                                  int max_chunks, hipStream_t st) {
+  switch (p.D) {
+    case 64: return launch_rows_d<64>(p, t, io, records, max_chunks, st);
+    case 128: return launch_rows_d<128>(p, t, io, records, max_chunks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

@@ -84,6 +84,11 @@ hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_unifor
                                int32_t* chunk0, int32_t* chunk_seq, int32_t max_chunks, hipStream_t st);
 hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                              int max_chunks, bool io_bf16, hipStream_t st);
+// The row-block prep kernel (bf16 inputs, dk = dv in {64, 128}, 16-byte
+// aligned q/k/v/alpha/conv history); launch_chunk_prep uses it when it applies.
+bool chunk_prep_rows_supported(const Params& p, const PrefillIO& io, bool io_bf16);
+hipError_t launch_chunk_prep_rows(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
+                                  int max_chunks, hipStream_t st);
 hipError_t launch_chunk_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
                              bool io_bf16, bool out_bf16, hipStream_t st);
 hipError_t launch_conv_state_out(const Params& p, const ChunkTable& t, const PrefillIO& io, bool io_bf16,

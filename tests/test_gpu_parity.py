@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from kda_inputs import BF16, FP32, make_problem, make_tokens, as_f64, workload_tiny_fp32
+from kda_inputs import BF16, FP32, make_problem, make_tokens, as_f64, f32_to_bf16_bits, workload_tiny_fp32
 from kda_inputs.torch_io import from_torch_bf16, problem_to_device, tokens_to_device
 from tests.helpers import check_bf16_output, max_over_rms, rel_fro
 
@@ -142,6 +142,26 @@ def test_test_hook_flags(kda):
     flags = oracle.FLAG_SKIP_CONV | oracle.FLAG_RAW_GATE | oracle.FLAG_RAW_BETA
     o, S, _ = run_varlen(kda, p, flags=flags)
     assert_parity(p, o, S, None, flags=flags)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_hook_flags(kda, D):
+    # the bf16 fast prep path with every test hook switched on
+    p = make_problem(342 + D, [90, 33], 2, D, D, BF16, state_seqs=[0], conv_state=True)
+    r = np.random.default_rng(1)
+    p.alpha = f32_to_bf16_bits((-r.random(p.alpha.shape) * 2).astype(np.float32))   # g in (-2, 0]
+    p.b = f32_to_bf16_bits(r.random(p.b.shape).astype(np.float32))                  # beta in [0, 1)
+    flags = oracle.FLAG_SKIP_CONV | oracle.FLAG_RAW_GATE | oracle.FLAG_RAW_BETA | oracle.FLAG_BETA_X2
+    o, S, cs = run_varlen(kda, p, flags=flags)
+    assert_parity(p, o, S, cs, flags=flags)
+
+
+def test_bf16_many_chunks_per_workgroup(kda):
+    # few heads and long sequences: each prep workgroup walks several chunks,
+    # with the next chunk's inputs prefetched while the current one computes
+    p = make_problem(347, [5000, 3333, 77], 2, 128, 128, BF16, state_seqs=[0, 2], conv_state=True)
+    o, S, cs = run_varlen(kda, p)
+    assert_parity(p, o, S, cs)
 
 
 def test_beta_x2_variant(kda):
