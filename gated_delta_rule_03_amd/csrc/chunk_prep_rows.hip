@@ -85,12 +85,12 @@ struct ChunkPos {
   int64_t tok0;
 };
 
-__device__ __forceinline__ ChunkPos chunk_pos(const ChunkTable& t, int c) {
+__device__ __forceinline__ ChunkPos chunk_pos(const int4& d) {
   ChunkPos cp;
-  cp.s = t.chunk_seq[c];
-  cp.tau0 = (c - t.chunk0[cp.s]) * kChunk;
-  cp.tok0 = static_cast<int64_t>(t.cu[cp.s]) + cp.tau0;
-  cp.len = min(kChunk, t.cu[cp.s + 1] - static_cast<int>(cp.tok0));
+  cp.s = d.x;
+  cp.tau0 = d.y;
+  cp.len = d.z;
+  cp.tok0 = d.w;
   return cp;
 }
 
@@ -106,6 +106,7 @@ struct RawChunk {
   uint4 x[kPer];      // staging rows, then written to LDS
   uint4 a[2];         // alpha of this lane's row and 16 channels
   uint16_t b;         // b of this lane's row
+  uint32_t zero;      // bit j: piece j stands for a missing history row (written as zeros)
 };
 
 }  // namespace
@@ -204,6 +205,9 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     const uint16_t* st_h = static_cast<const uint16_t*>(have_hist ? io.conv_in : io.q) +
                            (have_hist ? static_cast<size_t>(cp.s) * 3 * Ctot + st_tens * HD + static_cast<size_t>(h) * D + st_ch
                                       : 0);
+    // (the zeroing is applied when the pieces are written to LDS: a select
+    // here would wait for every load, and for every store before it)
+    nx.zero = 0u;
 #pragma unroll
     for (int j = 0; j < Raw::kPer; ++j) {
       const int sr = st_row0 + Raw::kSR * j;
@@ -211,9 +215,8 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       const bool hist = tau < 0;
       const int64_t tok = cp.tok0 + (hist ? 0 : min(sr - 3, cp.len - 1));   // any valid row for a history slot
       const uint16_t* px = hist && have_hist ? st_h + static_cast<size_t>(3 + tau) * Ctot : st_x + tok * HD;
-      const uint4 v = *reinterpret_cast<const uint4*>(px);
-      const bool zero = !stager || sr >= kRawRows || (hist && !have_hist);
-      nx.x[j] = zero ? make_uint4(0u, 0u, 0u, 0u) : v;
+      nx.x[j] = *reinterpret_cast<const uint4*>(px);
+      if (hist && !have_hist) nx.zero |= 1u << j;
     }
     const int64_t tok = cp.tok0 + min(L.r, cp.len - 1);
 #pragma unroll
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   Raw nxt;
   ChunkPos nxt_pos{};
   if (grp < total) {
-    nxt_pos = chunk_pos(t, grp);
+    nxt_pos = chunk_pos(t.desc[grp]);
     load_raw(nxt, nxt_pos, coords(tid));
   }
 
@@ -243,10 +246,20 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
     for (int j = 0; j < Raw::kPer; ++j) {
       const int sr = st_row0 + Raw::kSR * j;
-      if (stager && sr < kRawRows) *reinterpret_cast<uint4*>(&sRaw[sr * RAWS + 8 * st_col]) = nxt.x[j];
+      if (stager && sr < kRawRows)
+        *reinterpret_cast<uint4*>(&sRaw[sr * RAWS + 8 * st_col]) =
+            (nxt.zero >> j) & 1u ? make_uint4(0u, 0u, 0u, 0u) : nxt.x[j];
     }
-    const uint4 a_cur[2] = {nxt.a[0], nxt.a[1]};
-    const uint16_t b_cur = nxt.b;
+    uint32_t aw[8] = {nxt.a[0].x, nxt.a[0].y, nxt.a[0].z, nxt.a[0].w, nxt.a[1].x, nxt.a[1].y, nxt.a[1].z, nxt.a[1].w};
+    uint32_t b_cur = nxt.b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(aw[i]));   // arrived before the next load goes out
+    asm volatile("" : "+v"(b_cur));
+    const uint4 a_cur[2] = {make_uint4(aw[0], aw[1], aw[2], aw[3]), make_uint4(aw[4], aw[5], aw[6], aw[7])};
+    // where the chunk after this one lies: loaded now (after the wait for the
+    // staging rows, so that wait does not include it), used in phase 4; a
+    // clamped index rather than a select, which would wait for the load
+    const int4 next_desc = t.desc[min(c + G, total - 1)];
     __syncthreads();
 
     uint8_t* rec = records + (static_cast<size_t>(c) * H + h) * REC.bytes;
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     pin(gv);
     float beta = 0.f;
     if (live) {
-      const float bb = bf16_to_f32(b_cur);
+      const float bb = bf16_to_f32(static_cast<uint16_t>(b_cur));
       beta = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
       if (flags & KDA_FLAG_BETA_X2) beta *= 2.0f;
     }
@@ -546,14 +559,23 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     // ---- the next chunk's raw inputs go out now: phases 4 and 5 hold few
     //      registers, and they hide the loads' latency
     if (c + G < total) {
-      nxt_pos = chunk_pos(t, c + G);
+      // kept in vector registers until here, so that moving it to scalar
+      // registers does not wait for the load early
+      int nd[4] = {next_desc.x, next_desc.y, next_desc.z, next_desc.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(nd[i]));
+      nxt_pos = chunk_pos(make_int4(nd[0], nd[1], nd[2], nd[3]));
       load_raw(nxt, nxt_pos, L);
     }
 
     // ---- 4. Aqk pieces out; A pieces and the diagonal-block inverses to LDS; beta K+ to X^T
     {
       __bf16* Aq = reinterpret_cast<__bf16*>(rec + REC.Aqk);
-      for (int e = L.tid; e < 64 * 8; e += NT) {
+      // a fixed trip count, not a loop (a loop here makes the compiler wait
+      // for every outstanding load first)
+#pragma unroll
+      for (int it = 0; it < 64 * 8 / NT; ++it) {
+        const int e = L.tid + it * NT;
         const int rw = e >> 3, i0 = 8 * (e & 7);
         const float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
         const float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);

@@ -3,7 +3,8 @@
 // build_chunks_kernel turns sequence offsets (device cu_seqlens, or B equal
 // lengths) into a chunk table without any host synchronisation: chunk0[s] is
 // the first 64-token chunk of sequence s (an exclusive scan of ceil(len/64)),
-// chunk0[N] the number of chunks, and chunk_seq[c] the sequence owning chunk c.
+// chunk0[N] the number of chunks, chunk_seq[c] the sequence owning chunk c and
+// desc[c] where chunk c lies.
 // Chunks never straddle two sequences; the last chunk of a sequence may be
 // partial.  Grids of the chunk kernels are sized by a host upper bound and
 // blocks past chunk0[N] exit.
@@ -50,10 +51,14 @@ __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __res
 }
 
 // chunk_seq[c] = the last sequence whose first chunk is <= c (empty sequences
-// share their successor's first chunk and are skipped this way).  A separate
-// launch, so that every chunk0 entry written above is visible.
-__global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __restrict__ chunk0, int32_t N,
-                                                             int32_t* __restrict__ chunk_seq, int32_t max_chunks) {
+// share their successor's first chunk and are skipped this way), and the
+// chunk's descriptor (sequence, first token within it, token count, first
+// packed token), so that a kernel finds a chunk's place with one load.  A
+// separate launch, so that every chunk0 and cu entry written above is visible.
+__global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __restrict__ chunk0,
+                                                             const int32_t* __restrict__ cu, int32_t N,
+                                                             int32_t* __restrict__ chunk_seq, int4* __restrict__ desc,
+                                                             int32_t max_chunks) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= max_chunks || c >= chunk0[N]) return;
   int lo = 0, hi = N - 1;
@@ -62,14 +67,17 @@ __global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __re
     if (chunk0[mid] <= c) lo = mid; else hi = mid - 1;
   }
   chunk_seq[c] = lo;
+  const int tau0 = (c - chunk0[lo]) * kChunk;
+  const int tok0 = cu[lo] + tau0;
+  desc[c] = make_int4(lo, tau0, min(kChunk, cu[lo + 1] - tok0), tok0);
 }
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws, int32_t* chunk0,
-                               int32_t* chunk_seq, int32_t max_chunks, hipStream_t st) {
+                               int32_t* chunk_seq, int4* desc, int32_t max_chunks, hipStream_t st) {
   build_chunks_kernel<<<1, 1024, 0, st>>>(cu_in, N, T_uniform, cu_ws, chunk0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_chunks <= 0) return e;
-  fill_chunk_seq_kernel<<<(max_chunks + 255) / 256, 256, 0, st>>>(chunk0, N, chunk_seq, max_chunks);
+  fill_chunk_seq_kernel<<<(max_chunks + 255) / 256, 256, 0, st>>>(chunk0, cu_ws, N, chunk_seq, desc, max_chunks);
   return hipGetLastError();
 }
 

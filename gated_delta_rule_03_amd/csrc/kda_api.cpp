@@ -64,7 +64,7 @@ Params make_params(const kda_config_t* cfg) {
 int pieces(const kda_config_t* cfg) { return cfg->io_dtype == KDA_BF16 ? 2 : 3; }
 
 struct Layout {
-  size_t cu, chunk0, chunk_seq, records, total;
+  size_t cu, chunk0, chunk_seq, desc, records, total;
 };
 
 Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D, int NP) {
@@ -74,6 +74,7 @@ Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D, int NP) 
   L.cu = take((N + 1) * sizeof(int32_t));
   L.chunk0 = take((N + 1) * sizeof(int32_t));
   L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
+  L.desc = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int4));
   L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D), NP).bytes);
   L.total = off;
   return L;
@@ -110,14 +111,15 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   int32_t* cu_ws = reinterpret_cast<int32_t*>(ws + L.cu);
   int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
   int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
-  ChunkTable t{cu_ws, chunk0, chunk_seq, N};
+  int4* desc = reinterpret_cast<int4*>(ws + L.desc);
+  ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N};
   uint8_t* records = reinterpret_cast<uint8_t*>(ws + L.records);
   const bool io_bf16 = cfg->io_dtype == KDA_BF16;
   const bool out_bf16 = cfg->out_dtype == KDA_BF16;
   const int mc = static_cast<int>(max_chunks);
 
   kda_status_t s = stage(cfg, KDA_STAGE_CHUNK_TABLE, st, [&] {
-    return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, mc, st);
+    return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, desc, mc, st);
   });
   if (s != KDA_OK) return s;
   if (total_T > 0 && mc > 0) {

@@ -64,6 +64,7 @@ struct ChunkTable {
   const int32_t* cu;         // [N+1] token offsets
   const int32_t* chunk0;     // [N+1] first chunk of each sequence; chunk0[N] = total chunks
   const int32_t* chunk_seq;  // [max_chunks] sequence of each chunk
+  const int4* desc;          // [max_chunks] (sequence, first token in it, tokens, first packed token)
   int32_t N;
 };
 
@@ -81,7 +82,7 @@ struct PrefillIO {
 };
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws,
-                               int32_t* chunk0, int32_t* chunk_seq, int32_t max_chunks, hipStream_t st);
+                               int32_t* chunk0, int32_t* chunk_seq, int4* desc, int32_t max_chunks, hipStream_t st);
 hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                              int max_chunks, bool io_bf16, hipStream_t st);
 // The row-block prep kernel (bf16 inputs, dk = dv in {64, 128}, 16-byte
