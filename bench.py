@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import statistics
@@ -163,9 +164,25 @@ def roofline_for(kda, per_stage, B, T):
     else:
         roof = {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(name)
     roof.update({"avg_ms": round(ms, 4), "flops_per_launch": flops, "bytes_per_launch": nbytes,
                  "mfma_frac": round(mfma_frac, 4), "hbm_frac": round(hbm_frac, 4)})
     return roof
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of a stage's kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (scaled by a plain copy's readings), or
+    None when there are none or the kernel's source has changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][stage]
+        with open(os.path.join(ROOT, "gated_delta_rule_03_amd", "csrc", rec["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if sha == rec["source_sha256_16"] else None
 
 
 def bench_decode(kda, torch, ev, n_steps=128, warmup=3):
