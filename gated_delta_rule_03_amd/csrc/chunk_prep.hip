@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
           __bf16 pc[NP];
           split_pieces<NP>(qv * (eP * eBefore), pc);
 #pragma unroll
-          for (int k = 0; k < NP; ++k) Qp[k * (REC.tile_plane / 2) + r * D + ch] = pc[k];
+          for (int k = 0; k < NP; ++k) Qp[k * (REC.tile_plane / 2) + frag_index(r, ch, KP)] = pc[k];
         }
         eBefore *= eBt[J];
       }
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
       // k e^{Q_r + later block totals}, Q_r = in-block sum of g after token r;
       // built backwards
       // (8 tokens per 16-byte store of each piece plane)
-      bf16x8* KT = reinterpret_cast<bf16x8*>(rec + REC.KT) + ch * (kChunk / 8);
+      bf16x8* KT = reinterpret_cast<bf16x8*>(rec + REC.KT);
       {
         float after = 0.f, Qs = 0.f, tmp[8];
 #pragma unroll
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
           if (r % 8 == 0) {
             const SplitN<NP> sp = splitN<NP>(tmp);
 #pragma unroll
-            for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 16) + r / 8] = sp.v[k];
+            for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 16) + frag_index(ch, r, kChunk) / 8] = sp.v[k];
           }
         }
       }
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
             sA[r * LA + i] = 0.f;
           } else {
 #pragma unroll
-            for (int k = 0; k < NP; ++k) Aq[k * (REC.aqk_plane / 2) + r * kChunk + i] = static_cast<__bf16>(0.f);
+            for (int k = 0; k < NP; ++k) Aq[k * (REC.aqk_plane / 2) + frag_index(r, i, kChunk)] = static_cast<__bf16>(0.f);
           }
         }
         continue;
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
           __bf16 pc[NP];
           split_pieces<NP>((i <= r) ? acc[j] : 0.f, pc);
 #pragma unroll
-          for (int k = 0; k < NP; ++k) Aq[k * (REC.aqk_plane / 2) + r * kChunk + i] = pc[k];
+          for (int k = 0; k < NP; ++k) Aq[k * (REC.aqk_plane / 2) + frag_index(r, i, kChunk)] = pc[k];
         }
       }
     }
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
       __syncthreads();
     }
   }
-  // W token-major and U^T channel-major from X^T
+  // W and U^T from X^T, in fragment order
   {
     __bf16* W = reinterpret_cast<__bf16*>(rec + REC.W);
     for (int e = tid; e < kChunk * D; e += NT) {
@@ -414,12 +414,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
       __bf16 pc[NP];
       split_pieces<NP>(sX[cc * LX + r], pc);
 #pragma unroll
-      for (int k = 0; k < NP; ++k) W[k * (REC.tile_plane / 2) + e] = pc[k];
+      for (int k = 0; k < NP; ++k) W[k * (REC.tile_plane / 2) + frag_index(r, cc, KP)] = pc[k];
     }
     float4* UT = reinterpret_cast<float4*>(rec + REC.UT);
     for (int e = tid; e < D * kChunk / 4; e += NT) {
       const int cc = e / (kChunk / 4), v4 = e % (kChunk / 4);
-      UT[e] = *reinterpret_cast<const float4*>(&sX[(D + cc) * LX + 4 * v4]);
+      UT[ut_index(cc, 4 * v4) / 4] = *reinterpret_cast<const float4*>(&sX[(D + cc) * LX + 4 * v4]);
     }
   }
 }

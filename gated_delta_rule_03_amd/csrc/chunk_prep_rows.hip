@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
           __bf16 pc[NP];
           split_pieces<NP>(kt[i], pc);
 #pragma unroll
-          for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 2) + (c0 + i) * kChunk + r] = pc[k];
+          for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 2) + frag_index(c0 + i, r, kChunk)] = pc[k];
         }
         if (R == 3 && ln == 15) {   // e^{G_C} = e^{G before block 3} e^{P_63}
           float eg[8];
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         const SplitN<NP> qs = splitN<NP>(qo);
 #pragma unroll
         for (int k = 0; k < NP; ++k)
-          *reinterpret_cast<bf16x8*>(Qp + k * (REC.tile_plane / 2) + r * D + c0) = qs.v[k];
+          *reinterpret_cast<bf16x8*>(Qp + k * (REC.tile_plane / 2) + frag_index(r, c0, D)) = qs.v[k];
         compiler_fence();
       }
     }
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         const SplitN<NP> qs = splitN<NP>(qm), as = splitN<NP>(am);
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-          *reinterpret_cast<bf16x8*>(Aq + k * (REC.aqk_plane / 2) + rw * kChunk + i0) = qs.v[k];
+          *reinterpret_cast<bf16x8*>(Aq + k * (REC.aqk_plane / 2) + frag_index(rw, i0, kChunk)) = qs.v[k];
           *reinterpret_cast<bf16x8*>(&sAp[k][rw * LAP + i0]) = as.v[k];
         }
       }
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
       for (int bi = 0; bi < CBPW; ++bi) {
         const int cb = w + bi * NW;
-        if (cb < D / 16) {   // W, token-major: 8 channels of one token per lane and step
+        if (cb < D / 16) {   // W: 8 channels of one token per lane and step
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
             const int u = lane + 64 * k2, tok = u >> 1, c8 = 16 * cb + 8 * (u & 1);
@@ -711,14 +711,14 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
             const SplitN<NP> ws = splitN<NP>(xv);
 #pragma unroll
             for (int k = 0; k < NP; ++k)
-              *reinterpret_cast<bf16x8*>(W + k * (REC.tile_plane / 2) + tok * D + c8) = ws.v[k];
+              *reinterpret_cast<bf16x8*>(W + k * (REC.tile_plane / 2) + frag_index(tok, c8, D)) = ws.v[k];
           }
-        } else {             // U^T, channel-major fp32
+        } else {             // U^T, fp32
 #pragma unroll
           for (int k2 = 0; k2 < 4; ++k2) {
             const int u = lane + 64 * k2, m = u >> 4, t4 = u & 15;
             const int cu = 16 * cb - D + m;
-            *reinterpret_cast<float4*>(UT + cu * kChunk + 4 * t4) =
+            *reinterpret_cast<float4*>(UT + ut_index(cu, 4 * t4)) =
                 *reinterpret_cast<const float4*>(&sX[(16 * cb + m) * LX + 4 * t4]);
           }
         }

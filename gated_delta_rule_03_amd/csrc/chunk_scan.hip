@@ -52,15 +52,16 @@ __device__ __forceinline__ void load_ops(WaveOps<D, DVT, NP>& o, const uint8_t* 
                                          int nks_a) {
   constexpr Record REC = record_layout(D, NP);
   using Ops = WaveOps<D, DVT, NP>;
-  constexpr int KS = Ops::KS, CJ = Ops::CJ, CBW = Ops::CBW, CB = D / 16;
+  constexpr int KS = Ops::KS, CJ = Ops::CJ, CBW = Ops::CBW, CB = D / 16, KPD = 32 * KS;
   const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
   const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
   const int r0 = 16 * wave;
+  // every load below reads the wave's 1 KB fragment block, contiguous
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int ch0 = 32 * ks + 8 * q4;
     if (ch0 < D) {
-      const size_t el = static_cast<size_t>(r0 + ln) * D + ch0;
+      const size_t el = frag_index(r0 + ln, ch0, KPD);
       o.w[ks] = load_planes<NP>(rec + REC.W, REC.tile_plane, el);
       o.q[ks] = load_planes<NP>(rec + REC.Qp, REC.tile_plane, el);
     } else {
@@ -69,19 +70,18 @@ __device__ __forceinline__ void load_ops(WaveOps<D, DVT, NP>& o, const uint8_t* 
   }
 #pragma unroll
   for (int cj = 0; cj < CJ; ++cj)
-    o.u[cj] = *reinterpret_cast<const float4*>(UT + static_cast<size_t>(j0 + 16 * cj + ln) * kChunk + r0 + 4 * q4);
+    o.u[cj] = *reinterpret_cast<const float4*>(UT + ut_index(j0 + 16 * cj + ln, r0 + 4 * q4));
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     if (ks < nks_a)
-      o.a[ks] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, static_cast<size_t>(r0 + ln) * kChunk + 32 * ks + 8 * q4);
+      o.a[ks] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, frag_index(r0 + ln, 32 * ks + 8 * q4, kChunk));
 #pragma unroll
   for (int i = 0; i < CBW; ++i) {
     const int cb = wave + 4 * i;
     if (cb < CB) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        o.kt[i][ks] = load_planes<NP>(rec + REC.KT, REC.tile_plane,
-                                      static_cast<size_t>(16 * cb + ln) * kChunk + 32 * ks + 8 * q4);
+        o.kt[i][ks] = load_planes<NP>(rec + REC.KT, REC.tile_plane, frag_index(16 * cb + ln, 32 * ks + 8 * q4, kChunk));
       o.e[i] = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
     }
   }

@@ -12,24 +12,31 @@ namespace kda {
 constexpr int kChunk = 64;   // tokens per chunk of the chunked form
 constexpr int kSub = 16;     // tokens per decay sub-block inside a chunk
 
-// Per (chunk, head) record written by the chunk-prep kernel and read by the
-// chunk-scan kernel: the operands of the state recurrence in the layouts the
-// matrix-core operand loads read.  The four matrix operands are stored as NP
-// bf16 piece planes (x ~ p0 + p1 (+ p2), see mfma.h), so the sequential scan
-// loads them ready for the matrix cores; U and e^{G_C} stay fp32.
-//   W   [NP][64][D]   W = (I + A)^-1 Diag(beta) (K * e^G), token-major
-//   Qp  [NP][64][D]   Q+ = Q * e^G, token-major
-//   KT  [NP][D][64]   K~^T = (K * e^{G_C - G})^T, channel-major
-//   Aqk [NP][64][64]  the masked intra-chunk attention, token-major
-//   UT  [D][64]       U^T = ((I + A)^-1 Diag(beta) V)^T, fp32
-//   eGC [D]           e^{G_C}, the whole-chunk decay, fp32
+// Per (chunk, head) record written by the chunk-prep kernels and read by the
+// chunk-scan kernel: the operands of the state recurrence.  The four matrix
+// operands are stored as NP bf16 piece planes (x ~ p0 + p1 (+ p2), see mfma.h),
+// so the sequential scan loads them ready for the matrix cores; U and e^{G_C}
+// stay fp32.
+//   W   [NP][64][KPD]  W = (I + A)^-1 Diag(beta) (K * e^G), token rows
+//   Qp  [NP][64][KPD]  Q+ = Q * e^G, token rows
+//   KT  [NP][D][64]    K~^T = (K * e^{G_C - G})^T, channel rows
+//   Aqk [NP][64][64]   the masked intra-chunk attention, token rows
+//   UT  [D][64]        U^T = ((I + A)^-1 Diag(beta) V)^T, fp32
+//   eGC [D]            e^{G_C}, the whole-chunk decay, fp32
+// (KPD = max(D, 32): channel columns in whole 32-wide matrix-core steps.)
+//
+// Every tile is stored in matrix-core fragment order (frag_index, ut_index):
+// the 16 bytes that lane l of a wave loads for one 16x16x32 step sit at
+// ((row block * steps + step) * 64 + l) * 16, so each wave-wide load reads
+// 1 KB of contiguous memory, eight whole cache lines.
 struct Record {
   size_t W, Qp, KT, Aqk, UT, eGC, bytes;
-  size_t tile_plane, aqk_plane;   // bytes of one piece plane of a [64][D] tile / of Aqk
+  size_t tile_plane, aqk_plane;   // bytes of one piece plane of a [64][KPD] tile / of Aqk
 };
 
 __host__ __device__ constexpr Record record_layout(int D, int NP) {
-  const size_t tp = static_cast<size_t>(64) * D * 2;
+  const int KPD = D < 32 ? 32 : D;
+  const size_t tp = static_cast<size_t>(64) * KPD * 2;
   const size_t ap = static_cast<size_t>(64) * 64 * 2;
   Record r{};
   r.tile_plane = tp;
@@ -42,6 +49,20 @@ __host__ __device__ constexpr Record record_layout(int D, int NP) {
   r.eGC = r.UT + static_cast<size_t>(64) * D * 4;
   r.bytes = (r.eGC + static_cast<size_t>(D) * 4 + 255) / 256 * 256;
   return r;
+}
+
+// Element index of X[row][col] in a fragment-ordered bf16 tile with `cols`
+// columns (a multiple of 32): lane = row % 16 + 16 * (col % 32 / 8) of step
+// (row / 16, col / 32) holds columns col - col % 8 .. +7.
+__host__ __device__ constexpr size_t frag_index(int row, int col, int cols) {
+  return ((static_cast<size_t>(row >> 4) * (cols >> 5) + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 +
+         (col & 7);
+}
+
+// Element index of U^T[v][t] (64 token columns, fp32): lane = v % 16 +
+// 16 * (t % 16 / 4) of block (v / 16, t / 16) holds tokens t - t % 4 .. +3.
+__host__ __device__ constexpr size_t ut_index(int v, int t) {
+  return ((static_cast<size_t>(v >> 4) * 4 + (t >> 4)) * 64 + (v & 15) + 16 * ((t & 15) >> 2)) * 4 + (t & 3);
 }
 
 // Parameters every kernel that touches raw inputs needs.
