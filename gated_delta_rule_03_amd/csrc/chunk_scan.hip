@@ -26,14 +26,19 @@
 namespace kda {
 
 // One wave's record operands for one chunk, already split into bf16 pieces,
-// so that the next chunk's loads are in flight while the current computes.
+// in two halves by when they are used: OpsA before the first barrier of a
+// chunk (W S, Q+ S, Delta), OpsB after it (Aqk Delta, K~^T Delta, e^{G_C}).
 template <int D, int DVT, int NP>
-struct WaveOps {
+struct OpsA {
   static constexpr int KS = (D < 32 ? 32 : D) / 32;
   static constexpr int CJ = DVT / 16;
-  static constexpr int CBW = (D / 16 + 3) / 4;
   SplitN<NP> w[KS], q[KS];       // W, Q+ rows of this wave's tokens
   float4 u[CJ];                  // U^T, four tokens of one value column
+};
+
+template <int D, int DVT, int NP>
+struct OpsB {
+  static constexpr int CBW = (D / 16 + 3) / 4;
   SplitN<NP> a[2];               // Aqk rows (two 32-token steps)
   SplitN<NP> kt[CBW][2];         // K~^T rows of this wave's state rows
   float4 e[CBW];                 // e^{G_C} of this lane's four state rows
@@ -47,16 +52,14 @@ __device__ __forceinline__ SplitN<NP> load_planes(const uint8_t* base, size_t pl
   return s;
 }
 
+// Every load below reads the wave's 1 KB fragment block, contiguous.
 template <int D, int DVT, int NP>
-__device__ __forceinline__ void load_ops(WaveOps<D, DVT, NP>& o, const uint8_t* rec, int wave, int ln, int q4, int j0,
-                                         int nks_a) {
+__device__ __forceinline__ void load_ops_a(OpsA<D, DVT, NP>& o, const uint8_t* rec, int wave, int ln, int q4, int j0) {
   constexpr Record REC = record_layout(D, NP);
-  using Ops = WaveOps<D, DVT, NP>;
-  constexpr int KS = Ops::KS, CJ = Ops::CJ, CBW = Ops::CBW, CB = D / 16, KPD = 32 * KS;
+  using Ops = OpsA<D, DVT, NP>;
+  constexpr int KS = Ops::KS, CJ = Ops::CJ, KPD = 32 * KS;
   const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
-  const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
   const int r0 = 16 * wave;
-  // every load below reads the wave's 1 KB fragment block, contiguous
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int ch0 = 32 * ks + 8 * q4;
@@ -71,6 +74,15 @@ __device__ __forceinline__ void load_ops(WaveOps<D, DVT, NP>& o, const uint8_t* 
 #pragma unroll
   for (int cj = 0; cj < CJ; ++cj)
     o.u[cj] = *reinterpret_cast<const float4*>(UT + ut_index(j0 + 16 * cj + ln, r0 + 4 * q4));
+}
+
+template <int D, int DVT, int NP>
+__device__ __forceinline__ void load_ops_b(OpsB<D, DVT, NP>& o, const uint8_t* rec, int wave, int ln, int q4,
+                                           int nks_a) {
+  constexpr Record REC = record_layout(D, NP);
+  constexpr int CBW = OpsB<D, DVT, NP>::CBW, CB = D / 16;
+  const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
+  const int r0 = 16 * wave;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     if (ks < nks_a)
@@ -99,8 +111,10 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   constexpr int LST = KP + 8;             // row stride of S^T in LDS (bf16)
   constexpr int LDT = kChunk + 8;         // row stride of Delta^T in LDS (bf16)
   constexpr Record REC = record_layout(D, NP);
+  constexpr int LO = DVT + 4;              // row stride of a wave's output tile in LDS (fp32)
   __shared__ __align__(16) __bf16 sST[NP][DVT * LST];
   __shared__ __align__(16) __bf16 sDT[NP][DVT * LDT];
+  __shared__ __align__(16) float sO[4][16 * LO];   // each wave's 16 output rows, for row-contiguous stores
 
   const int H = p.H;
   // XCD-aware order: blockIdx = ((sh / 8) * NTILE + tile) * 8 + sh % 8
@@ -164,12 +178,23 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   const int seq_len = t.cu[s + 1] - t.cu[s];
   const int r0 = 16 * wave;                         // this wave's token rows
   const int nks_a = wave >= 2 ? 2 : 1;              // k steps of Aqk Delta (causal)
-  WaveOps<D, DVT, NP> cur, nxt;
-  if (c_first < c_end)
-    load_ops<D, DVT, NP>(cur, records + (static_cast<size_t>(c_first) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
-  for (int c = c_first; c < c_end; ++c) {
-    if (c + 1 < c_end)
-      load_ops<D, DVT, NP>(nxt, records + (static_cast<size_t>(c + 1) * H + h) * REC.bytes, wave, ln, q4, j0, nks_a);
+  // Two buffers of each operand half, for chunks of alternate parity.  Each
+  // buffer is refilled with chunk c + 2 as soon as chunk c has read it (the
+  // A half after the first barrier, the B half at the end of the chunk), so
+  // every record load is in flight for about one and a half chunks.
+  OpsA<D, DVT, NP> A0, A1;
+  OpsB<D, DVT, NP> B0, B1;
+  auto rec_of = [&](int c) { return records + (static_cast<size_t>(c) * H + h) * REC.bytes; };
+  if (c_first < c_end) {
+    load_ops_a<D, DVT, NP>(A0, rec_of(c_first), wave, ln, q4, j0);
+    load_ops_b<D, DVT, NP>(B0, rec_of(c_first), wave, ln, q4, nks_a);
+  }
+  if (c_first + 1 < c_end) {
+    load_ops_a<D, DVT, NP>(A1, rec_of(c_first + 1), wave, ln, q4, j0);
+    load_ops_b<D, DVT, NP>(B1, rec_of(c_first + 1), wave, ln, q4, nks_a);
+  }
+
+  auto chunk_step = [&](int c, OpsA<D, DVT, NP>& A, OpsB<D, DVT, NP>& B) {
     const int tau = (c - c_first) * kChunk;
     const int len = min(kChunk, seq_len - tau);
 
@@ -180,21 +205,19 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * q4;
-      const SplitN<NP>& aW = cur.w[ks];
-      const SplitN<NP>& aQ = cur.q[ks];
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         SplitN<NP> bS;
 #pragma unroll
         for (int k = 0; k < NP; ++k) bS.v[k] = load_bf16x8(&sST[k][(16 * cj + ln) * LST + ch0]);
-        accW[cj] = mfmaN<NP>(aW, bS, accW[cj]);
-        accQ[cj] = mfmaN<NP>(aQ, bS, accQ[cj]);
+        accW[cj] = mfmaN<NP>(A.w[ks], bS, accW[cj]);
+        accQ[cj] = mfmaN<NP>(A.q[ks], bS, accQ[cj]);
       }
     }
     // Delta = U - W S, published transposed for the B operands below
 #pragma unroll
     for (int cj = 0; cj < CJ; ++cj) {
-      const float4 u = cur.u[cj];
+      const float4 u = A.u[cj];
       const float dl[4] = {u.x - accW[cj][0], u.y - accW[cj][1], u.z - accW[cj][2], u.w - accW[cj][3]};
       bf16x4 pk[NP];
 #pragma unroll
@@ -208,13 +231,14 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
       for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4*>(&sDT[k][idx]) = pk[k];
     }
+    if (c + 2 < c_end) load_ops_a<D, DVT, NP>(A, rec_of(c + 2), wave, ln, q4, j0);
     __syncthreads();
 
     // ---- O = Q+ S + Aqk Delta;  S = e^{G_C} S + K~^T Delta
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       if (wave + 4 * i >= CB) continue;
-      const float4 e4 = cur.e[i];
+      const float4 e4 = B.e[i];
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         Sacc[i][cj][0] *= e4.x; Sacc[i][cj][1] *= e4.y; Sacc[i][cj][2] *= e4.z; Sacc[i][cj][3] *= e4.w;
@@ -223,32 +247,58 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int t0 = 32 * ks + 8 * q4;
-      const SplitN<NP>& aA = cur.a[ks];
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         SplitN<NP> bD;
 #pragma unroll
         for (int k = 0; k < NP; ++k) bD.v[k] = load_bf16x8(&sDT[k][(16 * cj + ln) * LDT + t0]);
-        if (ks < nks_a) accQ[cj] = mfmaN<NP>(aA, bD, accQ[cj]);
+        if (ks < nks_a) accQ[cj] = mfmaN<NP>(B.a[ks], bD, accQ[cj]);
 #pragma unroll
         for (int i = 0; i < CBW; ++i)
-          if (wave + 4 * i < CB) Sacc[i][cj] = mfmaN<NP>(cur.kt[i][ks], bD, Sacc[i][cj]);
+          if (wave + 4 * i < CB) Sacc[i][cj] = mfmaN<NP>(B.kt[i][ks], bD, Sacc[i][cj]);
       }
     }
-    // store this wave's output rows
+    if (c + 2 < c_end) load_ops_b<D, DVT, NP>(B, rec_of(c + 2), wave, ln, q4, nks_a);
+    // this wave's output rows: through its own LDS tile (LDS operations of a
+    // wave run in order), then stored row-contiguous, 8 or 16 bytes per
+    // access (few memory operations per chunk leave room for the record
+    // loads in flight: a wave may have at most 63 outstanding)
+    {
+      float* so = sO[wave];
 #pragma unroll
-    for (int cj = 0; cj < CJ; ++cj) {
+      for (int cj = 0; cj < CJ; ++cj)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r0 + 4 * q4 + j;
-        if (r < len)
-          st<OUT_BF16>(io.o, (static_cast<size_t>(seq0 + tau + r) * H + h) * D + j0 + 16 * cj + ln, accQ[cj][j]);
+        for (int j = 0; j < 4; ++j) so[(4 * q4 + j) * LO + 16 * cj + ln] = accQ[cj][j];
+      asm volatile("" ::: "memory");
+      constexpr int LPR = 64 / 16;            // lanes per output row
+      constexpr int CPL = DVT / LPR;          // columns per lane
+      const int orow = lane / LPR, oc0 = (lane % LPR) * CPL;
+      if (r0 + orow < len) {
+        const size_t base = (static_cast<size_t>(seq0 + tau + r0 + orow) * H + h) * D + j0 + oc0;
+        if constexpr (OUT_BF16) {
+#pragma unroll
+          for (int c4 = 0; c4 < CPL; c4 += 4) {   // four bf16 per 8-byte store
+            const float4 a = *reinterpret_cast<const float4*>(&so[orow * LO + oc0 + c4]);
+            const uint2 pk = make_uint2(f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16),
+                                        f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16));
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(io.o) + base + c4) = pk;
+          }
+        } else {
+#pragma unroll
+          for (int c4 = 0; c4 < CPL; c4 += 4)
+            *reinterpret_cast<float4*>(static_cast<float*>(io.o) + base + c4) =
+                *reinterpret_cast<const float4*>(&so[orow * LO + oc0 + c4]);
+        }
       }
     }
     // every wave is past its reads of S^T (barrier above): publish the new state
     publish_state();
     __syncthreads();
-    cur = nxt;
+  };
+
+  for (int c = c_first; c < c_end; c += 2) {
+    chunk_step(c, A0, B0);
+    if (c + 1 < c_end) chunk_step(c + 1, A1, B1);
   }
 
   if (io.S_out) {
