@@ -279,9 +279,9 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
           for (int c4 = 0; c4 < CPL; c4 += 4) {   // four bf16 per 8-byte store
             const float4 a = *reinterpret_cast<const float4*>(&so[orow * LO + oc0 + c4]);
-            const uint2 pk = make_uint2(f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16),
-                                        f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16));
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(io.o) + base + c4) = pk;
+            const bf16x4 pk = {static_cast<__bf16>(a.x), static_cast<__bf16>(a.y), static_cast<__bf16>(a.z),
+                               static_cast<__bf16>(a.w)};   // round to nearest even (v_cvt_pk_bf16_f32)
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(io.o) + base + c4) = pk;
           }
         } else {
 #pragma unroll
