@@ -205,15 +205,32 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     // (the zeroing is applied when the pieces are written to LDS: a select
     // here would wait for every load, and for every store before it)
     nx.zero = 0u;
+    if (cp.tau0 > 0) {
+      // every staging row is a token of this sequence: one base, one
+      // multiply-add per piece (rows past the chunk's end re-read its last)
+      const uint16_t* row0 = st_x + (cp.tok0 - 3) * static_cast<int64_t>(HD);
 #pragma unroll
-    for (int j = 0; j < Raw::kPer; ++j) {
-      const int sr = st_row0 + Raw::kSR * j;
-      const int tau = cp.tau0 + sr - 3;
-      const bool hist = tau < 0;
-      const int64_t tok = cp.tok0 + (hist ? 0 : min(sr - 3, cp.len - 1));   // any valid row for a history slot
-      const uint16_t* px = hist && have_hist ? st_h + static_cast<size_t>(3 + tau) * Ctot : st_x + tok * HD;
-      nx.x[j] = *reinterpret_cast<const uint4*>(px);
-      if (hist && !have_hist) nx.zero |= 1u << j;
+      for (int j = 0; j < Raw::kPer; ++j) {
+        const int sr = min(st_row0 + Raw::kSR * j, cp.len + 2);
+        nx.x[j] = *reinterpret_cast<const uint4*>(row0 + static_cast<int64_t>(sr) * HD);
+      }
+    } else {
+      // the sequence's first chunk: the three rows before it come from the
+      // conv history, or are zeros without one
+      const bool have_hist = io.conv_in != nullptr;
+      const uint16_t* st_h = static_cast<const uint16_t*>(have_hist ? io.conv_in : io.q) +
+                             (have_hist ? static_cast<size_t>(cp.s) * 3 * Ctot + st_tens * HD +
+                                              static_cast<size_t>(h) * D + st_ch
+                                        : 0);
+#pragma unroll
+      for (int j = 0; j < Raw::kPer; ++j) {
+        const int sr = st_row0 + Raw::kSR * j;
+        const bool hist = sr < 3;
+        const int64_t tok = cp.tok0 + (hist ? 0 : min(sr - 3, cp.len - 1));   // any valid row for a history slot
+        const uint16_t* px = hist && have_hist ? st_h + static_cast<size_t>(sr) * Ctot : st_x + tok * HD;
+        nx.x[j] = *reinterpret_cast<const uint4*>(px);
+        if (hist && !have_hist) nx.zero |= 1u << j;
+      }
     }
     const int64_t tok = cp.tok0 + min(L.r, cp.len - 1);
 #pragma unroll
