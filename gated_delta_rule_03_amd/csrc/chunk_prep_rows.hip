@@ -623,12 +623,21 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       }
       if (w == 0) {   // lane = (block, column) of the unit lower-triangular inverses
         const int Rb = lane >> 4, j = lane & 15;
+        // forward substitution down the column; each row's sum runs in four
+        // partial sums so the dependent chain is the 16 rows, not 120 FMAs
         float tcol[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float v = (i == j) ? 1.f : 0.f;
+          float a[16];
 #pragma unroll
-          for (int m = 0; m < i; ++m) v -= sA[(16 * Rb + i) * LA + 16 * Rb + m] * tcol[m];
+          for (int q = 0; q < 4; ++q) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sA[(16 * Rb + i) * LA + 16 * Rb + 4 * q]);
+            a[4 * q] = a4.x; a[4 * q + 1] = a4.y; a[4 * q + 2] = a4.z; a[4 * q + 3] = a4.w;
+          }
+          float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < i; ++m) ps[m & 3] += a[m] * tcol[m];
+          const float v = ((i == j) ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
           tcol[i] = (i < j) ? 0.f : v;
         }
 #pragma unroll
