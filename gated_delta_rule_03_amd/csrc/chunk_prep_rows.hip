@@ -64,6 +64,12 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// C += A B over one 16x16x4 fp32 matrix-core step: lane l gives A[l % 16][l / 16]
+// and B[l / 16][l % 16]; C is laid out as in the bf16 steps.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Pins computed values where they stand: the compiler may otherwise sink
@@ -119,8 +125,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   constexpr int KCS = D + 8;            // row stride of the k e^{-P} pieces (bf16)
   constexpr int LX = D == 64 ? kChunk + 8 : kChunk + 4;   // row stride of X^T (fp32)
   constexpr int LA = kChunk + 4;        // row stride of A, Aqk (fp32)
-  constexpr int LAP = kChunk + 8;       // row stride of the A pieces (bf16)
-  constexpr int LTP = 24;               // row stride of the T pieces (bf16)
+  constexpr int LT = 16 + 4;            // row stride of the diagonal-block inverses (fp32)
   constexpr int NCB = 2 * D / 16;       // 16-column blocks of X
   constexpr int CBPW = NCB / NW;        // ... per wave
   constexpr size_t kRawBytes = static_cast<size_t>(kRawRows) * RAWS * 2;
@@ -137,8 +142,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   __shared__ __align__(16) unsigned char sU[kUBytes];
   __shared__ __align__(16) float sA[64 * LA];            // A (rows scaled by beta)
   __shared__ __align__(16) float sAqk[64 * LA];
-  __shared__ __align__(16) __bf16 sAp[NP][64 * LAP];     // A pieces, blocks below the diagonal only
-  __shared__ __align__(16) __bf16 sTp[NP][4][16 * LTP];  // (I + A_RR)^-1 pieces
+  __shared__ __align__(16) float sT[4][16 * LT];         // (I + A_RR)^-1, fp32
   __shared__ __align__(16) uint2 sWb[3][D];              // conv taps of this head (q, k, v), 4 bf16 each
   __shared__ __align__(16) float sDtb[D];
   __shared__ __align__(16) float sBt[4][D];              // in-block totals of g
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       load_raw(nxt, nxt_pos, L);
     }
 
-    // ---- 4. Aqk pieces out; A pieces and the diagonal-block inverses to LDS; beta K+ to X^T
+    // ---- 4. Aqk pieces out; the diagonal-block inverses to LDS; beta K+ to X^T
     {
       __bf16* Aq = reinterpret_cast<__bf16*>(rec + REC.Aqk);
       // a fixed trip count, not a loop (a loop here makes the compiler wait
@@ -603,23 +607,14 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         const int rw = e >> 3, i0 = 8 * (e & 7);
         const float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
         const float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);
-        const float4 a0 = *reinterpret_cast<const float4*>(&sA[rw * LA + i0]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&sA[rw * LA + i0 + 4]);
         const float qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        const float aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        float qm[8], am[8];
-        const bool below = (i0 / 16) < (rw / 16);   // whole sub-block left of the diagonal block
+        float qm[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          qm[i] = (i0 + i <= rw) ? qa[i] : 0.f;
-          am[i] = below ? aa[i] : 0.f;
-        }
-        const SplitN<NP> qs = splitN<NP>(qm), as = splitN<NP>(am);
+        for (int i = 0; i < 8; ++i) qm[i] = (i0 + i <= rw) ? qa[i] : 0.f;
+        const SplitN<NP> qs = splitN<NP>(qm);
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
+        for (int k = 0; k < NP; ++k)
           *reinterpret_cast<bf16x8*>(Aq + k * (REC.aqk_plane / 2) + frag_index(rw, i0, kChunk)) = qs.v[k];
-          *reinterpret_cast<bf16x8*>(&sAp[k][rw * LAP + i0]) = as.v[k];
-        }
       }
       if (w == 0) {   // lane = (block, column) of the unit lower-triangular inverses
         const int Rb = lane >> 4, j = lane & 15;
@@ -641,12 +636,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
           tcol[i] = (i < j) ? 0.f : v;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __bf16 pc[NP];
-          split_pieces<NP>(tcol[i], pc);
-#pragma unroll
-          for (int k = 0; k < NP; ++k) sTp[k][Rb][i * LTP + j] = pc[k];
-        }
+        for (int i = 0; i < 16; ++i) sT[Rb][i * LT + j] = tcol[i];
       }
       // beta K+ = beta (k e^{P}) e^{G before the block}, over the k e^{-P} pieces
 #pragma unroll
@@ -672,60 +662,44 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     }
     __syncthreads();
 
-    // ---- 5. per wave: X = (I + A)^-1 B on its own column blocks, then W and U^T out
+    // ---- 5. per wave: X = (I + A)^-1 B on its own column blocks, on fp32
+    //      matrix-core steps, then W and U^T out
     {
 #pragma unroll
       for (int Rs = 0; Rs < 4; ++Rs) {
-        // Y = B_R - A_{R,<R} X_{<R}, over B_R in place
-#pragma unroll
-        for (int bi = 0; bi < CBPW; ++bi) {
-          const int cb = w + bi * NW;
-          float* xc = &sX[(16 * cb + ln) * LX];
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int ks = 0; ks < (Rs + 1) / 2; ++ks) {
-            SplitN<NP> a;
-#pragma unroll
-            for (int k = 0; k < NP; ++k)
-              a.v[k] = *reinterpret_cast<const bf16x8*>(&sAp[k][(16 * Rs + ln) * LAP + 32 * ks + 8 * q4]);
-            const float4 b0 = *reinterpret_cast<const float4*>(&xc[32 * ks + 8 * q4]);
-            const float4 b1 = *reinterpret_cast<const float4*>(&xc[32 * ks + 8 * q4 + 4]);
-            const float xb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            acc = mfmaN<NP>(a, splitN<NP>(xb), acc);
-          }
-          if (Rs > 0) {
-            float4* yr = reinterpret_cast<float4*>(&xc[16 * Rs + 4 * q4]);
-            const float4 bR = *yr;
-            *yr = make_float4(bR.x - acc[0], bR.y - acc[1], bR.z - acc[2], bR.w - acc[3]);
-          }
-        }
-        compiler_fence();
-        // X_R = T_R Y (K = 16: the upper half-wave contributes zeros)
-        f32x4 xr[CBPW];
+        f32x4 yv[CBPW];
+        // Y = B_R - A_{R,<R} X_{<R} (K = 16 Rs): lane group q4 takes k in
+        // [4 Rs q4, 4 Rs (q4 + 1)), contiguous in LDS for both operands
 #pragma unroll
         for (int bi = 0; bi < CBPW; ++bi) {
           const int cb = w + bi * NW;
           const float* xc = &sX[(16 * cb + ln) * LX];
-          SplitN<NP> ta, yb;
-          if (q4 < 2) {
+          f32x4 acc = zero4();
 #pragma unroll
-            for (int k = 0; k < NP; ++k) ta.v[k] = *reinterpret_cast<const bf16x8*>(&sTp[k][Rs][ln * LTP + 8 * q4]);
-            const float4 y0 = *reinterpret_cast<const float4*>(&xc[16 * Rs + 8 * q4]);
-            const float4 y1 = *reinterpret_cast<const float4*>(&xc[16 * Rs + 8 * q4 + 4]);
-            const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-            yb = splitN<NP>(yv);
-          } else {
-            ta = zero_split<NP>();
-            yb = zero_split<NP>();
+          for (int s4 = 0; s4 < Rs; ++s4) {
+            const int k0 = 4 * Rs * q4 + 4 * s4;
+            const float4 a4 = *reinterpret_cast<const float4*>(&sA[(16 * Rs + ln) * LA + k0]);
+            const float4 x4 = *reinterpret_cast<const float4*>(&xc[k0]);
+            acc = mfma_f32(a4.x, x4.x, acc);
+            acc = mfma_f32(a4.y, x4.y, acc);
+            acc = mfma_f32(a4.z, x4.z, acc);
+            acc = mfma_f32(a4.w, x4.w, acc);
           }
-          xr[bi] = mfmaN<NP>(ta, yb, zero4());
+          const float4 bR = *reinterpret_cast<const float4*>(&xc[16 * Rs + 4 * q4]);
+          yv[bi] = f32x4{bR.x - acc[0], bR.y - acc[1], bR.z - acc[2], bR.w - acc[3]};
         }
-        compiler_fence();
+        // X_R = T_R Y (K = 16): lane group q4 takes k = 4 q4 + s, which are
+        // exactly the rows of Y the lane holds
+        const float4 t4 = *reinterpret_cast<const float4*>(&sT[Rs][ln * LT + 4 * q4]);
 #pragma unroll
         for (int bi = 0; bi < CBPW; ++bi) {
           const int cb = w + bi * NW;
-          *reinterpret_cast<float4*>(&sX[(16 * cb + ln) * LX + 16 * Rs + 4 * q4]) =
-              make_float4(xr[bi][0], xr[bi][1], xr[bi][2], xr[bi][3]);
+          f32x4 x = zero4();
+          x = mfma_f32(t4.x, yv[bi][0], x);
+          x = mfma_f32(t4.y, yv[bi][1], x);
+          x = mfma_f32(t4.z, yv[bi][2], x);
+          x = mfma_f32(t4.w, yv[bi][3], x);
+          *reinterpret_cast<float4*>(&sX[(16 * cb + ln) * LX + 16 * Rs + 4 * q4]) = make_float4(x[0], x[1], x[2], x[3]);
         }
         compiler_fence();
       }
