@@ -42,20 +42,22 @@ __device__ __forceinline__ float dpp_row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
 
-// Sum over lanes 0..i of the lane's 16-lane row (inclusive prefix).
-__device__ __forceinline__ float row_prefix(float x) {
-  x += dpp_row_shr<1>(x);
-  x += dpp_row_shr<2>(x);
-  x += dpp_row_shr<4>(x);
-  x += dpp_row_shr<8>(x);
-  return x;
+// Sums over lanes 0..i of the lane's 16-lane row (inclusive prefixes), for N
+// values at once: written step by step across the values, so that each DPP
+// step's wait on the previous result is filled by the other values' steps.
+template <int N>
+__device__ __forceinline__ void row_prefix(float (&x)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row_shr<1>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row_shr<2>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row_shr<4>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row_shr<8>(x[j]);
 }
 
 
-// Keeps the compiler from moving memory accesses across this point: the LDS
-// hand-offs inside a wave rely on program order (a wave's LDS operations
-// execute in order), and it bounds how far loads are hoisted in unrolled
-// loops, which keeps the register count in check.
 __device__ __forceinline__ uint32_t word(const uint4& v, int j) { return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w)); }
 
 // a.lo b.lo + a.hi b.hi + c over bf16 pairs (v_dot2_f32_bf16).
@@ -70,15 +72,24 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Keeps the compiler from moving memory accesses across this point: the LDS
+// hand-offs inside a wave rely on program order (a wave's LDS operations
+// execute in order), and it bounds how far loads are hoisted in unrolled
+// loops, which keeps the register count in check.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Pins computed values where they stand: the compiler may otherwise sink
 // arithmetic past a barrier to its first use and keep all of its inputs
 // alive instead (here, hundreds of registers of raw inputs and conv taps).
+// Eight values go through one statement, so that the scheduler may still
+// interleave their computations (one statement per value orders them).
 template <int N>
 __device__ __forceinline__ void pin(float (&a)[N]) {
+  static_assert(N % 8 == 0, "pins go in groups of eight");
 #pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(a[i]));
+  for (int i = 0; i < N; i += 8)
+    asm volatile("" : "+v"(a[i]), "+v"(a[i + 1]), "+v"(a[i + 2]), "+v"(a[i + 3]), "+v"(a[i + 4]), "+v"(a[i + 5]),
+                 "+v"(a[i + 6]), "+v"(a[i + 7]));
 }
 
 // Position of one chunk in the packed batch.
@@ -113,7 +124,9 @@ struct RawChunk {
 
 }  // namespace
 
-template <int D>
+// kHooks: compiled with the input hooks (q, k, v already activated; g or beta
+// given directly); without them those selects cost nothing.
+template <int D, bool kHooks>
 __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(Params p, ChunkTable t, PrefillIO io,
                                                                                uint8_t* records) {
   constexpr int HF = D / 64;            // channel halves
@@ -166,7 +179,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   auto coords = [](int t) {
     LaneCoords L;
     L.tid = t;
-    L.w = t / kWave;
+    L.w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: scalar branches and loop counts
     L.lane = t % kWave;
     L.ln = L.lane & 15;
     L.q4 = L.lane >> 4;
@@ -179,7 +192,9 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   const size_t HD = static_cast<size_t>(H) * D;
   const size_t Ctot = 3 * HD;
   const uint32_t flags = p.flags;
-  const bool raw_conv = flags & KDA_FLAG_SKIP_CONV;
+  const bool raw_conv = kHooks && (flags & KDA_FLAG_SKIP_CONV);
+  const bool raw_gate = kHooks && (flags & KDA_FLAG_RAW_GATE);
+  const bool raw_beta = kHooks && (flags & KDA_FLAG_RAW_BETA);
   const bool l2 = !(flags & KDA_FLAG_SKIP_L2NORM);
   const float a_exp = expf(p.A_log[h]);
 
@@ -307,7 +322,10 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         __builtin_amdgcn_sched_barrier(0);
         // bf16 dot products over tap pairs: the inputs and taps are bf16, so
         // every product is exact and only the three additions round
-        float uo[8];
+        // SiLU is computed for every lane and then selected: written as a
+        // conditional, it becomes a branch per channel with the exponential
+        // chains serialised inside
+        float uo[8], rawx[8];
 #pragma unroll
         for (int jw = 0; jw < 4; ++jw) {   // channels c0 + 2 jw, c0 + 2 jw + 1
           const uint4 wt = wv[jw];
@@ -316,10 +334,17 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
                                      dot2_bf16(__builtin_amdgcn_perm(x3, x2, 0x05040100u), wt.y, 0.f));
           const float yo = dot2_bf16(__builtin_amdgcn_perm(x1, x0, 0x07060302u), wt.z,
                                      dot2_bf16(__builtin_amdgcn_perm(x3, x2, 0x07060302u), wt.w, 0.f));
-          uo[2 * jw] = live ? (raw_conv ? __uint_as_float(x3 << 16) : siluf_(ye)) : 0.f;
-          uo[2 * jw + 1] = live ? (raw_conv ? __uint_as_float(x3 & 0xffff0000u) : siluf_(yo)) : 0.f;
+          uo[2 * jw] = siluf_(ye);
+          uo[2 * jw + 1] = siluf_(yo);
+          rawx[2 * jw] = __uint_as_float(x3 << 16);
+          rawx[2 * jw + 1] = __uint_as_float(x3 & 0xffff0000u);
         }
         pin(uo);   // this group is computed before the next group's loads
+        // Rows past the chunk's end (copies of its last row) are left as they
+        // are: their beta and gate are zero, so their rows of A, beta K+,
+        // beta V and hence of W, U and the state update are exactly zero.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) uo[i] = raw_conv ? rawx[i] : uo[i];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           if (tens == 0) qv[8 * ks + i] = uo[i];
@@ -329,16 +354,23 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         compiler_fence();
       }
     }
+    // the gate likewise: computed for every lane, then selected
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c0 = 64 * hf + 32 * ks + 8 * q4;
       const uint32_t aw[4] = {a_cur[ks].x, a_cur[ks].y, a_cur[ks].z, a_cur[ks].w};
+      const float4 d0 = *reinterpret_cast<const float4*>(&dtb[c0]);
+      const float4 d1 = *reinterpret_cast<const float4*>(&dtb[c0 + 4]);
+      const float dt[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      float al[8], gc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float al = (i & 1) ? __uint_as_float(aw[i / 2] & 0xffff0000u) : __uint_as_float(aw[i / 2] << 16);
-        const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb[c0 + i], a_exp, p.lower_bound);
-        gv[8 * ks + i] = live ? g : 0.f;
+        al[i] = (i & 1) ? __uint_as_float(aw[i / 2] & 0xffff0000u) : __uint_as_float(aw[i / 2] << 16);
+        gc[i] = gate_value(al[i], dt[i], a_exp, p.lower_bound);
       }
+      pin(gc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gv[8 * ks + i] = live ? (raw_gate ? al[i] : gc[i]) : 0.f;
     }
     pin(qv);
     pin(kv);
@@ -347,7 +379,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     float beta = 0.f;
     if (live) {
       const float bb = bf16_to_f32(static_cast<uint16_t>(b_cur));
-      beta = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
+      beta = raw_beta ? bb : sigmoidf_(bb);
       if (flags & KDA_FLAG_BETA_X2) beta *= 2.0f;
     }
     if (hf == 0 && q4 == 0) sBeta[r] = beta;
@@ -372,10 +404,10 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     // pieces' resolution
     float P[16], eP[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      P[j] = row_prefix(gv[j]);
-      eP[j] = exp_fast(P[j]);
-    }
+    for (int j = 0; j < 16; ++j) P[j] = gv[j];
+    row_prefix(P);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) eP[j] = exp_fast(P[j]);
     pin(P);
     pin(eP);
     if (ln == 15) {
@@ -749,7 +781,10 @@ static hipError_t launch_rows_d(const Params& p, const ChunkTable& t, const Pref
   int groups = (ncu + p.H - 1) / p.H;
   groups = groups < 1 ? 1 : (groups > max_chunks ? max_chunks : groups);
   const dim3 grid(static_cast<unsigned>(p.H) * static_cast<unsigned>(groups));
-  chunk_prep_rows_kernel<D><<<grid, 64 * 4 * (D / 64), 0, st>>>(p, t, io, records);
+  if (p.flags & (KDA_FLAG_SKIP_CONV | KDA_FLAG_RAW_GATE | KDA_FLAG_RAW_BETA))
+    chunk_prep_rows_kernel<D, true><<<grid, 64 * 4 * (D / 64), 0, st>>>(p, t, io, records);
+  else
+    chunk_prep_rows_kernel<D, false><<<grid, 64 * 4 * (D / 64), 0, st>>>(p, t, io, records);
   return hipGetLastError();
 }
 

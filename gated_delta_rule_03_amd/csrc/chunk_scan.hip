@@ -83,6 +83,12 @@ __device__ __forceinline__ void load_ops_b(OpsB<D, DVT, NP>& o, const uint8_t* r
   constexpr int CBW = OpsB<D, DVT, NP>::CBW, CB = D / 16;
   const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
   const int r0 = 16 * wave;
+  // in the order of use: e^{G_C} first
+#pragma unroll
+  for (int i = 0; i < CBW; ++i) {
+    const int cb = wave + 4 * i;
+    if (CB % 4 == 0 || cb < CB) o.e[i] = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
+  }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     if (ks < nks_a)
@@ -90,11 +96,10 @@ __device__ __forceinline__ void load_ops_b(OpsB<D, DVT, NP>& o, const uint8_t* r
 #pragma unroll
   for (int i = 0; i < CBW; ++i) {
     const int cb = wave + 4 * i;
-    if (cb < CB) {
+    if (CB % 4 == 0 || cb < CB) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         o.kt[i][ks] = load_planes<NP>(rec + REC.KT, REC.tile_plane, frag_index(16 * cb + ln, 32 * ks + 8 * q4, kChunk));
-      o.e[i] = *reinterpret_cast<const float4*>(eGC + 16 * cb + 4 * q4);
     }
   }
 }
@@ -124,7 +129,11 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   if (sh >= n_sh) return;
   const int s = sh / H, h = sh % H;
   const int j0 = tile * DVT;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar branches
+  // every wave owns a state row block in each of its CBW slots when the
+  // blocks divide evenly (dk >= 64): then the test below is a constant
+  auto owns = [&](int i) { return CB % 4 == 0 || wave + 4 * i < CB; };
   const size_t sbase = (static_cast<size_t>(s) * H + h) * D * D;
 
   // ---- initial state into the accumulators and S^T into LDS
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       const int cb = wave + 4 * i;
-      if (cb >= CB) continue;
+      if (!owns(i)) continue;
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         bf16x4 pk[NP];   // the lane's four consecutive state rows, one 8-byte store per plane
@@ -177,41 +186,49 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   const int64_t seq0 = t.cu[s];
   const int seq_len = t.cu[s + 1] - t.cu[s];
   const int r0 = 16 * wave;                         // this wave's token rows
-  const int nks_a = wave >= 2 ? 2 : 1;              // k steps of Aqk Delta (causal)
-  // Two buffers of each operand half, for chunks of alternate parity.  Each
-  // buffer is refilled with chunk c + 2 as soon as chunk c has read it (the
-  // A half after the first barrier, the B half at the end of the chunk), so
-  // every record load is in flight for about one and a half chunks.
-  OpsA<D, DVT, NP> A0, A1;
-  OpsB<D, DVT, NP> B0, B1;
-  auto rec_of = [&](int c) { return records + (static_cast<size_t>(c) * H + h) * REC.bytes; };
+  // k steps of Aqk Delta: both for every wave; the record's Aqk is zero above
+  // the diagonal, and the waves that need both set the pace anyway
+  constexpr int nks_a = 2;
+  // One buffer of each operand half, refilled with chunk c + 1 as soon as
+  // chunk c has read it (the A half after the first barrier, the B half at the
+  // end of the chunk): each record load has about half a chunk in flight.  A
+  // second set of buffers (two chunks ahead) measured slower: it pushes the
+  // wave past the register file into copies through the accumulation
+  // registers.  The refills are unconditional (past the last chunk they
+  // re-read it): the same number of loads on every path lets the compiler
+  // wait for exactly the loads an operand needs, where a skipped refill makes
+  // it wait for all of them.
+  OpsA<D, DVT, NP> A0;
+  OpsB<D, DVT, NP> B0;
+  auto rec_of = [&](int c) { return records + (static_cast<size_t>(min(c, c_end - 1)) * H + h) * REC.bytes; };
   if (c_first < c_end) {
     load_ops_a<D, DVT, NP>(A0, rec_of(c_first), wave, ln, q4, j0);
     load_ops_b<D, DVT, NP>(B0, rec_of(c_first), wave, ln, q4, nks_a);
-  }
-  if (c_first + 1 < c_end) {
-    load_ops_a<D, DVT, NP>(A1, rec_of(c_first + 1), wave, ln, q4, j0);
-    load_ops_b<D, DVT, NP>(B1, rec_of(c_first + 1), wave, ln, q4, nks_a);
   }
 
   auto chunk_step = [&](int c, OpsA<D, DVT, NP>& A, OpsB<D, DVT, NP>& B) {
     const int tau = (c - c_first) * kChunk;
     const int len = min(kChunk, seq_len - tau);
 
-    // ---- W S and Q+ S for this wave's 16 token rows
+    // ---- W S and Q+ S for this wave's 16 token rows.  The S^T pieces of
+    //      each (k step, column block) are read one group ahead, so the LDS
+    //      latency hides behind the previous group's matrix-core steps.
     f32x4 accW[CJ], accQ[CJ];
 #pragma unroll
     for (int cj = 0; cj < CJ; ++cj) { accW[cj] = zero4(); accQ[cj] = zero4(); }
+    {
+      auto load_s = [&](int g) {
+        SplitN<NP> b;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch0 = 32 * ks + 8 * q4;
+        for (int k = 0; k < NP; ++k) b.v[k] = load_bf16x8(&sST[k][(16 * (g % CJ) + ln) * LST + 32 * (g / CJ) + 8 * q4]);
+        return b;
+      };
+      SplitN<NP> bS[2];
+      bS[0] = load_s(0);
 #pragma unroll
-      for (int cj = 0; cj < CJ; ++cj) {
-        SplitN<NP> bS;
-#pragma unroll
-        for (int k = 0; k < NP; ++k) bS.v[k] = load_bf16x8(&sST[k][(16 * cj + ln) * LST + ch0]);
-        accW[cj] = mfmaN<NP>(A.w[ks], bS, accW[cj]);
-        accQ[cj] = mfmaN<NP>(A.q[ks], bS, accQ[cj]);
+      for (int g = 0; g < KS * CJ; ++g) {
+        if (g + 1 < KS * CJ) bS[(g + 1) & 1] = load_s(g + 1);
+        mfmaN2<NP>(A.w[g / CJ], A.q[g / CJ], bS[g & 1], accW[g % CJ], accQ[g % CJ]);
       }
     }
     // Delta = U - W S, published transposed for the B operands below
@@ -231,34 +248,50 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
       for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4*>(&sDT[k][idx]) = pk[k];
     }
-    if (c + 2 < c_end) load_ops_a<D, DVT, NP>(A, rec_of(c + 2), wave, ln, q4, j0);
+    load_ops_a<D, DVT, NP>(A, rec_of(c + 1), wave, ln, q4, j0);
     __syncthreads();
 
     // ---- O = Q+ S + Aqk Delta;  S = e^{G_C} S + K~^T Delta
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
-      if (wave + 4 * i >= CB) continue;
-      const float4 e4 = B.e[i];
+      if (!owns(i)) continue;
+      float4 e4 = B.e[i];
+      // kept below the barrier: hoisted above it, this scaling would wait
+      // for the operand loads of the B half early
+      asm volatile("" : "+v"(e4.x), "+v"(e4.y), "+v"(e4.z), "+v"(e4.w));
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
         Sacc[i][cj][0] *= e4.x; Sacc[i][cj][1] *= e4.y; Sacc[i][cj][2] *= e4.z; Sacc[i][cj][3] *= e4.w;
       }
     }
+    {
+      // Delta pieces one (k step, column block) group ahead, as above; the
+      // passes of the group's independent products interleaved
+      auto load_d = [&](int g) {
+        SplitN<NP> b;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int t0 = 32 * ks + 8 * q4;
+        for (int k = 0; k < NP; ++k) b.v[k] = load_bf16x8(&sDT[k][(16 * (g % CJ) + ln) * LDT + 32 * (g / CJ) + 8 * q4]);
+        return b;
+      };
+      SplitN<NP> bD[2];
+      bD[0] = load_d(0);
 #pragma unroll
-      for (int cj = 0; cj < CJ; ++cj) {
-        SplitN<NP> bD;
+      for (int g = 0; g < 2 * CJ; ++g) {
+        if (g + 1 < 2 * CJ) bD[(g + 1) & 1] = load_d(g + 1);
+        const int ks = g / CJ, cj = g % CJ;
+        const SplitN<NP>& b = bD[g & 1];
 #pragma unroll
-        for (int k = 0; k < NP; ++k) bD.v[k] = load_bf16x8(&sDT[k][(16 * cj + ln) * LDT + t0]);
-        if (ks < nks_a) accQ[cj] = mfmaN<NP>(B.a[ks], bD, accQ[cj]);
+        for (int sum = NP - 1; sum >= 0; --sum)
 #pragma unroll
-        for (int i = 0; i < CBW; ++i)
-          if (wave + 4 * i < CB) Sacc[i][cj] = mfmaN<NP>(B.kt[i][ks], bD, Sacc[i][cj]);
+          for (int pi = 0; pi <= sum; ++pi) {
+            accQ[cj] = mfma(B.a[ks].v[pi], b.v[sum - pi], accQ[cj]);
+#pragma unroll
+            for (int i = 0; i < CBW; ++i)
+              if (owns(i)) Sacc[i][cj] = mfma(B.kt[i][ks].v[pi], b.v[sum - pi], Sacc[i][cj]);
+          }
       }
     }
-    if (c + 2 < c_end) load_ops_b<D, DVT, NP>(B, rec_of(c + 2), wave, ln, q4, nks_a);
+    load_ops_b<D, DVT, NP>(B, rec_of(c + 1), wave, ln, q4, nks_a);
     // this wave's output rows: through its own LDS tile (LDS operations of a
     // wave run in order), then stored row-contiguous, 8 or 16 bytes per
     // access (few memory operations per chunk leave room for the record
@@ -296,16 +329,13 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
     __syncthreads();
   };
 
-  for (int c = c_first; c < c_end; c += 2) {
-    chunk_step(c, A0, B0);
-    if (c + 1 < c_end) chunk_step(c + 1, A1, B1);
-  }
+  for (int c = c_first; c < c_end; ++c) chunk_step(c, A0, B0);
 
   if (io.S_out) {
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       const int cb = wave + 4 * i;
-      if (cb >= CB) continue;
+      if (!owns(i)) continue;
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj)
 #pragma unroll
