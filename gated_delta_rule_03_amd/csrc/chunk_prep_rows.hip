@@ -227,12 +227,14 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     if (cp.tau0 > 0) {
       // every staging row is a token of this sequence: one base, one
       // multiply-add per piece (rows past the chunk's end re-read its last)
+      // (element offsets in 32 bits: one multiply per lane, then an add and
+      // a clamp per piece)
       const uint16_t* row0 = st_x + (cp.tok0 - 3) * static_cast<int64_t>(HD);
+      const uint32_t hd = static_cast<uint32_t>(HD);
+      const uint32_t off0 = static_cast<uint32_t>(st_row0) * hd, last = static_cast<uint32_t>(cp.len + 2) * hd;
 #pragma unroll
-      for (int j = 0; j < Raw::kPer; ++j) {
-        const int sr = min(st_row0 + Raw::kSR * j, cp.len + 2);
-        nx.x[j] = *reinterpret_cast<const uint4*>(row0 + static_cast<int64_t>(sr) * HD);
-      }
+      for (int j = 0; j < Raw::kPer; ++j)
+        nx.x[j] = *reinterpret_cast<const uint4*>(row0 + min(off0 + static_cast<uint32_t>(Raw::kSR * j) * hd, last));
     } else {
       // the sequence's first chunk: the three rows before it come from the
       // conv history, or are zeros without one
@@ -433,8 +435,9 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         nq += sNorm[1][r][0];
         nk += sNorm[1][r][1];
       }
-      iq = (l2 ? 1.0f / sqrtf(nq + p.eps) : 1.0f) * p.scale;
-      ik = l2 ? 1.0f / sqrtf(nk + p.eps) : 1.0f;
+      // hardware reciprocal square root (~1 ulp): bf16 inputs only here
+      iq = (l2 ? __builtin_amdgcn_rsqf(nq + p.eps) : 1.0f) * p.scale;
+      ik = l2 ? __builtin_amdgcn_rsqf(nk + p.eps) : 1.0f;
     }
     float qP[16], kP[16];
     SplitN<NP> kcp[2];   // k e^{-P} pieces: the B operand of this lane's diagonal block
@@ -473,10 +476,12 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       // key side: k e^{P}, k e^{-P} pieces, K~^T, e^{G_C}
       __bf16* KT = reinterpret_cast<__bf16*>(rec + REC.KT);
       float* eGC = reinterpret_cast<float*>(rec + REC.eGC);
+      float ebs[2][8];   // e^{G before block R}: kept for the query side
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int c0 = 64 * hf + 32 * ks + 8 * q4;
-        float eb[8], after[8];
+        float (&eb)[8] = ebs[ks];
+        float after[8];
         before_after(c0, eb, after);
         const float4 bt0 = *reinterpret_cast<const float4*>(&sBt[R][c0]);
         const float4 bt1 = *reinterpret_cast<const float4*>(&sBt[R][c0 + 4]);
@@ -496,12 +501,19 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         kcp[ks] = splitN<NP>(kc);
 #pragma unroll
         for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x8*>(&sKc[k * 64 * KCS + r * KCS + c0]) = kcp[ks].v[k];
+        // channels c0 .. c0 + 7 lie in one 16-row block of the fragment order
+        // (c0 is a multiple of 8), eight elements apart
+        const size_t kt0 = frag_index(c0, r, kChunk);
+        uint16_t* KT16 = reinterpret_cast<uint16_t*>(KT) + kt0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __bf16 pc[NP];
-          split_pieces<NP>(kt[i], pc);
+        for (int i = 0; i < 8; i += 2) {
+          uint32_t w[NP];
+          split_pair<NP>(kt[i], kt[i + 1], w);
 #pragma unroll
-          for (int k = 0; k < NP; ++k) KT[k * (REC.tile_plane / 2) + frag_index(c0 + i, r, kChunk)] = pc[k];
+          for (int k = 0; k < NP; ++k) {
+            KT16[k * (REC.tile_plane / 2) + 8 * i] = static_cast<uint16_t>(w[k]);
+            KT16[k * (REC.tile_plane / 2) + 8 * (i + 1)] = static_cast<uint16_t>(w[k] >> 16);
+          }
         }
         if (R == 3 && ln == 15) {   // e^{G_C} = e^{G before block 3} e^{P_63}
           float eg[8];
@@ -517,8 +529,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int c0 = 64 * hf + 32 * ks + 8 * q4;
-        float eb[8], after[8];
-        before_after(c0, eb, after);
+        const float (&eb)[8] = ebs[ks];
         float qo[8], pq[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -618,7 +629,10 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 
     // ---- the next chunk's raw inputs go out now: phases 4 and 5 hold few
     //      registers, and they hide the loads' latency
-    if (c + G < total) {
+    // Unconditional (after the last chunk it loads that chunk again): with
+    // the same loads on every path the compiler waits only for the ones a
+    // value needs.
+    {
       // kept in vector registers until here, so that moving it to scalar
       // registers does not wait for the load early
       int nd[4] = {next_desc.x, next_desc.y, next_desc.z, next_desc.w};

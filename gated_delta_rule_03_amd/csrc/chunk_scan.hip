@@ -165,17 +165,13 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
       if (!owns(i)) continue;
 #pragma unroll
       for (int cj = 0; cj < CJ; ++cj) {
-        bf16x4 pk[NP];   // the lane's four consecutive state rows, one 8-byte store per plane
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          __bf16 pc[NP];
-          split_pieces<NP>(Sacc[i][cj][j], pc);
-#pragma unroll
-          for (int k = 0; k < NP; ++k) pk[k][j] = pc[k];
-        }
+        // the lane's four consecutive state rows, one 8-byte store per plane
+        uint32_t w01[NP], w23[NP];
+        split_pair<NP>(Sacc[i][cj][0], Sacc[i][cj][1], w01);
+        split_pair<NP>(Sacc[i][cj][2], Sacc[i][cj][3], w23);
         const int idx = (16 * cj + ln) * LST + 16 * cb + 4 * q4;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4*>(&sST[k][idx]) = pk[k];
+        for (int k = 0; k < NP; ++k) *reinterpret_cast<uint2*>(&sST[k][idx]) = make_uint2(w01[k], w23[k]);
       }
     }
   };
@@ -235,18 +231,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
 #pragma unroll
     for (int cj = 0; cj < CJ; ++cj) {
       const float4 u = A.u[cj];
-      const float dl[4] = {u.x - accW[cj][0], u.y - accW[cj][1], u.z - accW[cj][2], u.w - accW[cj][3]};
-      bf16x4 pk[NP];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        __bf16 pc[NP];
-        split_pieces<NP>(dl[j], pc);
-#pragma unroll
-        for (int k = 0; k < NP; ++k) pk[k][j] = pc[k];
-      }
+      uint32_t w01[NP], w23[NP];
+      split_pair<NP>(u.x - accW[cj][0], u.y - accW[cj][1], w01);
+      split_pair<NP>(u.z - accW[cj][2], u.w - accW[cj][3], w23);
       const int idx = (16 * cj + ln) * LDT + r0 + 4 * q4;
 #pragma unroll
-      for (int k = 0; k < NP; ++k) *reinterpret_cast<bf16x4*>(&sDT[k][idx]) = pk[k];
+      for (int k = 0; k < NP; ++k) *reinterpret_cast<uint2*>(&sDT[k][idx]) = make_uint2(w01[k], w23[k]);
     }
     load_ops_a<D, DVT, NP>(A, rec_of(c + 1), wave, ln, q4, j0);
     __syncthreads();

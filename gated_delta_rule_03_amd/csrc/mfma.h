@@ -67,16 +67,38 @@ __device__ __forceinline__ void split_pieces(float x, __bf16 (&pc)[NP]) {
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest even) in one packed word
+// (v_cvt_pk_bf16_f32): a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// The NP pieces of the pair (a, b), each a packed bf16 word.  The value of a
+// rounded half is read back from the packed word by a shift or a mask, not
+// by a second conversion.
+template <int NP>
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t (&w)[NP]) {
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    w[k] = pack_bf16x2(a, b);
+    if (k + 1 < NP) {
+      a -= __uint_as_float(w[k] << 16);
+      b -= __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+}
+
 template <int NP>
 __device__ __forceinline__ SplitN<NP> splitN(const float (&x)[8]) {
+  uint32_t w[4][NP];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) split_pair<NP>(x[2 * j], x[2 * j + 1], w[j]);
   SplitN<NP> s;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __bf16 pc[NP];
-    split_pieces<NP>(x[i], pc);
-#pragma unroll
-    for (int k = 0; k < NP; ++k) s.v[k][i] = pc[k];
-  }
+  for (int k = 0; k < NP; ++k) s.v[k] = __builtin_bit_cast(bf16x8, make_uint4(w[0][k], w[1][k], w[2][k], w[3][k]));
   return s;
 }
 
