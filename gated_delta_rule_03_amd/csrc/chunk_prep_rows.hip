@@ -98,6 +98,19 @@ struct ChunkPos {
   int64_t tok0;
 };
 
+// The same memory through the constant address space: a load at a uniform
+// index from it is a scalar load (its own counter, results in scalar
+// registers), where a global load would occupy the vector-memory counter and
+// be waited for together with the stores before it.
+__device__ __forceinline__ int scalar_load(const int* p, int i) {
+  return ((const __attribute__((address_space(4))) int*)(p))[i];
+}
+
+__device__ __forceinline__ int4 scalar_load_desc(const int4* d, int i) {
+  const int* p = reinterpret_cast<const int*>(d) + 4 * i;
+  return make_int4(scalar_load(p, 0), scalar_load(p, 1), scalar_load(p, 2), scalar_load(p, 3));
+}
+
 __device__ __forceinline__ ChunkPos chunk_pos(const int4& d) {
   ChunkPos cp;
   cp.s = d.x;
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 
   const int H = p.H;
   const int h = blockIdx.x % H, grp = blockIdx.x / H, G = gridDim.x / H;
-  const int total = t.chunk0[t.N];
+  const int total = scalar_load(t.chunk0, t.N);
   // Lane coordinates.  Inside the chunk loop they are re-derived from a copy
   // of the thread index the compiler cannot see through, so that it does not
   // hoist per-lane addresses out of the loop and keep them in registers for
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 
   // Every piece is loaded from a valid address and zeroed where the history
   // has no row (sequence start without a conv history) or past the staging rows.
-  auto load_raw = [&](Raw& nx, const ChunkPos& cp, const LaneCoords& L) {
+  auto load_rows = [&](Raw& nx, const ChunkPos& cp, const LaneCoords& L) {
     const int st_col = L.tid % Raw::kCols, st_row0 = L.tid / Raw::kCols;
     const bool stager = L.tid < Raw::kSR * Raw::kCols;
     const int st_tens = st_col / (D / 8), st_ch = 8 * (st_col % (D / 8));
@@ -223,61 +236,58 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
                                       : 0);
     // (the zeroing is applied when the pieces are written to LDS: a select
     // here would wait for every load, and for every store before it)
-    nx.zero = 0u;
-    if (cp.tau0 > 0) {
-      // every staging row is a token of this sequence: one base, one
-      // multiply-add per piece (rows past the chunk's end re-read its last)
-      // (element offsets in 32 bits: one multiply per lane, then an add and
-      // a clamp per piece)
-      const uint16_t* row0 = st_x + (cp.tok0 - 3) * static_cast<int64_t>(HD);
-      const uint32_t hd = static_cast<uint32_t>(HD);
-      const uint32_t off0 = static_cast<uint32_t>(st_row0) * hd, last = static_cast<uint32_t>(cp.len + 2) * hd;
-#pragma unroll
-      for (int j = 0; j < Raw::kPer; ++j)
-        nx.x[j] = *reinterpret_cast<const uint4*>(row0 + min(off0 + static_cast<uint32_t>(Raw::kSR * j) * hd, last));
+    //
+    // Staging row sr is token tok0 - 3 + sr of the sequence (rows past the
+    // chunk's end re-read its last token); in the sequence's first chunk rows
+    // 0..2 come from the conv history instead, or are zeros without one.
+    // Those rows can only be a thread's first piece (kSR >= 3), so only that
+    // piece's address is a select; written as a branch per piece, the two
+    // cases cost a divergent branch each.  Offsets are 32-bit element counts
+    // from one 64-bit base.
+    static_assert(Raw::kSR >= 3, "the history rows fall in each thread's first piece");
+    const uint16_t* row0 = st_x + (cp.tok0 - 3) * static_cast<int64_t>(HD);
+    const uint32_t hd = static_cast<uint32_t>(HD);
+    const uint32_t off0 = static_cast<uint32_t>(st_row0) * hd, last = static_cast<uint32_t>(cp.len + 2) * hd;
+    const bool hist0 = cp.tau0 == 0 && st_row0 < 3;
+    const uint16_t* p0 = row0 + min(off0, last);
+    if (have_hist) {   // uniform
+      p0 = hist0 ? st_h + static_cast<size_t>(st_row0) * Ctot : p0;
+      nx.zero = 0u;
     } else {
-      // the sequence's first chunk: the three rows before it come from the
-      // conv history, or are zeros without one
-      const bool have_hist = io.conv_in != nullptr;
-      const uint16_t* st_h = static_cast<const uint16_t*>(have_hist ? io.conv_in : io.q) +
-                             (have_hist ? static_cast<size_t>(cp.s) * 3 * Ctot + st_tens * HD +
-                                              static_cast<size_t>(h) * D + st_ch
-                                        : 0);
-#pragma unroll
-      for (int j = 0; j < Raw::kPer; ++j) {
-        const int sr = st_row0 + Raw::kSR * j;
-        const bool hist = sr < 3;
-        const int64_t tok = cp.tok0 + (hist ? 0 : min(sr - 3, cp.len - 1));   // any valid row for a history slot
-        const uint16_t* px = hist && have_hist ? st_h + static_cast<size_t>(sr) * Ctot : st_x + tok * HD;
-        nx.x[j] = *reinterpret_cast<const uint4*>(px);
-        if (hist && !have_hist) nx.zero |= 1u << j;
-      }
+      p0 = hist0 ? row0 + 3 * hd : p0;   // any valid row for a missing one
+      nx.zero = hist0 ? 1u : 0u;
     }
-    const int64_t tok = cp.tok0 + min(L.r, cp.len - 1);
+    nx.x[0] = *reinterpret_cast<const uint4*>(p0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      nx.a[ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(io.alpha) + tok * HD +
-                                                 static_cast<size_t>(h) * D + 64 * L.hf + 32 * ks + 8 * L.q4);
-    nx.b = static_cast<const uint16_t*>(io.b)[tok * H + h];
+    for (int j = 1; j < Raw::kPer; ++j)
+      nx.x[j] = *reinterpret_cast<const uint4*>(row0 + min(off0 + static_cast<uint32_t>(Raw::kSR * j) * hd, last));
+  };
+  // alpha and b of this lane's row: issued apart from the staging rows (in
+  // phase 3, which has no memory operations of its own), since a burst of
+  // loads this scattered holds up the wave that issues it
+  auto load_gate_inputs = [&](Raw& nx, const ChunkPos& cp, const LaneCoords& L) {
+    const uint32_t hd = static_cast<uint32_t>(HD);
+    const uint16_t* arow = static_cast<const uint16_t*>(io.alpha) + cp.tok0 * static_cast<int64_t>(HD) +
+                           static_cast<size_t>(h) * D + 64 * L.hf + 8 * L.q4;
+    const uint32_t rr = static_cast<uint32_t>(min(L.r, cp.len - 1));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) nx.a[ks] = *reinterpret_cast<const uint4*>(arow + rr * hd + 32 * ks);
+    nx.b = static_cast<const uint16_t*>(io.b)[(cp.tok0 + rr) * H + h];
   };
 
+  // The loop is rotated: a chunk's raw inputs are loaded at the start of the
+  // previous chunk's phase 1 and written to the staging rows at its end, so
+  // the wait for them counts only the memory operations of one iteration.
   Raw nxt;
-  ChunkPos nxt_pos{};
-  if (grp < total) {
-    nxt_pos = chunk_pos(t.desc[grp]);
-    load_raw(nxt, nxt_pos, coords(tid));
-  }
-
-  for (int c = grp; c < total; c += G) {
-    const ChunkPos cp = nxt_pos;
-    int tid_opaque = tid;
-    asm volatile("" : "+v"(tid_opaque));
-    const LaneCoords L = coords(tid_opaque);
-    const int w = L.w, lane = L.lane, ln = L.ln, q4 = L.q4, R = L.R, hf = L.hf, r = L.r;
+  ChunkPos cur_pos{}, nxt_pos{};
+  uint4 a_cur[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  uint32_t b_cur = 0u;
+  // the descriptor of the chunk after the next (a uniform index: a scalar
+  // load, one chunk ahead of its use)
+  int4 desc_ahead = make_int4(0, 0, 0, 0);
+  auto stage = [&](const LaneCoords& L) {
     const int st_col = L.tid % Raw::kCols, st_row0 = L.tid / Raw::kCols;
     const bool stager = L.tid < Raw::kSR * Raw::kCols;
-    __syncthreads();   // the previous chunk is done with sU, sA, sAqk
-    // ---- staging rows into LDS; the next chunk's loads go out
 #pragma unroll
     for (int j = 0; j < Raw::kPer; ++j) {
       const int sr = st_row0 + Raw::kSR * j;
@@ -286,16 +296,39 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
             (nxt.zero >> j) & 1u ? make_uint4(0u, 0u, 0u, 0u) : nxt.x[j];
     }
     uint32_t aw[8] = {nxt.a[0].x, nxt.a[0].y, nxt.a[0].z, nxt.a[0].w, nxt.a[1].x, nxt.a[1].y, nxt.a[1].z, nxt.a[1].w};
-    uint32_t b_cur = nxt.b;
+    uint32_t bw = nxt.b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(aw[i]));   // arrived before the next load goes out
-    asm volatile("" : "+v"(b_cur));
-    const uint4 a_cur[2] = {make_uint4(aw[0], aw[1], aw[2], aw[3]), make_uint4(aw[4], aw[5], aw[6], aw[7])};
-    // where the chunk after this one lies: loaded now (after the wait for the
-    // staging rows, so that wait does not include it), used in phase 4; a
-    // clamped index rather than a select, which would wait for the load
-    const int4 next_desc = t.desc[min(c + G, total - 1)];
-    __syncthreads();
+    asm volatile("" : "+v"(bw));
+    a_cur[0] = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+    a_cur[1] = make_uint4(aw[4], aw[5], aw[6], aw[7]);
+    b_cur = bw;
+  };
+  if (grp < total) {
+    cur_pos = chunk_pos(scalar_load_desc(t.desc, grp));
+    load_rows(nxt, cur_pos, coords(tid));
+    load_gate_inputs(nxt, cur_pos, coords(tid));
+    desc_ahead = scalar_load_desc(t.desc, min(grp + G, total - 1));
+    stage(coords(tid));
+  }
+
+  for (int c = grp; c < total; c += G) {
+    const ChunkPos cp = cur_pos;
+    int tid_opaque = tid;
+    asm volatile("" : "+v"(tid_opaque));
+    const LaneCoords L = coords(tid_opaque);
+    const int w = L.w, lane = L.lane, ln = L.ln, q4 = L.q4, R = L.R, hf = L.hf, r = L.r;
+    __syncthreads();   // the staging rows are written
+
+    // ---- the next chunk's staging rows go out now, ahead of phase 1: it
+    //      issues no memory operations of its own, so the loads leave before
+    //      the record stores of phase 2 and do not queue behind them.  Always
+    //      issued (after the last chunk they load that chunk again): with the
+    //      same loads on every path the compiler waits only for the ones a
+    //      value needs.
+    nxt_pos = chunk_pos(desc_ahead);
+    load_rows(nxt, nxt_pos, L);
+    desc_ahead = scalar_load_desc(t.desc, min(c + 2 * G, total - 1));
 
     uint8_t* rec = records + (static_cast<size_t>(c) * H + h) * REC.bytes;
     const bool live = r < cp.len;
@@ -552,6 +585,8 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     pin(kP);
     __syncthreads();
 
+    load_gate_inputs(nxt, nxt_pos, L);
+
     // ---- 3. this wave's channel half of A and Aqk, sub-blocks (R, I <= R).
     //      The upper half stores its partial sums, then the lower half adds its
     //      own (held in registers) on top: lower + upper, the same every time.
@@ -626,21 +661,6 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       }
     }
     __syncthreads();
-
-    // ---- the next chunk's raw inputs go out now: phases 4 and 5 hold few
-    //      registers, and they hide the loads' latency
-    // Unconditional (after the last chunk it loads that chunk again): with
-    // the same loads on every path the compiler waits only for the ones a
-    // value needs.
-    {
-      // kept in vector registers until here, so that moving it to scalar
-      // registers does not wait for the load early
-      int nd[4] = {next_desc.x, next_desc.y, next_desc.z, next_desc.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(nd[i]));
-      nxt_pos = chunk_pos(make_int4(nd[0], nd[1], nd[2], nd[3]));
-      load_raw(nxt, nxt_pos, L);
-    }
 
     // ---- 4. Aqk pieces out; the diagonal-block inverses to LDS; beta K+ to X^T
     {
@@ -777,6 +797,9 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         }
       }
     }
+    __syncthreads();   // every wave is done with the shared region
+    stage(L);
+    cur_pos = nxt_pos;
   }
 }
 
