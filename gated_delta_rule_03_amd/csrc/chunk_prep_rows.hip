@@ -7,7 +7,7 @@
 //  * Persistent workgroups with a fixed head.  Workgroup (h, grp) walks the
 //    chunks grp, grp + G, ... of head h; the raw q/k/v rows (with the three
 //    conv rows before the chunk), alpha and b of the NEXT chunk are loaded
-//    into registers during the last phases of the current one, so the input
+//    into registers while the current one is processed, so the input
 //    latency is hidden.  The conv weights and dt_bias of the head stay in LDS.
 //  * Wave (R, half) owns token rows 16R..16R+15 and key channels
 //    64 half .. 64 half + 63.  A lane holds one token row r and 16 channels
@@ -19,9 +19,11 @@
 //    The conv runs as bf16 dot products over tap pairs.
 //  * The two channel halves of A and Aqk meet in LDS: the upper half stores
 //    its partial sums and the lower half adds its own on top, in that order.
-//  * The solve of (I + A) X = [beta K+ | beta V] runs per wave on the wave's
-//    own 16-column blocks of X with A and the inverted diagonal blocks split
-//    into bf16 pieces once, in LDS; no workgroup barrier inside it.
+//  * The solve of (I + A) X = [beta K+ | beta V] forms T = (I + A)^-1 first:
+//    the inverses of the four diagonal blocks by forward substitution, then
+//    each 16-column block of T on fp32 matrix-core steps.  X = T B is then a
+//    plain product on the bf16 matrix cores (pieces as everywhere else), each
+//    wave on its own 16-column blocks of X.
 // Row R of a wave is chosen so that the two waves sharing a SIMD (w, w + 4)
 // own row blocks R and 3 - R: the triangular A work is then even per SIMD.
 #include "kda_device.h"
@@ -728,47 +730,96 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     }
     __syncthreads();
 
-    // ---- 5. per wave: X = (I + A)^-1 B on its own column blocks, on fp32
-    //      matrix-core steps, then W and U^T out
-    {
+    // ---- 4b. T = (I + A)^-1, unit lower triangular: wave J < 4 forms its
+    //      16-column block by blocked forward substitution on fp32
+    //      matrix-core steps (its earlier blocks stay in its registers, laid
+    //      out as the B operand of the next steps), and writes it as bf16
+    //      pieces in fragment order over the free Aqk area
+    __bf16* sTp = reinterpret_cast<__bf16*>(sAqk);
+    static_assert(NP * 64 * 64 * 2 <= 64 * LA * 4, "T's pieces fit the Aqk area");
+    if (w < 4) {
+      const int J = w;
+      f32x4 xb[4];
+      auto put = [&](int Rs, const f32x4& x) {   // lane holds T[16 Rs + 4 q4 + i][16 J + ln]
+        uint32_t w01[NP], w23[NP];
+        split_pair<NP>(x[0], x[1], w01);
+        split_pair<NP>(x[2], x[3], w23);
+        uint16_t* tp = reinterpret_cast<uint16_t*>(sTp);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const size_t e = k * 4096 + frag_index(16 * Rs + 4 * q4, 16 * J + ln, 64);
+          // rows 4 q4 .. 4 q4 + 3 of one column: eight elements apart
+          tp[e] = static_cast<uint16_t>(w01[k]);
+          tp[e + 8] = static_cast<uint16_t>(w01[k] >> 16);
+          tp[e + 16] = static_cast<uint16_t>(w23[k]);
+          tp[e + 24] = static_cast<uint16_t>(w23[k] >> 16);
+        }
+      };
 #pragma unroll
       for (int Rs = 0; Rs < 4; ++Rs) {
-        f32x4 yv[CBPW];
-        // Y = B_R - A_{R,<R} X_{<R} (K = 16 Rs): lane group q4 takes k in
-        // [4 Rs q4, 4 Rs (q4 + 1)), contiguous in LDS for both operands
+        if (Rs < J) {
+          // blocks above the diagonal that the products below read as
+          // k padding (T_{0,1}, T_{2,3}) are zero
+          if ((Rs == 0 && J == 1) || (Rs == 2 && J == 3)) put(Rs, zero4());
+          continue;
+        }
+        f32x4 y;
+        if (Rs == J) {   // the identity's block
 #pragma unroll
-        for (int bi = 0; bi < CBPW; ++bi) {
-          const int cb = w + bi * NW;
-          const float* xc = &sX[(16 * cb + ln) * LX];
+          for (int i = 0; i < 4; ++i) y[i] = (4 * q4 + i == ln) ? 1.f : 0.f;
+        } else {         // Y = - A_{Rs, J..Rs-1} X_{J..Rs-1}: k = 4 q4 + s within each block
           f32x4 acc = zero4();
 #pragma unroll
-          for (int s4 = 0; s4 < Rs; ++s4) {
-            const int k0 = 4 * Rs * q4 + 4 * s4;
-            const float4 a4 = *reinterpret_cast<const float4*>(&sA[(16 * Rs + ln) * LA + k0]);
-            const float4 x4 = *reinterpret_cast<const float4*>(&xc[k0]);
-            acc = mfma_f32(a4.x, x4.x, acc);
-            acc = mfma_f32(a4.y, x4.y, acc);
-            acc = mfma_f32(a4.z, x4.z, acc);
-            acc = mfma_f32(a4.w, x4.w, acc);
+          for (int M = 0; M < 3; ++M) {
+            if (M < J || M >= Rs) continue;
+            const float4 a4 = *reinterpret_cast<const float4*>(&sA[(16 * Rs + ln) * LA + 16 * M + 4 * q4]);
+            acc = mfma_f32(a4.x, xb[M][0], acc);
+            acc = mfma_f32(a4.y, xb[M][1], acc);
+            acc = mfma_f32(a4.z, xb[M][2], acc);
+            acc = mfma_f32(a4.w, xb[M][3], acc);
           }
-          const float4 bR = *reinterpret_cast<const float4*>(&xc[16 * Rs + 4 * q4]);
-          yv[bi] = f32x4{bR.x - acc[0], bR.y - acc[1], bR.z - acc[2], bR.w - acc[3]};
+          y = f32x4{-acc[0], -acc[1], -acc[2], -acc[3]};
         }
-        // X_R = T_R Y (K = 16): lane group q4 takes k = 4 q4 + s, which are
-        // exactly the rows of Y the lane holds
+        // X_Rs = T_{Rs,Rs} Y: the lane's own rows of Y are its k = 4 q4 + s
         const float4 t4 = *reinterpret_cast<const float4*>(&sT[Rs][ln * LT + 4 * q4]);
-#pragma unroll
-        for (int bi = 0; bi < CBPW; ++bi) {
-          const int cb = w + bi * NW;
-          f32x4 x = zero4();
-          x = mfma_f32(t4.x, yv[bi][0], x);
-          x = mfma_f32(t4.y, yv[bi][1], x);
-          x = mfma_f32(t4.z, yv[bi][2], x);
-          x = mfma_f32(t4.w, yv[bi][3], x);
-          *reinterpret_cast<float4*>(&sX[(16 * cb + ln) * LX + 16 * Rs + 4 * q4]) = make_float4(x[0], x[1], x[2], x[3]);
-        }
-        compiler_fence();
+        f32x4 x = zero4();
+        x = mfma_f32(t4.x, y[0], x);
+        x = mfma_f32(t4.y, y[1], x);
+        x = mfma_f32(t4.z, y[2], x);
+        x = mfma_f32(t4.w, y[3], x);
+        xb[Rs] = x;
+        put(Rs, x);
       }
+    }
+    __syncthreads();
+
+    // ---- 5. per wave, on its own column blocks of X^T:
+    //      X = T [beta K+ | beta V] (bf16 pieces, k steps up to the diagonal),
+    //      then W and U^T out
+    {
+#pragma unroll
+      for (int bi = 0; bi < CBPW; ++bi) {
+        const int cb = w + bi * NW;
+        float* xc = &sX[(16 * cb + ln) * LX];
+        SplitN<NP> bB[2];   // B: tokens 32 ks + 8 q4 .. + 7 of this lane's column
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) bB[ks] = load_split<NP>(xc + 32 * ks + 8 * q4);
+        compiler_fence();   // read before this wave overwrites the column below
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 1 && R < 2) continue;   // T_{R, >= 32} = 0 for R < 2
+            SplitN<NP> aT;
+#pragma unroll
+            for (int k = 0; k < NP; ++k) aT.v[k] = load_bf16x8(&sTp[k * 4096 + frag_index(16 * R + ln, 32 * ks + 8 * q4, 64)]);
+            acc = mfmaN<NP>(aT, bB[ks], acc);
+          }
+          *reinterpret_cast<float4*>(&xc[16 * R + 4 * q4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+      compiler_fence();
       __bf16* W = reinterpret_cast<__bf16*>(rec + REC.W);
       float* UT = reinterpret_cast<float*>(rec + REC.UT);
 #pragma unroll
