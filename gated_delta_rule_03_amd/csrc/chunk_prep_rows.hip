@@ -594,45 +594,9 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     //      own (held in registers) on top: lower + upper, the same every time.
     {
       f32x4 keepA[4], keepQ[4];
-      float E[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) E[j] = 1.f;
-#pragma unroll
-      for (int I = 3; I >= 0; --I) {
-        keepA[I] = keepQ[I] = zero4();
-        if (I > R) continue;
-        if (I < R) {   // E = e^{sum of the block totals of blocks I .. R-1}
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int c0 = 64 * hf + 32 * ks + 8 * q4;
-            const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[I][c0]);
-            const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[I][c0 + 4]);
-            const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) E[8 * ks + i] *= ev[i];
-          }
-        }
-        f32x4 accA = zero4(), accQ = zero4();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c0 = 64 * hf + 32 * ks + 8 * q4;
-          SplitN<NP> bk;
-          if (I == R) {
-            bk = kcp[ks];
-          } else {
-#pragma unroll
-            for (int k = 0; k < NP; ++k)
-              bk.v[k] = *reinterpret_cast<const bf16x8*>(&sKc[k * 64 * KCS + (16 * I + ln) * KCS + c0]);
-          }
-          float ra[8], rq[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ra[i] = kP[8 * ks + i] * E[8 * ks + i];
-            rq[i] = qP[8 * ks + i] * E[8 * ks + i];
-          }
-          accA = mfmaN<NP>(splitN<NP>(ra), bk, accA);
-          accQ = mfmaN<NP>(splitN<NP>(rq), bk, accQ);
-        }
+      for (int I = 0; I < 4; ++I) keepA[I] = keepQ[I] = zero4();
+      auto finish = [&](int I, const f32x4& accA, const f32x4& accQ) {
         if (HF == 1 || hf == 1) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -644,7 +608,51 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
           keepA[I] = accA;
           keepQ[I] = accQ;
         }
-        compiler_fence();
+      };
+      // the diagonal block: the row operands as they are (no decay between)
+      {
+        f32x4 accA = zero4(), accQ = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float ra[8], rq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ra[i] = kP[8 * ks + i];
+            rq[i] = qP[8 * ks + i];
+          }
+          mfmaN2<NP>(splitN<NP>(ra), splitN<NP>(rq), kcp[ks], accA, accQ);
+        }
+        finish(R, accA, accQ);
+      }
+      // blocks I = R - 1, ..., 0: E = e^{sum of the block totals of blocks I .. R-1}
+      float E[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) E[j] = 1.f;
+#pragma unroll
+      for (int d = 1; d < 4; ++d) {
+        const int I = R - d;
+        if (I < 0) continue;
+        f32x4 accA = zero4(), accQ = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c0 = 64 * hf + 32 * ks + 8 * q4;
+          const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[I][c0]);
+          const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[I][c0 + 4]);
+          const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+          SplitN<NP> bk;
+#pragma unroll
+          for (int k = 0; k < NP; ++k)
+            bk.v[k] = *reinterpret_cast<const bf16x8*>(&sKc[k * 64 * KCS + (16 * I + ln) * KCS + c0]);
+          float ra[8], rq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            E[8 * ks + i] *= ev[i];
+            ra[i] = kP[8 * ks + i] * E[8 * ks + i];
+            rq[i] = qP[8 * ks + i] * E[8 * ks + i];
+          }
+          mfmaN2<NP>(splitN<NP>(ra), splitN<NP>(rq), bk, accA, accQ);
+        }
+        finish(I, accA, accQ);
       }
       if constexpr (HF == 2) {
         __syncthreads();
