@@ -9,16 +9,17 @@
 //    conv rows before the chunk), alpha and b of the NEXT chunk are loaded
 //    into registers while the current one is processed, so the input
 //    latency is hidden.  The conv weights and dt_bias of the head stay in LDS.
-//  * Wave (R, half) owns token rows 16R..16R+15 and key channels
-//    64 half .. 64 half + 63.  A lane holds one token row r and 16 channels
-//    (two groups of 8 at 32-channel spacing), which is exactly the A operand
-//    of a 16x16x32 matrix-core step, so the row operands of A = beta K K^T
-//    and Aqk = Q K^T (with their decays) never leave registers.  The token
+//  * Wave (R, g) owns token rows 16R..16R+15 and key channels CW g ..
+//    CW g + CW - 1 (CW = 64 at dk = 128, 32 at dk = 64).  A lane holds one
+//    token row r and CW / 4 channels (groups of 8 at 32-channel spacing),
+//    which is exactly the A operand of 16x16x32 matrix-core steps, so the
+//    row operands of A = beta K K^T and Aqk = Q K^T (with their decays) never
+//    leave registers.  The token
 //    prefix sums of g inside a 16-row block are DPP scans across the 16
 //    lanes of a row, and e^{P} is formed once per element for both q and k.
 //    The conv runs as bf16 dot products over tap pairs.
-//  * The two channel halves of A and Aqk meet in LDS: the upper half stores
-//    its partial sums and the lower half adds its own on top, in that order.
+//  * The channel groups' partial sums of A and Aqk meet in LDS: group 1
+//    stores and group 0 adds its own on top, in that order.
 //  * The solve of (I + A) X = [beta K+ | beta V] forms T = (I + A)^-1 first:
 //    the inverses of the four diagonal blocks by forward substitution, then
 //    each 16-column block of T on fp32 matrix-core steps.  X = T B is then a
@@ -36,6 +37,11 @@ namespace {
 
 constexpr int kRawRows = kChunk + 3;   // the chunk's rows and the three conv rows before it
 constexpr int kRowsNP = 2;             // bf16 pieces per operand (bf16 inputs)
+// Channels per wave: 64 at dk = 128 (8 waves); 32 at dk = 64 (8 waves rather
+// than 4).  Measured on the 32K prefill, 16 waves of 32 channels at dk = 128
+// were 39% slower than 8 of 64 (128 registers, with spills).
+template <int D>
+constexpr int rows_cw() { return D == 128 ? 64 : 32; }
 
 // Lane i of each 16-lane row reads lane i - N of the same row; lanes
 // shifted in from outside the row read 0.
@@ -126,27 +132,30 @@ __device__ __forceinline__ ChunkPos chunk_pos(const int4& d) {
 // q | k | v staging rows are 3D/8 pieces of 16 bytes wide; thread t stages
 // piece column t % (3D/8) of rows t / (3D/8) + SR j (SR staging rows per pass
 // of the block), so that its tensor and channels stay fixed.
-template <int D, int NT>
+template <int D, int NT, int KSW>
 struct RawChunk {
   static constexpr int kCols = 3 * D / 8;
   static constexpr int kSR = NT / kCols;                       // rows per pass
   static constexpr int kPer = (kRawRows + kSR - 1) / kSR;      // passes
   uint4 x[kPer];      // staging rows, then written to LDS
-  uint4 a[2];         // alpha of this lane's row and 16 channels
+  uint4 a[KSW];       // alpha of this lane's row and its channels
   uint16_t b;         // b of this lane's row
   uint32_t zero;      // bit j: piece j stands for a missing history row (written as zeros)
 };
 
 }  // namespace
 
+// CW: channels per wave (64: 2 waves per SIMD at dk = 128; 32: 4 waves).
 // kHooks: compiled with the input hooks (q, k, v already activated; g or beta
 // given directly); without them those selects cost nothing.
-template <int D, bool kHooks>
-__global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(Params p, ChunkTable t, PrefillIO io,
+template <int D, int CW, bool kHooks>
+__global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(Params p, ChunkTable t, PrefillIO io,
                                                                                uint8_t* records) {
-  constexpr int HF = D / 64;            // channel halves
-  constexpr int NW = 4 * HF;            // waves
+  constexpr int CQ = D / CW;            // channel groups
+  constexpr int NW = 4 * CQ;            // waves
   constexpr int NT = 64 * NW;
+  constexpr int KSW = CW / 32;          // 32-channel matrix-core k steps per wave
+  constexpr int CPL = 8 * KSW;          // channels per lane
   constexpr int NP = kRowsNP;
   constexpr Record REC = record_layout(D, NP);
   constexpr int RAWS = 3 * D + 8;       // staging row stride (bf16)
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   constexpr size_t kXBytes = static_cast<size_t>(2 * D) * LX * 4;
   constexpr size_t kUBytes = kRawBytes > kKcBytes ? (kRawBytes > kXBytes ? kRawBytes : kXBytes)
                                                   : (kKcBytes > kXBytes ? kKcBytes : kXBytes);
-  using Raw = RawChunk<D, NT>;
+  using Raw = RawChunk<D, NT, KSW>;
   static_assert(CBPW * NW == NCB, "column blocks must divide evenly over the waves");
   static_assert(kKcBytes <= static_cast<size_t>(D) * LX * 4, "the beta V^T rows of X^T must start past the k e^{-P} pieces");
 
@@ -170,12 +179,16 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   __shared__ __align__(16) unsigned char sU[kUBytes];
   __shared__ __align__(16) float sA[64 * LA];            // A (rows scaled by beta)
   __shared__ __align__(16) float sAqk[64 * LA];
+  // with four channel groups the partial sums of A and Aqk meet in two pairs
+  // of buffers (groups 0, 1 and 2, 3); their readers add the pairs
+  __shared__ __align__(16) float sA2[CQ > 2 ? 64 * LA : 4];
+  __shared__ __align__(16) float sAqk2[CQ > 2 ? 64 * LA : 4];
   __shared__ __align__(16) float sT[4][16 * LT];         // (I + A_RR)^-1, fp32
   __shared__ __align__(16) uint2 sWb[3][D];              // conv taps of this head (q, k, v), 4 bf16 each
   __shared__ __align__(16) float sDtb[D];
   __shared__ __align__(16) float sBt[4][D];              // in-block totals of g
   __shared__ __align__(16) float sEBt[4][D];             // their exponentials
-  __shared__ float sNorm[HF][64][2];                     // partial sums of q^2, k^2
+  __shared__ float sNorm[CQ][64][2];                     // partial sums of q^2, k^2
   __shared__ float sBeta[64];
   __bf16* sRaw = reinterpret_cast<__bf16*>(sU);
   __bf16* sKc = reinterpret_cast<__bf16*>(sU);
@@ -188,8 +201,11 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   // of the thread index the compiler cannot see through, so that it does not
   // hoist per-lane addresses out of the loop and keep them in registers for
   // its whole length (that alone would cost about 150 registers).
+  // Waves w, w + 4, ... share a SIMD; their row blocks are a permutation of
+  // 0..3 when there are four of them, and R, 3 - R for two, so the
+  // triangular A work is even per SIMD.
   struct LaneCoords {
-    int tid, w, lane, ln, q4, R, hf, r;
+    int tid, w, lane, ln, q4, R, cq, r;
   };
   auto coords = [](int t) {
     LaneCoords L;
@@ -198,9 +214,11 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     L.lane = t % kWave;
     L.ln = L.lane & 15;
     L.q4 = L.lane >> 4;
-    L.R = L.w < 4 ? L.w : 7 - L.w;   // row block
-    L.hf = L.w / 4;                  // channel half
-    L.r = 16 * L.R + L.ln;           // this lane's token row
+    const int s = L.w & 3, k = L.w >> 2;
+    const int base = (k & 2) ? ((s + 2) & 3) : s;
+    L.R = (k & 1) ? 3 - base : base;   // row block
+    L.cq = k;                          // channel group
+    L.r = 16 * L.R + L.ln;             // this lane's token row
     return L;
   };
   const int tid = threadIdx.x;
@@ -270,10 +288,10 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   auto load_gate_inputs = [&](Raw& nx, const ChunkPos& cp, const LaneCoords& L) {
     const uint32_t hd = static_cast<uint32_t>(HD);
     const uint16_t* arow = static_cast<const uint16_t*>(io.alpha) + cp.tok0 * static_cast<int64_t>(HD) +
-                           static_cast<size_t>(h) * D + 64 * L.hf + 8 * L.q4;
+                           static_cast<size_t>(h) * D + CW * L.cq + 8 * L.q4;
     const uint32_t rr = static_cast<uint32_t>(min(L.r, cp.len - 1));
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) nx.a[ks] = *reinterpret_cast<const uint4*>(arow + rr * hd + 32 * ks);
+    for (int ks = 0; ks < KSW; ++ks) nx.a[ks] = *reinterpret_cast<const uint4*>(arow + rr * hd + 32 * ks);
     nx.b = static_cast<const uint16_t*>(io.b)[(cp.tok0 + rr) * H + h];
   };
 
@@ -282,7 +300,9 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
   // the wait for them counts only the memory operations of one iteration.
   Raw nxt;
   ChunkPos cur_pos{}, nxt_pos{};
-  uint4 a_cur[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  uint4 a_cur[KSW];
+#pragma unroll
+  for (int ks = 0; ks < KSW; ++ks) a_cur[ks] = make_uint4(0u, 0u, 0u, 0u);
   uint32_t b_cur = 0u;
   // the descriptor of the chunk after the next (a uniform index: a scalar
   // load, one chunk ahead of its use)
@@ -297,13 +317,15 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         *reinterpret_cast<uint4*>(&sRaw[sr * RAWS + 8 * st_col]) =
             (nxt.zero >> j) & 1u ? make_uint4(0u, 0u, 0u, 0u) : nxt.x[j];
     }
-    uint32_t aw[8] = {nxt.a[0].x, nxt.a[0].y, nxt.a[0].z, nxt.a[0].w, nxt.a[1].x, nxt.a[1].y, nxt.a[1].z, nxt.a[1].w};
     uint32_t bw = nxt.b;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(aw[i]));   // arrived before the next load goes out
+    for (int ks = 0; ks < KSW; ++ks) {
+      uint32_t aw[4] = {nxt.a[ks].x, nxt.a[ks].y, nxt.a[ks].z, nxt.a[ks].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(aw[i]));   // arrived before the next load goes out
+      a_cur[ks] = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+    }
     asm volatile("" : "+v"(bw));
-    a_cur[0] = make_uint4(aw[0], aw[1], aw[2], aw[3]);
-    a_cur[1] = make_uint4(aw[4], aw[5], aw[6], aw[7]);
     b_cur = bw;
   };
   if (grp < total) {
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     int tid_opaque = tid;
     asm volatile("" : "+v"(tid_opaque));
     const LaneCoords L = coords(tid_opaque);
-    const int w = L.w, lane = L.lane, ln = L.ln, q4 = L.q4, R = L.R, hf = L.hf, r = L.r;
+    const int w = L.w, lane = L.lane, ln = L.ln, q4 = L.q4, R = L.R, cq = L.cq, r = L.r;
     __syncthreads();   // the staging rows are written
 
     // ---- the next chunk's staging rows go out now, ahead of phase 1: it
@@ -343,12 +365,12 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     const float* dtb = sDtb + inv;
 
     // ---- 1. conv + SiLU of this lane's row (q, k, v), gate, beta
-    float qv[16], kv[16], vv[16], gv[16];
+    float qv[CPL], kv[CPL], vv[CPL], gv[CPL];
 #pragma unroll
     for (int tens = 0; tens < 3; ++tens) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KSW; ++ks) {
+        const int c0 = CW * cq + 32 * ks + 8 * q4;
         // all eight LDS reads of the group go out together, then the math
         // (left to itself the scheduler waits for each tap read in turn)
         uint4 xm[4], wv[4];
@@ -393,8 +415,8 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     }
     // the gate likewise: computed for every lane, then selected
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c0 = 64 * hf + 32 * ks + 8 * q4;
+    for (int ks = 0; ks < KSW; ++ks) {
+      const int c0 = CW * cq + 32 * ks + 8 * q4;
       const uint32_t aw[4] = {a_cur[ks].x, a_cur[ks].y, a_cur[ks].z, a_cur[ks].w};
       const float4 d0 = *reinterpret_cast<const float4*>(&dtb[c0]);
       const float4 d1 = *reinterpret_cast<const float4*>(&dtb[c0 + 4]);
@@ -419,11 +441,11 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       beta = raw_beta ? bb : sigmoidf_(bb);
       if (flags & KDA_FLAG_BETA_X2) beta *= 2.0f;
     }
-    if (hf == 0 && q4 == 0) sBeta[r] = beta;
+    if (cq == 0 && q4 == 0) sBeta[r] = beta;
     {
       float sq = 0.f, sk = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < CPL; ++j) {
         sq += qv[j] * qv[j];
         sk += kv[j] * kv[j];
       }
@@ -432,25 +454,25 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       sq += __shfl_xor(sq, 32);
       sk += __shfl_xor(sk, 32);
       if (q4 == 0) {
-        sNorm[hf][r][0] = sq;
-        sNorm[hf][r][1] = sk;
+        sNorm[cq][r][0] = sq;
+        sNorm[cq][r][1] = sk;
       }
     }
     // in-block decay sums P_r (through token r); e^{P_r} through the hardware
     // exponential: its ~1e-5 relative error at |P| ~ 80 is below the bf16
     // pieces' resolution
-    float P[16], eP[16];
+    float P[CPL], eP[CPL];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) P[j] = gv[j];
+    for (int j = 0; j < CPL; ++j) P[j] = gv[j];
     row_prefix(P);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) eP[j] = exp_fast(P[j]);
+    for (int j = 0; j < CPL; ++j) eP[j] = exp_fast(P[j]);
     pin(P);
     pin(eP);
     if (ln == 15) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KSW; ++ks) {
+        const int c0 = CW * cq + 32 * ks + 8 * q4;
         *reinterpret_cast<float4*>(&sBt[R][c0]) = make_float4(P[8 * ks], P[8 * ks + 1], P[8 * ks + 2], P[8 * ks + 3]);
         *reinterpret_cast<float4*>(&sBt[R][c0 + 4]) =
             make_float4(P[8 * ks + 4], P[8 * ks + 5], P[8 * ks + 6], P[8 * ks + 7]);
@@ -466,16 +488,17 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     float iq, ik;
     {
       float nq = sNorm[0][r][0], nk = sNorm[0][r][1];
-      if constexpr (HF == 2) {
-        nq += sNorm[1][r][0];
-        nk += sNorm[1][r][1];
+#pragma unroll
+      for (int g = 1; g < CQ; ++g) {
+        nq += sNorm[g][r][0];
+        nk += sNorm[g][r][1];
       }
       // hardware reciprocal square root (~1 ulp): bf16 inputs only here
       iq = (l2 ? __builtin_amdgcn_rsqf(nq + p.eps) : 1.0f) * p.scale;
       ik = l2 ? __builtin_amdgcn_rsqf(nk + p.eps) : 1.0f;
     }
-    float qP[16], kP[16];
-    SplitN<NP> kcp[2];   // k e^{-P} pieces: the B operand of this lane's diagonal block
+    float qP[CPL], kP[CPL];
+    SplitN<NP> kcp[KSW];   // k e^{-P} pieces: the B operand of this lane's diagonal block
     // e^{G before block R} and the sum of the later block totals, per channel
     auto before_after = [&](int c0, float (&eb)[8], float (&after)[8]) {
 #pragma unroll
@@ -502,8 +525,8 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       // beta V^T straight to its rows of X^T, which lie past the k e^{-P}
       // pieces in the shared region (beta K+ follows in phase 4)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KSW; ++ks) {
+        const int c0 = CW * cq + 32 * ks + 8 * q4;
 #pragma unroll
         for (int i = 0; i < 8; ++i) sX[(D + c0 + i) * LX + r] = beta * vv[8 * ks + i];
       }
@@ -511,10 +534,10 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       // key side: k e^{P}, k e^{-P} pieces, K~^T, e^{G_C}
       __bf16* KT = reinterpret_cast<__bf16*>(rec + REC.KT);
       float* eGC = reinterpret_cast<float*>(rec + REC.eGC);
-      float ebs[2][8];   // e^{G before block R}: kept for the query side
+      float ebs[KSW][8];   // e^{G before block R}: kept for the query side
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KSW; ++ks) {
+        const int c0 = CW * cq + 32 * ks + 8 * q4;
         float (&eb)[8] = ebs[ks];
         float after[8];
         before_after(c0, eb, after);
@@ -562,8 +585,8 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       // query side: Q+ = q e^{G_r} out, q e^{P} kept
       __bf16* Qp = reinterpret_cast<__bf16*>(rec + REC.Qp);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KSW; ++ks) {
+        const int c0 = CW * cq + 32 * ks + 8 * q4;
         const float (&eb)[8] = ebs[ks];
         float qo[8], pq[8];
 #pragma unroll
@@ -589,20 +612,23 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 
     load_gate_inputs(nxt, nxt_pos, L);
 
-    // ---- 3. this wave's channel half of A and Aqk, sub-blocks (R, I <= R).
-    //      The upper half stores its partial sums, then the lower half adds its
-    //      own (held in registers) on top: lower + upper, the same every time.
+    // ---- 3. this wave's channel group's part of A and Aqk, sub-blocks
+    //      (R, I <= R).  Groups 1 (and 3) store their partial sums, then
+    //      groups 0 (and 2) add their own (held in registers) on top: the same
+    //      order every time.
     {
       f32x4 keepA[4], keepQ[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) keepA[I] = keepQ[I] = zero4();
+      float* const dA = (CQ > 2 && cq >= 2) ? sA2 : sA;
+      float* const dQ = (CQ > 2 && cq >= 2) ? sAqk2 : sAqk;
       auto finish = [&](int I, const f32x4& accA, const f32x4& accQ) {
-        if (HF == 1 || hf == 1) {
+        if (CQ == 1 || (cq & 1)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
-            sA[row * LA + col] = sBeta[row] * accA[j];
-            sAqk[row * LA + col] = accQ[j];
+            dA[row * LA + col] = sBeta[row] * accA[j];
+            dQ[row * LA + col] = accQ[j];
           }
         } else {
           keepA[I] = accA;
@@ -613,7 +639,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       {
         f32x4 accA = zero4(), accQ = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KSW; ++ks) {
           float ra[8], rq[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -625,17 +651,17 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         finish(R, accA, accQ);
       }
       // blocks I = R - 1, ..., 0: E = e^{sum of the block totals of blocks I .. R-1}
-      float E[16];
+      float E[CPL];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) E[j] = 1.f;
+      for (int j = 0; j < CPL; ++j) E[j] = 1.f;
 #pragma unroll
       for (int d = 1; d < 4; ++d) {
         const int I = R - d;
         if (I < 0) continue;
         f32x4 accA = zero4(), accQ = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c0 = 64 * hf + 32 * ks + 8 * q4;
+        for (int ks = 0; ks < KSW; ++ks) {
+          const int c0 = CW * cq + 32 * ks + 8 * q4;
           const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[I][c0]);
           const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[I][c0 + 4]);
           const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
@@ -654,17 +680,17 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
         }
         finish(I, accA, accQ);
       }
-      if constexpr (HF == 2) {
+      if constexpr (CQ > 1) {
         __syncthreads();
-        if (hf == 0) {
+        if ((cq & 1) == 0) {
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
             if (I > R) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
-              sA[row * LA + col] = sBeta[row] * keepA[I][j] + sA[row * LA + col];
-              sAqk[row * LA + col] = keepQ[I][j] + sAqk[row * LA + col];
+              dA[row * LA + col] = sBeta[row] * keepA[I][j] + dA[row * LA + col];
+              dQ[row * LA + col] = keepQ[I][j] + dQ[row * LA + col];
             }
           }
         }
@@ -672,17 +698,34 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
     }
     __syncthreads();
 
+    // A as its readers see it: with four channel groups, the sum of the pairs
+    auto load_a4 = [&](int idx) {
+      float4 a4 = *reinterpret_cast<const float4*>(&sA[idx]);
+      if constexpr (CQ > 2) {
+        const float4 u4 = *reinterpret_cast<const float4*>(&sA2[idx]);
+        a4 = make_float4(a4.x + u4.x, a4.y + u4.y, a4.z + u4.z, a4.w + u4.w);
+      }
+      return a4;
+    };
+
     // ---- 4. Aqk pieces out; the diagonal-block inverses to LDS; beta K+ to X^T
     {
       __bf16* Aq = reinterpret_cast<__bf16*>(rec + REC.Aqk);
       // a fixed trip count, not a loop (a loop here makes the compiler wait
       // for every outstanding load first)
 #pragma unroll
-      for (int it = 0; it < 64 * 8 / NT; ++it) {
+      for (int it = 0; it < (64 * 8 + NT - 1) / NT; ++it) {
         const int e = L.tid + it * NT;
+        if (NT > 64 * 8 && e >= 64 * 8) break;
         const int rw = e >> 3, i0 = 8 * (e & 7);
-        const float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
-        const float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);
+        float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
+        float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);
+        if constexpr (CQ > 2) {
+          const float4 u0 = *reinterpret_cast<const float4*>(&sAqk2[rw * LA + i0]);
+          const float4 u1 = *reinterpret_cast<const float4*>(&sAqk2[rw * LA + i0 + 4]);
+          q0 = make_float4(q0.x + u0.x, q0.y + u0.y, q0.z + u0.z, q0.w + u0.w);
+          q1 = make_float4(q1.x + u1.x, q1.y + u1.y, q1.z + u1.z, q1.w + u1.w);
+        }
         const float qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         float qm[8];
 #pragma unroll
@@ -702,7 +745,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
           float a[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 a4 = *reinterpret_cast<const float4*>(&sA[(16 * Rb + i) * LA + 16 * Rb + 4 * q]);
+            const float4 a4 = load_a4((16 * Rb + i) * LA + 16 * Rb + 4 * q);
             a[4 * q] = a4.x; a[4 * q + 1] = a4.y; a[4 * q + 2] = a4.z; a[4 * q + 3] = a4.w;
           }
           float ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -716,8 +759,8 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
       }
       // beta K+ = beta (k e^{P}) e^{G before the block}, over the k e^{-P} pieces
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 64 * hf + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KSW; ++ks) {
+        const int c0 = CW * cq + 32 * ks + 8 * q4;
         float eb[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) eb[i] = 1.f;
@@ -780,7 +823,7 @@ __global__ __launch_bounds__(64 * 4 * (D / 64), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
           for (int M = 0; M < 3; ++M) {
             if (M < J || M >= Rs) continue;
-            const float4 a4 = *reinterpret_cast<const float4*>(&sA[(16 * Rs + ln) * LA + 16 * M + 4 * q4]);
+            const float4 a4 = load_a4((16 * Rs + ln) * LA + 16 * M + 4 * q4);
             acc = mfma_f32(a4.x, xb[M][0], acc);
             acc = mfma_f32(a4.y, xb[M][1], acc);
             acc = mfma_f32(a4.z, xb[M][2], acc);
@@ -878,9 +921,9 @@ static hipError_t launch_rows_d(const Params& p, const ChunkTable& t, const Pref
   groups = groups < 1 ? 1 : (groups > max_chunks ? max_chunks : groups);
   const dim3 grid(static_cast<unsigned>(p.H) * static_cast<unsigned>(groups));
   if (p.flags & (KDA_FLAG_SKIP_CONV | KDA_FLAG_RAW_GATE | KDA_FLAG_RAW_BETA))
-    chunk_prep_rows_kernel<D, true><<<grid, 64 * 4 * (D / 64), 0, st>>>(p, t, io, records);
+    chunk_prep_rows_kernel<D, rows_cw<D>(), true><<<grid, 64 * 4 * (D / rows_cw<D>()), 0, st>>>(p, t, io, records);
   else
-    chunk_prep_rows_kernel<D, false><<<grid, 64 * 4 * (D / 64), 0, st>>>(p, t, io, records);
+    chunk_prep_rows_kernel<D, rows_cw<D>(), false><<<grid, 64 * 4 * (D / rows_cw<D>()), 0, st>>>(p, t, io, records);
   return hipGetLastError();
 }
 
