@@ -622,7 +622,9 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       for (int I = 0; I < 4; ++I) keepA[I] = keepQ[I] = zero4();
       float* const dA = (CQ > 2 && cq >= 2) ? sA2 : sA;
       float* const dQ = (CQ > 2 && cq >= 2) ? sAqk2 : sAqk;
-      auto finish = [&](int I, const f32x4& accA, const f32x4& accQ) {
+      // kept sums are indexed by d = R - I, which is static in the unrolled
+      // loops (an index by I would be a dynamic register index)
+      auto finish = [&](int d, int I, const f32x4& accA, const f32x4& accQ) {
         if (CQ == 1 || (cq & 1)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -631,8 +633,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
             dQ[row * LA + col] = accQ[j];
           }
         } else {
-          keepA[I] = accA;
-          keepQ[I] = accQ;
+          keepA[d] = accA;
+          keepQ[d] = accQ;
         }
       };
       // the diagonal block: the row operands as they are (no decay between)
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
           }
           mfmaN2<NP>(splitN<NP>(ra), splitN<NP>(rq), kcp[ks], accA, accQ);
         }
-        finish(R, accA, accQ);
+        finish(0, R, accA, accQ);
       }
       // blocks I = R - 1, ..., 0: E = e^{sum of the block totals of blocks I .. R-1}
       float E[CPL];
@@ -678,19 +680,20 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
           }
           mfmaN2<NP>(splitN<NP>(ra), splitN<NP>(rq), bk, accA, accQ);
         }
-        finish(I, accA, accQ);
+        finish(d, I, accA, accQ);
       }
       if constexpr (CQ > 1) {
         __syncthreads();
         if ((cq & 1) == 0) {
 #pragma unroll
-          for (int I = 0; I < 4; ++I) {
-            if (I > R) continue;
+          for (int d = 0; d < 4; ++d) {
+            const int I = R - d;
+            if (I < 0) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
-              dA[row * LA + col] = sBeta[row] * keepA[I][j] + dA[row * LA + col];
-              dQ[row * LA + col] = keepQ[I][j] + dQ[row * LA + col];
+              dA[row * LA + col] = sBeta[row] * keepA[d][j] + dA[row * LA + col];
+              dQ[row * LA + col] = keepQ[d][j] + dQ[row * LA + col];
             }
           }
         }
@@ -711,12 +714,15 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     // ---- 4. Aqk pieces out; the diagonal-block inverses to LDS; beta K+ to X^T
     {
       __bf16* Aq = reinterpret_cast<__bf16*>(rec + REC.Aqk);
-      // a fixed trip count, not a loop (a loop here makes the compiler wait
-      // for every outstanding load first)
+      // by waves 1 .. NW - 1 only: wave 0 forms the diagonal-block inverses
+      // below, the longest task of this phase.  A fixed trip count, not a
+      // loop (a loop here makes the compiler wait for every outstanding
+      // load first).
+      constexpr int NAQ = NT - kWave;
 #pragma unroll
-      for (int it = 0; it < (64 * 8 + NT - 1) / NT; ++it) {
-        const int e = L.tid + it * NT;
-        if (NT > 64 * 8 && e >= 64 * 8) break;
+      for (int it = 0; it < (64 * 8 + NAQ - 1) / NAQ; ++it) {
+        const int e = L.tid - kWave + it * NAQ;
+        if (w == 0 || e >= 64 * 8) break;
         const int rw = e >> 3, i0 = 8 * (e & 7);
         float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
         float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);
@@ -814,11 +820,16 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
           if ((Rs == 0 && J == 1) || (Rs == 2 && J == 3)) put(Rs, zero4());
           continue;
         }
-        f32x4 y;
-        if (Rs == J) {   // the identity's block
+        if (Rs == J) {   // X_JJ = T_JJ, read as it is
+          f32x4 x;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = (4 * q4 + i == ln) ? 1.f : 0.f;
-        } else {         // Y = - A_{Rs, J..Rs-1} X_{J..Rs-1}: k = 4 q4 + s within each block
+          for (int i = 0; i < 4; ++i) x[i] = sT[J][(4 * q4 + i) * LT + ln];
+          xb[Rs] = x;
+          put(Rs, x);
+          continue;
+        }
+        f32x4 y;
+        {                // Y = - A_{Rs, J..Rs-1} X_{J..Rs-1}: k = 4 q4 + s within each block
           f32x4 acc = zero4();
 #pragma unroll
           for (int M = 0; M < 3; ++M) {

@@ -104,9 +104,12 @@ __device__ __forceinline__ void load_ops_b(OpsB<D, DVT, NP>& o, const uint8_t* r
   }
 }
 
+// gate >= 0: this launch is one of two value-tile widths and runs only when
+// the chunk table's choice (chunk0[N+1]) equals gate; its workgroups exit
+// at once otherwise.
 template <int D, int DVT, int NP, bool OUT_BF16>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t, PrefillIO io, const uint8_t* records,
-                                                         int n_sh) {
+                                                         int n_sh, int gate) {
   constexpr int NTILE = D / DVT;
   constexpr int KP = D < 32 ? 32 : D;     // channel extent in whole 32-wide steps
   constexpr int KS = KP / 32;             // k steps over channels
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   const int tile = (bx / 8) % NTILE;
   const int sh = (bx / 8 / NTILE) * 8 + bx % 8;
   if (sh >= n_sh) return;
+  if (gate >= 0 && t.chunk0[t.N + 1] != gate) return;
   const int s = sh / H, h = sh % H;
   const int j0 = tile * DVT;
   const int tid = threadIdx.x, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
@@ -346,40 +350,46 @@ static int pick_dvt(int D, int n_sh) {
 
 template <int D, int DVT>
 static hipError_t launch_scan_dt(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
-                                 bool io_bf16, bool out_bf16, hipStream_t st) {
+                                 bool io_bf16, bool out_bf16, int gate, hipStream_t st) {
   const int n_sh = t.N * p.H;
   const int groups = (n_sh + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * (D / DVT)));
   if (io_bf16) {
-    if (out_bf16) chunk_scan_kernel<D, DVT, 2, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
-    else chunk_scan_kernel<D, DVT, 2, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
+    if (out_bf16) chunk_scan_kernel<D, DVT, 2, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh, gate);
+    else chunk_scan_kernel<D, DVT, 2, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh, gate);
   } else {
-    if (out_bf16) chunk_scan_kernel<D, DVT, 3, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
-    else chunk_scan_kernel<D, DVT, 3, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh);
+    if (out_bf16) chunk_scan_kernel<D, DVT, 3, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh, gate);
+    else chunk_scan_kernel<D, DVT, 3, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh, gate);
   }
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_scan_d(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
-                                bool io_bf16, bool out_bf16, hipStream_t st) {
+                                bool io_bf16, bool out_bf16, bool device_choice, hipStream_t st) {
   const int dvt = pick_dvt(D, t.N * p.H);
   if constexpr (D >= 64) {
-    if (dvt == 64) return launch_scan_dt<D, 64>(p, t, io, records, io_bf16, out_bf16, st);
+    if (dvt == 64) {
+      if (!device_choice) return launch_scan_dt<D, 64>(p, t, io, records, io_bf16, out_bf16, -1, st);
+      // both widths, each running only if the chunk table chose it
+      const hipError_t e = launch_scan_dt<D, 64>(p, t, io, records, io_bf16, out_bf16, 0, st);
+      if (e != hipSuccess) return e;
+      return launch_scan_dt<D, 32>(p, t, io, records, io_bf16, out_bf16, 1, st);
+    }
   }
   if constexpr (D >= 32) {
-    if (dvt == 32) return launch_scan_dt<D, 32>(p, t, io, records, io_bf16, out_bf16, st);
+    if (dvt == 32) return launch_scan_dt<D, 32>(p, t, io, records, io_bf16, out_bf16, -1, st);
   }
-  return launch_scan_dt<D, 16>(p, t, io, records, io_bf16, out_bf16, st);
+  return launch_scan_dt<D, 16>(p, t, io, records, io_bf16, out_bf16, -1, st);
 }
 
 hipError_t launch_chunk_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
-                             bool io_bf16, bool out_bf16, hipStream_t st) {
+                             bool io_bf16, bool out_bf16, bool device_choice, hipStream_t st) {
   switch (p.D) {
-    case 16: return launch_scan_d<16>(p, t, io, records, io_bf16, out_bf16, st);
-    case 32: return launch_scan_d<32>(p, t, io, records, io_bf16, out_bf16, st);
-    case 64: return launch_scan_d<64>(p, t, io, records, io_bf16, out_bf16, st);
-    case 128: return launch_scan_d<128>(p, t, io, records, io_bf16, out_bf16, st);
+    case 16: return launch_scan_d<16>(p, t, io, records, io_bf16, out_bf16, device_choice, st);
+    case 32: return launch_scan_d<32>(p, t, io, records, io_bf16, out_bf16, device_choice, st);
+    case 64: return launch_scan_d<64>(p, t, io, records, io_bf16, out_bf16, device_choice, st);
+    case 128: return launch_scan_d<128>(p, t, io, records, io_bf16, out_bf16, device_choice, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -9,6 +9,16 @@
 // partial.  Grids of the chunk kernels are sized by a host upper bound and
 // blocks past chunk0[N] exit.
 //
+// It also picks the scan's value-tile width for packed batches of unequal
+// lengths (chunk0[N+1]): the scan's length is that of its longest
+// sequences, and when those (the ones with more than half the longest
+// one's chunks) cannot give every compute unit a workgroup at the wide tile
+// (64 value columns), the narrow one (32) halves the work of each chunk
+// step on that critical path.  Measured on eight packed sequences of
+// 1K..129K tokens (32 heads, dk = dv = 128), the narrow tile took the varlen
+// prefill from 17.2 to 15.3 ms; on four equal 32K sequences it was slower
+// (2.81 ms against 2.31 ms for the scan), which the rule leaves wide.
+//
 // conv_state_out_kernel writes each sequence's conv history for continuation:
 // its last three raw inputs per channel (reaching into the incoming history
 // when the sequence is shorter than three tokens), oldest first.
@@ -19,20 +29,29 @@ namespace kda {
 
 __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __restrict__ cu_in, int32_t N,
                                                             int32_t T_uniform, int32_t* __restrict__ cu_ws,
-                                                            int32_t* __restrict__ chunk0) {
+                                                            int32_t* __restrict__ chunk0, int32_t long_tiles,
+                                                            int32_t ncu) {
   __shared__ int32_t scan[1024];
-  __shared__ int32_t carry_s;
+  __shared__ int32_t carry_s, max_s, long_s;
   const int tid = threadIdx.x;
+  auto chunks_of = [&](int s) {
+    const int len = cu_in ? (cu_in[s + 1] - cu_in[s]) : T_uniform;
+    return (len + kChunk - 1) / kChunk;
+  };
   for (int s = tid; s <= N; s += 1024) cu_ws[s] = cu_in ? cu_in[s] : s * T_uniform;
-  if (tid == 0) carry_s = 0;
+  if (tid == 0) {
+    carry_s = 0;
+    max_s = 0;
+    long_s = 0;
+  }
   __syncthreads();
   for (int base = 0; base < N; base += 1024) {
     const int s = base + tid;
-    int nc = 0;
-    if (s < N) {
-      const int len = cu_in ? (cu_in[s + 1] - cu_in[s]) : T_uniform;
-      nc = (len + kChunk - 1) / kChunk;
-    }
+    const int nc = s < N ? chunks_of(s) : 0;
+    int wmax = nc;   // one shared atomic per wave
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) wmax = max(wmax, __shfl_xor(wmax, m));
+    if ((tid & 63) == 0) atomicMax(&max_s, wmax);
     scan[tid] = nc;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -47,7 +66,23 @@ __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __res
     if (tid == 0) carry_s = carry + scan[1023];
     __syncthreads();
   }
-  if (tid == 0) chunk0[N] = carry_s;
+  // the value-tile choice: long_tiles = wide tiles per (sequence, head) of
+  // the long sequences, summed over them against the compute units
+  const int mx = max_s;
+  int n_long = 0;
+  if (cu_in) {
+    for (int s = tid; s < N; s += 1024) n_long += 2 * chunks_of(s) > mx ? 1 : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) n_long += __shfl_xor(n_long, m);
+    if ((tid & 63) == 0) atomicAdd(&long_s, n_long);
+  } else if (tid == 0) {
+    long_s = mx > 0 ? N : 0;   // equal lengths: every sequence is a long one
+  }
+  __syncthreads();
+  if (tid == 0) {
+    chunk0[N] = carry_s;
+    chunk0[N + 1] = static_cast<int64_t>(long_s) * long_tiles < ncu ? 1 : 0;
+  }
 }
 
 // chunk_seq[c] = the last sequence whose first chunk is <= c (empty sequences
@@ -72,9 +107,28 @@ __global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __re
   desc[c] = make_int4(lo, tau0, min(kChunk, cu[lo + 1] - tok0), tok0);
 }
 
+hipError_t device_cus(int* ncu) {
+  static int cus[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int& n = cus[dev & 63];
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  *ncu = n;
+  return hipSuccess;
+}
+
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws, int32_t* chunk0,
-                               int32_t* chunk_seq, int4* desc, int32_t max_chunks, hipStream_t st) {
-  build_chunks_kernel<<<1, 1024, 0, st>>>(cu_in, N, T_uniform, cu_ws, chunk0);
+                               int32_t* chunk_seq, int4* desc, int32_t max_chunks, int32_t H, int32_t D,
+                               hipStream_t st) {
+  int ncu = 0;
+  hipError_t e0 = device_cus(&ncu);
+  if (e0 != hipSuccess) return e0;
+  const int long_tiles = H * (D >= 64 ? D / 64 : 1);
+  build_chunks_kernel<<<1, 1024, 0, st>>>(cu_in, N, T_uniform, cu_ws, chunk0, long_tiles, ncu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_chunks <= 0) return e;
   fill_chunk_seq_kernel<<<(max_chunks + 255) / 256, 256, 0, st>>>(chunk0, cu_ws, N, chunk_seq, desc, max_chunks);

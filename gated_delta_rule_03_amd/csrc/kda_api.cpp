@@ -72,7 +72,7 @@ Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D, int NP) 
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   L.cu = take((N + 1) * sizeof(int32_t));
-  L.chunk0 = take((N + 1) * sizeof(int32_t));
+  L.chunk0 = take((N + 2) * sizeof(int32_t));
   L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
   L.desc = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int4));
   L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D), NP).bytes);
@@ -119,14 +119,19 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   const int mc = static_cast<int>(max_chunks);
 
   kda_status_t s = stage(cfg, KDA_STAGE_CHUNK_TABLE, st, [&] {
-    return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, desc, mc, st);
+    return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, desc, mc, p.H, p.D, st);
   });
   if (s != KDA_OK) return s;
   if (total_T > 0 && mc > 0) {
     s = stage(cfg, KDA_STAGE_CHUNK_PREP, st, [&] { return kda::launch_chunk_prep(p, t, io, records, mc, io_bf16, st); });
     if (s != KDA_OK) return s;
   }
-  s = stage(cfg, KDA_STAGE_CHUNK_SCAN, st, [&] { return kda::launch_chunk_scan(p, t, io, records, io_bf16, out_bf16, st); });
+  // equal lengths: the host knows the batch shape; packed sequences of any
+  // lengths: the value-tile width is chosen on the device
+  const bool device_choice = cu_in != nullptr;
+  s = stage(cfg, KDA_STAGE_CHUNK_SCAN, st, [&] {
+    return kda::launch_chunk_scan(p, t, io, records, io_bf16, out_bf16, device_choice, st);
+  });
   if (s != KDA_OK) return s;
   if (io.conv_out) {
     s = stage(cfg, KDA_STAGE_CONV_STATE, st, [&] { return kda::launch_conv_state_out(p, t, io, io_bf16, st); });

@@ -83,7 +83,8 @@ struct Params {
 // Device-side description of a packed batch, built by the chunk-table kernel.
 struct ChunkTable {
   const int32_t* cu;         // [N+1] token offsets
-  const int32_t* chunk0;     // [N+1] first chunk of each sequence; chunk0[N] = total chunks
+  const int32_t* chunk0;     // [N+2] first chunk of each sequence; chunk0[N] = total chunks;
+                             // chunk0[N+1] = 1 when the scan takes its narrow value tile
   const int32_t* chunk_seq;  // [max_chunks] sequence of each chunk
   const int4* desc;          // [max_chunks] (sequence, first token in it, tokens, first packed token)
   int32_t N;
@@ -103,7 +104,10 @@ struct PrefillIO {
 };
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws,
-                               int32_t* chunk0, int32_t* chunk_seq, int4* desc, int32_t max_chunks, hipStream_t st);
+                               int32_t* chunk0, int32_t* chunk_seq, int4* desc, int32_t max_chunks, int32_t H,
+                               int32_t D, hipStream_t st);
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* ncu);
 hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                              int max_chunks, bool io_bf16, hipStream_t st);
 // The row-block prep kernel (bf16 inputs, dk = dv in {64, 128}, 16-byte
@@ -111,8 +115,11 @@ hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const Prefill
 bool chunk_prep_rows_supported(const Params& p, const PrefillIO& io, bool io_bf16);
 hipError_t launch_chunk_prep_rows(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                                   int max_chunks, hipStream_t st);
+// device_choice: the value-tile width between the wide and the narrow one
+// is taken on the device from chunk0[N+1] (sequence lengths the host does
+// not see); otherwise from the batch shape alone.
 hipError_t launch_chunk_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const uint8_t* records,
-                             bool io_bf16, bool out_bf16, hipStream_t st);
+                             bool io_bf16, bool out_bf16, bool device_choice, hipStream_t st);
 hipError_t launch_conv_state_out(const Params& p, const ChunkTable& t, const PrefillIO& io, bool io_bf16,
                                  hipStream_t st);
 

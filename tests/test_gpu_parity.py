@@ -92,6 +92,22 @@ def test_fp32_varlen_ragged(kda, D):
     assert_parity(p, o, S, cs)
 
 
+@pytest.mark.parametrize("lens", [
+    [700, 3, 64, 0, 65, 130, 1, 64],        # one sequence sets the scan's length: narrow value tile
+    [200, 190, 256, 129, 250, 200, 193, 240],  # all of similar length: wide value tile
+])
+def test_bf16_varlen_value_tile_choice(kda, lens):
+    """16 heads x 8 sequences at dk = dv = 128 launch both value-tile widths
+    of the scan, gated on the chunk table's device-side choice: with one
+    long sequence (11 chunks against at most 3) its 16 x 2 wide tiles leave
+    most compute units idle and the narrow tile runs; with eight sequences
+    of 3..4 chunks the wide one does.  Either way the result must match."""
+    p = make_problem(640 + len(lens) + lens[0], lens, 16, 128, 128, BF16, state_seqs=[0, 2, 5],
+                     conv_state=True)
+    o, S, cs = run_varlen(kda, p)
+    assert_parity(p, o, S, cs)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_bf16_varlen_ragged(kda, D):
     p = make_problem(300 + D, [5, 200, 1, 64, 65, 2, 300], 4, D, D, BF16, state_seqs=[1, 3, 6],
