@@ -685,6 +685,22 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       if constexpr (CQ > 1) {
         __syncthreads();
         if ((cq & 1) == 0) {
+          // every read goes out before the first add: one LDS round trip
+          // for the whole update, not one per element
+          float oa[4][4], oq[4][4], bt[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bt[j] = sBeta[16 * R + 4 * q4 + j];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int I = max(R - d, 0);   // rows past the diagonal's left end are read but not written
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
+              oa[d][j] = dA[row * LA + col];
+              oq[d][j] = dQ[row * LA + col];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
             const int I = R - d;
@@ -692,8 +708,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
-              dA[row * LA + col] = sBeta[row] * keepA[d][j] + dA[row * LA + col];
-              dQ[row * LA + col] = keepQ[d][j] + dQ[row * LA + col];
+              dA[row * LA + col] = bt[j] * keepA[d][j] + oa[d][j];
+              dQ[row * LA + col] = keepQ[d][j] + oq[d][j];
             }
           }
         }
@@ -743,17 +759,32 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       }
       if (w == 0) {   // lane = (block, column) of the unit lower-triangular inverses
         const int Rb = lane >> 4, j = lane & 15;
+        // the strictly lower triangle of the lane's block, all 36 row pieces
+        // read before the substitution starts: read row by row inside it,
+        // each row's LDS latency sat on the dependent chain
+        constexpr int kPieces = 36;   // sum over rows i of ceil(i / 4)
+        float4 al[kPieces];
+        {
+          int k = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int q = 0; q < (i + 3) / 4; ++q) al[k++] = load_a4((16 * Rb + i) * LA + 16 * Rb + 4 * q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // forward substitution down the column; each row's sum runs in four
         // partial sums so the dependent chain is the 16 rows, not 120 FMAs
         float tcol[16];
+        int k0 = 0;   // the row's first piece in al[]
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float a[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 a4 = load_a4((16 * Rb + i) * LA + 16 * Rb + 4 * q);
+          for (int q = 0; q < (i + 3) / 4; ++q) {
+            const float4 a4 = al[k0 + q];
             a[4 * q] = a4.x; a[4 * q + 1] = a4.y; a[4 * q + 2] = a4.z; a[4 * q + 3] = a4.w;
           }
+          k0 += (i + 3) / 4;
           float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < i; ++m) ps[m & 3] += a[m] * tcol[m];
