@@ -76,17 +76,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// The NP pieces of the pair (a, b), each a packed bf16 word.  The value of a
-// rounded half is read back from the packed word by a shift or a mask, not
-// by a second conversion.
+// x - (the low or the high bf16 half of the packed word w), in one packed
+// bf16 dot product with (-1, 0) or (0, -1): both products are exact and the
+// difference of x and its own bf16 rounding is exact in fp32, so no rounding
+// takes place.  (A shift or a mask and a subtraction would take two
+// instructions.)
+// The constant words are passed through a scalar register the compiler cannot
+// see into.  Written as constants, (-1, 0) is encoded as the inline constant
+// -1.0, which the hardware applies to both halves of a packed bf16 operand
+// (measured: the result was x minus both halves), not to the low one alone.
+__device__ __forceinline__ uint32_t sreg(uint32_t c) {
+  asm("" : "+s"(c));   // not volatile: equal uses share one register
+  return c;
+}
+__device__ __forceinline__ float minus_lo(uint32_t w, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, sreg(0x0000bf80u)),
+                                         x, false);
+}
+__device__ __forceinline__ float minus_hi(uint32_t w, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, sreg(0xbf800000u)),
+                                         x, false);
+}
+
+// The NP pieces of the pair (a, b), each a packed bf16 word: piece k + 1
+// splits what is left after piece k.
 template <int NP>
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t (&w)[NP]) {
 #pragma unroll
   for (int k = 0; k < NP; ++k) {
     w[k] = pack_bf16x2(a, b);
     if (k + 1 < NP) {
-      a -= __uint_as_float(w[k] << 16);
-      b -= __uint_as_float(w[k] & 0xffff0000u);
+      a = minus_lo(w[k], a);
+      b = minus_hi(w[k], b);
     }
   }
 }
