@@ -339,6 +339,290 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   }
 }
 
+// The same scan with the chunk output on waves of its own (dk = dv in {64,
+// 128}): eight waves per workgroup, two per SIMD.  Waves 0-3 carry the state
+// chain, S -> Delta = U - W S -> S' = e^{G_C} S + K~^T Delta, and waves 4-7
+// form O = Q+ S + Aqk Delta for the same token rows and store it.  The output
+// is off the chain: its matrix-core steps and the loads of Q+ and Aqk (a
+// third of the record) overlap the chain waves' waits instead of adding to
+// them.  Both roles meet at the same two barriers per chunk: after the first,
+// Delta is in LDS and the output waves are done reading S; after the second,
+// the new S is in LDS and Delta has been read.
+template <int D, int DVT, int NP>
+struct ChainOps {
+  static constexpr int KS = D / 32, CJ = DVT / 16, CBW = D / 64;
+  SplitN<NP> w[KS];          // W rows of the wave's tokens
+  float4 u[CJ];              // U^T, four tokens of one value column
+  float4 e[CBW];             // e^{G_C} of the lane's four state rows
+  SplitN<NP> kt[CBW][2];     // K~^T rows of the wave's state rows
+};
+
+template <int D, int NP>
+struct OutOps {
+  static constexpr int KS = D / 32;
+  SplitN<NP> q[KS];          // Q+ rows of the wave's tokens
+  SplitN<NP> a[2];           // Aqk rows
+};
+
+template <int D, int DVT, int NP, bool OUT_BF16>
+__global__ __launch_bounds__(512) void chunk_scan_split_kernel(Params p, ChunkTable t, PrefillIO io,
+                                                               const uint8_t* records, int n_sh, int gate) {
+  static_assert(D == 64 || D == 128, "state row blocks must divide evenly over four waves");
+  constexpr int NTILE = D / DVT;
+  constexpr int KS = D / 32;              // k steps over channels
+  constexpr int CJ = DVT / 16;            // 16-column blocks of the tile
+  constexpr int CBW = D / 64;             // state row blocks per chain wave
+  constexpr int LST = D + 8;              // row stride of S^T in LDS (bf16)
+  constexpr int LDT = kChunk + 8;         // row stride of Delta^T in LDS (bf16)
+  constexpr Record REC = record_layout(D, NP);
+  constexpr int LO = DVT + 4;             // row stride of an output wave's tile in LDS (fp32)
+  static_assert((KS * CJ) % 2 == 0 && (2 * CJ) % 2 == 0, "k-step groups go in pairs");
+  __shared__ __align__(16) __bf16 sST[NP][DVT * LST];
+  __shared__ __align__(16) __bf16 sDT[NP][DVT * LDT];
+  __shared__ __align__(16) float sO[4][16 * LO];
+
+  const int H = p.H;
+  const int bx = blockIdx.x;
+  const int tile = (bx / 8) % NTILE;
+  const int sh = (bx / 8 / NTILE) * 8 + bx % 8;
+  if (sh >= n_sh) return;
+  if (gate >= 0 && t.chunk0[t.N + 1] != gate) return;
+  const int s = sh / H, h = sh % H;
+  const int j0 = tile * DVT;
+  const int tid = threadIdx.x, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int rw = wave & 3;                // token row block (both roles) / state row blocks rw + 4i
+  const int r0 = 16 * rw;
+  const size_t sbase = (static_cast<size_t>(s) * H + h) * D * D;
+  const int c_first = t.chunk0[s], c_end = t.chunk0[s + 1];
+  const int64_t seq0 = t.cu[s];
+  const int seq_len = t.cu[s + 1] - t.cu[s];
+  auto rec_of = [&](int c) { return records + (static_cast<size_t>(min(c, c_end - 1)) * H + h) * REC.bytes; };
+  // the S^T or Delta^T pieces of one (k step, column block) group
+  auto load_s = [&](int g) {
+    SplitN<NP> b;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) b.v[k] = load_bf16x8(&sST[k][(16 * (g % CJ) + ln) * LST + 32 * (g / CJ) + 8 * q4]);
+    return b;
+  };
+  auto load_d = [&](int g) {
+    SplitN<NP> b;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) b.v[k] = load_bf16x8(&sDT[k][(16 * (g % CJ) + ln) * LDT + 32 * (g / CJ) + 8 * q4]);
+    return b;
+  };
+
+  if (wave < 4) {
+    // ================= the state chain
+    using Ops = ChainOps<D, DVT, NP>;
+    auto load_a = [&](Ops& o, const uint8_t* rec) {
+      const float* UT = reinterpret_cast<const float*>(rec + REC.UT);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        o.w[ks] = load_planes<NP>(rec + REC.W, REC.tile_plane, frag_index(r0 + ln, 32 * ks + 8 * q4, D));
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj)
+        o.u[cj] = *reinterpret_cast<const float4*>(UT + ut_index(j0 + 16 * cj + ln, r0 + 4 * q4));
+    };
+    auto load_b = [&](Ops& o, const uint8_t* rec) {
+      const float* eGC = reinterpret_cast<const float*>(rec + REC.eGC);
+#pragma unroll
+      for (int i = 0; i < CBW; ++i) o.e[i] = *reinterpret_cast<const float4*>(eGC + 16 * (rw + 4 * i) + 4 * q4);
+#pragma unroll
+      for (int i = 0; i < CBW; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          o.kt[i][ks] = load_planes<NP>(rec + REC.KT, REC.tile_plane,
+                                        frag_index(16 * (rw + 4 * i) + ln, 32 * ks + 8 * q4, kChunk));
+    };
+    f32x4 Sacc[CBW][CJ];
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          Sacc[i][cj][j] = io.S0 ? io.S0[sbase + static_cast<size_t>(16 * (rw + 4 * i) + 4 * q4 + j) * D + j0 + 16 * cj + ln]
+                                 : 0.f;
+    auto publish_state = [&]() {
+#pragma unroll
+      for (int i = 0; i < CBW; ++i)
+#pragma unroll
+        for (int cj = 0; cj < CJ; ++cj) {
+          uint32_t w01[NP], w23[NP];
+          split_pair<NP>(Sacc[i][cj][0], Sacc[i][cj][1], w01);
+          split_pair<NP>(Sacc[i][cj][2], Sacc[i][cj][3], w23);
+          const int idx = (16 * cj + ln) * LST + 16 * (rw + 4 * i) + 4 * q4;
+#pragma unroll
+          for (int k = 0; k < NP; ++k) *reinterpret_cast<uint2*>(&sST[k][idx]) = make_uint2(w01[k], w23[k]);
+        }
+    };
+    publish_state();
+    Ops ops;
+    if (c_first < c_end) {
+      load_a(ops, rec_of(c_first));
+      load_b(ops, rec_of(c_first));
+    }
+    __syncthreads();
+    for (int c = c_first; c < c_end; ++c) {
+      // W S for this wave's 16 token rows; S^T pieces one group pair ahead
+      f32x4 accW[CJ];
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) accW[cj] = zero4();
+      {
+        SplitN<NP> bS[2][2];
+        bS[0][0] = load_s(0);
+        bS[0][1] = load_s(1);
+#pragma unroll
+        for (int g = 0; g < KS * CJ; g += 2) {
+          const int cur = (g / 2) & 1;
+          if (g + 2 < KS * CJ) {
+            bS[cur ^ 1][0] = load_s(g + 2);
+            bS[cur ^ 1][1] = load_s(g + 3);
+          }
+          mfmaNx2<NP>(ops.w[g / CJ], bS[cur][0], accW[g % CJ], ops.w[(g + 1) / CJ], bS[cur][1], accW[(g + 1) % CJ]);
+        }
+      }
+      // Delta = U - W S, published transposed
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) {
+        const float4 u = ops.u[cj];
+        uint32_t w01[NP], w23[NP];
+        split_pair<NP>(u.x - accW[cj][0], u.y - accW[cj][1], w01);
+        split_pair<NP>(u.z - accW[cj][2], u.w - accW[cj][3], w23);
+        const int idx = (16 * cj + ln) * LDT + r0 + 4 * q4;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) *reinterpret_cast<uint2*>(&sDT[k][idx]) = make_uint2(w01[k], w23[k]);
+      }
+      load_a(ops, rec_of(c + 1));
+      __syncthreads();
+      // S = e^{G_C} S + K~^T Delta
+#pragma unroll
+      for (int i = 0; i < CBW; ++i) {
+        float4 e4 = ops.e[i];
+        asm volatile("" : "+v"(e4.x), "+v"(e4.y), "+v"(e4.z), "+v"(e4.w));
+#pragma unroll
+        for (int cj = 0; cj < CJ; ++cj) {
+          Sacc[i][cj][0] *= e4.x; Sacc[i][cj][1] *= e4.y; Sacc[i][cj][2] *= e4.z; Sacc[i][cj][3] *= e4.w;
+        }
+      }
+      {
+        SplitN<NP> bD[2];
+        bD[0] = load_d(0);
+#pragma unroll
+        for (int g = 0; g < 2 * CJ; ++g) {
+          if (g + 1 < 2 * CJ) bD[(g + 1) & 1] = load_d(g + 1);
+          const int ks = g / CJ, cj = g % CJ;
+          if constexpr (CBW == 2) {
+            mfmaN2<NP>(ops.kt[0][ks], ops.kt[1][ks], bD[g & 1], Sacc[0][cj], Sacc[1][cj]);
+          } else {
+            Sacc[0][cj] = mfmaN<NP>(ops.kt[0][ks], bD[g & 1], Sacc[0][cj]);
+          }
+        }
+      }
+      load_b(ops, rec_of(c + 1));
+      publish_state();   // every wave is past its reads of S^T (first barrier)
+      __syncthreads();
+    }
+    if (io.S_out) {
+#pragma unroll
+      for (int i = 0; i < CBW; ++i)
+#pragma unroll
+        for (int cj = 0; cj < CJ; ++cj)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            io.S_out[sbase + static_cast<size_t>(16 * (rw + 4 * i) + 4 * q4 + j) * D + j0 + 16 * cj + ln] = Sacc[i][cj][j];
+    }
+  } else {
+    // ================= the output
+    using Ops = OutOps<D, NP>;
+    auto load_a = [&](Ops& o, const uint8_t* rec) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        o.q[ks] = load_planes<NP>(rec + REC.Qp, REC.tile_plane, frag_index(r0 + ln, 32 * ks + 8 * q4, D));
+    };
+    auto load_b = [&](Ops& o, const uint8_t* rec) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        o.a[ks] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, frag_index(r0 + ln, 32 * ks + 8 * q4, kChunk));
+    };
+    Ops ops;
+    if (c_first < c_end) {
+      load_a(ops, rec_of(c_first));
+      load_b(ops, rec_of(c_first));
+    }
+    __syncthreads();
+    for (int c = c_first; c < c_end; ++c) {
+      const int tau = (c - c_first) * kChunk;
+      const int len = min(kChunk, seq_len - tau);
+      f32x4 accQ[CJ];
+#pragma unroll
+      for (int cj = 0; cj < CJ; ++cj) accQ[cj] = zero4();
+      {
+        SplitN<NP> bS[2][2];
+        bS[0][0] = load_s(0);
+        bS[0][1] = load_s(1);
+#pragma unroll
+        for (int g = 0; g < KS * CJ; g += 2) {
+          const int cur = (g / 2) & 1;
+          if (g + 2 < KS * CJ) {
+            bS[cur ^ 1][0] = load_s(g + 2);
+            bS[cur ^ 1][1] = load_s(g + 3);
+          }
+          mfmaNx2<NP>(ops.q[g / CJ], bS[cur][0], accQ[g % CJ], ops.q[(g + 1) / CJ], bS[cur][1], accQ[(g + 1) % CJ]);
+        }
+      }
+      load_a(ops, rec_of(c + 1));
+      __syncthreads();
+      {
+        SplitN<NP> bD[2][2];
+        bD[0][0] = load_d(0);
+        bD[0][1] = load_d(1);
+#pragma unroll
+        for (int g = 0; g < 2 * CJ; g += 2) {
+          const int cur = (g / 2) & 1;
+          if (g + 2 < 2 * CJ) {
+            bD[cur ^ 1][0] = load_d(g + 2);
+            bD[cur ^ 1][1] = load_d(g + 3);
+          }
+          mfmaNx2<NP>(ops.a[g / CJ], bD[cur][0], accQ[g % CJ], ops.a[(g + 1) / CJ], bD[cur][1], accQ[(g + 1) % CJ]);
+        }
+      }
+      load_b(ops, rec_of(c + 1));
+      // the wave's output rows through its own LDS tile, then row-contiguous stores
+      {
+        float* so = sO[rw];
+#pragma unroll
+        for (int cj = 0; cj < CJ; ++cj)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) so[(4 * q4 + j) * LO + 16 * cj + ln] = accQ[cj][j];
+        asm volatile("" ::: "memory");
+        constexpr int LPR = 64 / 16;
+        constexpr int CPL = DVT / LPR;
+        const int orow = lane / LPR, oc0 = (lane % LPR) * CPL;
+        if (r0 + orow < len) {
+          const size_t base = (static_cast<size_t>(seq0 + tau + r0 + orow) * H + h) * D + j0 + oc0;
+          if constexpr (OUT_BF16) {
+#pragma unroll
+            for (int c4 = 0; c4 < CPL; c4 += 4) {
+              const float4 a = *reinterpret_cast<const float4*>(&so[orow * LO + oc0 + c4]);
+              const bf16x4 pk = {static_cast<__bf16>(a.x), static_cast<__bf16>(a.y), static_cast<__bf16>(a.z),
+                                 static_cast<__bf16>(a.w)};
+              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(io.o) + base + c4) = pk;
+            }
+          } else {
+#pragma unroll
+            for (int c4 = 0; c4 < CPL; c4 += 4)
+              *reinterpret_cast<float4*>(static_cast<float*>(io.o) + base + c4) =
+                  *reinterpret_cast<const float4*>(&so[orow * LO + oc0 + c4]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // Value-tile width: the widest tile that still gives every CU a workgroup.
 // (Narrower tiles do not buy a second resident workgroup per CU: the
 // prefetched operands keep a wave near the register-file limit.)
@@ -354,6 +638,16 @@ static hipError_t launch_scan_dt(const Params& p, const ChunkTable& t, const Pre
   const int n_sh = t.N * p.H;
   const int groups = (n_sh + 7) / 8;
   const dim3 grid(static_cast<unsigned>(groups * 8 * (D / DVT)));
+  if constexpr (D == 64 || D == 128) {   // the output on waves of its own
+    if (io_bf16) {
+      if (out_bf16) chunk_scan_split_kernel<D, DVT, 2, true><<<grid, 512, 0, st>>>(p, t, io, records, n_sh, gate);
+      else chunk_scan_split_kernel<D, DVT, 2, false><<<grid, 512, 0, st>>>(p, t, io, records, n_sh, gate);
+    } else {
+      if (out_bf16) chunk_scan_split_kernel<D, DVT, 3, true><<<grid, 512, 0, st>>>(p, t, io, records, n_sh, gate);
+      else chunk_scan_split_kernel<D, DVT, 3, false><<<grid, 512, 0, st>>>(p, t, io, records, n_sh, gate);
+    }
+    return hipGetLastError();
+  }
   if (io_bf16) {
     if (out_bf16) chunk_scan_kernel<D, DVT, 2, true><<<grid, 256, 0, st>>>(p, t, io, records, n_sh, gate);
     else chunk_scan_kernel<D, DVT, 2, false><<<grid, 256, 0, st>>>(p, t, io, records, n_sh, gate);

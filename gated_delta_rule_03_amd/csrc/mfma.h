@@ -57,6 +57,20 @@ __device__ __forceinline__ void mfmaN2(const SplitN<NP>& a1, const SplitN<NP>& a
     }
 }
 
+// Two independent products, c1 += a1 b1 and c2 += a2 b2, their passes
+// interleaved.
+template <int NP>
+__device__ __forceinline__ void mfmaNx2(const SplitN<NP>& a1, const SplitN<NP>& b1, f32x4& c1, const SplitN<NP>& a2,
+                                        const SplitN<NP>& b2, f32x4& c2) {
+#pragma unroll
+  for (int sum = NP - 1; sum >= 0; --sum)
+#pragma unroll
+    for (int i = 0; i <= sum; ++i) {
+      c1 = mfma(a1.v[i], b1.v[sum - i], c1);
+      c2 = mfma(a2.v[i], b2.v[sum - i], c2);
+    }
+}
+
 // The NP bf16 pieces of one fp32 value.
 template <int NP>
 __device__ __forceinline__ void split_pieces(float x, __bf16 (&pc)[NP]) {
