@@ -19,6 +19,9 @@
 // likewise for Aqk Delta and K~^T Delta.
 // Workgroups of the same (sequence, head) sit on the same XCD, so the
 // record's second reader finds it in that XCD's L2.
+//
+// At dk = dv in {64, 128} the launcher takes chunk_scan_split_kernel below
+// instead: the same steps with the output on four waves of their own.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "mfma.h"
