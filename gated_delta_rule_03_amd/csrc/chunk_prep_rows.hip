@@ -535,6 +535,7 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       __bf16* KT = reinterpret_cast<__bf16*>(rec + REC.KT);
       float* eGC = reinterpret_cast<float*>(rec + REC.eGC);
       float ebs[KSW][8];   // e^{G before block R}: kept for the query side
+      float fas[KSW][8];   // e^{-Bt_R} for an even block R, else 1: kept for the query side
 #pragma unroll
       for (int ks = 0; ks < KSW; ++ks) {
         const int c0 = CW * cq + 32 * ks + 8 * q4;
@@ -544,13 +545,35 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
         const float4 bt0 = *reinterpret_cast<const float4*>(&sBt[R][c0]);
         const float4 bt1 = *reinterpret_cast<const float4*>(&sBt[R][c0 + 4]);
         const float bt[8] = {bt0.x, bt0.y, bt0.z, bt0.w, bt1.x, bt1.y, bt1.z, bt1.w};
+        // The operands of A and Aqk take their decays from the middle of the
+        // row block pair (2p, 2p + 1), the end of block 2p: row r of block R
+        // carries e^{G_r - G_mid}, column s carries e^{G_mid - G_s}.  For an
+        // odd block that is e^{P}, e^{-P} (P the in-block sum); for an even
+        // block e^{P - Bt_R}, e^{Bt_R - P} (Bt_R its total).  Either way an
+        // exponent spans one block, as for in-block references, and the
+        // blocks of one pair need no factor between them.
+        float fb[8];
+        float (&fa)[8] = fas[ks];
+        if ((R & 1) == 0) {
+          const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[R][c0]);
+          const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[R][c0 + 4]);
+          const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            fb[i] = ev[i];
+            fa[i] = rcp_fast(ev[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) fa[i] = fb[i] = 1.f;
+        }
         float kc[8], kt[8], pk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int j = 8 * ks + i;
           const float kk = kv[j] * ik;
-          pk[i] = kk * eP[j];                                   // row operand of the A sub-blocks
-          kc[i] = kk * rcp_fast(eP[j]);                         // column operand k e^{-P}
+          pk[i] = kk * (eP[j] * fa[i]);                         // row operand of the A sub-blocks
+          kc[i] = kk * (fb[i] * rcp_fast(eP[j]));               // column operand (factor in [e^{Bt_R}, 1])
           kt[i] = kk * exp_fast((bt[i] - P[j]) + after[i]);     // K~ = k e^{G_C - G_r}
         }
         pin(pk);
@@ -588,13 +611,14 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       for (int ks = 0; ks < KSW; ++ks) {
         const int c0 = CW * cq + 32 * ks + 8 * q4;
         const float (&eb)[8] = ebs[ks];
+        const float (&fa)[8] = fas[ks];
         float qo[8], pq[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int j = 8 * ks + i;
           const float qq = qv[j] * iq;
           qo[i] = qq * (eP[j] * eb[i]);
-          pq[i] = qq * eP[j];
+          pq[i] = qq * (eP[j] * fa[i]);
         }
         pin(pq);
 #pragma unroll
@@ -622,9 +646,11 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       for (int I = 0; I < 4; ++I) keepA[I] = keepQ[I] = zero4();
       float* const dA = (CQ > 2 && cq >= 2) ? sA2 : sA;
       float* const dQ = (CQ > 2 && cq >= 2) ? sAqk2 : sAqk;
-      // kept sums are indexed by d = R - I, which is static in the unrolled
-      // loops (an index by I would be a dynamic register index)
-      auto finish = [&](int d, int I, const f32x4& accA, const f32x4& accQ) {
+      // Kept sums are indexed by a static slot: 0 the diagonal block (I = R),
+      // 1 the other block of the pair (I = R - 1, R odd), 2 and 3 the blocks
+      // of the first pair seen from the second (I = 1, 0; R >= 2).  (An index
+      // by I would be a dynamic register index.)
+      auto finish = [&](int slot, int I, const f32x4& accA, const f32x4& accQ) {
         if (CQ == 1 || (cq & 1)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -633,13 +659,20 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
             dQ[row * LA + col] = accQ[j];
           }
         } else {
-          keepA[d] = accA;
-          keepQ[d] = accQ;
+          keepA[slot] = accA;
+          keepQ[slot] = accQ;
         }
       };
-      // the diagonal block: the row operands as they are (no decay between)
+      auto col_operand = [&](int I, int c0) {   // the column operand of block I
+        SplitN<NP> bk;
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+          bk.v[k] = *reinterpret_cast<const bf16x8*>(&sKc[k * 64 * KCS + (16 * I + ln) * KCS + c0]);
+        return bk;
+      };
+      // the blocks of this wave's own pair: one split of the row operands
       {
-        f32x4 accA = zero4(), accQ = zero4();
+        SplitN<NP> sa[KSW], sq[KSW];
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
           float ra[8], rq[8];
@@ -648,39 +681,56 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
             ra[i] = kP[8 * ks + i];
             rq[i] = qP[8 * ks + i];
           }
-          mfmaN2<NP>(splitN<NP>(ra), splitN<NP>(rq), kcp[ks], accA, accQ);
+          sa[ks] = splitN<NP>(ra);
+          sq[ks] = splitN<NP>(rq);
         }
-        finish(0, R, accA, accQ);
+        {
+          f32x4 accA = zero4(), accQ = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks) mfmaN2<NP>(sa[ks], sq[ks], kcp[ks], accA, accQ);
+          finish(0, R, accA, accQ);
+        }
+        if (R & 1) {
+          f32x4 accA = zero4(), accQ = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks)
+            mfmaN2<NP>(sa[ks], sq[ks], col_operand(R - 1, CW * cq + 32 * ks + 8 * q4), accA, accQ);
+          finish(1, R - 1, accA, accQ);
+        }
       }
-      // blocks I = R - 1, ..., 0: E = e^{sum of the block totals of blocks I .. R-1}
-      float E[CPL];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) E[j] = 1.f;
-#pragma unroll
-      for (int d = 1; d < 4; ++d) {
-        const int I = R - d;
-        if (I < 0) continue;
-        f32x4 accA = zero4(), accQ = zero4();
+      // the first pair's blocks from the second: the row operands times
+      // e^{Bt_2} and then e^{Bt_1}, the decay between the two pairs' middles.
+      // One factor at a time: e^{Bt_1 + Bt_2} alone underflows for strong
+      // decays where the row operand times it does not (for block 2 the
+      // first factor brings the operand back to e^{P} <= 1).
+      if (R >= 2) {
+        SplitN<NP> sa[KSW], sq[KSW];
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
           const int c0 = CW * cq + 32 * ks + 8 * q4;
-          const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[I][c0]);
-          const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[I][c0 + 4]);
-          const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-          SplitN<NP> bk;
-#pragma unroll
-          for (int k = 0; k < NP; ++k)
-            bk.v[k] = *reinterpret_cast<const bf16x8*>(&sKc[k * 64 * KCS + (16 * I + ln) * KCS + c0]);
+          const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[1][c0]);
+          const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[1][c0 + 4]);
+          const float4 f0 = *reinterpret_cast<const float4*>(&sEBt[2][c0]);
+          const float4 f1 = *reinterpret_cast<const float4*>(&sEBt[2][c0 + 4]);
+          const float x1[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+          const float x2[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
           float ra[8], rq[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            E[8 * ks + i] *= ev[i];
-            ra[i] = kP[8 * ks + i] * E[8 * ks + i];
-            rq[i] = qP[8 * ks + i] * E[8 * ks + i];
+            ra[i] = (kP[8 * ks + i] * x2[i]) * x1[i];
+            rq[i] = (qP[8 * ks + i] * x2[i]) * x1[i];
           }
-          mfmaN2<NP>(splitN<NP>(ra), splitN<NP>(rq), bk, accA, accQ);
+          sa[ks] = splitN<NP>(ra);
+          sq[ks] = splitN<NP>(rq);
         }
-        finish(d, I, accA, accQ);
+#pragma unroll
+        for (int I = 1; I >= 0; --I) {
+          f32x4 accA = zero4(), accQ = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks)
+            mfmaN2<NP>(sa[ks], sq[ks], col_operand(I, CW * cq + 32 * ks + 8 * q4), accA, accQ);
+          finish(3 - I, I, accA, accQ);
+        }
       }
       if constexpr (CQ > 1) {
         __syncthreads();
@@ -688,28 +738,30 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
           // every read goes out before the first add: one LDS round trip
           // for the whole update, not one per element
           float oa[4][4], oq[4][4], bt[4];
+          // each slot's block, and whether this wave has one there (unused
+          // slots read block 0 and write nothing)
+          const int slot_I[4] = {R, (R & 1) ? R - 1 : 0, R >= 2 ? 1 : 0, 0};
+          const bool slot_ok[4] = {true, (R & 1) != 0, R >= 2, R >= 2};
 #pragma unroll
           for (int j = 0; j < 4; ++j) bt[j] = sBeta[16 * R + 4 * q4 + j];
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int I = max(R - d, 0);   // rows past the diagonal's left end are read but not written
+          for (int sl = 0; sl < 4; ++sl) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
-              oa[d][j] = dA[row * LA + col];
-              oq[d][j] = dQ[row * LA + col];
+              const int row = 16 * R + 4 * q4 + j, col = 16 * slot_I[sl] + ln;
+              oa[sl][j] = dA[row * LA + col];
+              oq[sl][j] = dQ[row * LA + col];
             }
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int I = R - d;
-            if (I < 0) continue;
+          for (int sl = 0; sl < 4; ++sl) {
+            if (!slot_ok[sl]) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int row = 16 * R + 4 * q4 + j, col = 16 * I + ln;
-              dA[row * LA + col] = bt[j] * keepA[d][j] + oa[d][j];
-              dQ[row * LA + col] = keepQ[d][j] + oq[d][j];
+              const int row = 16 * R + 4 * q4 + j, col = 16 * slot_I[sl] + ln;
+              dA[row * LA + col] = bt[j] * keepA[sl][j] + oa[sl][j];
+              dQ[row * LA + col] = keepQ[sl][j] + oq[sl][j];
             }
           }
         }
@@ -794,26 +846,30 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
         for (int i = 0; i < 16; ++i) sT[Rb][i * LT + j] = tcol[i];
       }
-      // beta K+ = beta (k e^{P}) e^{G before the block}, over the k e^{-P} pieces
+      // beta K+ = beta k e^{G_r}: the row operand times the decay to the
+      // middle of its block pair (e^{Bt_0}, or e^{Bt_2} e^{Bt_1} e^{Bt_0}),
+      // one factor at a time from the last block back (the product of the
+      // factors alone can underflow where the result does not), over the
+      // column operand pieces
 #pragma unroll
       for (int ks = 0; ks < KSW; ++ks) {
         const int c0 = CW * cq + 32 * ks + 8 * q4;
-        float eb[8];
+        const float beta = sBeta[r];
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) eb[i] = 1.f;
+        for (int i = 0; i < 8; ++i) v[i] = beta * kP[8 * ks + i];
 #pragma unroll
-        for (int J = 0; J < 3; ++J) {
-          if (J < R) {
+        for (int J = 2; J >= 0; --J) {
+          if (J == 0 || R >= 2) {
             const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[J][c0]);
             const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[J][c0 + 4]);
             const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) eb[i] *= ev[i];
+            for (int i = 0; i < 8; ++i) v[i] *= ev[i];
           }
         }
-        const float beta = sBeta[r];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sX[(c0 + i) * LX + r] = (beta * kP[8 * ks + i]) * eb[i];
+        for (int i = 0; i < 8; ++i) sX[(c0 + i) * LX + r] = v[i];
       }
     }
     __syncthreads();
