@@ -149,6 +149,18 @@ def test_slow_decay_keeps_initial_state_visible(kda):
     assert np.max(np.abs(o.double().cpu().numpy() - o0)) > 0.1   # the state matters here
 
 
+def test_strong_decay(kda):
+    """A_log = 1.2 gives g ~ -2.7 per token: 16-token block totals near -43,
+    so the decay across two blocks (e^-86) sits at the bottom of fp32's range
+    and across three blocks (e^-130) below it.  Decay factors formed on their
+    own underflow here where the operands they scale do not; the result must
+    still match."""
+    p = make_problem(331, [256, 130], 2, 128, 128, BF16, state_seqs=[0, 1], state_std=0.5, conv_state=True)
+    p.A_log = np.full_like(p.A_log, 1.2)
+    o, S, cs = run_varlen(kda, p)
+    assert_parity(p, o, S, cs)
+
+
 def test_test_hook_flags(kda):
     # q, k, v taken as given, g and beta given directly: the bare recurrence
     p = make_problem(340, [90], 2, 64, 64, FP32, state_seqs=[0])
