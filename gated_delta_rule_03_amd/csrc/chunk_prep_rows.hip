@@ -785,13 +785,17 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       // by waves 1 .. NW - 1 only: wave 0 forms the diagonal-block inverses
       // below, the longest task of this phase.  A fixed trip count, not a
       // loop (a loop here makes the compiler wait for every outstanding
-      // load first).
+      // load first).  The 8-column groups of token rows 0..31 past column
+      // 31 are zero and are not written (the scan does not read them): 384
+      // groups, 128 of rows 0..31 then 256 of rows 32..63.
       constexpr int NAQ = NT - kWave;
+      constexpr int NGRP = 32 * 4 + 32 * 8;
 #pragma unroll
-      for (int it = 0; it < (64 * 8 + NAQ - 1) / NAQ; ++it) {
+      for (int it = 0; it < (NGRP + NAQ - 1) / NAQ; ++it) {
         const int e = L.tid - kWave + it * NAQ;
-        if (w == 0 || e >= 64 * 8) break;
-        const int rw = e >> 3, i0 = 8 * (e & 7);
+        if (w == 0 || e >= NGRP) break;
+        const int rw = e < 128 ? e >> 2 : 32 + ((e - 128) >> 3);
+        const int i0 = e < 128 ? 8 * (e & 3) : 8 * ((e - 128) & 7);
         float4 q0 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0]);
         float4 q1 = *reinterpret_cast<const float4*>(&sAqk[rw * LA + i0 + 4]);
         if constexpr (CQ > 2) {

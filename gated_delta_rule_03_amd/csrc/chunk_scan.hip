@@ -544,10 +544,13 @@ __global__ __launch_bounds__(512) void chunk_scan_split_kernel(Params p, ChunkTa
       for (int ks = 0; ks < KS; ++ks)
         o.q[ks] = load_planes<NP>(rec + REC.Qp, REC.tile_plane, frag_index(r0 + ln, 32 * ks + 8 * q4, D));
     };
+    // Aqk is zero above the diagonal: token rows 0..31 have nothing past
+    // column 31, and the row prep does not write those fragments
+    const bool aqk_full = rw >= 2;
     auto load_b = [&](Ops& o, const uint8_t* rec) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        o.a[ks] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, frag_index(r0 + ln, 32 * ks + 8 * q4, kChunk));
+      o.a[0] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, frag_index(r0 + ln, 8 * q4, kChunk));
+      if (aqk_full) o.a[1] = load_planes<NP>(rec + REC.Aqk, REC.aqk_plane, frag_index(r0 + ln, 32 + 8 * q4, kChunk));
+      else o.a[1] = zero_split<NP>();
     };
     Ops ops;
     if (c_first < c_end) {
@@ -588,6 +591,7 @@ __global__ __launch_bounds__(512) void chunk_scan_split_kernel(Params p, ChunkTa
             bD[cur ^ 1][0] = load_d(g + 2);
             bD[cur ^ 1][1] = load_d(g + 3);
           }
+          if (CJ >= 2 && g >= CJ && !aqk_full) continue;   // the zero k step
           mfmaNx2<NP>(ops.a[g / CJ], bD[cur][0], accQ[g % CJ], ops.a[(g + 1) / CJ], bD[cur][1], accQ[(g + 1) % CJ]);
         }
       }
