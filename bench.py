@@ -44,7 +44,9 @@ FLOPS_PER_CHUNK_HEAD = {
     "chunk_prep": CHUNK * (2 * CHUNK * (3 * D + D) + 2 * CHUNK * CHUNK / 3.0),
     "chunk_scan": CHUNK * (6.0 * D * D + 2.0 * CHUNK * D),
 }
-RECORD_BYTES = 4 * 64 * D * 4 + 64 * 64 * 4 + D * 4          # one per chunk-head (fp32)
+# one record per chunk-head, fp32-equivalent: W, Q+, K~^T, U^T (64 x d each),
+# the lower triangle of Aqk with its diagonal, e^{G_C}
+RECORD_BYTES = 4 * 64 * D * 4 + (64 * 65 // 2) * 4 + D * 4
 BYTES_PER_CHUNK_HEAD = {
     "chunk_prep": CHUNK * (4 * 2 * D + 2) + RECORD_BYTES,
     "chunk_scan": RECORD_BYTES + CHUNK * 2 * D,
