@@ -158,7 +158,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
   constexpr int CPL = 8 * KSW;          // channels per lane
   constexpr int NP = kRowsNP;
   constexpr Record REC = record_layout(D, NP);
-  constexpr int RAWS = 3 * D + 8;       // staging row stride (bf16)
+  constexpr int RAWS = 2 * D + 8;       // staging row stride of q | k (bf16)
+  constexpr int RAWV = D + 8;           // staging row stride of v (bf16)
   constexpr int KCS = D + 8;            // row stride of the k e^{-P} pieces (bf16)
   constexpr int LX = D == 64 ? kChunk + 8 : kChunk + 4;   // row stride of X^T (fp32)
   constexpr int LA = kChunk + 4;        // row stride of A, Aqk (fp32)
@@ -184,6 +185,9 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
   __shared__ __align__(16) float sA2[CQ > 2 ? 64 * LA : 4];
   __shared__ __align__(16) float sAqk2[CQ > 2 ? 64 * LA : 4];
   __shared__ __align__(16) float sT[4][16 * LT];         // (I + A_RR)^-1, fp32
+  // v's staging rows, apart from q | k: v is convolved in phase 4b, by the
+  // waves that have no part in forming T there
+  __shared__ __align__(16) __bf16 sRawV[kRawRows * RAWV];
   __shared__ __align__(16) uint2 sWb[3][D];              // conv taps of this head (q, k, v), 4 bf16 each
   __shared__ __align__(16) float sDtb[D];
   __shared__ __align__(16) float sBt[4][D];              // in-block totals of g
@@ -310,11 +314,14 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
   auto stage = [&](const LaneCoords& L) {
     const int st_col = L.tid % Raw::kCols, st_row0 = L.tid / Raw::kCols;
     const bool stager = L.tid < Raw::kSR * Raw::kCols;
+    const bool st_v = st_col >= 2 * D / 8;   // a piece of v
+    __bf16* const st_dst = st_v ? sRawV + 8 * (st_col - 2 * D / 8) : sRaw + 8 * st_col;
+    const int st_stride = st_v ? RAWV : RAWS;
 #pragma unroll
     for (int j = 0; j < Raw::kPer; ++j) {
       const int sr = st_row0 + Raw::kSR * j;
       if (stager && sr < kRawRows)
-        *reinterpret_cast<uint4*>(&sRaw[sr * RAWS + 8 * st_col]) =
+        *reinterpret_cast<uint4*>(st_dst + sr * st_stride) =
             (nxt.zero >> j) & 1u ? make_uint4(0u, 0u, 0u, 0u) : nxt.x[j];
     }
     uint32_t bw = nxt.b;
@@ -364,10 +371,11 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     const uint2* tapw = &sWb[0][0] + inv;
     const float* dtb = sDtb + inv;
 
-    // ---- 1. conv + SiLU of this lane's row (q, k, v), gate, beta
-    float qv[CPL], kv[CPL], vv[CPL], gv[CPL];
+    // ---- 1. conv + SiLU of this lane's row (q, k; v follows in phase 4b),
+    //      gate, beta
+    float qv[CPL], kv[CPL], gv[CPL];
 #pragma unroll
-    for (int tens = 0; tens < 3; ++tens) {
+    for (int tens = 0; tens < 2; ++tens) {
 #pragma unroll
       for (int ks = 0; ks < KSW; ++ks) {
         const int c0 = CW * cq + 32 * ks + 8 * q4;
@@ -407,8 +415,7 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           if (tens == 0) qv[8 * ks + i] = uo[i];
-          else if (tens == 1) kv[8 * ks + i] = uo[i];
-          else vv[8 * ks + i] = uo[i];
+          else kv[8 * ks + i] = uo[i];
         }
         compiler_fence();
       }
@@ -433,7 +440,6 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     }
     pin(qv);
     pin(kv);
-    pin(vv);
     pin(gv);
     float beta = 0.f;
     if (live) {
@@ -522,15 +528,6 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
       }
     };
     {
-      // beta V^T straight to its rows of X^T, which lie past the k e^{-P}
-      // pieces in the shared region (beta K+ follows in phase 4)
-#pragma unroll
-      for (int ks = 0; ks < KSW; ++ks) {
-        const int c0 = CW * cq + 32 * ks + 8 * q4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sX[(D + c0 + i) * LX + r] = beta * vv[8 * ks + i];
-      }
-      compiler_fence();
       // key side: k e^{P}, k e^{-P} pieces, K~^T, e^{G_C}
       __bf16* KT = reinterpret_cast<__bf16*>(rec + REC.KT);
       float* eGC = reinterpret_cast<float*>(rec + REC.eGC);
@@ -942,6 +939,47 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
         x = mfma_f32(t4.w, y[3], x);
         xb[Rs] = x;
         put(Rs, x);
+      }
+    } else {
+      // conv + SiLU of v and beta V^T to its rows of X^T (past the k e^{-P}
+      // pieces, untouched since phase 2): lane l of wave w takes token row l
+      // and a range of 8-channel groups, reads as in phase 1.  At dk = 128
+      // waves 4..7 take 3, 4, 4, 5 of the 16 groups: they share their SIMDs
+      // with waves 0..3, whose parts of T shrink from column block 0 to 3
+      // (measured at 4 groups each, wave 4 took 4.3K cycles and wave 7 2.9K).
+      // Rows past the chunk's end have beta 0.
+      constexpr int NG = D / 8;
+      const int k4 = w - 4;
+      const int gs = NG == 16 ? (k4 == 0 ? 0 : (k4 == 1 ? 3 : (k4 == 2 ? 7 : 11))) : k4 * (NG / 4);
+      const int ge = NG == 16 ? (k4 == 0 ? 3 : (k4 == 1 ? 7 : (k4 == 2 ? 11 : 16))) : (k4 + 1) * (NG / 4);
+      const int row = lane;
+      const float bv = sBeta[row];
+#pragma unroll
+      for (int g8 = 0; g8 < (NG == 16 ? 5 : NG / 4); ++g8) {
+        if (gs + g8 >= ge) break;
+        const int c0 = 8 * (gs + g8);
+        uint4 xm[4], wv[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xm[m] = *reinterpret_cast<const uint4*>(&sRawV[(row + m) * RAWV + c0]);
+#pragma unroll
+        for (int jw = 0; jw < 4; ++jw) wv[jw] = *reinterpret_cast<const uint4*>(&tapw[2 * D + c0 + 2 * jw]);
+        __builtin_amdgcn_sched_barrier(0);
+        float uo[8];
+#pragma unroll
+        for (int jw = 0; jw < 4; ++jw) {
+          const uint4 wt = wv[jw];
+          const uint32_t x0 = word(xm[0], jw), x1 = word(xm[1], jw), x2 = word(xm[2], jw), x3 = word(xm[3], jw);
+          const float ye = dot2_bf16(__builtin_amdgcn_perm(x1, x0, 0x05040100u), wt.x,
+                                     dot2_bf16(__builtin_amdgcn_perm(x3, x2, 0x05040100u), wt.y, 0.f));
+          const float yo = dot2_bf16(__builtin_amdgcn_perm(x1, x0, 0x07060302u), wt.z,
+                                     dot2_bf16(__builtin_amdgcn_perm(x3, x2, 0x07060302u), wt.w, 0.f));
+          const float se = siluf_(ye), so = siluf_(yo);
+          uo[2 * jw] = raw_conv ? __uint_as_float(x3 << 16) : se;
+          uo[2 * jw + 1] = raw_conv ? __uint_as_float(x3 & 0xffff0000u) : so;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sX[(D + c0 + i) * LX + row] = bv * uo[i];
+        compiler_fence();
       }
     }
     __syncthreads();
