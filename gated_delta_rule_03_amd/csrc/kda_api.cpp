@@ -17,7 +17,9 @@ constexpr size_t kAlign = 256;
 constexpr uint32_t kKnownFlags = KDA_FLAG_SKIP_CONV | KDA_FLAG_SKIP_L2NORM | KDA_FLAG_RAW_GATE |
                                  KDA_FLAG_RAW_BETA | KDA_FLAG_BETA_X2;
 // Sub-block decay factors e^{-P} of 16 tokens stay finite in fp32 when every
-// log decay is >= -5.4 (16 * 5.4 = 86.4 < ln FLT_MAX).
+// log decay is >= -5.4 (16 * 5.4 = 86.4 < ln FLT_MAX).  A lower bound below
+// it (down to -inf, no clamp) routes a prefill to the recurrent form, whose
+// state is only ever multiplied by e^g <= 1.
 constexpr float kChunkedGateFloor = -5.4f;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -36,13 +38,16 @@ kda_status_t check_config(const kda_config_t* cfg, bool chunked) {
   if (chunked && cfg->chunk_size != kda::kChunk) return KDA_ERR_UNSUPPORTED;
   if (std::isnan(cfg->gate_lower_bound) || std::isnan(cfg->l2norm_eps) || std::isnan(cfg->scale))
     return KDA_ERR_INVALID_ARGUMENT;
-  if (chunked && !(cfg->flags & KDA_FLAG_RAW_GATE) && !(cfg->gate_lower_bound >= kChunkedGateFloor))
-    return KDA_ERR_UNSUPPORTED;
   if (!cfg->A_log || !cfg->dt_bias) return KDA_ERR_INVALID_ARGUMENT;
   if (!(cfg->flags & KDA_FLAG_SKIP_CONV) && (!cfg->conv_w_q || !cfg->conv_w_k || !cfg->conv_w_v))
     return KDA_ERR_INVALID_ARGUMENT;
   return KDA_OK;
 }
+
+// The prefill form a configuration takes: chunked unless the gate's lower
+// bound is below the floor.  With KDA_FLAG_RAW_GATE the bound is not applied
+// to g, but it still selects the form.
+bool recurrent_form(const kda_config_t* cfg) { return !(cfg->gate_lower_bound >= kChunkedGateFloor); }
 
 Params make_params(const kda_config_t* cfg) {
   Params p;
@@ -67,7 +72,10 @@ struct Layout {
   size_t cu, chunk0, chunk_seq, desc, records, total;
 };
 
-Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D, int NP) {
+// records: the chunked form's per-(chunk, head) records, or the recurrent
+// form's per-(head, token) records.
+Layout make_layout(const kda_config_t* cfg, int64_t N, int64_t max_chunks, int64_t total_T) {
+  const int64_t H = cfg->num_heads, D = cfg->head_k_dim;
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
@@ -75,7 +83,10 @@ Layout make_layout(int64_t N, int64_t max_chunks, int64_t H, int64_t D, int NP) 
   L.chunk0 = take((N + 2) * sizeof(int32_t));
   L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
   L.desc = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int4));
-  L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D), NP).bytes);
+  if (recurrent_form(cfg))
+    L.records = take(static_cast<size_t>(H) * total_T * kda::recurrent_record_bytes(static_cast<int>(D)));
+  else
+    L.records = take(static_cast<size_t>(max_chunks) * H * kda::record_layout(static_cast<int>(D), pieces(cfg)).bytes);
   L.total = off;
   return L;
 }
@@ -106,7 +117,7 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
                          const int32_t* cu_in, int32_t T_uniform, const PrefillIO& io, void* workspace,
                          hipStream_t st) {
   const Params p = make_params(cfg);
-  const Layout L = make_layout(N, max_chunks, p.H, p.D, pieces(cfg));
+  const Layout L = make_layout(cfg, N, max_chunks, total_T);
   char* ws = static_cast<char*>(workspace);
   int32_t* cu_ws = reinterpret_cast<int32_t*>(ws + L.cu);
   int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
@@ -122,17 +133,28 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
     return kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, desc, mc, p.H, p.D, st);
   });
   if (s != KDA_OK) return s;
-  if (total_T > 0 && mc > 0) {
-    s = stage(cfg, KDA_STAGE_CHUNK_PREP, st, [&] { return kda::launch_chunk_prep(p, t, io, records, mc, io_bf16, st); });
+  if (recurrent_form(cfg)) {
+    float* recs = reinterpret_cast<float*>(records);
+    s = stage(cfg, KDA_STAGE_CHUNK_PREP, st,
+              [&] { return kda::launch_token_prep(p, t, io, recs, total_T, mc, io_bf16, st); });
+    if (s != KDA_OK) return s;
+    s = stage(cfg, KDA_STAGE_CHUNK_SCAN, st,
+              [&] { return kda::launch_recurrent_scan(p, t, io, recs, total_T, out_bf16, st); });
+    if (s != KDA_OK) return s;
+  } else {
+    if (total_T > 0 && mc > 0) {
+      s = stage(cfg, KDA_STAGE_CHUNK_PREP, st,
+                [&] { return kda::launch_chunk_prep(p, t, io, records, mc, io_bf16, st); });
+      if (s != KDA_OK) return s;
+    }
+    // equal lengths: the host knows the batch shape; packed sequences of any
+    // lengths: the value-tile width is chosen on the device
+    const bool device_choice = cu_in != nullptr;
+    s = stage(cfg, KDA_STAGE_CHUNK_SCAN, st, [&] {
+      return kda::launch_chunk_scan(p, t, io, records, io_bf16, out_bf16, device_choice, st);
+    });
     if (s != KDA_OK) return s;
   }
-  // equal lengths: the host knows the batch shape; packed sequences of any
-  // lengths: the value-tile width is chosen on the device
-  const bool device_choice = cu_in != nullptr;
-  s = stage(cfg, KDA_STAGE_CHUNK_SCAN, st, [&] {
-    return kda::launch_chunk_scan(p, t, io, records, io_bf16, out_bf16, device_choice, st);
-  });
-  if (s != KDA_OK) return s;
   if (io.conv_out) {
     s = stage(cfg, KDA_STAGE_CONV_STATE, st, [&] { return kda::launch_conv_state_out(p, t, io, io_bf16, st); });
     if (s != KDA_OK) return s;
@@ -161,12 +183,12 @@ size_t kda_prefill_workspace_bytes(const kda_config_t* cfg, int32_t B, int32_t T
   if (check_config(cfg, true) != KDA_OK || B < 0 || T < 0) return 0;
   const int64_t mc = chunks_uniform(B, T);
   if (static_cast<int64_t>(B) * T > INT32_MAX || mc > INT32_MAX) return 0;
-  return make_layout(B, mc, cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
+  return make_layout(cfg, B, mc, static_cast<int64_t>(B) * T).total;
 }
 
 size_t kda_varlen_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t total_T) {
   if (check_config(cfg, true) != KDA_OK || N < 0 || total_T < 0) return 0;
-  return make_layout(N, chunks_varlen(N, total_T), cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
+  return make_layout(cfg, N, chunks_varlen(N, total_T), total_T).total;
 }
 
 kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const void* q, const void* k, const void* v,
@@ -180,7 +202,7 @@ kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const vo
   if (B == 0) return KDA_OK;
   if (T > 0 && (!q || !k || !v || !alpha || !b || !o)) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t mc = chunks_uniform(B, T);
-  const size_t need = make_layout(B, mc, cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
+  const size_t need = make_layout(cfg, B, mc, static_cast<int64_t>(B) * T).total;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};
@@ -200,7 +222,7 @@ kda_status_t kda_varlen_prefill(const kda_config_t* cfg, int32_t N, int32_t tota
   if (total_T > 0 && (!q || !k || !v || !alpha || !b || !o)) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t mc = chunks_varlen(N, total_T);
   if (mc > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  const size_t need = make_layout(N, mc, cfg->num_heads, cfg->head_k_dim, pieces(cfg)).total;
+  const size_t need = make_layout(cfg, N, mc, total_T).total;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};

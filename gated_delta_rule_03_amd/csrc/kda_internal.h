@@ -123,6 +123,16 @@ hipError_t launch_chunk_scan(const Params& p, const ChunkTable& t, const Prefill
 hipError_t launch_conv_state_out(const Params& p, const ChunkTable& t, const PrefillIO& io, bool io_bf16,
                                  hipStream_t st);
 
+// The recurrent-form prefill (gates below the chunked form's floor): a token
+// preprocess writing one fp32 record of recurrent_record_bytes(D) per (head,
+// packed token) into `recs` ([H][total_T] records), and the sequential scan
+// over those records, one workgroup per (sequence, head, value tile).
+size_t recurrent_record_bytes(int D);
+hipError_t launch_token_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, float* recs,
+                             int64_t total_T, int max_chunks, bool io_bf16, hipStream_t st);
+hipError_t launch_recurrent_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const float* recs,
+                                 int64_t total_T, bool out_bf16, hipStream_t st);
+
 struct DecodeIO {
   const void* q;
   const void* k;

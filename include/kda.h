@@ -74,8 +74,10 @@ typedef enum kda_dtype {
 /* Stages of a call, for the optional per-stage timing hook below. */
 typedef enum kda_stage {
     KDA_STAGE_CHUNK_TABLE = 0,  /* packed-batch chunk table (device cu_seqlens scan)          */
-    KDA_STAGE_CHUNK_PREP = 1,   /* preprocess + intra-chunk solve, parallel over chunks       */
-    KDA_STAGE_CHUNK_SCAN = 2,   /* inter-chunk state propagation + chunk output, sequential   */
+    KDA_STAGE_CHUNK_PREP = 1,   /* preprocess + intra-chunk solve, parallel over chunks
+                                   (recurrent form: the per-token preprocess)                 */
+    KDA_STAGE_CHUNK_SCAN = 2,   /* inter-chunk state propagation + chunk output, sequential
+                                   (recurrent form: the token-by-token state scan)            */
     KDA_STAGE_CONV_STATE = 3,   /* conv history out                                           */
     KDA_STAGE_DECODE = 4,       /* the decode step kernel                                     */
     KDA_NUM_STAGES = 5
@@ -88,9 +90,14 @@ typedef struct kda_config {
     int32_t io_dtype;         /* kda_dtype_t of q, k, v, alpha, b, conv weights, conv history */
     int32_t out_dtype;        /* kda_dtype_t of o                                       */
     float scale;              /* multiplies the normalised q; 1.0 as on the pages       */
-    float gate_lower_bound;   /* -5.0 (safe gate).  The chunked prefill needs >= -5.4
-                                 (KDA_ERR_UNSUPPORTED otherwise); the decode step takes
-                                 any value, -INFINITY disabling the clamp              */
+    float gate_lower_bound;   /* -5.0 (safe gate); any value, -INFINITY disabling the
+                                 clamp.  It also picks the prefill's form: >= -5.4 the
+                                 chunked form; below, the token-by-token recurrence
+                                 (exact for any gate, ~2.3x slower; its workspace holds
+                                 (4*dk + 4) fp32 per head and token).  With
+                                 KDA_FLAG_RAW_GATE the bound is not applied to g but
+                                 still picks the form: the chunked one needs every
+                                 g >= -5.4                                            */
     float l2norm_eps;         /* q / sqrt(|q|^2 + eps); 1e-6                            */
     int32_t chunk_size;       /* 64                                                     */
     uint32_t flags;           /* KDA_FLAG_* test hooks, normally 0                      */

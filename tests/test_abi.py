@@ -102,7 +102,7 @@ def test_null_required_pointer(kda, missing):
 
 @pytest.mark.parametrize("field,val", [("head_k_dim", 48), ("head_v_dim", 32), ("io_dtype", 7),
                                        ("out_dtype", 3), ("chunk_size", 32), ("flags", 1 << 9),
-                                       ("gate_lower_bound", float("-inf")), ("num_heads", 70000)])
+                                       ("num_heads", 70000)])
 def test_unsupported_configuration(kda, field, val):
     cfg, _ = make_cfg(kda, **{field: val})
     st, bufs = call_prefill(kda, cfg)
@@ -141,6 +141,28 @@ def test_workspace_query_grows_with_size(kda):
     c = lib.kda_varlen_workspace_bytes(ctypes.byref(cfg), 2, 128)
     assert 0 < a < b <= c
     assert a % 256 == 0
+
+
+def test_workspace_of_the_recurrent_form(kda):
+    """A gate lower bound below the chunked form's floor (-5.4) selects the
+    recurrent form, whose workspace holds one fp32 record of 4 dk + 4 floats
+    per (head, token) besides the chunk table."""
+    lib = kda.library()
+    H, D, B, T = 4, 64, 2, 300
+    rec = H * B * T * (4 * D + 4) * 4
+    for lb in (float("-inf"), -5.41, -30.0):
+        cfg, _ = make_cfg(kda, H=H, dk=D, dv=D, gate_lower_bound=lb)
+        a = lib.kda_prefill_workspace_bytes(ctypes.byref(cfg), B, T)
+        v = lib.kda_varlen_workspace_bytes(ctypes.byref(cfg), B, B * T)
+        assert rec < a < rec + 64 * 1024 and a % 256 == 0
+        assert rec < v < rec + 64 * 1024
+        st, bufs = call_prefill(kda, cfg, ws_bytes=100)   # validated as usual before any launch
+        assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL and all(b.untouched() for b in bufs.values())
+    # at the floor itself the chunked form's per-(chunk, head) records are sized
+    cfg, _ = make_cfg(kda, H=H, dk=D, dv=D, gate_lower_bound=-5.4)
+    chunked = lib.kda_prefill_workspace_bytes(ctypes.byref(cfg), B, T)
+    assert chunked > 0 and chunked != lib.kda_prefill_workspace_bytes(
+        ctypes.byref(make_cfg(kda, H=H, dk=D, dv=D, gate_lower_bound=-6.0)[0]), B, T)
 
 
 def test_empty_batches_are_noops(kda):
