@@ -32,6 +32,7 @@ FLAG_BETA_X2 = 16
 
 DEFAULT_LOWER_BOUND = -5.0   # safe gate (Ling-3.0-flash-VL page, section "KDA 层的安全门")
 DEFAULT_EPS = 1e-6           # L2-norm epsilon (not stated on the pages; a reading)
+DEFAULT_ONORM_EPS = 1e-6     # o_norm epsilon (not stated on the pages; a reading)
 
 
 def build(force: bool = False) -> str:
@@ -64,6 +65,8 @@ def _load():
             dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_uint,
             dp, dp, dp, dp, dp]
+        lib.kda_oracle_output_gate.restype = None
+        lib.kda_oracle_output_gate.argtypes = [ctypes.c_long, ctypes.c_int, dp, dp, dp, ctypes.c_double, dp]
         lib.kda_oracle_recurrence.restype = None
         lib.kda_oracle_recurrence.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, ctypes.c_long]
@@ -200,3 +203,20 @@ def decode_reference(S, conv_state, tokens, params, H, dk, dv, io, *, scale=1.0,
     o, S_new, cout, _ = forward(prob, scale=scale, lower_bound=lower_bound, eps=eps, flags=flags,
                                items=items, nthreads=nthreads)
     return o, S_new, cout
+
+
+def output_gate(o, gate, weight, eps: float = DEFAULT_ONORM_EPS):
+    """The output epilogue: y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate)
+    per (token, head) row, the mean over the row's dv channels (AliceAI page,
+    sections 二 and 三: ``o_norm`` and the sigmoid output gate).
+    o, gate [..., dv] (float64 or stored arrays widened by the caller);
+    weight [dv].  Returns y with o's shape, float64."""
+    lib = _load()
+    o = np.ascontiguousarray(np.asarray(o, dtype=np.float64))
+    gate = np.ascontiguousarray(np.asarray(gate, dtype=np.float64))
+    w = np.ascontiguousarray(np.asarray(weight, dtype=np.float64))
+    assert o.shape == gate.shape and o.shape[-1] == w.size
+    dv = o.shape[-1]
+    y = np.empty_like(o)
+    lib.kda_oracle_output_gate(int(o.size // dv) if dv else 0, dv, _p(o), _p(gate), _p(w), float(eps), _p(y))
+    return y

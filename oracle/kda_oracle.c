@@ -27,8 +27,17 @@
  *   S <- S + k_t d^T
  *   o_t = q_t^T S                    (the output reads the updated state)
  *
+ * The output epilogue (kda_oracle_output_gate below): the same AliceAI page,
+ * section 三, puts KDA's output through `o_norm` and a sigmoid gate (the
+ * full-attention layers' `output * sigmoid(output_gate)` is likened to it),
+ * and its section 二 lists `output_gate` among the per-token control inputs:
+ *   y_t[j] = o_t[j] / sqrt(mean_j' o_t[j']^2 + eps_o) * w[j] * sigmoid(gate_t[j])
+ * per (token, head), the mean over the head's dv channels.
+ *
  * Readings where the pages are silent (each one is a choice, listed in the
  * design notes): eps = 1e-6 inside the square root; scale defaults to 1;
+ * o_norm is an RMS norm over one head's dv outputs with one weight per
+ * channel shared by the heads, its epsilon a parameter (1e-6 by default);
  * the safe gate is a clamp applied after the product; the conv history holds
  * the last three raw (pre-conv) inputs per channel, oldest first, with the
  * channels ordered q | k | v.
@@ -290,4 +299,23 @@ int kda_oracle_forward(int nseq, const int64_t *cu, int H, int dk, int dv,
         }
     }
     return nthreads;
+}
+
+/*
+ * The output epilogue over n_rows (token, head) rows of dv outputs each:
+ * o, gate, y [n_rows][dv]; w [dv] (one weight per channel, shared by the
+ * heads).  y may alias o.
+ */
+void kda_oracle_output_gate(long n_rows, int dv, const double *o, const double *gate, const double *w,
+                            double eps, double *y)
+{
+    for (long r = 0; r < n_rows; ++r) {
+        const double *orow = o + (size_t)r * dv;
+        const double *grow = gate + (size_t)r * dv;
+        double ss = 0.0;
+        for (int j = 0; j < dv; ++j) ss += orow[j] * orow[j];
+        const double rms = sqrt(ss / dv + eps);
+        for (int j = 0; j < dv; ++j)
+            y[(size_t)r * dv + j] = orow[j] / rms * w[j] * orc_sigmoid(grow[j]);
+    }
 }

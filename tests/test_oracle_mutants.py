@@ -39,6 +39,12 @@ MUTANTS = {
     "scale_on_k": ("for (int i = 0; i < dk; ++i) qh[(size_t)t * dk + i] *= scale;",
                    "for (int i = 0; i < dk; ++i) kh[(size_t)t * dk + i] *= scale;"),
     "conv_out_shift": ("const int tt = L - 3 + m;", "const int tt = L - 4 + m;"),
+    "onorm_sum_not_mean": ("const double rms = sqrt(ss / dv + eps);", "const double rms = sqrt(ss + eps);"),
+    "onorm_eps_outside": ("const double rms = sqrt(ss / dv + eps);", "const double rms = sqrt(ss / dv) + eps;"),
+    "onorm_weight_ch0": ("orow[j] / rms * w[j] * orc_sigmoid(grow[j]);", "orow[j] / rms * w[0] * orc_sigmoid(grow[j]);"),
+    "ogate_sign": ("orow[j] / rms * w[j] * orc_sigmoid(grow[j]);", "orow[j] / rms * w[j] * orc_sigmoid(-grow[j]);"),
+    "ogate_row0": ("const double *grow = gate + (size_t)r * dv;", "const double *grow = gate;"),
+    "ogate_silu": ("orow[j] / rms * w[j] * orc_sigmoid(grow[j]);", "orow[j] / rms * w[j] * grow[j] * orc_sigmoid(grow[j]);"),
     "state_not_loaded": ("memcpy(S, J->S0 + ((size_t)n * H + h) * dk * dv, sizeof(double) * (size_t)dk * dv);",
                          "memset(S, 0, sizeof(double) * (size_t)dk * dv);"),
 }
@@ -60,6 +66,10 @@ CHECKS = [
     lambda: pins.test_beta_is_sigmoid(None),
     lambda: pins.test_conv_state_out_short_sequences(None),
     lambda: pins.test_forward_equals_preprocess_then_recurrence(None),
+    lambda: pins.test_output_gate_unit_rms_and_scale_invariance(None),
+    lambda: pins.test_output_gate_eps_inside_the_root(None),
+    lambda: pins.test_output_gate_logistic_gate_and_channel_weights(None),
+    lambda: pins.test_output_gate_rows_are_independent(None),
 ]
 
 

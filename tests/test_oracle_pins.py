@@ -279,3 +279,70 @@ def test_items_subset_matches_full(oracle_lib):
     o2, S2, _, _ = oracle.forward(p, items=[1, 5])
     assert np.array_equal(o2[:9, 1], o[:9, 1]) and np.array_equal(S2[1, 2], S[1, 2])
     assert np.isnan(o2[:9, 0]).all()
+
+
+# ---- the output epilogue: o_norm (RMS over a head's dv outputs) x sigmoid gate
+# (AliceAI page, sections 二 and 三).  Properties that fix every part of it:
+# the mean over the row (not a sum, not over other heads), eps inside the
+# square root, a per-channel weight, and the logistic function of the gate.
+
+def _og_rows(seed, rows, dv):
+    r = np.random.default_rng(seed)
+    o = r.standard_normal((rows, dv)) * r.uniform(0.1, 10.0, size=(rows, 1))
+    g = r.standard_normal((rows, dv)) * 3
+    return o, g
+
+
+def test_output_gate_unit_rms_and_scale_invariance(oracle_lib):
+    o, _ = _og_rows(11, 12, 16)
+    big = np.full_like(o, 60.0)           # sigmoid(60) = 1 - 9e-27: the gate fully open
+    y = oracle.output_gate(o, big, np.ones(16), eps=0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)
+    for c in (1e-3, 7.5):
+        np.testing.assert_allclose(oracle.output_gate(c * o, big, np.ones(16), eps=0.0), y, rtol=1e-13)
+    np.testing.assert_allclose(oracle.output_gate(-o, big, np.ones(16), eps=0.0), -y, rtol=1e-13)
+
+
+def test_output_gate_eps_inside_the_root(oracle_lib):
+    # rows of +-sqrt(m): mean square exactly m; with eps = m every |y| is 1/sqrt(2)
+    dv = 8
+    signs = np.array([1, -1, 1, 1, -1, -1, 1, -1], dtype=np.float64)
+    for m in (0.25, 4.0, 9.0):
+        o = (np.sqrt(m) * signs)[None, :]
+        y = oracle.output_gate(o, np.full_like(o, 60.0), np.ones(dv), eps=m)
+        np.testing.assert_allclose(y[0], signs / np.sqrt(2.0), rtol=1e-13)
+
+
+def test_output_gate_logistic_gate_and_channel_weights(oracle_lib):
+    o, g = _og_rows(12, 6, 16)
+    w = np.linspace(-2.0, 3.0, 16)
+    full = oracle.output_gate(o, np.full_like(g, 60.0), w)
+    # sigmoid(g) + sigmoid(-g) = 1: the two gated outputs add up to the open one
+    np.testing.assert_allclose(oracle.output_gate(o, g, w) + oracle.output_gate(o, -g, w), full,
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.output_gate(o, np.zeros_like(g), w), 0.5 * full, rtol=1e-13)
+    np.testing.assert_allclose(oracle.output_gate(o, np.full_like(g, np.log(3.0)), w), 0.75 * full,
+                               rtol=1e-13)
+    # a one-hot weight passes exactly one channel of every row
+    for j in (0, 5, 15):
+        e = np.zeros(16)
+        e[j] = 1.0
+        y = oracle.output_gate(o, g, e)
+        assert np.all(np.delete(y, j, axis=1) == 0.0)
+        assert np.all(y[:, j] != 0.0)
+
+
+def test_output_gate_rows_are_independent(oracle_lib):
+    o, g = _og_rows(13, 10, 32)
+    w = np.random.default_rng(14).uniform(0.5, 1.5, 32)
+    y = oracle.output_gate(o, g, w)
+    o2, g2 = o.copy(), g.copy()
+    o2[3] = np.random.default_rng(15).standard_normal(32) * 100
+    g2[7] = -g2[7]
+    y2 = oracle.output_gate(o2, g2, w)
+    same = [r for r in range(10) if r not in (3, 7)]
+    assert np.array_equal(y[same], y2[same])
+    assert not np.allclose(y[3], y2[3]) and not np.allclose(y[7], y2[7])
+    # [T, H, dv] layout: each (token, head) row is normalised on its own
+    y3 = oracle.output_gate(o.reshape(5, 2, 32), g.reshape(5, 2, 32), w)
+    assert np.array_equal(y3.reshape(10, 32), y)
