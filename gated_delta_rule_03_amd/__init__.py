@@ -39,11 +39,11 @@ FLAG_RAW_GATE = 1 << 2
 FLAG_RAW_BETA = 1 << 3
 FLAG_BETA_X2 = 1 << 4
 
-STAGES = ("chunk_table", "chunk_prep", "chunk_scan", "conv_state", "decode")
+STAGES = ("chunk_table", "chunk_prep", "chunk_scan", "conv_state", "decode", "output_gate")
 NUM_STAGES = len(STAGES)
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
-            "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step")
+            "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_output_gate")
 
 
 class KdaError(RuntimeError):
@@ -94,6 +94,8 @@ def _load_library():
     lib.kda_varlen_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_output_gate.restype = ctypes.c_int
+    lib.kda_output_gate.argtypes = [cfgp, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp]
     return lib
 
 
@@ -248,3 +250,19 @@ def kda_decode_step(cfg: Config, q, k, v, alpha, b, state, conv_state, *, o=None
                               _ptr(state), _ptr(conv_state), _ptr(o), _stream(stream))
     _check(st, "kda_decode_step")
     return o
+
+
+def kda_output_gate(cfg: Config, o, gate, o_norm_weight, eps: float = 1e-6, *, y=None, stream=None):
+    """The output epilogue: y = o / sqrt(mean(o^2) + eps) * o_norm_weight * sigmoid(gate)
+    per (token, head) row.  o [..., H, dv] out_dtype; gate the same shape in
+    io_dtype; o_norm_weight [dv] fp32.  y defaults to a new tensor; pass
+    y=o to work in place.  Returns y."""
+    if o.shape != gate.shape or o.shape[-1] != cfg.head_v_dim or o.shape[-2] != cfg.num_heads:
+        raise ValueError("o and gate must both be [..., num_heads, head_v_dim]")
+    n_tokens = o.numel() // (cfg.num_heads * cfg.head_v_dim) if o.numel() else 0
+    if y is None:
+        y = torch.empty_like(o)
+    st = _lib.kda_output_gate(ctypes.byref(cfg.c_struct()), n_tokens, _ptr(o), _ptr(gate), _ptr(o_norm_weight),
+                              float(eps), _ptr(y), _stream(stream))
+    _check(st, "kda_output_gate")
+    return y

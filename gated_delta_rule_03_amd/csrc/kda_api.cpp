@@ -166,7 +166,7 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
 
 extern "C" {
 
-int32_t kda_version(void) { return 100; }
+int32_t kda_version(void) { return 101; }
 
 const char* kda_status_string(kda_status_t status) {
   switch (status) {
@@ -243,6 +243,28 @@ kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return stage(cfg, KDA_STAGE_DECODE, st, [&] {
     return kda::launch_decode(p, io, N, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16, st);
+  });
+}
+
+kda_status_t kda_output_gate(const kda_config_t* cfg, int64_t n_tokens, const void* o, const void* gate,
+                             const float* o_norm_weight, float eps, void* y, void* stream) {
+  if (!cfg) return KDA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_heads < 1 || cfg->head_v_dim < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_heads > 65535) return KDA_ERR_UNSUPPORTED;
+  const int dv = cfg->head_v_dim;
+  if (dv != 16 && dv != 32 && dv != 64 && dv != 128) return KDA_ERR_UNSUPPORTED;
+  if ((cfg->io_dtype != KDA_BF16 && cfg->io_dtype != KDA_FP32) ||
+      (cfg->out_dtype != KDA_BF16 && cfg->out_dtype != KDA_FP32))
+    return KDA_ERR_UNSUPPORTED;
+  if (n_tokens < 0 || std::isnan(eps) || eps < 0.f) return KDA_ERR_INVALID_ARGUMENT;
+  if (n_tokens > INT64_MAX / cfg->num_heads / dv) return KDA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return KDA_OK;
+  if (!o || !gate || !o_norm_weight || !y) return KDA_ERR_INVALID_ARGUMENT;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = n_tokens * cfg->num_heads;
+  return stage(cfg, KDA_STAGE_OUTPUT_GATE, st, [&] {
+    return kda::launch_output_gate(dv, rows, o, gate, o_norm_weight, eps, y, cfg->out_dtype == KDA_BF16,
+                                   cfg->io_dtype == KDA_BF16, st);
   });
 }
 

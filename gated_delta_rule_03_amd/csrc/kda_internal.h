@@ -133,6 +133,11 @@ hipError_t launch_token_prep(const Params& p, const ChunkTable& t, const Prefill
 hipError_t launch_recurrent_scan(const Params& p, const ChunkTable& t, const PrefillIO& io, const float* recs,
                                  int64_t total_T, bool out_bf16, hipStream_t st);
 
+// The output epilogue over `rows` (token, head) rows of D outputs:
+// y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate); y may alias o.
+hipError_t launch_output_gate(int D, int64_t rows, const void* o, const void* gate, const float* w, float eps,
+                              void* y, bool o_bf16, bool g_bf16, hipStream_t st);
+
 struct DecodeIO {
   const void* q;
   const void* k;

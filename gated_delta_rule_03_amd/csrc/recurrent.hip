@@ -36,28 +36,6 @@ constexpr int kTokBlock = 16;       // tokens staged per LDS block
 
 __host__ __device__ constexpr int rec_floats(int D) { return 4 * D + 4; }
 
-// One DPP move within rows of 16 lanes (gfx9 encodings): quad_perm
-// [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
-// row_mirror = 0x140.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over aligned groups of W = 8 or 16 lanes, in every lane of the group:
-// pairs, quads, then the mirrored half row (lane i with 7 - i joins the two
-// quads of a half) and, for 16, the mirrored row (lane i with 15 - i joins
-// the halves).
-template <int W>
-__device__ __forceinline__ float lane_group_sum(float x) {
-  static_assert(W == 8 || W == 16, "DPP row groups of 8 or 16 lanes");
-  x += dpp_mov<0xB1>(x);
-  x += dpp_mov<0x4E>(x);
-  x += dpp_mov<0x141>(x);
-  if constexpr (W == 16) x += dpp_mov<0x140>(x);
-  return x;
-}
-
 }  // namespace
 
 size_t recurrent_record_bytes(int D) { return static_cast<size_t>(rec_floats(D)) * 4; }

@@ -80,7 +80,8 @@ typedef enum kda_stage {
                                    (recurrent form: the token-by-token state scan)            */
     KDA_STAGE_CONV_STATE = 3,   /* conv history out                                           */
     KDA_STAGE_DECODE = 4,       /* the decode step kernel                                     */
-    KDA_NUM_STAGES = 5
+    KDA_STAGE_OUTPUT_GATE = 5,  /* the o_norm + sigmoid output-gate epilogue                  */
+    KDA_NUM_STAGES = 6
 } kda_stage_t;
 
 typedef struct kda_config {
@@ -188,6 +189,29 @@ kda_status_t kda_decode_step(const kda_config_t *cfg, int32_t N,
                              const void *q, const void *k, const void *v,
                              const void *alpha, const void *b,
                              float *state, void *conv_state, void *o, void *stream);
+
+/*
+ * The layer's output epilogue on n_tokens x H rows of dv outputs (AliceAI
+ * page, section 三: KDA's output goes through o_norm and a sigmoid gate;
+ * section 二: output_gate is one of the per-token control inputs):
+ *   y[t][h][j] = o[t][h][j] / sqrt(mean_j' o[t][h][j']^2 + eps)
+ *                * o_norm_weight[j] * sigmoid(gate[t][h][j])
+ * The pages give neither the norm's epsilon nor its weight's shape: o_norm
+ * is read as an RMS norm over one head's dv outputs with one weight per
+ * channel shared by the heads (eps 1e-6 in the reference setting).
+ *   o              [n_tokens][H][dv] out_dtype, as written by the calls above
+ *   gate           [n_tokens][H][dv] io_dtype, the output-gate projection
+ *                  before the sigmoid
+ *   o_norm_weight  [dv] fp32
+ *   eps            >= 0 (NaN or negative: KDA_ERR_INVALID_ARGUMENT)
+ *   y              [n_tokens][H][dv] out_dtype; may alias o (in place)
+ * Only num_heads, head_v_dim, io_dtype, out_dtype and stage_events of cfg
+ * are used.  Needs no workspace.  n_tokens == 0 is a no-op.
+ */
+kda_status_t kda_output_gate(const kda_config_t *cfg, int64_t n_tokens,
+                             const void *o, const void *gate,
+                             const float *o_norm_weight, float eps,
+                             void *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,9 @@ Distributions (second parameter of N(.,.) is the standard deviation):
   dt_bias           ~ N(0, 0.1)  fp32      [H*dk]
   initial state     ~ N(0, 0.02) fp32      [N, H, dk, dv]   (where requested)
   conv state        ~ N(0, 1)              [N, 3, H*(2dk+dv)] (where requested)
+  output epilogue:  gate ~ N(0, 2) [T, H, dv]; o_norm weight ~ U(0.5, 1.5) fp32
+                    [dv]; a stand-alone o ~ N(0, s_row^2) [T, H, dv] with
+                    log10 s_row ~ U(-2, 1) per (token, head) row
 """
 from __future__ import annotations
 
@@ -34,6 +37,7 @@ FP32 = "fp32"
 T_Q, T_K, T_V, T_ALPHA, T_B = 0, 1, 2, 3, 4
 T_WQ, T_WK, T_WV, T_ALOG, T_DTB = 5, 6, 7, 8, 9
 T_S0, T_CONV = 10, 11
+T_GATE, T_ONW, T_O, T_OSCALE = 12, 13, 14, 15
 
 
 def rng(workload_id: int, tensor_id: int, step: int = 0) -> np.random.Generator:
@@ -164,6 +168,23 @@ def make_problem(workload_id: int, seqlens: Sequence[int], H: int, dk: int, dv: 
     if conv_state:
         cs = _normal(workload_id, T_CONV, (N, 3, H * (2 * dk + dv)), 1.0, dtype=io)
     return Problem(seqlens, H, dk, dv, io, q, k, v, alpha, b, w_q, w_k, w_v, A_log, dt_bias, S0, cs)
+
+
+def make_output_gate_inputs(workload_id: int, n_tokens: int, H: int, dv: int, io: str, step: int = 0):
+    """Inputs of the output epilogue: gate [n_tokens, H, dv] (io dtype) and the
+    o_norm weight [dv] (fp32)."""
+    gate = _normal(workload_id, T_GATE, (n_tokens, H, dv), 2.0, step=step, dtype=io)
+    w = rng(workload_id, T_ONW).uniform(0.5, 1.5, size=(dv,)).astype(np.float32)
+    return gate, w
+
+
+def make_epilogue_o(workload_id: int, n_tokens: int, H: int, dv: int, dtype: str, step: int = 0):
+    """A stand-alone attention output [n_tokens, H, dv] whose rows have scales
+    spread over three decades (the epilogue normalises each row)."""
+    scale = 10.0 ** rng(workload_id, T_OSCALE, step).uniform(-2.0, 1.0, size=(n_tokens, H, 1))
+    x = rng(workload_id, T_O, step).standard_normal((n_tokens, H, dv), dtype=np.float32) * scale.astype(np.float32)
+    x = x.astype(np.float32)
+    return f32_to_bf16_bits(x) if dtype == BF16 else x
 
 
 # --------------------------------------------------------------------------

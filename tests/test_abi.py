@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(kda):
 
 
 def test_version_and_status_strings(kda):
-    assert kda.version() == 100
+    assert kda.version() == 101
     for code, name in ((0, "KDA_OK"), (1, "KDA_ERR_INVALID_ARGUMENT"), (2, "KDA_ERR_UNSUPPORTED"),
                        (3, "KDA_ERR_WORKSPACE_TOO_SMALL"), (4, "KDA_ERR_HIP")):
         assert kda.status_string(code) == name
@@ -190,4 +190,27 @@ def test_varlen_and_decode_validation(kda):
     assert lib.kda_decode_step(ctypes.byref(cfg), 4, p, p, p, p, p, None, p, p, None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert lib.kda_decode_step(ctypes.byref(cfg), 4, p, p, p, p, p, p, None, p, None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert lib.kda_decode_step(ctypes.byref(cfg), -2, p, p, p, p, p, p, p, p, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert c.untouched()
+
+
+def test_output_gate_validation(kda):
+    lib = kda.library()
+    c = Canary(1 << 12)
+    p = c.ptr
+    cfg, _ = make_cfg(kda, H=4, dk=64, dv=64)
+    og = lambda cfg_, n, o, g, w, eps, y: lib.kda_output_gate(
+        None if cfg_ is None else ctypes.byref(cfg_), n, o, g, w, eps, y, None)
+    assert og(None, 4, p, p, p, 1e-6, p) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert og(cfg, -1, p, p, p, 1e-6, p) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert og(cfg, 4, p, p, p, float("nan"), p) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert og(cfg, 4, p, p, p, -1e-3, p) == kda.KDA_ERR_INVALID_ARGUMENT
+    for missing in range(4):
+        args = [p, p, p, p]
+        args[missing] = None
+        assert og(cfg, 4, args[0], args[1], args[2], 1e-6, args[3]) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert og(make_cfg(kda, H=4, dk=64, dv=48)[0], 4, p, p, p, 1e-6, p) == kda.KDA_ERR_UNSUPPORTED
+    assert og(make_cfg(kda, H=4, dk=64, dv=64, out_dtype=5)[0], 4, p, p, p, 1e-6, p) == kda.KDA_ERR_UNSUPPORTED
+    # the epilogue does not need the prefill's parameters, and 0 tokens is a no-op
+    assert og(make_cfg(kda, H=4, dk=64, dv=64, A_log=None, conv_w_q=None)[0], 0, None, None, None, 1e-6,
+              None) == kda.KDA_OK
     assert c.untouched()
