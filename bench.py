@@ -270,6 +270,90 @@ def bench_varlen(kda, torch, ev, steps=3, warmup=1):
             "ms_per_step": round(ms, 3), "tokens_per_s": round(total / ms * 1e3, 1)}
 
 
+# Peak of fp32 VALU lane operations (non-packed, as this library is built):
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def bench_prefill_no_clamp(kda, torch, ev, dp, steps=5, warmup=2):
+    """The same 32K prefill with the gate's clamp off (lower bound -inf): the
+    recurrent form (token pre-pass + register-resident recurrent scan)."""
+    dev = torch.device("cuda:0")
+    B, T = 4, 32768
+    cfg = dp.config(out_dtype=torch.bfloat16, gate_lower_bound=float("-inf"))
+    tz = dp.tensors
+    q, k, v = (tz[n].view(B, T, -1) for n in ("q", "k", "v"))
+    alpha, b = tz["alpha"].view(B, T, H, D), tz["b"].view(B, T, H)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_prefill(cfg, q, k, v, alpha, b, tz["initial_state"], tz["conv_state"], o=o, final_state=S_out,
+                        workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    stages = [kda.STAGES.index(n) for n in ("chunk_prep", "chunk_scan")]
+    arrays = [ev.stage_array(stages) for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(steps):
+        cfg.stage_events = arrays[i]
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    cfg.stage_events = None
+    per = stage_means(ev, arrays, stages)
+    prep_ms, scan_ms = per[stages[0]], per[stages[1]]
+    ms = wall / steps * 1e3
+    lane_ops = 4 * D * D * B * T * H            # decay multiply, two dot-product FMAs, rank-1 update
+    tops = lane_ops / (scan_ms * 1e-3) / 1e12
+    log(f"[bench] prefill without clamp: {ms:.2f} ms/step (pre-pass {prep_ms:.3f}, scan {scan_ms:.3f})")
+    del ws
+    return {"workload": "kda prefill B=4 T=32768 H=32 dk=dv=128, bf16, gate lower bound -inf (recurrent form)",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(B * T / ms * 1e3, 1),
+            "stage_ms": {"token_prep": round(prep_ms, 4), "recurrent_scan": round(scan_ms, 4)},
+            "roofline": {"kernel": "recurrent_scan", "bound": "alu", "achieved": round(tops, 3),
+                         "peak": round(VALU_PEAK_TOPS, 2), "unit": "T fp32 VALU lane-ops/s",
+                         "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": None, "lane_ops_per_launch": lane_ops}}
+
+
+def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
+    """The o_norm x sigmoid-gate epilogue on the 32K prefill's output shape
+    (4 x 32768 tokens x 32 heads x 128, bf16 o and gate), in place."""
+    dev = torch.device("cuda:0")
+    n = 4 * 32768
+    g = torch.Generator(device=dev)
+    g.manual_seed(5_000_011)
+    o = torch.randn((n, H, D), generator=g, device=dev).to(torch.bfloat16)
+    gate = (torch.randn((n, H, D), generator=g, device=dev) * 2).to(torch.bfloat16)
+    w = torch.rand((D,), generator=g, device=dev) + 0.5
+    cfg = kda.Config(A_log=None, dt_bias=None, conv_w_q=None, conv_w_k=None, conv_w_v=None, num_heads=H,
+                     head_k_dim=D, head_v_dim=D, io_dtype=torch.bfloat16, out_dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        kda.kda_output_gate(cfg, o, gate, w, y=o, stream=stream)
+    st = kda.STAGES.index("output_gate")
+    arrays = [ev.stage_array([st]) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        cfg.stage_events = arrays[i]
+        kda.kda_output_gate(cfg, o, gate, w, y=o, stream=stream)
+    torch.cuda.synchronize()
+    cfg.stage_events = None
+    us = 1e3 * stage_means(ev, arrays, [st])[st]
+    nbytes = n * H * D * 2 * 3 + D * 4           # o and gate in, y out (bf16), weight
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] output gate: {us:.1f} us/launch, {gbs:.0f} GB/s")
+    return {"workload": "kda o_norm x sigmoid output gate, 131072 tokens x 32 heads x 128, bf16, in place",
+            "us_per_launch": round(us, 2),
+            "roofline": {"kernel": "output_gate", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": nbytes}}
+
+
 def cpu_baseline(dp, seqs=2):
     """The fp64 oracle on the first `seqs` sequences of the prefill workload
     (all heads, full length), on all host cores."""
@@ -302,7 +386,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decode, varlen, no-clamp prefill and output-gate measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (to scale HBM traffic counters)")
     args = ap.parse_args()
@@ -347,6 +432,8 @@ def main():
     if not args.no_extras:
         result["decode"] = bench_decode(kda, torch, ev)
         result["varlen"] = bench_varlen(kda, torch, ev)
+        result["prefill_no_clamp"] = bench_prefill_no_clamp(kda, torch, ev, dp)
+        result["output_gate"] = bench_output_gate(kda, torch, ev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dp)
     print(json.dumps(result), flush=True)
