@@ -232,7 +232,7 @@ def bench_decode(kda, torch, ev, n_steps=128, warmup=3):
             "us_per_step": round(mean_us, 2), "us_per_step_p50": round(statistics.median(us), 2),
             "wall_us_per_step": round(wall / n_steps * 1e6, 2),
             "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                          "bytes_per_launch": bytes_step}}
 
 
@@ -317,7 +317,8 @@ def bench_prefill_no_clamp(kda, torch, ev, dp, steps=5, warmup=2):
             "stage_ms": {"token_prep": round(prep_ms, 4), "recurrent_scan": round(scan_ms, 4)},
             "roofline": {"kernel": "recurrent_scan", "bound": "alu", "achieved": round(tops, 3),
                          "peak": round(VALU_PEAK_TOPS, 2), "unit": "T fp32 VALU lane-ops/s",
-                         "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": None, "lane_ops_per_launch": lane_ops}}
+                         "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": measured_traffic("recurrent_scan"),
+                         "lane_ops_per_launch": lane_ops}}
 
 
 def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
@@ -350,7 +351,8 @@ def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
     return {"workload": "kda o_norm x sigmoid output gate, 131072 tokens x 32 heads x 128, bf16, in place",
             "us_per_launch": round(us, 2),
             "roofline": {"kernel": "output_gate", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("output_gate"),
                          "bytes_per_launch": nbytes}}
 
 
