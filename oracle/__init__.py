@@ -120,6 +120,9 @@ def forward(p: Problem, *, scale: float = 1.0, lower_bound: float = DEFAULT_LOWE
     if cs is not None and cs.dtype == np.uint16:
         cs = as_f64(cs, BF16)
     cs = None if cs is None else np.ascontiguousarray(np.asarray(cs, dtype=np.float64))
+    # the C code trusts these shapes
+    assert S0 is None or S0.shape == (N, H, dk, dv)
+    assert cs is None or cs.shape == (N, 3, p.ctot)
     total = p.total_T
     o = np.full((total, H, dv), np.nan)
     S = np.full((N, H, dk, dv), np.nan)
@@ -220,3 +223,54 @@ def output_gate(o, gate, weight, eps: float = DEFAULT_ONORM_EPS):
     y = np.empty_like(o)
     lib.kda_oracle_output_gate(int(o.size // dv) if dv else 0, dv, _p(o), _p(gate), _p(w), float(eps), _p(y))
     return y
+
+
+def decode_multi_reference(state_pool, conv_pool, slots, tokens, params, H, dk, dv, io, K, n_commit=None, *,
+                           scale=1.0, lower_bound=DEFAULT_LOWER_BOUND, eps=DEFAULT_EPS, flags=0,
+                           nthreads: Optional[int] = None):
+    """K tokens for each of N sequences whose state and conv history live in
+    pools, found through ``slots`` (a negative slot: the sequence is skipped).
+
+    state_pool [P, H, dk, dv]; conv_pool [P, 3, Ctot] (stored dtype); slots [N];
+    tokens = (q, k, v, alpha, b) packed sequence-major, N*K tokens; params as
+    in ``decode_reference``; n_commit [N] (tokens whose updates are kept,
+    0..K) or None for K.  The outputs of all K tokens follow the token loop
+    from the slot's state; the pools receive the state and conv history after
+    the first n_commit[n] tokens -- the same loop over fewer tokens (sequences
+    of length 0 pass both through).  Returns (o [N, K, H, dv] with NaN rows for
+    skipped sequences, state_pool', conv_pool') in float64."""
+    q, k, v, alpha, b = tokens
+    w_q, w_k, w_v, A_log, dt_bias = params
+    slots = np.asarray(slots)
+    N = slots.size
+    assert state_pool.shape[1:] == (H, dk, dv) and conv_pool.shape[1:] == (3, H * (2 * dk + dv))
+    assert slots.max(initial=-1) < state_pool.shape[0] == conv_pool.shape[0]
+    assert all(a.shape[0] == N * K for a in tokens)
+    commit = np.full(N, K) if n_commit is None else np.clip(np.asarray(n_commit), 0, K)
+    S_pool = np.array(state_pool, dtype=np.float64, copy=True)
+    cs_pool = np.array(as_f64(conv_pool, BF16) if conv_pool.dtype == np.uint16 else conv_pool, dtype=np.float64,
+                       copy=True)
+    o = np.full((N, K, H, dv), np.nan)
+    act = [n for n in range(N) if slots[n] >= 0]
+    if not act:
+        return o, S_pool, cs_pool
+    tok = np.concatenate([np.arange(n * K, (n + 1) * K) for n in act])
+    sel = lambda a: np.ascontiguousarray(a[tok])
+    S0 = np.stack([S_pool[slots[n]] for n in act])
+    C0 = np.stack([cs_pool[slots[n]] for n in act])
+    full = Problem([K] * len(act), H, dk, dv, io, sel(q), sel(k), sel(v), sel(alpha), sel(b),
+                   w_q, w_k, w_v, A_log, dt_bias, S0, C0)
+    kw = dict(scale=scale, lower_bound=lower_bound, eps=eps, flags=flags, nthreads=nthreads)
+    o_all, _, _, _ = forward(full, **kw)
+    for i, n in enumerate(act):
+        o[n] = o_all[i * K:(i + 1) * K]
+    # the committed prefix of every sequence: the same loop over its first n_commit tokens
+    tok_c = np.concatenate([np.arange(n * K, n * K + int(commit[n])) for n in act]).astype(np.int64)
+    selc = lambda a: np.ascontiguousarray(a[tok_c])
+    part = Problem([int(commit[n]) for n in act], H, dk, dv, io, selc(q), selc(k), selc(v), selc(alpha), selc(b),
+                   w_q, w_k, w_v, A_log, dt_bias, S0, C0)
+    _, S_c, c_c, _ = forward(part, **kw)
+    for i, n in enumerate(act):
+        S_pool[slots[n]] = S_c[i]
+        cs_pool[slots[n]] = c_c[i]
+    return o, S_pool, cs_pool

@@ -346,3 +346,36 @@ def test_output_gate_rows_are_independent(oracle_lib):
     # [T, H, dv] layout: each (token, head) row is normalised on its own
     y3 = oracle.output_gate(o.reshape(5, 2, 32), g.reshape(5, 2, 32), w)
     assert np.array_equal(y3.reshape(10, 32), y)
+
+
+def test_decode_multi_reference_composes_the_token_loop(oracle_lib):
+    """K tokens through slots equal K one-token decode steps on the gathered
+    states; committing m < K tokens leaves the state of the m-th step, and 0
+    leaves the pools untouched."""
+    from kda_inputs import BF16, make_tokens, workload_decode
+    K, P = 3, 5
+    dp = workload_decode(N=P, H=2, d=16, steps=1, workload_id=77)   # a pool of 5 states and histories
+    pool = dp.state.astype(np.float64) * 5
+    cpool = dp.conv_state
+    params = (dp.w_q, dp.w_k, dp.w_v, dp.A_log, dp.dt_bias)
+    toks = make_tokens(79, 3 * K, 2, 16, 16, BF16)
+    slots = np.array([4, -1, 1])
+    o, Sp, Cp = oracle.decode_multi_reference(pool, cpool, slots, toks, params, 2, 16, 16, BF16, K)
+    assert np.all(np.isnan(o[1])) and np.array_equal(Sp[[0, 2, 3]], pool[[0, 2, 3]])
+    from kda_inputs import as_f64
+    for n in (0, 2):
+        S, C = pool[slots[n]][None], cpool[slots[n]][None]
+        for t in range(K):
+            one = tuple(a[n * K + t:n * K + t + 1] for a in toks)
+            o1, S, C = oracle.decode_reference(S, C, one, params, 2, 16, 16, BF16)
+            assert np.allclose(o1[0], o[n, t], rtol=1e-12, atol=1e-14)
+        assert np.allclose(S[0], Sp[slots[n]], rtol=1e-12, atol=1e-14)
+        assert np.array_equal(C[0], Cp[slots[n]])
+    # commit counts: 0 keeps the pools, m keeps the m-th state
+    o2, Sp2, Cp2 = oracle.decode_multi_reference(pool, cpool, slots, toks, params, 2, 16, 16, BF16, K,
+                                                 n_commit=[0, 3, 1])
+    assert np.array_equal(o2[[0, 2]], o[[0, 2]])
+    assert np.array_equal(Sp2[4], pool[4]) and np.array_equal(Cp2[4], as_f64(cpool[4], BF16))
+    one = tuple(a[2 * K:2 * K + 1] for a in toks)
+    _, S1, C1 = oracle.decode_reference(pool[1][None], cpool[1][None], one, params, 2, 16, 16, BF16)
+    assert np.allclose(S1[0], Sp2[1], rtol=1e-12, atol=1e-14) and np.array_equal(C1[0], Cp2[1])
