@@ -43,7 +43,8 @@ STAGES = ("chunk_table", "chunk_prep", "chunk_scan", "conv_state", "decode", "ou
 NUM_STAGES = len(STAGES)
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
-            "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_output_gate")
+            "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_decode_multi",
+            "kda_output_gate")
 
 
 class KdaError(RuntimeError):
@@ -94,6 +95,8 @@ def _load_library():
     lib.kda_varlen_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_decode_multi.restype = ctypes.c_int
+    lib.kda_decode_multi.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_output_gate.restype = ctypes.c_int
     lib.kda_output_gate.argtypes = [cfgp, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp]
     return lib
@@ -249,6 +252,26 @@ def kda_decode_step(cfg: Config, q, k, v, alpha, b, state, conv_state, *, o=None
     st = _lib.kda_decode_step(ctypes.byref(cfg.c_struct()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
                               _ptr(state), _ptr(conv_state), _ptr(o), _stream(stream))
     _check(st, "kda_decode_step")
+    return o
+
+
+def kda_decode_multi(cfg: Config, q, k, v, alpha, b, state_pool, conv_pool, *, slots=None, n_commit=None, o=None,
+                     stream=None):
+    """K tokens for each of N sequences through state / conv-history pools:
+    q, k [N, K, H*dk]; v [N, K, H*dv]; alpha [N, K, H, dk]; b [N, K, H];
+    state_pool [P, H, dk, dv] fp32 and conv_pool [P, 3, Ctot] are updated in
+    place (rows slots[n], after the first n_commit[n] tokens).  slots and
+    n_commit are int32 device tensors [N] or None.  Returns o [N, K, H, dv]."""
+    N, K = q.shape[0], q.shape[1]
+    for t in (slots, n_commit):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != N):
+            raise ValueError("slots and n_commit must be int32 tensors of N entries")
+    if o is None:
+        o = torch.empty((N, K, cfg.num_heads, cfg.head_v_dim), dtype=cfg.out_dtype, device=q.device)
+    st = _lib.kda_decode_multi(ctypes.byref(cfg.c_struct()), N, K, _ptr(slots), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(alpha), _ptr(b), _ptr(state_pool), _ptr(conv_pool), _ptr(o), _ptr(n_commit),
+                               _stream(stream))
+    _check(st, "kda_decode_multi")
     return o
 
 

@@ -160,6 +160,177 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
   }
 }
 
+// K tokens per sequence (multi-token decode, speculative verify and commit),
+// the state and conv history found in pools through a slot per sequence.
+// The state is read once; the per-token steps are those of decode_kernel,
+// with the conv window of each channel kept in its thread's registers.  The
+// state after the first `commit` tokens goes back to the pool (none for 0),
+// and so does the conv history after them; every token's output is written.
+template <int D, bool IO_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
+  constexpr int NT = kDecodeThreads;
+  constexpr int C4 = D / 4;
+  constexpr int RPP = NT / C4;
+  constexpr int RPT = (D + RPP - 1) / RPP;
+  static_assert(3 * D <= NT, "one conv channel per thread");
+  __shared__ float u_s[3 * D];
+  __shared__ float e_s[D];
+  __shared__ float red[2][RPP][D];
+  __shared__ float d_s[D];
+  __shared__ float scal[4];
+
+  const int tid = threadIdx.x;
+  const int H = p.H;
+  const int n = blockIdx.x / H, h = blockIdx.x % H;
+  const int slot = io.slots ? io.slots[n] : n;
+  if (slot < 0) return;
+  const int commit = io.n_commit ? min(max(io.n_commit[n], 0), K) : K;
+  const size_t HD = static_cast<size_t>(H) * D;
+  const size_t Ctot = 3 * HD;
+  const uint32_t flags = p.flags;
+
+  const int col4 = tid % C4, rg = tid / C4;
+  f32x4v* Sp = reinterpret_cast<f32x4v*>(io.state_pool + (static_cast<size_t>(slot) * H + h) * D * D);
+  f32x4v Sv[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = rg + rr * RPP;
+    if (r < D) Sv[rr] = __builtin_nontemporal_load(&Sp[static_cast<size_t>(r) * C4 + col4]);
+  }
+
+  // this thread's conv channel (q, k or v) and its window of raw inputs
+  const bool conv_lane = tid < 3 * D;
+  const int grp = tid / D, ci = tid % D;
+  const size_t ch = static_cast<size_t>(grp) * HD + static_cast<size_t>(h) * D + ci;
+  const size_t cb = static_cast<size_t>(slot) * 3 * Ctot + ch;
+  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, h0 = 0.f, h1 = 0.f, h2 = 0.f;
+  const void* xsrc = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
+  if (conv_lane) {
+    const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
+    if (!(flags & KDA_FLAG_SKIP_CONV)) {
+      const size_t wi = (static_cast<size_t>(h) * D + ci) * 4;
+      w0 = ld<IO_BF16>(w, wi); w1 = ld<IO_BF16>(w, wi + 1); w2 = ld<IO_BF16>(w, wi + 2); w3 = ld<IO_BF16>(w, wi + 3);
+    }
+    h0 = ld<IO_BF16>(io.conv_pool, cb);
+    h1 = ld<IO_BF16>(io.conv_pool, cb + Ctot);
+    h2 = ld<IO_BF16>(io.conv_pool, cb + 2 * Ctot);
+  }
+  float k0 = h0, k1 = h1, k2 = h2;   // the window after the committed tokens
+  const float a_exp = expf(p.A_log[h]);
+
+  for (int t = 0; t < K; ++t) {
+    const size_t tok = static_cast<size_t>(n) * K + t;
+    if (conv_lane) {
+      const float xt = ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci);
+      u_s[tid] = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h0 + w1 * h1 + w2 * h2 + w3 * xt);
+      h0 = h1; h1 = h2; h2 = xt;
+      if (t + 1 == commit) { k0 = h0; k1 = h1; k2 = h2; }
+    }
+    for (int i = tid; i < D; i += NT) {
+      const float al = ld<IO_BF16>(io.alpha, tok * HD + static_cast<size_t>(h) * D + i);
+      const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, p.dt_bias[h * D + i], a_exp, p.lower_bound);
+      e_s[i] = expf(g);
+    }
+    if (tid == 0) {
+      const float bb = ld<IO_BF16>(io.b, tok * H + h);
+      float be = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
+      if (flags & KDA_FLAG_BETA_X2) be *= 2.0f;
+      scal[2] = be;
+    }
+    __syncthreads();
+    {
+      const int wv = tid / kWave, lane = tid % kWave;
+      if (wv < 3) {
+        float sum = 0.0f;
+        for (int i = lane; i < D; i += kWave) {
+          const float a = u_s[(wv == 1 ? D : 0) + i];
+          const float b2 = u_s[(wv == 0 ? 0 : D) + i];
+          sum += a * b2;
+        }
+        sum = group_sum<kWave>(sum);
+        if (lane == 0) scal[wv == 2 ? 3 : wv] = sum;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
+      const float iq = norm ? 1.0f / sqrtf(scal[0] + p.eps) : 1.0f;
+      const float ik = norm ? 1.0f / sqrtf(scal[1] + p.eps) : 1.0f;
+      scal[3] = scal[3] * iq * ik * p.scale;
+      scal[0] = iq * p.scale;
+      scal[1] = ik;
+    }
+    __syncthreads();
+    const float qs = scal[0], ks = scal[1], beta = scal[2], qk = scal[3];
+
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int r = rg + rr * RPP;
+      if (r < D) {
+        const float e = e_s[r];
+        Sv[rr].x *= e; Sv[rr].y *= e; Sv[rr].z *= e; Sv[rr].w *= e;
+        const float kr = u_s[D + r] * ks, qr = u_s[r] * qs;
+        pk[0] += kr * Sv[rr].x; pk[1] += kr * Sv[rr].y; pk[2] += kr * Sv[rr].z; pk[3] += kr * Sv[rr].w;
+        pq[0] += qr * Sv[rr].x; pq[1] += qr * Sv[rr].y; pq[2] += qr * Sv[rr].z; pq[3] += qr * Sv[rr].w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      red[0][rg][col4 * 4 + j] = pk[j];
+      red[1][rg][col4 * 4 + j] = pq[j];
+    }
+    __syncthreads();
+    for (int j = tid; j < D; j += NT) {
+      float pp = 0.f, rq = 0.f;
+#pragma unroll 8
+      for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][j]; rq += red[1][g2][j]; }
+      const float delta = beta * (u_s[2 * D + j] - pp);
+      d_s[j] = delta;
+      st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + j, rq + qk * delta);
+    }
+    __syncthreads();
+    const float d0 = d_s[col4 * 4], d1 = d_s[col4 * 4 + 1], d2 = d_s[col4 * 4 + 2], d3 = d_s[col4 * 4 + 3];
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int r = rg + rr * RPP;
+      if (r < D) {
+        const float kr = u_s[D + r] * ks;
+        Sv[rr].x += kr * d0; Sv[rr].y += kr * d1; Sv[rr].z += kr * d2; Sv[rr].w += kr * d3;
+        if (t + 1 == commit) __builtin_nontemporal_store(Sv[rr], &Sp[static_cast<size_t>(r) * C4 + col4]);
+      }
+    }
+    __syncthreads();   // u_s, e_s, d_s and scal are rewritten by the next token
+  }
+  if (conv_lane && commit > 0) {
+    st<IO_BF16>(io.conv_pool, cb, k0);
+    st<IO_BF16>(io.conv_pool, cb + Ctot, k1);
+    st<IO_BF16>(io.conv_pool, cb + 2 * Ctot, k2);
+  }
+}
+
+template <int D>
+static hipError_t launch_decode_multi_d(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16,
+                                        bool out_bf16, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
+  if (io_bf16 && out_bf16) decode_multi_kernel<D, true, true><<<grid, block, 0, st>>>(p, io, K);
+  else if (io_bf16) decode_multi_kernel<D, true, false><<<grid, block, 0, st>>>(p, io, K);
+  else if (out_bf16) decode_multi_kernel<D, false, true><<<grid, block, 0, st>>>(p, io, K);
+  else decode_multi_kernel<D, false, false><<<grid, block, 0, st>>>(p, io, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_multi(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16, bool out_bf16,
+                               hipStream_t st) {
+  switch (p.D) {
+    case 16: return launch_decode_multi_d<16>(p, io, N, K, io_bf16, out_bf16, st);
+    case 32: return launch_decode_multi_d<32>(p, io, N, K, io_bf16, out_bf16, st);
+    case 64: return launch_decode_multi_d<64>(p, io, N, K, io_bf16, out_bf16, st);
+    case 128: return launch_decode_multi_d<128>(p, io, N, K, io_bf16, out_bf16, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D>
 static hipError_t launch_decode_d(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16,
                                   hipStream_t st) {

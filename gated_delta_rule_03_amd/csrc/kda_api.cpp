@@ -246,6 +246,24 @@ kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, 
   });
 }
 
+kda_status_t kda_decode_multi(const kda_config_t* cfg, int32_t N, int32_t K, const int32_t* slots, const void* q,
+                              const void* k, const void* v, const void* alpha, const void* b, float* state_pool,
+                              void* conv_pool, void* o, const int32_t* n_commit, void* stream) {
+  kda_status_t s = check_config(cfg, false);
+  if (s != KDA_OK) return s;
+  if (N < 0 || K < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (K > 64) return KDA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(N) * cfg->num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !alpha || !b || !state_pool || !conv_pool || !o) return KDA_ERR_INVALID_ARGUMENT;
+  const Params p = make_params(cfg);
+  kda::DecodeMultiIO io{slots, n_commit, q, k, v, alpha, b, state_pool, conv_pool, o};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return stage(cfg, KDA_STAGE_DECODE, st, [&] {
+    return kda::launch_decode_multi(p, io, N, K, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16, st);
+  });
+}
+
 kda_status_t kda_output_gate(const kda_config_t* cfg, int64_t n_tokens, const void* o, const void* gate,
                              const float* o_norm_weight, float eps, void* y, void* stream) {
   if (!cfg) return KDA_ERR_INVALID_ARGUMENT;

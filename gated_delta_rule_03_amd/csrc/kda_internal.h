@@ -151,4 +151,21 @@ struct DecodeIO {
 
 hipError_t launch_decode(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16, hipStream_t st);
 
+// K tokens per sequence through state / conv-history pools.
+struct DecodeMultiIO {
+  const int32_t* slots;      // [N] pool index per sequence (negative: skipped), or null for n
+  const int32_t* n_commit;   // [N] tokens whose updates are kept (0..K), or null for K
+  const void* q;             // [N][K][H*dk]
+  const void* k;
+  const void* v;
+  const void* alpha;         // [N][K][H][dk]
+  const void* b;             // [N][K][H]
+  float* state_pool;         // [P][H][dk][dv]
+  void* conv_pool;           // [P][3][Ctot]
+  void* o;                   // [N][K][H][dv]
+};
+
+hipError_t launch_decode_multi(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16, bool out_bf16,
+                               hipStream_t st);
+
 }  // namespace kda

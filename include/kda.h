@@ -79,7 +79,7 @@ typedef enum kda_stage {
     KDA_STAGE_CHUNK_SCAN = 2,   /* inter-chunk state propagation + chunk output, sequential
                                    (recurrent form: the token-by-token state scan)            */
     KDA_STAGE_CONV_STATE = 3,   /* conv history out                                           */
-    KDA_STAGE_DECODE = 4,       /* the decode step kernel                                     */
+    KDA_STAGE_DECODE = 4,       /* the decode step kernel (also kda_decode_multi)             */
     KDA_STAGE_OUTPUT_GATE = 5,  /* the o_norm + sigmoid output-gate epilogue                  */
     KDA_NUM_STAGES = 6
 } kda_stage_t;
@@ -189,6 +189,37 @@ kda_status_t kda_decode_step(const kda_config_t *cfg, int32_t N,
                              const void *q, const void *k, const void *v,
                              const void *alpha, const void *b,
                              float *state, void *conv_state, void *o, void *stream);
+
+/*
+ * Serving decode: K tokens for each of N sequences whose state and conv
+ * history live in caller-owned pools (AliceAI page, section 五: the
+ * recurrent state and the conv states are what decode carries; section 六:
+ * speculative decoding with MTP drafts one extra token per forward, whose
+ * outputs a verify pass needs before the accepted tokens are kept).
+ *   slots          [N] int32, device: the pool row of each sequence; a
+ *                  negative slot skips the sequence (its outputs are not
+ *                  written).  NULL: sequence n uses row n.  Slots of one call
+ *                  must be distinct.
+ *   q, k           [N][K][H*dk]  io_dtype     v [N][K][H*dv]
+ *   alpha          [N][K][H][dk] io_dtype     b [N][K][H]
+ *   state_pool     [P][H][dk][dv] fp32, device (P > every slot)
+ *   conv_pool      [P][3][Ctot] io_dtype, raw-input history, oldest first
+ *   o              [N][K][H][dv] out_dtype: the outputs of all K tokens,
+ *                  each reading the state updated by the tokens before it
+ *   n_commit       [N] int32, device: keep the updates of the first
+ *                  n_commit[n] tokens (clamped to 0..K): the pools receive
+ *                  the state and conv history after them.  0 leaves the
+ *                  pools untouched (a verify pass); NULL keeps all K.
+ * The state is read once and written at most once per call, so K tokens cost
+ * about the HBM traffic of one decode step.  A rejected draft is rolled back
+ * by committing fewer tokens, e.g. a verify call with n_commit = 0 and then a
+ * call over the accepted tokens only.  K in 1..64.  Needs no workspace.
+ */
+kda_status_t kda_decode_multi(const kda_config_t *cfg, int32_t N, int32_t K, const int32_t *slots,
+                              const void *q, const void *k, const void *v,
+                              const void *alpha, const void *b,
+                              float *state_pool, void *conv_pool, void *o,
+                              const int32_t *n_commit, void *stream);
 
 /*
  * The layer's output epilogue on n_tokens x H rows of dv outputs (AliceAI

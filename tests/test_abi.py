@@ -214,3 +214,22 @@ def test_output_gate_validation(kda):
     assert og(make_cfg(kda, H=4, dk=64, dv=64, A_log=None, conv_w_q=None)[0], 0, None, None, None, 1e-6,
               None) == kda.KDA_OK
     assert c.untouched()
+
+
+def test_decode_multi_validation(kda):
+    lib = kda.library()
+    c = Canary(1 << 12)
+    p = c.ptr
+    cfg, _ = make_cfg(kda)
+    dm = lambda cfg_, N, K, ptrs: lib.kda_decode_multi(ctypes.byref(cfg_), N, K, None, *ptrs, None, None)
+    full = [p] * 8
+    assert dm(cfg, 2, 0, full) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert dm(cfg, -1, 2, full) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert dm(cfg, 2, 65, full) == kda.KDA_ERR_UNSUPPORTED
+    for missing in range(8):
+        ptrs = list(full)
+        ptrs[missing] = None
+        assert dm(cfg, 2, 3, ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert dm(cfg, 0, 3, [None] * 8) == kda.KDA_OK
+    assert dm(make_cfg(kda, dv=32)[0], 2, 3, full) == kda.KDA_ERR_UNSUPPORTED
+    assert c.untouched()
