@@ -236,6 +236,59 @@ def bench_decode(kda, torch, ev, n_steps=128, warmup=3):
                          "bytes_per_launch": bytes_step}}
 
 
+def bench_decode_multi(kda, torch, ev, n_calls=64, warmup=3, K=2):
+    """Serving decode with one MTP draft: 256 sequences x K = 2 tokens through
+    slots into a pool of 320 rows, the draft of every other sequence
+    rejected (commit 1 or 2)."""
+    from kda_inputs import BF16, make_params
+    from kda_inputs.device_gen import device_tokens
+    from kda_inputs.torch_io import make_config
+    dev = torch.device("cuda:0")
+    N, P, wid = 256, 320, 6
+
+    class Prm:
+        pass
+    p = Prm()
+    p.H, p.dk, p.dv, p.io = H, D, D, BF16
+    p.w_q, p.w_k, p.w_v, p.A_log, p.dt_bias = make_params(wid, H, D, D, BF16)
+    cfg = make_config(p, dev, torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(6_000_029)
+    S = (torch.randn((P, H, D, D), generator=g, device=dev) * 0.02).contiguous()
+    cs = torch.randn((P, 3, H * 3 * D), generator=g, device=dev).to(torch.bfloat16)
+    slots = torch.randperm(P, generator=g, device=dev)[:N].to(torch.int32)
+    commit = (1 + torch.arange(N, device=dev) % 2).to(torch.int32)
+    calls = []
+    for c in range(n_calls):
+        t = device_tokens(wid, N * K, H, D, D, BF16, dev, step=c + 1)
+        calls.append((t[0].view(N, K, -1), t[1].view(N, K, -1), t[2].view(N, K, -1), t[3].view(N, K, H, D),
+                      t[4].view(N, K, H)))
+    o = torch.empty((N, K, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        kda.kda_decode_multi(cfg, *calls[i], S, cs, slots=slots, n_commit=commit, o=o, stream=stream)
+    st = kda.STAGES.index("decode")
+    arrays = [ev.stage_array([st]) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for i in range(n_calls):
+        cfg.stage_events = arrays[i]
+        kda.kda_decode_multi(cfg, *calls[i], S, cs, slots=slots, n_commit=commit, o=o, stream=stream)
+    torch.cuda.synchronize()
+    cfg.stage_events = None
+    us = [1e3 * ev.ms(a[2 * st], a[2 * st + 1]) for a in arrays]
+    mean_us = sum(us) / len(us)
+    ctot = H * 3 * D
+    nbytes = (2 * N * H * D * D * 4 + 2 * N * 3 * ctot * 2 + N * K * (ctot + H * D + H) * 2 + N * K * H * D * 2)
+    gbs = nbytes / (mean_us * 1e-6) / 1e9
+    log(f"[bench] decode multi (K={K}): mean {mean_us:.1f} us/call, {gbs:.0f} GB/s")
+    return {"workload": f"kda serving decode, 256 sequences x {K} tokens (one MTP draft) through slots of a 320-row "
+                        "pool, commit 1 or 2, H=32, dk=dv=128, bf16 in, fp32 state",
+            "us_per_call": round(mean_us, 2), "us_per_token_step": round(mean_us / K, 2),
+            "roofline": {"kernel": "decode_multi", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": nbytes}}
+
+
 def bench_varlen(kda, torch, ev, steps=3, warmup=1):
     from kda_inputs import BF16, VARLEN_LENGTHS
     from kda_inputs.device_gen import DeviceProblem
@@ -433,6 +486,7 @@ def main():
     }
     if not args.no_extras:
         result["decode"] = bench_decode(kda, torch, ev)
+        result["decode_multi"] = bench_decode_multi(kda, torch, ev)
         result["varlen"] = bench_varlen(kda, torch, ev)
         result["prefill_no_clamp"] = bench_prefill_no_clamp(kda, torch, ev, dp)
         result["output_gate"] = bench_output_gate(kda, torch, ev)

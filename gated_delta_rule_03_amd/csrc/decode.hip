@@ -24,6 +24,8 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // Eight waves per (sequence, head): a 64 KB in-place tile streams measurably
 // faster with 512 threads than with 256 (more bytes in flight per workgroup).
 constexpr int kDecodeThreads = 512;
+// Tokens whose inputs the multi-token decode stages at once.
+constexpr int kMultiGroup = 8;
 
 template <int D, bool IO_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, DecodeIO io) {
@@ -172,9 +174,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
   constexpr int C4 = D / 4;
   constexpr int RPP = NT / C4;
   constexpr int RPT = (D + RPP - 1) / RPP;
-  static_assert(3 * D <= NT, "one conv channel per thread");
+  constexpr int KG = kMultiGroup;
+  static_assert(3 * D <= NT && D <= NT, "one conv channel and one gate channel per thread");
+  __shared__ float x_s[KG][3 * D];   // raw q | k | v of a group of tokens
+  __shared__ float eg_s[KG][D];      // exp(g) of the group's tokens
+  __shared__ float b_s[KG];          // beta of the group's tokens
   __shared__ float u_s[3 * D];
-  __shared__ float e_s[D];
   __shared__ float red[2][RPP][D];
   __shared__ float d_s[D];
   __shared__ float scal[4];
@@ -217,90 +222,107 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
   }
   float k0 = h0, k1 = h1, k2 = h2;   // the window after the committed tokens
   const float a_exp = expf(p.A_log[h]);
+  const float dtb = tid < D ? p.dt_bias[h * D + tid] : 0.f;
 
-  for (int t = 0; t < K; ++t) {
-    const size_t tok = static_cast<size_t>(n) * K + t;
-    if (conv_lane) {
-      const float xt = ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci);
-      u_s[tid] = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h0 + w1 * h1 + w2 * h2 + w3 * xt);
-      h0 = h1; h1 = h2; h2 = xt;
-      if (t + 1 == commit) { k0 = h0; k1 = h1; k2 = h2; }
-    }
-    for (int i = tid; i < D; i += NT) {
-      const float al = ld<IO_BF16>(io.alpha, tok * HD + static_cast<size_t>(h) * D + i);
-      const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, p.dt_bias[h * D + i], a_exp, p.lower_bound);
-      e_s[i] = expf(g);
-    }
-    if (tid == 0) {
-      const float bb = ld<IO_BF16>(io.b, tok * H + h);
-      float be = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
-      if (flags & KDA_FLAG_BETA_X2) be *= 2.0f;
-      scal[2] = be;
-    }
-    __syncthreads();
+  for (int t0 = 0; t0 < K; t0 += KG) {
+    // the group's raw inputs, gates and betas, all loads issued together (the
+    // first group's right behind the state loads); the token loop below then
+    // touches global memory only to store outputs
+    const int kg = min(KG, K - t0);
     {
-      const int wv = tid / kWave, lane = tid % kWave;
-      if (wv < 3) {
-        float sum = 0.0f;
-        for (int i = lane; i < D; i += kWave) {
-          const float a = u_s[(wv == 1 ? D : 0) + i];
-          const float b2 = u_s[(wv == 0 ? 0 : D) + i];
-          sum += a * b2;
+      float xr[KG], ar[KG];
+      float br = 0.f;
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        const size_t tok = static_cast<size_t>(n) * K + t0 + min(j, kg - 1);
+        xr[j] = conv_lane ? ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci) : 0.f;
+        ar[j] = tid < D ? ld<IO_BF16>(io.alpha, tok * HD + static_cast<size_t>(h) * D + tid) : 0.f;
+      }
+      if (tid < kg) br = ld<IO_BF16>(io.b, (static_cast<size_t>(n) * K + t0 + tid) * H + h);
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        if (conv_lane) x_s[j][tid] = xr[j];
+        if (tid < D) {
+          const float g = (flags & KDA_FLAG_RAW_GATE) ? ar[j] : gate_value(ar[j], dtb, a_exp, p.lower_bound);
+          eg_s[j][tid] = expf(g);
         }
-        sum = group_sum<kWave>(sum);
-        if (lane == 0) scal[wv == 2 ? 3 : wv] = sum;
+      }
+      if (tid < kg) {
+        float be = (flags & KDA_FLAG_RAW_BETA) ? br : sigmoidf_(br);
+        if (flags & KDA_FLAG_BETA_X2) be *= 2.0f;
+        b_s[tid] = be;
       }
     }
     __syncthreads();
-    if (tid == 0) {
+
+    for (int j = 0; j < kg; ++j) {
+      const int t = t0 + j;
+      const size_t tok = static_cast<size_t>(n) * K + t;
+      if (conv_lane) {
+        const float xt = x_s[j][tid];
+        u_s[tid] = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h0 + w1 * h1 + w2 * h2 + w3 * xt);
+        h0 = h1; h1 = h2; h2 = xt;
+        if (t + 1 == commit) { k0 = h0; k1 = h1; k2 = h2; }
+      }
+      __syncthreads();
+      {
+        const int wv = tid / kWave, lane = tid % kWave;
+        if (wv < 3) {
+          float sum = 0.0f;
+          for (int i = lane; i < D; i += kWave) {
+            const float a = u_s[(wv == 1 ? D : 0) + i];
+            const float b2 = u_s[(wv == 0 ? 0 : D) + i];
+            sum += a * b2;
+          }
+          sum = group_sum<kWave>(sum);
+          if (lane == 0) scal[wv == 2 ? 3 : wv] = sum;
+        }
+      }
+      __syncthreads();
       const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
       const float iq = norm ? 1.0f / sqrtf(scal[0] + p.eps) : 1.0f;
       const float ik = norm ? 1.0f / sqrtf(scal[1] + p.eps) : 1.0f;
-      scal[3] = scal[3] * iq * ik * p.scale;
-      scal[0] = iq * p.scale;
-      scal[1] = ik;
-    }
-    __syncthreads();
-    const float qs = scal[0], ks = scal[1], beta = scal[2], qk = scal[3];
+      const float qs = iq * p.scale, ks = ik, beta = b_s[j], qk = scal[3] * iq * ik * p.scale;
 
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+      float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-      const int r = rg + rr * RPP;
-      if (r < D) {
-        const float e = e_s[r];
-        Sv[rr].x *= e; Sv[rr].y *= e; Sv[rr].z *= e; Sv[rr].w *= e;
-        const float kr = u_s[D + r] * ks, qr = u_s[r] * qs;
-        pk[0] += kr * Sv[rr].x; pk[1] += kr * Sv[rr].y; pk[2] += kr * Sv[rr].z; pk[3] += kr * Sv[rr].w;
-        pq[0] += qr * Sv[rr].x; pq[1] += qr * Sv[rr].y; pq[2] += qr * Sv[rr].z; pq[3] += qr * Sv[rr].w;
+      for (int rr = 0; rr < RPT; ++rr) {
+        const int r = rg + rr * RPP;
+        if (r < D) {
+          const float e = eg_s[j][r];
+          Sv[rr].x *= e; Sv[rr].y *= e; Sv[rr].z *= e; Sv[rr].w *= e;
+          const float kr = u_s[D + r] * ks, qr = u_s[r] * qs;
+          pk[0] += kr * Sv[rr].x; pk[1] += kr * Sv[rr].y; pk[2] += kr * Sv[rr].z; pk[3] += kr * Sv[rr].w;
+          pq[0] += qr * Sv[rr].x; pq[1] += qr * Sv[rr].y; pq[2] += qr * Sv[rr].z; pq[3] += qr * Sv[rr].w;
+        }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      red[0][rg][col4 * 4 + j] = pk[j];
-      red[1][rg][col4 * 4 + j] = pq[j];
-    }
-    __syncthreads();
-    for (int j = tid; j < D; j += NT) {
-      float pp = 0.f, rq = 0.f;
+      for (int jj = 0; jj < 4; ++jj) {
+        red[0][rg][col4 * 4 + jj] = pk[jj];
+        red[1][rg][col4 * 4 + jj] = pq[jj];
+      }
+      __syncthreads();
+      for (int c = tid; c < D; c += NT) {
+        float pp = 0.f, rq = 0.f;
 #pragma unroll 8
-      for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][j]; rq += red[1][g2][j]; }
-      const float delta = beta * (u_s[2 * D + j] - pp);
-      d_s[j] = delta;
-      st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + j, rq + qk * delta);
-    }
-    __syncthreads();
-    const float d0 = d_s[col4 * 4], d1 = d_s[col4 * 4 + 1], d2 = d_s[col4 * 4 + 2], d3 = d_s[col4 * 4 + 3];
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-      const int r = rg + rr * RPP;
-      if (r < D) {
-        const float kr = u_s[D + r] * ks;
-        Sv[rr].x += kr * d0; Sv[rr].y += kr * d1; Sv[rr].z += kr * d2; Sv[rr].w += kr * d3;
-        if (t + 1 == commit) __builtin_nontemporal_store(Sv[rr], &Sp[static_cast<size_t>(r) * C4 + col4]);
+        for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][c]; rq += red[1][g2][c]; }
+        const float delta = beta * (u_s[2 * D + c] - pp);
+        d_s[c] = delta;
+        st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + c, rq + qk * delta);
       }
+      __syncthreads();
+      const float d0 = d_s[col4 * 4], d1 = d_s[col4 * 4 + 1], d2 = d_s[col4 * 4 + 2], d3 = d_s[col4 * 4 + 3];
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        const int r = rg + rr * RPP;
+        if (r < D) {
+          const float kr = u_s[D + r] * ks;
+          Sv[rr].x += kr * d0; Sv[rr].y += kr * d1; Sv[rr].z += kr * d2; Sv[rr].w += kr * d3;
+          if (t + 1 == commit) __builtin_nontemporal_store(Sv[rr], &Sp[static_cast<size_t>(r) * C4 + col4]);
+        }
+      }
+      __syncthreads();   // u_s, d_s and scal are rewritten by the next token, x_s / eg_s by the next group
     }
-    __syncthreads();   // u_s, e_s, d_s and scal are rewritten by the next token
   }
   if (conv_lane && commit > 0) {
     st<IO_BF16>(io.conv_pool, cb, k0);
