@@ -285,7 +285,8 @@ def bench_decode_multi(kda, torch, ev, n_calls=64, warmup=3, K=2):
                         "pool, commit 1 or 2, H=32, dk=dv=128, bf16 in, fp32 state",
             "us_per_call": round(mean_us, 2), "us_per_token_step": round(mean_us / K, 2),
             "roofline": {"kernel": "decode_multi", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_multi"),
                          "bytes_per_launch": nbytes}}
 
 
@@ -409,7 +410,7 @@ def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
                          "bytes_per_launch": nbytes}}
 
 
-def cpu_baseline(dp, seqs=2):
+def cpu_baseline(dp, seqs=4):
     """The fp64 oracle on the first `seqs` sequences of the prefill workload
     (all heads, full length), on all host cores."""
     import numpy as np

@@ -245,3 +245,17 @@ def test_prefill_then_decode_continues_long_prefill(kda):
     assert max_over_rms(o_cat, o_full.double().cpu().numpy()) <= 2e-3
     assert rel_fro(S.double().cpu().numpy(), S_full.double().cpu().numpy()) <= 1e-3
     assert torch.equal(cs, cs_full)
+
+
+@pytest.mark.parametrize("io", [BF16, FP32])
+def test_more_than_1024_sequences(kda, io):
+    """2500 packed sequences of 0..5 tokens: the chunk table's exclusive scan
+    runs over several 1024-sequence passes, empty sequences share chunk
+    indices, and every sequence passes its state and conv history through its
+    own short chunk."""
+    lens = np.random.default_rng(2500).integers(0, 6, size=2500).tolist()
+    d = 64 if io == BF16 else 32
+    p = make_problem(2500 + (io == FP32), lens, 2, d, d, io, state_seqs=list(range(0, 2500, 3)), state_std=0.2,
+                     conv_state=True)
+    o, S, cs = run_varlen(kda, p)
+    assert_parity(p, o, S, cs)
