@@ -124,3 +124,16 @@ def test_multi_serving_shape(kda):
     o_ref, S_ref, c_ref = oracle.decode_multi_reference(pool.state, pool.conv_state, slots, toks, params, H, d, d,
                                                         BF16, K, n_commit=commit)
     check(pool, BF16, o, S, cs, o_ref, S_ref, c_ref, list(range(N)), slots)
+
+
+def test_multi_across_staging_groups(kda):
+    """K = 19 tokens: the inputs are staged eight tokens at a time (groups of
+    8, 8 and 3), and the commit counts fall inside and on group edges."""
+    N, K, P, H, d = 6, 19, 7, 4, 128
+    pool, cfg, S, cs, toks, dtoks, params = setup(2000, N, K, P, H, d, BF16)
+    slots, commit = [5, 0, 6, 2, 1, 3], [0, 7, 8, 9, 16, 19]
+    o = kda.kda_decode_multi(cfg, *dtoks, S, cs, slots=i32(slots), n_commit=i32(commit))
+    torch.cuda.synchronize()
+    o_ref, S_ref, c_ref = oracle.decode_multi_reference(pool.state, pool.conv_state, slots, toks, params, H, d, d,
+                                                        BF16, K, n_commit=commit)
+    check(pool, BF16, o, S, cs, o_ref, S_ref, c_ref, list(range(N)), [0, 6, 2, 1, 3])
