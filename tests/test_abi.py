@@ -233,3 +233,12 @@ def test_decode_multi_validation(kda):
     assert dm(cfg, 0, 3, [None] * 8) == kda.KDA_OK
     assert dm(make_cfg(kda, dv=32)[0], 2, 3, full) == kda.KDA_ERR_UNSUPPORTED
     assert c.untouched()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with a message
+    before touching any device."""
+    r = subprocess.run([os.sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
