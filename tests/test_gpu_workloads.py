@@ -60,12 +60,12 @@ def test_prefill_4k_every_head(kda, out):
     assert np.array_equal(as_f64(from_torch_bf16(cs), BF16), c_ref)
 
 
-def _sampled_check(dp, o, S_out, items, label):
+def _sampled_check(dp, o, S_out, items, label, **oracle_kw):
     o_all, ref_all = [], []
     cu = dp.cu_seqlens
     for n, h in items:
         hp = dp.head_problem(n, h)
-        o_ref, S_ref, _, _ = oracle.forward(hp, with_conv_out=False)
+        o_ref, S_ref, _, _ = oracle.forward(hp, with_conv_out=False, **oracle_kw)
         og = o[cu[n]:cu[n + 1], h].double().cpu().numpy()
         o_all.append(og)
         ref_all.append(o_ref[:, 0])
@@ -96,6 +96,26 @@ def test_prefill_32k_sampled(kda):
         last = torch.cat([tz["q"][(n + 1) * T - 3:(n + 1) * T], tz["k"][(n + 1) * T - 3:(n + 1) * T],
                           tz["v"][(n + 1) * T - 3:(n + 1) * T]], dim=1)
         assert torch.equal(cs[n], last)
+
+
+def test_prefill_32k_no_clamp_sampled(kda):
+    """The 32K prefill with the gate's clamp off (lower bound -inf), in the
+    launch configuration the benchmark times: the recurrent form."""
+    from kda_inputs.device_gen import DeviceProblem
+    dev = torch.device("cuda:0")
+    B, T = 4, 32768
+    dp = DeviceProblem(3, [T] * B, H, D, D, BF16, dev, state_seqs=list(range(B)))
+    cfg = dp.config(out_dtype=torch.bfloat16, gate_lower_bound=float("-inf"))
+    tz = dp.tensors
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((B, H, D, D), device=dev)
+    kda.kda_prefill(cfg, tz["q"].view(B, T, -1), tz["k"].view(B, T, -1), tz["v"].view(B, T, -1),
+                    tz["alpha"].view(B, T, H, D), tz["b"].view(B, T, H), tz["initial_state"], tz["conv_state"],
+                    o=o, final_state=S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    _sampled_check(dp, o.view(B * T, H, D), S, [(0, 3), (1, 17), (2, 30), (3, 8)], "32K prefill without clamp",
+                   lower_bound=float("-inf"))
 
 
 def test_varlen_262k_sampled(kda):
