@@ -106,3 +106,20 @@ def test_recurrent_form_matches_chunked_above_floor(kda):
     assert_parity(p, o_r, S_r, None)
     scale = float(torch.sqrt(torch.mean(o_c.double() ** 2)))
     assert float((o_r - o_c).abs().max()) <= 2e-5 * scale
+
+
+@pytest.mark.parametrize("lower_bound", [-5.0, NO_CLAMP])
+def test_state_and_conv_history_updated_in_place(kda, lower_bound):
+    """final_state may alias initial_state and conv_state_out may alias
+    conv_state_in (both prefill forms): the call continues in place."""
+    from kda_inputs.torch_io import problem_to_device
+    p = make_problem(990, [300, 1, 70, 0, 129], 4, 128, 128, BF16, state_seqs=[0, 1, 2, 3, 4], state_std=0.3,
+                     conv_state=True)
+    strong_gates(p, [2.5, 0.0, 1.4, -1.0])
+    dev = torch.device("cuda:0")
+    cfg, t = problem_to_device(p, dev, out_dtype=torch.float32, gate_lower_bound=lower_bound)
+    S, cs = t["initial_state"], t["conv_state"]
+    o, _, _ = kda.kda_varlen_prefill(cfg, t["cu_seqlens"], t["q"], t["k"], t["v"], t["alpha"], t["b"], S, cs,
+                                     final_state=S, conv_state_out=cs)
+    torch.cuda.synchronize()
+    assert_parity(p, o, S, cs, oracle_kw={"lower_bound": lower_bound})
