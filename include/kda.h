@@ -24,6 +24,14 @@
  * (AliceAI page, section 四: kernel-1 = 3 history elements), stored oldest
  * first with channels ordered q | k | v:  Ctot = H * (2*dk + dv).
  *
+ * Entry points: kda_prefill (B equal-length sequences) and kda_varlen_prefill
+ * (packed sequences), each in the chunked form or, for gates below -5.4, the
+ * token recurrence; kda_decode_step (one token per sequence, in place);
+ * kda_decode_multi (K tokens per sequence through state / conv-history pools,
+ * with commit counts for speculative decoding); kda_output_gate (the layer's
+ * o_norm x sigmoid output epilogue); plus the workspace queries, the version
+ * and status strings.
+ *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, contiguous, row-major in the
  *    layout given, 16-byte aligned.  The caller owns every buffer; the library
