@@ -138,3 +138,22 @@ def test_output_gate_after_decode(kda):
     params = (dp.w_q, dp.w_k, dp.w_v, dp.A_log, dp.dt_bias)
     o_ref, _, _ = oracle.decode_reference(dp.state, dp.conv_state, toks, params, dp.H, dp.dk, dp.dv, dp.io)
     check_composed(y, o_ref, as_f64(gate, BF16), w, 2e-3, o_bf16=True)
+
+
+def test_output_gate_grid_stride(kda):
+    """17.3 M rows of 16 (270000 tokens x 64 heads): more rows than the
+    launch's 2^20 workgroups cover at once, so groups stride over rows."""
+    n, H, d = 270000, 64, 16
+    assert n * H > (1 << 20) * 16
+    dev = torch.device("cuda:0")
+    cfg = epilogue_cfg(H, d, BF16, BF16)
+    o = make_epilogue_o(1250, n, H, d, BF16)
+    gate, w = make_output_gate_inputs(1250, n, H, d, BF16)
+    y = kda.kda_output_gate(cfg, to_torch(o, BF16, dev), to_torch(gate, BF16, dev), torch.from_numpy(w).to(dev))
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.random.default_rng(6).choice(n * H, size=4096, replace=False),
+                           np.arange(n * H - 64, n * H), np.arange((1 << 20) * 16 - 32, (1 << 20) * 16 + 32)])
+    y_rows = from_torch_bf16(y).reshape(n * H, d)[rows]
+    ref = oracle.output_gate(as_f64(o.reshape(n * H, d)[rows], BF16), as_f64(gate.reshape(n * H, d)[rows], BF16), w)
+    ok, e = check_bf16_output(as_f64(y_rows, BF16), ref, 1e-5)
+    assert ok, f"bf16 y error {e:.3e}"
