@@ -71,7 +71,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
 
   // head-fastest order: the resident workgroups cover every head of a few
   // chunks, so each raw token row is read whole while it is open in DRAM
-  const int h = blockIdx.x, c = blockIdx.y;
+  // one-dimensional grid, head fastest (grid dimension y holds at most 65536)
+  const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
+  const int c = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   if (c >= t.chunk0[t.N]) return;
   const int H = p.H;
   const int s = t.chunk_seq[c];
@@ -427,7 +429,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
 template <int D>
 static hipError_t launch_prep_d(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                                 int max_chunks, bool io_bf16, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(p.H), static_cast<unsigned>(max_chunks));
+  const int64_t blocks = static_cast<int64_t>(p.H) * max_chunks;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (io_bf16) chunk_prep_kernel<D, true><<<grid, kPrepThreads, 0, st>>>(p, t, io, records);
   else chunk_prep_kernel<D, false><<<grid, kPrepThreads, 0, st>>>(p, t, io, records);
   return hipGetLastError();

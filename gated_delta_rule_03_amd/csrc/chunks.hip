@@ -137,9 +137,12 @@ hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_unifor
 
 template <bool IO_BF16>
 __global__ __launch_bounds__(256) void conv_state_out_kernel(ChunkTable t, PrefillIO io, int H, int D) {
-  const int s = blockIdx.y;
+  // one-dimensional grid: bps blocks of 256 channels per sequence (grid
+  // dimension y holds at most 65536 sequences)
   const size_t Ctot = static_cast<size_t>(3) * H * D;
-  const size_t c = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const unsigned bps = static_cast<unsigned>((Ctot + 255) / 256);
+  const int s = static_cast<int>(blockIdx.x / bps);
+  const size_t c = static_cast<size_t>(blockIdx.x % bps) * 256 + threadIdx.x;
   if (c >= Ctot) return;
   const int64_t t0 = t.cu[s];
   const int L = t.cu[s + 1] - t.cu[s];
@@ -161,7 +164,9 @@ __global__ __launch_bounds__(256) void conv_state_out_kernel(ChunkTable t, Prefi
 hipError_t launch_conv_state_out(const Params& p, const ChunkTable& t, const PrefillIO& io, bool io_bf16,
                                  hipStream_t st) {
   const size_t Ctot = static_cast<size_t>(3) * p.H * p.D;
-  const dim3 grid(static_cast<unsigned>((Ctot + 255) / 256), static_cast<unsigned>(t.N));
+  const int64_t blocks = static_cast<int64_t>((Ctot + 255) / 256) * t.N;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (io_bf16) conv_state_out_kernel<true><<<grid, 256, 0, st>>>(t, io, p.H, p.D);
   else conv_state_out_kernel<false><<<grid, 256, 0, st>>>(t, io, p.H, p.D);
   return hipGetLastError();

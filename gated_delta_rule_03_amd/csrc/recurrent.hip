@@ -54,7 +54,9 @@ __global__ __launch_bounds__(4 * D) void token_prep_kernel(Params p, ChunkTable 
   __shared__ __align__(16) float sQ[kChunk * LQ];
   __shared__ __align__(16) float sK[kChunk * LQ];
 
-  const int h = blockIdx.x, c = blockIdx.y;
+  // one-dimensional grid, head fastest (grid dimension y holds at most 65536)
+  const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
+  const int c = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   if (c >= t.chunk0[t.N]) return;
   const int H = p.H;
   const int4 dsc = t.desc[c];      // (sequence, first token in it, tokens, first packed token)
@@ -346,7 +348,9 @@ __global__ __launch_bounds__(kWave * NW) void recurrent_scan_kernel(Params p, co
 template <int D>
 static hipError_t launch_token_prep_d(const Params& p, const ChunkTable& t, const PrefillIO& io, float* recs,
                                       int64_t total_T, int max_chunks, bool io_bf16, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(p.H), static_cast<unsigned>(max_chunks));
+  const int64_t blocks = static_cast<int64_t>(p.H) * max_chunks;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (io_bf16)
     token_prep_kernel<D, true><<<grid, 4 * D, 0, st>>>(p, t, recs, total_T, io.conv_in, io.q, io.k, io.v, io.alpha, io.b);
   else

@@ -258,3 +258,16 @@ def test_more_than_1024_sequences(kda, io):
                      conv_state=True)
     o, S, cs = run_varlen(kda, p)
     assert_parity(p, o, S, cs)
+
+
+@pytest.mark.parametrize("lower_bound", [-5.0, float("-inf")])
+def test_more_chunks_and_sequences_than_a_grid_dimension(kda, lower_bound):
+    """70000 packed sequences of 0..2 tokens (fp32, dk = 16, one head): more
+    chunks and more sequences than the 65536 a grid's second dimension holds,
+    through the chunk prep (or the recurrent form's token pre-pass) and the
+    conv-history writer."""
+    lens = np.random.default_rng(70000).integers(0, 3, size=70000).tolist()
+    p = make_problem(7000, lens, 1, 16, 16, FP32, state_seqs=list(range(0, 70000, 7)), state_std=0.3,
+                     conv_state=True)
+    o, S, cs = run_varlen(kda, p, gate_lower_bound=lower_bound)
+    assert_parity(p, o, S, cs, oracle_kw={"lower_bound": lower_bound})
