@@ -1048,14 +1048,9 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 template <int D>
 static hipError_t launch_rows_d(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                                 int max_chunks, hipStream_t st) {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  int& ncu = cus[dev & 63];
-  if (ncu == 0) {
-    const hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
+  int ncu = 0;
+  const hipError_t e = device_cus(&ncu);
+  if (e != hipSuccess) return e;
   // one resident workgroup per compute unit; each walks the chunks of one head
   int groups = (ncu + p.H - 1) / p.H;
   groups = groups < 1 ? 1 : (groups > max_chunks ? max_chunks : groups);

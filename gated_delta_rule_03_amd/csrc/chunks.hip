@@ -107,18 +107,13 @@ __global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __re
   desc[c] = make_int4(lo, tau0, min(kChunk, cu[lo + 1] - tok0), tok0);
 }
 
+// The compute-unit count of the current device, queried on every call (the
+// runtime answers from its own device table): the library keeps no state.
 hipError_t device_cus(int* ncu) {
-  static int cus[64] = {0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int& n = cus[dev & 63];
-  if (n == 0) {
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
-  *ncu = n;
-  return hipSuccess;
+  return hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev);
 }
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws, int32_t* chunk0,

@@ -45,6 +45,10 @@ MUTANTS = {
     "ogate_sign": ("orow[j] / rms * w[j] * orc_sigmoid(grow[j]);", "orow[j] / rms * w[j] * orc_sigmoid(-grow[j]);"),
     "ogate_row0": ("const double *grow = gate + (size_t)r * dv;", "const double *grow = gate;"),
     "ogate_silu": ("orow[j] / rms * w[j] * orc_sigmoid(grow[j]);", "orow[j] / rms * w[j] * grow[j] * orc_sigmoid(grow[j]);"),
+    "skip_conv_applies_silu": ("val = x[(size_t)t * row + c];",
+                               "val = x[(size_t)t * row + c] * orc_sigmoid(x[(size_t)t * row + c]);"),
+    "raw_gate_clamped": ("gi = al;", "gi = al < lb ? lb : al;"),
+    "raw_beta_sigmoid": ("(flags & ORC_FLAG_RAW_BETA) ? bb : orc_sigmoid(bb)", "orc_sigmoid(bb)"),
     "state_not_loaded": ("memcpy(S, J->S0 + ((size_t)n * H + h) * dk * dv, sizeof(double) * (size_t)dk * dv);",
                          "memset(S, 0, sizeof(double) * (size_t)dk * dv);"),
 }
@@ -65,6 +69,9 @@ CHECKS = [
     lambda: pins.test_gate_special_values(None),
     lambda: pins.test_beta_is_sigmoid(None),
     lambda: pins.test_conv_state_out_short_sequences(None),
+    lambda: pins.test_skip_conv_passes_raw_inputs(None),
+    lambda: pins.test_raw_gate_is_alpha_unclamped(None),
+    lambda: pins.test_raw_beta_is_b(None),
     lambda: pins.test_forward_equals_preprocess_then_recurrence(None),
     lambda: pins.test_output_gate_unit_rms_and_scale_invariance(None),
     lambda: pins.test_output_gate_eps_inside_the_root(None),

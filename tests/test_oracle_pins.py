@@ -214,6 +214,58 @@ def test_beta_is_sigmoid(oracle_lib):
     assert np.all(beta0 == 0.5)
 
 
+# ---------------------------------------------------------------- test hooks
+# The flags that feed the recurrence post-activation inputs.  Each hook must
+# hand its input through untouched: no conv, no SiLU, no clamp, no sigmoid.
+
+def test_skip_conv_passes_raw_inputs(oracle_lib):
+    p = small_problem(14, [23], H=2, dk=8, dv=6, state=False, conv=True)
+    for h in range(2):
+        qh, kh, vh, _, _ = oracle.preprocess_head(p, 0, h,
+                                                  flags=oracle.FLAG_SKIP_CONV | oracle.FLAG_SKIP_L2NORM)
+        for got, x, d in ((qh, p.q, 8), (kh, p.k, 8), (vh, p.v, 6)):
+            assert np.array_equal(got, as_f64(x, p.io)[:, h * d:(h + 1) * d])
+    # with the L2 norm on, SKIP_CONV fed SiLU(conv(x)) (computed by torch's
+    # conv1d, stored as fp32) reproduces the default path from raw x up to
+    # that fp32 rounding of the activations
+    p2 = small_problem(15, [31], H=2, dk=8, dv=6, state=False, conv=False)
+    acts = []
+    for x, w in ((p2.q, p2.w_q), (p2.k, p2.w_k), (p2.v, p2.w_v)):
+        u, _ = _torch_conv_silu(as_f64(x, p2.io), as_f64(w, p2.io))
+        acts.append(np.ascontiguousarray(u, dtype=np.float32))
+    pre = Problem(p2.seqlens, p2.H, p2.dk, p2.dv, FP32, acts[0], acts[1], acts[2], p2.alpha, p2.b,
+                  p2.w_q, p2.w_k, p2.w_v, p2.A_log, p2.dt_bias)
+    for h in range(2):
+        ref = oracle.preprocess_head(p2, 0, h)
+        got = oracle.preprocess_head(pre, 0, h, flags=oracle.FLAG_SKIP_CONV)
+        for a, b in zip(got, ref):
+            assert np.allclose(a, b, rtol=2e-6, atol=1e-7)
+
+
+def test_raw_gate_is_alpha_unclamped(oracle_lib):
+    p = small_problem(16, [12], H=2, dk=8, dv=8, state=False, conv=False)
+    r = np.random.default_rng(16)
+    p.alpha = r.uniform(-30.0, 0.5, size=p.alpha.shape).astype(np.float32)   # far below the -5 bound
+    p.alpha[0, 0, :3] = [-5.0, -5.0000001, 0.0]
+    for h in range(2):
+        _, _, _, g, _ = oracle.preprocess_head(p, 0, h, flags=oracle.FLAG_RAW_GATE)
+        assert np.array_equal(g, p.alpha[:, h, :].astype(np.float64))
+        _, _, _, g2, _ = oracle.preprocess_head(p, 0, h, flags=oracle.FLAG_RAW_GATE, lower_bound=-1.0)
+        assert np.array_equal(g2, g)
+    assert (p.alpha < -5.0).any()
+
+
+def test_raw_beta_is_b(oracle_lib):
+    p = small_problem(17, [15], H=3, dk=4, dv=4, state=False, conv=False)
+    r = np.random.default_rng(17)
+    p.b = r.uniform(-0.5, 1.5, size=p.b.shape).astype(np.float32)
+    for h in range(3):
+        _, _, _, _, beta = oracle.preprocess_head(p, 0, h, flags=oracle.FLAG_RAW_BETA)
+        assert np.array_equal(beta, p.b[:, h].astype(np.float64))
+        _, _, _, _, beta2 = oracle.preprocess_head(p, 0, h, flags=oracle.FLAG_RAW_BETA | oracle.FLAG_BETA_X2)
+        assert np.array_equal(beta2, 2.0 * p.b[:, h].astype(np.float64))
+
+
 # ---------------------------------------------------------------- whole forward
 def test_forward_equals_preprocess_then_recurrence(oracle_lib):
     p = small_problem(9, [33, 17], H=2, dk=8, dv=6)
