@@ -32,25 +32,23 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix
 CHUNK = 64
 
-# Algorithmic work per chunk-head (C = 64 tokens of one head), d = 128, from
-# the chunked form's operation count (per token-head: 2C(3dk + 2dv) + 6 dk dv
-# + 2C^2/3 FLOPs in total):
-#   chunk_prep  A, Aqk, W, U and the solve:      C * (2C(3dk + dv) + 2C^2/3)
-#   chunk_scan  W S, K~^T Delta, Q+ S, Aqk Delta: C * (6 dk dv + 2 C dv)
-# and the bytes each stage must move at least: prep reads the raw bf16 q, k,
-# v, alpha (4 x 2d per token-head) and b, and writes its per-chunk record;
-# scan reads the record and writes o (bf16).
-FLOPS_PER_CHUNK_HEAD = {
-    "chunk_prep": CHUNK * (2 * CHUNK * (3 * D + D) + 2 * CHUNK * CHUNK / 3.0),
-    "chunk_scan": CHUNK * (6.0 * D * D + 2.0 * CHUNK * D),
-}
-# one record per chunk-head, fp32-equivalent: W, Q+, K~^T, U^T (64 x d each),
-# the lower triangle of Aqk with its diagonal, e^{G_C}
-RECORD_BYTES = 4 * 64 * D * 4 + (64 * 65 // 2) * 4 + D * 4
-BYTES_PER_CHUNK_HEAD = {
-    "chunk_prep": CHUNK * (4 * 2 * D + 2) + RECORD_BYTES,
-    "chunk_scan": RECORD_BYTES + CHUNK * 2 * D,
-}
+# Algorithmic work of the chunked prefill per token-head (d = 128):
+#   minimum HBM bytes: raw bf16 q, k, v (3 x 2d) and alpha (2d) and b (2) in,
+#   bf16 o (2d) out = 1282 B; per (sequence, head) the fp32 state in and out
+#   and per sequence the conv history (3 raw inputs per channel) in and out.
+#   FLOPs of the chunked form: 2C(3dk + 2dv) + 6 dk dv + 2C^2/3 = 182,955, all
+#   matrix products except the C^2 solve.  The matrix cores issue every
+#   product three times (two bf16 pieces per operand: hi*hi, hi*lo, lo*hi).
+BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 2 + 2 * D
+FLOPS_PER_TOKEN_HEAD = 2 * CHUNK * (3 * D + 2 * D) + 6 * D * D + 2 * CHUNK * CHUNK / 3.0
+MFMA_PASSES = 3
+
+
+def prefill_alg_bytes(B, T, conv_in=False):
+    """Minimum HBM bytes of one prefill call of B sequences x T tokens."""
+    ctot = H * 3 * D
+    return (B * T * H * BYTES_PER_TOKEN_HEAD + 2 * B * H * D * D * 4
+            + (2 if conv_in else 1) * B * 3 * ctot * 2)
 
 
 def log(*a):
@@ -145,31 +143,37 @@ def bench_prefill(kda, torch, ev, steps, warmup):
     return dp, wall, gpu_ms, per_stage
 
 
-def roofline_for(kda, per_stage, B, T):
-    """Roofline object for the stage with the largest mean duration: the
-    matrix-core fraction (algorithmic FLOPs against the dense bf16 peak) and
-    the HBM fraction (the stage's minimum bytes against 8 TB/s); the larger
-    one names the bound."""
-    chunk_heads = B * ((T + CHUNK - 1) // CHUNK) * H
+def roofline_for(kda, per_stage, ms_step, B, T):
+    """Roofline object of the prefill: the path's algorithmic bytes (1282 B
+    per token-head plus state and conv history) over the mean duration of the
+    stage that takes longest, against 8 TB/s.  Beside it: the matrix-core
+    fraction of the whole step (algorithmic FLOPs, and as issued with the
+    three compensated passes) against the dense bf16 peak, and the HBM bytes
+    the counters measured for that kernel and for the whole path."""
     name_of = {i: n for i, n in enumerate(kda.STAGES)}
     s_dom = max(per_stage, key=per_stage.get)
     name = name_of[s_dom]
     ms = per_stage[s_dom]
-    flops = FLOPS_PER_CHUNK_HEAD.get(name, 0.0) * chunk_heads
-    nbytes = BYTES_PER_CHUNK_HEAD.get(name, 0.0) * chunk_heads
-    tf = flops / (ms * 1e-3) / 1e12
+    nbytes = prefill_alg_bytes(B, T)
+    flops = FLOPS_PER_TOKEN_HEAD * B * T * H
     gbs = nbytes / (ms * 1e-3) / 1e9
-    mfma_frac, hbm_frac = tf / BF16_MFMA_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
-    if mfma_frac >= hbm_frac:
-        roof = {"kernel": name, "bound": "mfma", "achieved": round(tf, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(mfma_frac, 4), "traffic": None}
-    else:
-        roof = {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": None}
-    roof["traffic"] = measured_traffic(name)
-    roof.update({"avg_ms": round(ms, 4), "flops_per_launch": flops, "bytes_per_launch": nbytes,
-                 "mfma_frac": round(mfma_frac, 4), "hbm_frac": round(hbm_frac, 4)})
-    return roof
+    traffic = measured_traffic(name)
+    path_traffic = [measured_traffic(n) for n in ("chunk_prep", "chunk_scan")]
+    path_traffic = None if None in path_traffic else sum(path_traffic)
+    tf_step = flops / (ms_step * 1e-3) / 1e12
+    return {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "avg_ms": round(ms, 4), "bytes_per_launch": nbytes,
+            "bytes_basis": "algorithmic: 1282 B per token-head (bf16 q, k, v, alpha, b in; bf16 o out) "
+                           "+ fp32 state in/out + conv history out",
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / nbytes, 3),
+            "path_traffic": path_traffic,
+            "path_traffic_over_algorithmic": None if path_traffic is None else round(path_traffic / nbytes, 3),
+            "flops_per_step": flops,
+            "mfma_frac": round(tf_step / BF16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_frac_issued": round(MFMA_PASSES * tf_step / BF16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_basis": "182,955 FLOP per token-head over the step time vs 2.5 PFLOP/s dense bf16; "
+                          "'issued' counts the 3 compensated bf16 passes"}
 
 
 def measured_traffic(stage):
@@ -324,6 +328,56 @@ def bench_varlen(kda, torch, ev, steps=3, warmup=1):
             "ms_per_step": round(ms, 3), "tokens_per_s": round(total / ms * 1e3, 1)}
 
 
+def bench_prefill_4k(kda, torch, ev, steps=20, warmup=3):
+    """The short prefill (B=1, T=4096, zero initial state).  Its 0.17 GB of
+    inputs fit in the 256 MB Infinity Cache, so it is timed twice: back to back
+    (warm) and with a 1 GiB buffer written before every call (scrubbed)."""
+    from kda_inputs import BF16
+    from kda_inputs.device_gen import DeviceProblem
+    dev = torch.device("cuda:0")
+    T = 4096
+    dp = DeviceProblem(2, [T], H, D, D, BF16, dev)
+    cfg = dp.config(out_dtype=torch.bfloat16)
+    tz = dp.tensors
+    q, k, v = (tz[n].view(1, T, -1) for n in ("q", "k", "v"))
+    alpha, b = tz["alpha"].view(1, T, H, D), tz["b"].view(1, T, H)
+    o = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    cs_out = torch.empty((1, 3, dp.ctot), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, 1, T), dtype=torch.uint8, device=dev)
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_prefill(cfg, q, k, v, alpha, b, None, None, o=o, final_state=S_out, conv_state_out=cs_out,
+                        workspace=ws, stream=stream)
+
+    out = {}
+    for mode in ("warm", "scrubbed"):
+        for _ in range(warmup):
+            step()
+        pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in pairs:
+            if mode == "scrubbed":
+                scrub.fill_(1.0)
+            ev.record(e0, stream.cuda_stream)
+            step()
+            ev.record(e1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        vals = [ev.ms(a, b_) for a, b_ in pairs]
+        out[mode] = statistics.median(vals)
+    nbytes = prefill_alg_bytes(1, T)
+    log(f"[bench] 4K prefill: warm {out['warm'] * 1e3:.1f} us, scrubbed {out['scrubbed'] * 1e3:.1f} us")
+    del ws, scrub
+    return {"workload": "kda chunked prefill B=1 T=4096 H=32 dk=dv=128, bf16, zero initial state, bf16 o",
+            "us_warm_p50": round(out["warm"] * 1e3, 2), "us_scrubbed_p50": round(out["scrubbed"] * 1e3, 2),
+            "tokens_per_s_warm": round(T / out["warm"] * 1e3, 1),
+            "tokens_per_s_scrubbed": round(T / out["scrubbed"] * 1e3, 1),
+            "path_hbm_frac_scrubbed": round(nbytes / (out["scrubbed"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_call": nbytes}
+
+
 # Peak of fp32 VALU lane operations (non-packed, as this library is built):
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -410,9 +464,21 @@ def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
                          "bytes_per_launch": nbytes}}
 
 
-def cpu_baseline(dp, seqs=4):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(dp, seqs=4, single_items=6):
     """The fp64 oracle on the first `seqs` sequences of the prefill workload
-    (all heads, full length), on all host cores."""
+    (all heads, full length) on all host cores the process may use, and on
+    one thread over `single_items` (sequence, head) pairs of full length."""
     import numpy as np
     import torch
     import oracle
@@ -430,10 +496,20 @@ def cpu_baseline(dp, seqs=4):
     t0 = time.perf_counter()
     _, _, _, threads = oracle.forward(p, with_conv_out=False)
     dt = time.perf_counter() - t0
-    log(f"[bench] cpu oracle: {n_tok} tokens x {dp.H} heads in {dt:.1f}s on {threads} threads")
+    items = [(i * 37) % (seqs * dp.H) for i in range(single_items)]
+    t1 = time.perf_counter()
+    oracle.forward(p, with_conv_out=False, items=items, nthreads=1)
+    dt1 = time.perf_counter() - t1
+    tok_1 = single_items * T / dp.H / dt1          # tokens/s of all heads, from token-heads/s
+    log(f"[bench] cpu oracle: {n_tok} tokens x {dp.H} heads in {dt:.1f}s on {threads} threads; "
+        f"1 thread: {single_items} x {T} token-heads in {dt1:.1f}s")
     return {"value": round(n_tok / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 token-by-token oracle on {seqs} of the 4 sequences (all {dp.H} heads, all {T} tokens "
-                      f"each, {n_tok} tokens), wall {dt:.1f}s"}
+                      f"each, {n_tok} tokens), wall {dt:.1f}s",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(tok_1, 1), "unit": "tokens/s",
+                           "sample": f"{single_items} (sequence, head) pairs x {T} tokens on 1 thread, "
+                                     f"wall {dt1:.1f}s, scaled to tokens/s of all {dp.H} heads"}}
 
 
 def main():
@@ -443,7 +519,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the decode, varlen, no-clamp prefill and output-gate measurements")
+                    help="skip the 4K prefill, decode, varlen, no-clamp prefill and output-gate measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (to scale HBM traffic counters)")
     args = ap.parse_args()
@@ -470,8 +546,8 @@ def main():
     dp, wall, gpu_ms, per_stage = bench_prefill(kda, torch, ev, args.steps, args.warmup)
     ms_step = wall / args.steps * 1e3
     value = B * T / (wall / args.steps)
-    roof = roofline_for(kda, per_stage, B, T)
-    path_gbs = B * T * H * (4 * 2 * D + 2 + 2 * D) / (ms_step * 1e-3) / 1e9
+    roof = roofline_for(kda, per_stage, ms_step, B, T)
+    path_gbs = prefill_alg_bytes(B, T) / (ms_step * 1e-3) / 1e9
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128,T=32K) + decode step us; % of roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -486,6 +562,7 @@ def main():
         "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
     }
     if not args.no_extras:
+        result["prefill_4k"] = bench_prefill_4k(kda, torch, ev)
         result["decode"] = bench_decode(kda, torch, ev)
         result["decode_multi"] = bench_decode_multi(kda, torch, ev)
         result["varlen"] = bench_varlen(kda, torch, ev)

@@ -84,6 +84,25 @@ class DeviceProblem:
         from .torch_io import make_config
         return make_config(self, self.device, out_dtype, **kw)
 
+    def seq_problem(self, n: int) -> Problem:
+        """Host copy of the stored inputs of sequence n, all heads, as a
+        one-sequence problem."""
+        cu = self.cu_seqlens
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        T = self.tensors
+
+        def host(x):
+            x = x.contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).cpu().numpy().view(np.uint16)
+            return x.cpu().numpy()
+
+        cs = None if self.conv_state is None else self.conv_state[n:n + 1]
+        S0 = None if self.initial_state is None else self.initial_state[n:n + 1]
+        return Problem([t1 - t0], self.H, self.dk, self.dv, self.io,
+                       host(T["q"][t0:t1]), host(T["k"][t0:t1]), host(T["v"][t0:t1]), host(T["alpha"][t0:t1]),
+                       host(T["b"][t0:t1]), self.w_q, self.w_k, self.w_v, self.A_log, self.dt_bias, S0, cs)
+
     def head_problem(self, n: int, h: int, t_end: Optional[int] = None) -> Problem:
         """Host copy of the stored inputs of sequence n, head h (optionally only
         its first t_end tokens) as a one-sequence, one-head problem."""

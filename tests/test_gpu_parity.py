@@ -244,6 +244,11 @@ def test_prefill_then_decode_continues_long_prefill(kda):
     assert max_over_rms(o_cat, o_full.double().cpu().numpy()) <= 2e-3
     assert rel_fro(S.double().cpu().numpy(), S_full.double().cpu().numpy()) <= 1e-3
     assert torch.equal(cs, cs_full)
+    # and both against the oracle's single long prefill
+    o_ref, S_ref, c_ref, _ = oracle.forward(p)
+    assert max_over_rms(o_cat, o_ref) <= 2e-3
+    assert rel_fro(S.double().cpu().numpy(), S_ref) <= 1e-3
+    assert np.array_equal(as_f64(from_torch_bf16(cs), BF16), c_ref)
 
 
 @pytest.mark.parametrize("io", [BF16, FP32])

@@ -1,10 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (bf16 outputs), against the fp64 oracle.
 
-The 4K prefill is checked everywhere; the larger workloads on sampled
-(sequence, head) pairs that the oracle computes one at a time from the exact
-stored input bytes, plus whole-output properties (finite everywhere, exact
-conv history).  Bounds: bf16 inputs / fp32 state, max|o - o_ref| <= 2e-3
+Every workload is checked everywhere: every output and the final state of
+every (sequence, head), from the exact stored input bytes, plus the conv
+history bit for bit.  Bounds: bf16 inputs / fp32 state, max|o - o_ref| <= 2e-3
 RMS(o_ref) (+ half a bf16 ulp for the bf16 store) and relative Frobenius
 state error <= 1e-3.
 """
@@ -60,27 +59,33 @@ def test_prefill_4k_every_head(kda, out):
     assert np.array_equal(as_f64(from_torch_bf16(cs), BF16), c_ref)
 
 
-def _sampled_check(dp, o, S_out, items, label, **oracle_kw):
-    o_all, ref_all = [], []
+def _every_head_check(dp, o, S_out, label, **oracle_kw):
+    """o and the final state of every (sequence, head) against the oracle,
+    one sequence at a time (all heads threaded), from the stored bytes."""
     cu = dp.cu_seqlens
-    for n, h in items:
-        hp = dp.head_problem(n, h)
-        o_ref, S_ref, _, _ = oracle.forward(hp, with_conv_out=False, **oracle_kw)
-        og = o[cu[n]:cu[n + 1], h].double().cpu().numpy()
-        o_all.append(og)
-        ref_all.append(o_ref[:, 0])
-        es = rel_fro(S_out[n, h].double().cpu().numpy(), S_ref[0, 0])
-        print(f"{label} seq {n} head {h} ({hp.seqlens[0]} tokens): state {es:.3e}")
-        assert es <= 1e-3
-    _bf16_check(np.concatenate(o_all), np.concatenate(ref_all), label)
+    worst_o, worst_s = 0.0, 0.0
+    for n in range(len(dp.seqlens)):
+        sp = dp.seq_problem(n)
+        o_ref, S_ref, _, _ = oracle.forward(sp, with_conv_out=False, **oracle_kw)
+        og = o[cu[n]:cu[n + 1]].double().cpu().numpy()
+        ok, e = check_bf16_output(og, o_ref, 2e-3)
+        del og, o_ref
+        Sg = S_out[n].double().cpu().numpy()
+        es = max(rel_fro(Sg[h], S_ref[0, h]) for h in range(dp.H))
+        print(f"{label} seq {n} ({sp.seqlens[0]} tokens, all {dp.H} heads): o {e:.3e} x RMS, worst head state {es:.3e}",
+              flush=True)
+        assert ok, f"{label} seq {n}: bf16 output beyond 2e-3 RMS + half ulp ({e:.3e} x RMS)"
+        assert es <= 1e-3, f"{label} seq {n}: state error {es:.3e}"
+        worst_o, worst_s = max(worst_o, e), max(worst_s, es)
+    return worst_o, worst_s
 
 
-def test_prefill_32k_sampled(kda):
+def _prefill_32k(kda, lower_bound=-5.0):
     from kda_inputs.device_gen import DeviceProblem
     dev = torch.device("cuda:0")
     B, T = 4, 32768
     dp = DeviceProblem(3, [T] * B, H, D, D, BF16, dev, state_seqs=list(range(B)))
-    cfg = dp.config(out_dtype=torch.bfloat16)
+    cfg = dp.config(out_dtype=torch.bfloat16, gate_lower_bound=lower_bound)
     tz = dp.tensors
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
     S = torch.empty((B, H, D, D), device=dev)
@@ -90,35 +95,30 @@ def test_prefill_32k_sampled(kda):
                     o=o, final_state=S, conv_state_out=cs)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    _sampled_check(dp, o.view(B * T, H, D), S, [(0, 0), (1, 13), (2, 22), (3, 31)], "32K prefill")
     # conv history: the last three raw inputs of every sequence, exactly
     for n in range(B):
         last = torch.cat([tz["q"][(n + 1) * T - 3:(n + 1) * T], tz["k"][(n + 1) * T - 3:(n + 1) * T],
                           tz["v"][(n + 1) * T - 3:(n + 1) * T]], dim=1)
         assert torch.equal(cs[n], last)
+    return dp, o.view(B * T, H, D), S
 
 
-def test_prefill_32k_no_clamp_sampled(kda):
-    """The 32K prefill with the gate's clamp off (lower bound -inf), in the
-    launch configuration the benchmark times: the recurrent form."""
-    from kda_inputs.device_gen import DeviceProblem
-    dev = torch.device("cuda:0")
-    B, T = 4, 32768
-    dp = DeviceProblem(3, [T] * B, H, D, D, BF16, dev, state_seqs=list(range(B)))
-    cfg = dp.config(out_dtype=torch.bfloat16, gate_lower_bound=float("-inf"))
-    tz = dp.tensors
-    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
-    S = torch.empty((B, H, D, D), device=dev)
-    kda.kda_prefill(cfg, tz["q"].view(B, T, -1), tz["k"].view(B, T, -1), tz["v"].view(B, T, -1),
-                    tz["alpha"].view(B, T, H, D), tz["b"].view(B, T, H), tz["initial_state"], tz["conv_state"],
-                    o=o, final_state=S)
-    torch.cuda.synchronize()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    _sampled_check(dp, o.view(B * T, H, D), S, [(0, 3), (1, 17), (2, 30), (3, 8)], "32K prefill without clamp",
-                   lower_bound=float("-inf"))
+def test_prefill_32k_every_head(kda):
+    """The long-context prefill (B=4, T=32768, H=32, d=128, S0 ~ N(0, 0.02))
+    in the launch configuration the benchmark times: every output and the
+    final state of all 128 (sequence, head) pairs."""
+    dp, o, S = _prefill_32k(kda)
+    _every_head_check(dp, o, S, "32K prefill")
 
 
-def test_varlen_262k_sampled(kda):
+def test_prefill_32k_no_clamp_every_head(kda):
+    """The same prefill with the gate's clamp off (lower bound -inf): the
+    recurrent form, every (sequence, head)."""
+    dp, o, S = _prefill_32k(kda, lower_bound=float("-inf"))
+    _every_head_check(dp, o, S, "32K prefill without clamp", lower_bound=float("-inf"))
+
+
+def test_varlen_262k_every_head(kda):
     from kda_inputs.device_gen import DeviceProblem
     dev = torch.device("cuda:0")
     dp = DeviceProblem(5, VARLEN_LENGTHS, H, D, D, BF16, dev, state_seqs=[1, 3, 5, 7])
@@ -131,37 +131,36 @@ def test_varlen_262k_sampled(kda):
                            tz["initial_state"], None, o=o, final_state=S)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    _sampled_check(dp, o, S, [(0, 3), (1, 10), (4, 17), (7, 31)], "varlen")
+    _every_head_check(dp, o, S, "varlen")
 
 
-def test_decode_256x128_sampled(kda):
+def test_decode_256x128_every_pair(kda):
+    """128 decode steps of 256 sequences x 32 heads, every output of every
+    step, the final state of all 8192 (sequence, head) pairs and every conv
+    history.  The reference is the oracle's token loop over each sequence's
+    128 tokens from its state and history: a chain of one-token decode steps
+    is that same loop continued (pinned on the CPU by the continuation test),
+    so one oracle call covers all steps."""
+    from kda_inputs import Problem
     dp = workload_decode()                      # N=256, H=32, d=128, 128 steps
     dev = torch.device("cuda:0")
     cfg, S, cs = decode_to_device(dp, dev, out_dtype=torch.bfloat16)
-    items = [(0, 0), (17, 5), (128, 16), (200, 27), (255, 31)]
-    # fp64 reference state of the sampled (sequence, head) pairs
-    Sref = {it: dp.state[it[0], it[1]].astype(np.float64) for it in items}
-    cref = {it: dp.conv_state[it[0]] for it in items}
-    params = (dp.w_q, dp.w_k, dp.w_v, dp.A_log, dp.dt_bias)
-    o_all, ref_all = [], []
-    for step in range(dp.steps):
-        toks = dp.tokens(step)
-        o = kda.kda_decode_step(cfg, *tokens_to_device(toks, dp.io, dev), S, cs)
-        og = o.double().cpu().numpy()
-        for (n, h) in items:
-            tok1 = tuple(a[n:n + 1] for a in toks)
-            oi, Si, ci = oracle.decode_reference(Sref[(n, h)][None, None].repeat(H, axis=1), cref[(n, h)][None],
-                                                 tok1, params, H, D, D, dp.io, items=[h])
-            Sref[(n, h)] = Si[0, h]
-            # the history shifts by one raw input (q | k | v channels of this token)
-            newest = np.concatenate([tok1[0][0], tok1[1][0], tok1[2][0]])[None]
-            cref[(n, h)] = np.concatenate([cref[(n, h)][1:], newest], 0)
-            o_all.append(og[n, h])
-            ref_all.append(oi[0, h])
+    N, steps = dp.N, dp.steps
+    o_all = torch.empty((steps, N, H, D), dtype=torch.bfloat16, device=dev)
+    toks = [dp.tokens(step) for step in range(steps)]
+    for step in range(steps):
+        kda.kda_decode_step(cfg, *tokens_to_device(toks[step], dp.io, dev), S, cs, o=o_all[step])
     torch.cuda.synchronize()
-    _bf16_check(np.stack(o_all), np.stack(ref_all), "decode 128 steps")
-    for (n, h) in items:
-        es = rel_fro(S[n, h].double().cpu().numpy(), Sref[(n, h)])
-        print(f"decode seq {n} head {h}: state after 128 steps {es:.3e}")
-        assert es <= 1e-3
-        assert np.array_equal(from_torch_bf16(cs[n]), cref[(n, h)])
+    # packed sequence-major: row n*steps + s is step s of sequence n
+    seq_major = [np.ascontiguousarray(np.stack([t[i] for t in toks], axis=1).reshape(N * steps, *toks[0][i].shape[1:]))
+                 for i in range(5)]
+    p = Problem([steps] * N, H, D, D, dp.io, *seq_major, dp.w_q, dp.w_k, dp.w_v, dp.A_log, dp.dt_bias,
+                dp.state, dp.conv_state)
+    o_ref, S_ref, c_ref, _ = oracle.forward(p)
+    og = o_all.permute(1, 0, 2, 3).reshape(N * steps, H, D).double().cpu().numpy()
+    _bf16_check(og, o_ref, "decode 256 x 128 steps, every output")
+    Sg = S.double().cpu().numpy()
+    es = max(rel_fro(Sg[n, h], S_ref[n, h]) for n in range(N) for h in range(H))
+    print(f"decode: worst state error after 128 steps over 8192 pairs {es:.3e}")
+    assert es <= 1e-3
+    assert np.array_equal(as_f64(from_torch_bf16(cs), BF16), c_ref)
