@@ -9,6 +9,9 @@ Entry points (same names as the C ABI):
   kda_prefill(cfg, q, k, v, alpha, b, ...)          B equal-length sequences
   kda_varlen_prefill(cfg, cu_seqlens, q, ...)       packed sequences
   kda_decode_step(cfg, q, k, v, alpha, b, state, conv_state, o=None)
+  kda_decode_multi(cfg, q, ..., state_pool, conv_pool, slots=, n_commit=)
+  kda_decode_step_gated / kda_decode_multi_gated   the same, output epilogue fused
+  kda_output_gate(cfg, o, gate, o_norm_weight)     the output epilogue alone
   kda_prefill_workspace_bytes / kda_varlen_workspace_bytes
 """
 from __future__ import annotations
@@ -44,7 +47,7 @@ NUM_STAGES = len(STAGES)
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
             "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_decode_multi",
-            "kda_output_gate")
+            "kda_decode_step_gated", "kda_decode_multi_gated", "kda_output_gate")
 
 
 class KdaError(RuntimeError):
@@ -97,6 +100,11 @@ def _load_library():
     lib.kda_decode_step.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_multi.restype = ctypes.c_int
     lib.kda_decode_multi.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_decode_step_gated.restype = ctypes.c_int
+    lib.kda_decode_step_gated.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.kda_decode_multi_gated.restype = ctypes.c_int
+    lib.kda_decode_multi_gated.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_float, vp, vp, vp]
     lib.kda_output_gate.restype = ctypes.c_int
     lib.kda_output_gate.argtypes = [cfgp, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp]
     return lib
@@ -273,6 +281,38 @@ def kda_decode_multi(cfg: Config, q, k, v, alpha, b, state_pool, conv_pool, *, s
                                _stream(stream))
     _check(st, "kda_decode_multi")
     return o
+
+
+def kda_decode_step_gated(cfg: Config, q, k, v, alpha, b, state, conv_state, gate, o_norm_weight,
+                          eps: float = 1e-6, *, y=None, stream=None):
+    """kda_decode_step with the output epilogue fused: gate [N, H, dv] (io
+    dtype), o_norm_weight [dv] fp32.  Returns y [N, H, dv] (out dtype) =
+    o / sqrt(mean(o^2) + eps) * o_norm_weight * sigmoid(gate) per row."""
+    N = q.shape[0]
+    if y is None:
+        y = torch.empty((N, cfg.num_heads, cfg.head_v_dim), dtype=cfg.out_dtype, device=q.device)
+    st = _lib.kda_decode_step_gated(ctypes.byref(cfg.c_struct()), N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                    _ptr(b), _ptr(state), _ptr(conv_state), _ptr(gate), _ptr(o_norm_weight),
+                                    float(eps), _ptr(y), _stream(stream))
+    _check(st, "kda_decode_step_gated")
+    return y
+
+
+def kda_decode_multi_gated(cfg: Config, q, k, v, alpha, b, state_pool, conv_pool, gate, o_norm_weight,
+                           eps: float = 1e-6, *, slots=None, n_commit=None, y=None, stream=None):
+    """kda_decode_multi with the output epilogue fused: gate [N, K, H, dv]
+    (io dtype), o_norm_weight [dv] fp32.  Returns y [N, K, H, dv]."""
+    N, K = q.shape[0], q.shape[1]
+    for t in (slots, n_commit):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != N):
+            raise ValueError("slots and n_commit must be int32 tensors of N entries")
+    if y is None:
+        y = torch.empty((N, K, cfg.num_heads, cfg.head_v_dim), dtype=cfg.out_dtype, device=q.device)
+    st = _lib.kda_decode_multi_gated(ctypes.byref(cfg.c_struct()), N, K, _ptr(slots), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(alpha), _ptr(b), _ptr(state_pool), _ptr(conv_pool), _ptr(gate),
+                                     _ptr(o_norm_weight), float(eps), _ptr(y), _ptr(n_commit), _stream(stream))
+    _check(st, "kda_decode_multi_gated")
+    return y
 
 
 def kda_output_gate(cfg: Config, o, gate, o_norm_weight, eps: float = 1e-6, *, y=None, stream=None):

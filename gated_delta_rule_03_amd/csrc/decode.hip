@@ -27,7 +27,11 @@ constexpr int kDecodeThreads = 512;
 // Tokens whose inputs the multi-token decode stages at once.
 constexpr int kMultiGroup = 8;
 
-template <int D, bool IO_BF16, bool OUT_BF16>
+// With GATED the output row goes through the layer's epilogue before it is
+// stored (y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), AliceAI page,
+// section 三): the workgroup holds the whole row of dv outputs, so the row's
+// sum of squares is one reduction over the waves that own it.
+template <int D, bool IO_BF16, bool OUT_BF16, bool GATED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, DecodeIO io) {
   constexpr int NT = kDecodeThreads;
   constexpr int C4 = D / 4;                  // float4 columns per state row
@@ -38,6 +42,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
   __shared__ float red[2][RPP][D];           // per-row-group partial k^T S~, q^T S~
   __shared__ float d_s[D];                   // delta
   __shared__ float scal[4];                  // q scale * inv|q|, inv|k|, beta, q.k
+  constexpr int OW = (D + kWave - 1) / kWave;  // waves holding the output row
+  __shared__ float osum[OW];                 // per-wave sums of o^2 (epilogue)
+  static_assert(D <= kDecodeThreads, "one output column per thread");
 
   const int tid = threadIdx.x;
   const int H = p.H;
@@ -86,6 +93,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
     const float al = ld<IO_BF16>(io.alpha, (static_cast<size_t>(n) * H + h) * D + i);
     const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, p.dt_bias[h * D + i], a_exp, p.lower_bound);
     e_s[i] = expf(g);
+  }
+  // epilogue operands of this thread's output column
+  float gsig = 0.f, onw = 0.f;
+  if constexpr (GATED) {
+    if (tid < D) {
+      gsig = sigmoidf_(ld<IO_BF16>(io.gate, (static_cast<size_t>(n) * H + h) * D + tid));
+      onw = io.onw[tid];
+    }
   }
   if (tid == 0) {
     const float bb = ld<IO_BF16>(io.b, static_cast<size_t>(n) * H + h);
@@ -140,15 +155,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
     red[1][rg][col4 * 4 + j] = pq[j];
   }
   __syncthreads();
-  for (int j = tid; j < D; j += NT) {
+  float o_j = 0.f;
+  if (tid < D) {
+    const int j = tid;
     float pp = 0.f, rq = 0.f;
 #pragma unroll 8
     for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][j]; rq += red[1][g2][j]; }
     const float delta = beta * (u_s[2 * D + j] - pp);
     d_s[j] = delta;
-    st<OUT_BF16>(io.o, (static_cast<size_t>(n) * H + h) * D + j, rq + qk * delta);
+    o_j = rq + qk * delta;
+    if constexpr (!GATED) st<OUT_BF16>(io.o, (static_cast<size_t>(n) * H + h) * D + j, o_j);
+  }
+  if constexpr (GATED) {
+    if (tid < OW * kWave) {                     // whole waves: lanes past D add 0
+      const float ss = group_sum<kWave>(o_j * o_j);
+      if ((tid % kWave) == 0) osum[tid / kWave] = ss;
+    }
   }
   __syncthreads();
+  if constexpr (GATED) {
+    if (tid < D) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < OW; ++w) ss += osum[w];
+      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + io.oeps);
+      st<OUT_BF16>(io.o, (static_cast<size_t>(n) * H + h) * D + tid, o_j * inv * onw * gsig);
+    }
+  }
   const float d0 = d_s[col4 * 4], d1 = d_s[col4 * 4 + 1], d2 = d_s[col4 * 4 + 2], d3 = d_s[col4 * 4 + 3];
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) {
@@ -168,7 +201,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
 // with the conv window of each channel kept in its thread's registers.  The
 // state after the first `commit` tokens goes back to the pool (none for 0),
 // and so does the conv history after them; every token's output is written.
-template <int D, bool IO_BF16, bool OUT_BF16>
+// GATED: every token's output row goes through the epilogue, as in
+// decode_kernel.
+template <int D, bool IO_BF16, bool OUT_BF16, bool GATED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
   constexpr int NT = kDecodeThreads;
   constexpr int C4 = D / 4;
@@ -183,6 +218,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
   __shared__ float red[2][RPP][D];
   __shared__ float d_s[D];
   __shared__ float scal[4];
+  constexpr int OW = (D + kWave - 1) / kWave;
+  __shared__ float osum[OW];
 
   const int tid = threadIdx.x;
   const int H = p.H;
@@ -223,6 +260,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
   float k0 = h0, k1 = h1, k2 = h2;   // the window after the committed tokens
   const float a_exp = expf(p.A_log[h]);
   const float dtb = tid < D ? p.dt_bias[h * D + tid] : 0.f;
+  float onw = 0.f;
+  if constexpr (GATED) onw = tid < D ? io.onw[tid] : 0.f;
 
   for (int t0 = 0; t0 < K; t0 += KG) {
     // the group's raw inputs, gates and betas, all loads issued together (the
@@ -301,16 +340,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
         red[0][rg][col4 * 4 + jj] = pk[jj];
         red[1][rg][col4 * 4 + jj] = pq[jj];
       }
+      // the epilogue's gate of this token, loaded before the barrier
+      float gsig = 0.f;
+      if constexpr (GATED) {
+        if (tid < D) gsig = sigmoidf_(ld<IO_BF16>(io.gate, tok * HD + static_cast<size_t>(h) * D + tid));
+      }
       __syncthreads();
-      for (int c = tid; c < D; c += NT) {
+      float o_c = 0.f;
+      if (tid < D) {
+        const int c = tid;
         float pp = 0.f, rq = 0.f;
 #pragma unroll 8
         for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][c]; rq += red[1][g2][c]; }
         const float delta = beta * (u_s[2 * D + c] - pp);
         d_s[c] = delta;
-        st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + c, rq + qk * delta);
+        o_c = rq + qk * delta;
+        if constexpr (!GATED) st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + c, o_c);
+      }
+      if constexpr (GATED) {
+        if (tid < OW * kWave) {
+          const float ss = group_sum<kWave>(o_c * o_c);
+          if ((tid % kWave) == 0) osum[tid / kWave] = ss;
+        }
       }
       __syncthreads();
+      if constexpr (GATED) {
+        if (tid < D) {
+          float ss = 0.f;
+#pragma unroll
+          for (int w = 0; w < OW; ++w) ss += osum[w];
+          const float inv = 1.0f / sqrtf(ss * (1.0f / D) + io.oeps);
+          st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + tid, o_c * inv * onw * gsig);
+        }
+      }
       const float d0 = d_s[col4 * 4], d1 = d_s[col4 * 4 + 1], d2 = d_s[col4 * 4 + 2], d3 = d_s[col4 * 4 + 3];
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
@@ -321,7 +383,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
           if (t + 1 == commit) __builtin_nontemporal_store(Sv[rr], &Sp[static_cast<size_t>(r) * C4 + col4]);
         }
       }
-      __syncthreads();   // u_s, d_s and scal are rewritten by the next token, x_s / eg_s by the next group
+      __syncthreads();   // u_s, d_s, scal, osum are rewritten by the next token, x_s / eg_s by the next group
     }
   }
   if (conv_lane && commit > 0) {
@@ -331,15 +393,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
   }
 }
 
+template <int D, bool GATED>
+static hipError_t launch_decode_multi_g(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16,
+                                        bool out_bf16, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
+  if (io_bf16 && out_bf16) decode_multi_kernel<D, true, true, GATED><<<grid, block, 0, st>>>(p, io, K);
+  else if (io_bf16) decode_multi_kernel<D, true, false, GATED><<<grid, block, 0, st>>>(p, io, K);
+  else if (out_bf16) decode_multi_kernel<D, false, true, GATED><<<grid, block, 0, st>>>(p, io, K);
+  else decode_multi_kernel<D, false, false, GATED><<<grid, block, 0, st>>>(p, io, K);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_decode_multi_d(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16,
                                         bool out_bf16, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
-  if (io_bf16 && out_bf16) decode_multi_kernel<D, true, true><<<grid, block, 0, st>>>(p, io, K);
-  else if (io_bf16) decode_multi_kernel<D, true, false><<<grid, block, 0, st>>>(p, io, K);
-  else if (out_bf16) decode_multi_kernel<D, false, true><<<grid, block, 0, st>>>(p, io, K);
-  else decode_multi_kernel<D, false, false><<<grid, block, 0, st>>>(p, io, K);
-  return hipGetLastError();
+  return io.gate ? launch_decode_multi_g<D, true>(p, io, N, K, io_bf16, out_bf16, st)
+                 : launch_decode_multi_g<D, false>(p, io, N, K, io_bf16, out_bf16, st);
 }
 
 hipError_t launch_decode_multi(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16, bool out_bf16,
@@ -353,15 +422,22 @@ hipError_t launch_decode_multi(const Params& p, const DecodeMultiIO& io, int N, 
   }
 }
 
+template <int D, bool GATED>
+static hipError_t launch_decode_g(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16,
+                                  hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
+  if (io_bf16 && out_bf16) decode_kernel<D, true, true, GATED><<<grid, block, 0, st>>>(p, io);
+  else if (io_bf16) decode_kernel<D, true, false, GATED><<<grid, block, 0, st>>>(p, io);
+  else if (out_bf16) decode_kernel<D, false, true, GATED><<<grid, block, 0, st>>>(p, io);
+  else decode_kernel<D, false, false, GATED><<<grid, block, 0, st>>>(p, io);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_decode_d(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16,
                                   hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
-  if (io_bf16 && out_bf16) decode_kernel<D, true, true><<<grid, block, 0, st>>>(p, io);
-  else if (io_bf16) decode_kernel<D, true, false><<<grid, block, 0, st>>>(p, io);
-  else if (out_bf16) decode_kernel<D, false, true><<<grid, block, 0, st>>>(p, io);
-  else decode_kernel<D, false, false><<<grid, block, 0, st>>>(p, io);
-  return hipGetLastError();
+  return io.gate ? launch_decode_g<D, true>(p, io, N, io_bf16, out_bf16, st)
+                 : launch_decode_g<D, false>(p, io, N, io_bf16, out_bf16, st);
 }
 
 hipError_t launch_decode(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16, hipStream_t st) {

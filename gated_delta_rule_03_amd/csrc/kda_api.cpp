@@ -166,7 +166,7 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
 
 extern "C" {
 
-int32_t kda_version(void) { return 101; }
+int32_t kda_version(void) { return 102; }
 
 const char* kda_status_string(kda_status_t status) {
   switch (status) {
@@ -229,9 +229,15 @@ kda_status_t kda_varlen_prefill(const kda_config_t* cfg, int32_t N, int32_t tota
   return run_prefill(cfg, N, total_T, mc, cu_seqlens, 0, io, workspace, static_cast<hipStream_t>(stream));
 }
 
-kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, const void* k, const void* v,
-                             const void* alpha, const void* b, float* state, void* conv_state, void* o,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the plain and the gated decode entry points; gate == nullptr for
+// the plain one.
+kda_status_t decode_step(const kda_config_t* cfg, int32_t N, const void* q, const void* k, const void* v,
+                         const void* alpha, const void* b, float* state, void* conv_state, const void* gate,
+                         const float* onw, float oeps, void* o, void* stream) {
   kda_status_t s = check_config(cfg, false);
   if (s != KDA_OK) return s;
   if (N < 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -239,16 +245,17 @@ kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, 
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !alpha || !b || !state || !conv_state || !o) return KDA_ERR_INVALID_ARGUMENT;
   const Params p = make_params(cfg);
-  kda::DecodeIO io{q, k, v, alpha, b, state, conv_state, o};
+  kda::DecodeIO io{q, k, v, alpha, b, state, conv_state, o, gate, onw, oeps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return stage(cfg, KDA_STAGE_DECODE, st, [&] {
     return kda::launch_decode(p, io, N, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16, st);
   });
 }
 
-kda_status_t kda_decode_multi(const kda_config_t* cfg, int32_t N, int32_t K, const int32_t* slots, const void* q,
-                              const void* k, const void* v, const void* alpha, const void* b, float* state_pool,
-                              void* conv_pool, void* o, const int32_t* n_commit, void* stream) {
+kda_status_t decode_multi(const kda_config_t* cfg, int32_t N, int32_t K, const int32_t* slots, const void* q,
+                          const void* k, const void* v, const void* alpha, const void* b, float* state_pool,
+                          void* conv_pool, const void* gate, const float* onw, float oeps, void* o,
+                          const int32_t* n_commit, void* stream) {
   kda_status_t s = check_config(cfg, false);
   if (s != KDA_OK) return s;
   if (N < 0 || K < 1) return KDA_ERR_INVALID_ARGUMENT;
@@ -257,11 +264,49 @@ kda_status_t kda_decode_multi(const kda_config_t* cfg, int32_t N, int32_t K, con
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !alpha || !b || !state_pool || !conv_pool || !o) return KDA_ERR_INVALID_ARGUMENT;
   const Params p = make_params(cfg);
-  kda::DecodeMultiIO io{slots, n_commit, q, k, v, alpha, b, state_pool, conv_pool, o};
+  kda::DecodeMultiIO io{slots, n_commit, q, k, v, alpha, b, state_pool, conv_pool, o, gate, onw, oeps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return stage(cfg, KDA_STAGE_DECODE, st, [&] {
     return kda::launch_decode_multi(p, io, N, K, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16, st);
   });
+}
+
+bool bad_epilogue_args(const void* gate, const float* onw, float eps) {
+  return !gate || !onw || std::isnan(eps) || eps < 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_decode_step(const kda_config_t* cfg, int32_t N, const void* q, const void* k, const void* v,
+                             const void* alpha, const void* b, float* state, void* conv_state, void* o,
+                             void* stream) {
+  return decode_step(cfg, N, q, k, v, alpha, b, state, conv_state, nullptr, nullptr, 0.f, o, stream);
+}
+
+kda_status_t kda_decode_step_gated(const kda_config_t* cfg, int32_t N, const void* q, const void* k, const void* v,
+                                   const void* alpha, const void* b, float* state, void* conv_state,
+                                   const void* gate, const float* o_norm_weight, float eps, void* y, void* stream) {
+  if (cfg && N > 0 && bad_epilogue_args(gate, o_norm_weight, eps)) return KDA_ERR_INVALID_ARGUMENT;
+  return decode_step(cfg, N, q, k, v, alpha, b, state, conv_state, gate, o_norm_weight, eps, y, stream);
+}
+
+kda_status_t kda_decode_multi(const kda_config_t* cfg, int32_t N, int32_t K, const int32_t* slots, const void* q,
+                              const void* k, const void* v, const void* alpha, const void* b, float* state_pool,
+                              void* conv_pool, void* o, const int32_t* n_commit, void* stream) {
+  return decode_multi(cfg, N, K, slots, q, k, v, alpha, b, state_pool, conv_pool, nullptr, nullptr, 0.f, o,
+                      n_commit, stream);
+}
+
+kda_status_t kda_decode_multi_gated(const kda_config_t* cfg, int32_t N, int32_t K, const int32_t* slots,
+                                    const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                                    float* state_pool, void* conv_pool, const void* gate,
+                                    const float* o_norm_weight, float eps, void* y, const int32_t* n_commit,
+                                    void* stream) {
+  if (cfg && N > 0 && bad_epilogue_args(gate, o_norm_weight, eps)) return KDA_ERR_INVALID_ARGUMENT;
+  return decode_multi(cfg, N, K, slots, q, k, v, alpha, b, state_pool, conv_pool, gate, o_norm_weight, eps, y,
+                      n_commit, stream);
 }
 
 kda_status_t kda_output_gate(const kda_config_t* cfg, int64_t n_tokens, const void* o, const void* gate,

@@ -106,7 +106,7 @@ struct PrefillIO {
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws,
                                int32_t* chunk0, int32_t* chunk_seq, int4* desc, int32_t max_chunks, int32_t H,
                                int32_t D, hipStream_t st);
-// Compute units of the current device (cached per device).
+// Compute units of the current device (queried on every call).
 hipError_t device_cus(int* ncu);
 hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,
                              int max_chunks, bool io_bf16, hipStream_t st);
@@ -146,7 +146,10 @@ struct DecodeIO {
   const void* b;
   float* state;
   void* conv_state;
-  void* o;
+  void* o;                   // o, or y when gate is set
+  const void* gate;          // [N][H][dv] io dtype: the output epilogue's gate, or null for plain o
+  const float* onw;          // [dv] o_norm weight (with gate)
+  float oeps;                // o_norm epsilon (with gate)
 };
 
 hipError_t launch_decode(const Params& p, const DecodeIO& io, int N, bool io_bf16, bool out_bf16, hipStream_t st);
@@ -162,7 +165,10 @@ struct DecodeMultiIO {
   const void* b;             // [N][K][H]
   float* state_pool;         // [P][H][dk][dv]
   void* conv_pool;           // [P][3][Ctot]
-  void* o;                   // [N][K][H][dv]
+  void* o;                   // [N][K][H][dv]: o, or y when gate is set
+  const void* gate;          // [N][K][H][dv] io dtype, or null for plain o
+  const float* onw;          // [dv] o_norm weight (with gate)
+  float oeps;                // o_norm epsilon (with gate)
 };
 
 hipError_t launch_decode_multi(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16, bool out_bf16,

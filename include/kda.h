@@ -28,9 +28,10 @@
  * (packed sequences), each in the chunked form or, for gates below -5.4, the
  * token recurrence; kda_decode_step (one token per sequence, in place);
  * kda_decode_multi (K tokens per sequence through state / conv-history pools,
- * with commit counts for speculative decoding); kda_output_gate (the layer's
- * o_norm x sigmoid output epilogue); plus the workspace queries, the version
- * and status strings.
+ * with commit counts for speculative decoding); kda_decode_step_gated and
+ * kda_decode_multi_gated (the same with the output epilogue fused);
+ * kda_output_gate (the layer's o_norm x sigmoid output epilogue); plus the
+ * workspace queries, the version and status strings.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, contiguous, row-major in the
@@ -228,6 +229,36 @@ kda_status_t kda_decode_multi(const kda_config_t *cfg, int32_t N, int32_t K, con
                               const void *alpha, const void *b,
                               float *state_pool, void *conv_pool, void *o,
                               const int32_t *n_commit, void *stream);
+
+/*
+ * kda_decode_step and kda_decode_multi with the layer's output epilogue
+ * (kda_output_gate below) fused into the step: each (sequence, head)
+ * workgroup holds the whole row of dv outputs, so the row is normalised and
+ * gated before it is stored and o never goes to memory
+ * (AliceAI page, section 三: KDA's output goes through o_norm and a sigmoid
+ * gate).  Arguments as for the plain calls, plus:
+ *   gate           the output-gate projection before the sigmoid, io_dtype,
+ *                  laid out like o: [N][H][dv] (step), [N][K][H][dv] (multi)
+ *   o_norm_weight  [dv] fp32, one weight per channel shared by the heads
+ *   eps            o_norm epsilon, >= 0 (NaN or negative, or a NULL gate or
+ *                  weight: KDA_ERR_INVALID_ARGUMENT)
+ *   y              out_dtype, in place of o: y = o / sqrt(mean(o^2) + eps)
+ *                  * o_norm_weight * sigmoid(gate), per (token, head) row
+ * The state and conv history are updated exactly as by the plain calls.
+ */
+kda_status_t kda_decode_step_gated(const kda_config_t *cfg, int32_t N,
+                                   const void *q, const void *k, const void *v,
+                                   const void *alpha, const void *b,
+                                   float *state, void *conv_state,
+                                   const void *gate, const float *o_norm_weight, float eps,
+                                   void *y, void *stream);
+
+kda_status_t kda_decode_multi_gated(const kda_config_t *cfg, int32_t N, int32_t K, const int32_t *slots,
+                                    const void *q, const void *k, const void *v,
+                                    const void *alpha, const void *b,
+                                    float *state_pool, void *conv_pool,
+                                    const void *gate, const float *o_norm_weight, float eps,
+                                    void *y, const int32_t *n_commit, void *stream);
 
 /*
  * The layer's output epilogue on n_tokens x H rows of dv outputs (AliceAI

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(kda):
 
 
 def test_version_and_status_strings(kda):
-    assert kda.version() == 101
+    assert kda.version() == 102
     for code, name in ((0, "KDA_OK"), (1, "KDA_ERR_INVALID_ARGUMENT"), (2, "KDA_ERR_UNSUPPORTED"),
                        (3, "KDA_ERR_WORKSPACE_TOO_SMALL"), (4, "KDA_ERR_HIP")):
         assert kda.status_string(code) == name
@@ -242,3 +242,28 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_gated_decode_validation(kda):
+    """The fused-epilogue decode calls validate the epilogue's arguments (gate,
+    weight, eps) as well as the decode's, before any launch."""
+    lib = kda.library()
+    c = Canary(1 << 12)
+    p = c.ptr
+    cfg, _ = make_cfg(kda)
+    ds = lambda N, gate, w, eps, ptrs=(p,) * 7: lib.kda_decode_step_gated(
+        ctypes.byref(cfg), N, *ptrs, gate, w, eps, p, None)
+    assert ds(2, None, p, 1e-6) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert ds(2, p, None, 1e-6) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert ds(2, p, p, float("nan")) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert ds(2, p, p, -1.0) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert ds(2, p, p, 1e-6, (p, p, p, p, p, None, p)) == kda.KDA_ERR_INVALID_ARGUMENT   # no state
+    assert ds(0, None, None, 1e-6) == kda.KDA_OK
+    dm = lambda N, K, gate, w, eps: lib.kda_decode_multi_gated(ctypes.byref(cfg), N, K, None, p, p, p, p, p, p, p,
+                                                              gate, w, eps, p, None, None)
+    assert dm(2, 3, None, p, 1e-6) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert dm(2, 3, p, None, 1e-6) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert dm(2, 3, p, p, -0.5) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert dm(2, 65, p, p, 1e-6) == kda.KDA_ERR_UNSUPPORTED
+    assert dm(0, 3, None, None, 1e-6) == kda.KDA_OK
+    assert c.untouched()

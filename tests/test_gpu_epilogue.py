@@ -157,3 +157,63 @@ def test_output_gate_grid_stride(kda):
     ref = oracle.output_gate(as_f64(o.reshape(n * H, d)[rows], BF16), as_f64(gate.reshape(n * H, d)[rows], BF16), w)
     ok, e = check_bf16_output(as_f64(y_rows, BF16), ref, 1e-5)
     assert ok, f"bf16 y error {e:.3e}"
+
+
+# ---- the epilogue fused into the decode step and the serving decode: o never
+# leaves the workgroup; y is checked against the oracle's output epilogue
+# applied to the oracle's decode output, at the composed bound above, and the
+# state and conv history must equal the plain call's bit for bit.
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("io,out", [(BF16, BF16), (BF16, FP32), (FP32, FP32)])
+def test_decode_step_gated(kda, d, io, out):
+    from kda_inputs import workload_decode
+    from kda_inputs.torch_io import decode_to_device, tokens_to_device
+    N, H, steps = 7, 3, 3
+    dp = workload_decode(N=N, H=H, d=d, steps=steps, io=io, workload_id=1500 + d)
+    dev = torch.device("cuda:0")
+    cfg, S, cs = decode_to_device(dp, dev, out_dtype=torch.bfloat16 if out == BF16 else torch.float32)
+    _, S2, cs2 = decode_to_device(dp, dev)
+    params = (dp.w_q, dp.w_k, dp.w_v, dp.A_log, dp.dt_bias)
+    S_ref, c_ref = dp.state.astype(np.float64), dp.conv_state
+    core = 2e-3 if io == BF16 else 1e-5
+    for step in range(steps):
+        toks = dp.tokens(step)
+        gate, w = make_output_gate_inputs(1500 + d, N, H, d, io, step=step)
+        dt = tokens_to_device(toks, io, dev)
+        y = kda.kda_decode_step_gated(cfg, *dt, S, cs, to_torch(gate, io, dev), torch.from_numpy(w).to(dev),
+                                      eps=1e-6)
+        kda.kda_decode_step(cfg, *dt, S2, cs2)
+        torch.cuda.synchronize()
+        o_ref, S_ref, c_ref = oracle.decode_reference(S_ref, c_ref, toks, params, H, d, d, io)
+        check_composed(y, o_ref, as_f64(gate, io), w, core, o_bf16=False)
+        assert torch.equal(S, S2) and torch.equal(cs, cs2)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("io", [BF16, FP32])
+def test_decode_multi_gated(kda, d, io):
+    from kda_inputs import make_tokens, workload_decode
+    from kda_inputs.torch_io import decode_to_device, tokens_to_device
+    N, K, P, H = 5, 3, 8, 4
+    pool = workload_decode(N=P, H=H, d=d, steps=1, io=io, workload_id=1600 + d)
+    dev = torch.device("cuda:0")
+    cfg, S, cs = decode_to_device(pool, dev, out_dtype=torch.bfloat16)
+    _, S2, cs2 = decode_to_device(pool, dev)
+    toks = make_tokens(1601 + d, N * K, H, d, d, io)
+    q, k, v, alpha, b = tokens_to_device(toks, io, dev)
+    dt = (q.view(N, K, -1), k.view(N, K, -1), v.view(N, K, -1), alpha.view(N, K, H, d), b.view(N, K, H))
+    gate, w = make_output_gate_inputs(1602 + d, N * K, H, d, io)
+    slots, commit = [6, -1, 0, 3, 7], [3, 0, 1, 2, 0]
+    it = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
+    y = kda.kda_decode_multi_gated(cfg, *dt, S, cs, to_torch(gate, io, dev).view(N, K, H, d),
+                                   torch.from_numpy(w).to(dev), slots=it(slots), n_commit=it(commit))
+    kda.kda_decode_multi(cfg, *dt, S2, cs2, slots=it(slots), n_commit=it(commit))
+    torch.cuda.synchronize()
+    params = (pool.w_q, pool.w_k, pool.w_v, pool.A_log, pool.dt_bias)
+    o_ref, _, _ = oracle.decode_multi_reference(pool.state, pool.conv_state, np.array(slots), toks, params,
+                                                H, d, d, io, K, n_commit=commit)
+    active = [n for n in range(N) if slots[n] >= 0]
+    g64 = as_f64(gate, io).reshape(N, K, H, d)
+    check_composed(y[active], o_ref[active], g64[active], w, 2e-3 if io == BF16 else 1e-5, o_bf16=False)
+    assert torch.equal(S, S2) and torch.equal(cs, cs2)
