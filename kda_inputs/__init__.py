@@ -32,6 +32,7 @@ import numpy as np
 
 BF16 = "bf16"
 FP32 = "fp32"
+FP64 = "fp64"   # float64 storage: only for oracle-side tests (finite differences)
 
 # tensor ids inside the seed sequence
 T_Q, T_K, T_V, T_ALPHA, T_B = 0, 1, 2, 3, 4
@@ -71,9 +72,11 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 value of a stored tensor (bf16 bits or float32)."""
+    """Exact float64 value of a stored tensor (bf16 bits, float32 or float64)."""
     if dtype == BF16:
         return bf16_bits_to_f32(x).astype(np.float64)
+    if dtype == FP64:
+        return np.asarray(x, dtype=np.float64)
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 

@@ -22,6 +22,7 @@ from kda_inputs import BF16, FP32, Problem, as_f64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "kda_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
 
 FLAG_SKIP_CONV = 1
@@ -36,11 +37,13 @@ DEFAULT_ONORM_EPS = 1e-6     # o_norm epsilon (not stated on the pages; a readin
 
 
 def build(force: bool = False) -> str:
-    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so``."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile the C oracle (forward and gradient) with gcc into
+    ``oracle/libkda_oracle.so``."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD))
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall",
-                               "-o", tmp, _SRC, "-lm", "-lpthread"])
+                               "-o", tmp, _SRC, _SRC_BWD, "-lm", "-lpthread"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -67,6 +70,17 @@ def _load():
             dp, dp, dp, dp, dp]
         lib.kda_oracle_output_gate.restype = None
         lib.kda_oracle_output_gate.argtypes = [ctypes.c_long, ctypes.c_int, dp, dp, dp, ctypes.c_double, dp]
+        lib.kda_oracle_backward.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [
+            ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_uint,
+            dp, dp, dp, dp,
+            dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_recurrence_bwd.restype = None
+        lib.kda_oracle_recurrence_bwd.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, ctypes.c_long, dp,
+            dp, dp, dp, dp, dp, dp]
         lib.kda_oracle_recurrence.restype = None
         lib.kda_oracle_recurrence.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, ctypes.c_long]
@@ -187,6 +201,73 @@ def recurrence(q, k, v, g, beta, S0=None):
     o = np.zeros((L, dv))
     lib.kda_oracle_recurrence(L, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(o), dv)
     return o, S
+
+
+def backward(p: Problem, dO, dST=None, *, scale: float = 1.0, lower_bound: float = DEFAULT_LOWER_BOUND,
+             eps: float = DEFAULT_EPS, flags: int = 0, initial_state=None, conv_state=None,
+             nthreads: Optional[int] = None):
+    """Gradient of a packed problem's outputs (o and the final state) with
+    respect to every input: the vector-Jacobian product for the loss
+    gradients dO [total_T, H, dv] and dST [N, H, dk, dv] (None: the final
+    state does not enter the loss).
+
+    Returns a dict of float64 arrays: dq, dk [total_T, H*dk]; dv [total_T,
+    H*dv]; dalpha [total_T, H, dk]; db [total_T, H]; dS0 [N, H, dk, dv];
+    dconv [N, 3, Ctot] (gradient w.r.t. the incoming conv history);
+    dw_q, dw_k [H*dk, 4]; dw_v [H*dv, 4]; ddt_bias [H*dk]; dA_log [H]."""
+    lib = _load()
+    io = p.io
+    H, dk, dv = p.H, p.dk, p.dv
+    N = len(p.seqlens)
+    cu = np.ascontiguousarray(p.cu_seqlens, dtype=np.int64)
+    q, k, v = _f64(p.q, io), _f64(p.k, io), _f64(p.v, io)
+    alpha, b = _f64(p.alpha, io), _f64(p.b, io)
+    w_q, w_k, w_v = _f64(p.w_q, io), _f64(p.w_k, io), _f64(p.w_v, io)
+    A_log = np.ascontiguousarray(p.A_log, dtype=np.float64)
+    dt_bias = np.ascontiguousarray(p.dt_bias, dtype=np.float64)
+    S0 = initial_state if initial_state is not None else p.initial_state
+    S0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+    cs = conv_state if conv_state is not None else p.conv_state
+    if cs is not None and cs.dtype == np.uint16:
+        cs = as_f64(cs, BF16)
+    cs = None if cs is None else np.ascontiguousarray(np.asarray(cs, dtype=np.float64))
+    dO = np.ascontiguousarray(np.asarray(dO, dtype=np.float64))
+    dST = None if dST is None else np.ascontiguousarray(np.asarray(dST, dtype=np.float64))
+    T = p.total_T
+    assert dO.shape == (T, H, dv) and (dST is None or dST.shape == (N, H, dk, dv))
+    assert S0 is None or S0.shape == (N, H, dk, dv)
+    assert cs is None or cs.shape == (N, 3, p.ctot)
+    out = {"dq": np.zeros((T, H * dk)), "dk": np.zeros((T, H * dk)), "dv": np.zeros((T, H * dv)),
+           "dalpha": np.zeros((T, H, dk)), "db": np.zeros((T, H)), "dS0": np.zeros((N, H, dk, dv)),
+           "dconv": np.zeros((N, 3, p.ctot)), "dw_q": np.zeros((H * dk, 4)), "dw_k": np.zeros((H * dk, 4)),
+           "dw_v": np.zeros((H * dv, 4)), "ddt_bias": np.zeros(H * dk), "dA_log": np.zeros(H)}
+    nt = nthreads if nthreads is not None else default_threads()
+    lib.kda_oracle_backward(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        _p(q), _p(k), _p(v), _p(alpha), _p(b), _p(w_q), _p(w_k), _p(w_v), _p(A_log), _p(dt_bias),
+        float(scale), float(lower_bound), float(eps), int(flags), _p(S0), _p(cs), _p(dO), _p(dST),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dalpha"]), _p(out["db"]), _p(out["dS0"]),
+        _p(out["dconv"]), _p(out["dw_q"]), _p(out["dw_k"]), _p(out["dw_v"]), _p(out["ddt_bias"]),
+        _p(out["dA_log"]), int(nt))
+    return out
+
+
+def recurrence_backward(q, k, v, g, beta, S0, dO, dST=None):
+    """Gradient of the token recurrence alone (one head, post-preprocess
+    inputs): returns (dq, dk, dv, dg, dbeta, dS0), float64."""
+    lib = _load()
+    q, k, v, g = (np.ascontiguousarray(np.asarray(a, dtype=np.float64)) for a in (q, k, v, g))
+    beta = np.ascontiguousarray(np.asarray(beta, dtype=np.float64))
+    L, dk = q.shape
+    dv = v.shape[1]
+    S0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64))
+    dO = np.ascontiguousarray(np.asarray(dO, dtype=np.float64))
+    dST = None if dST is None else np.ascontiguousarray(np.asarray(dST, dtype=np.float64))
+    dq, dkk, dg = np.zeros((L, dk)), np.zeros((L, dk)), np.zeros((L, dk))
+    dvv, dbeta, dS0 = np.zeros((L, dv)), np.zeros(L), np.zeros((dk, dv))
+    lib.kda_oracle_recurrence_bwd(L, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(dO), dv, _p(dST),
+                                  _p(dq), _p(dkk), _p(dvv), _p(dg), _p(dbeta), _p(dS0))
+    return dq, dkk, dvv, dg, dbeta, dS0
 
 
 def decode_reference(S, conv_state, tokens, params, H, dk, dv, io, *, scale=1.0,
