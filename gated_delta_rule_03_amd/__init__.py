@@ -47,7 +47,10 @@ NUM_STAGES = len(STAGES)
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
             "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_decode_multi",
-            "kda_decode_step_gated", "kda_decode_multi_gated", "kda_output_gate")
+            "kda_decode_step_gated", "kda_decode_multi_gated", "kda_output_gate", "kda_varlen_prefill_noalloc")
+
+# the fixed scratch behind kda_varlen_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class KdaError(RuntimeError):
@@ -96,6 +99,8 @@ def _load_library():
     lib.kda_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_varlen_prefill.restype = ctypes.c_int
     lib.kda_varlen_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_varlen_prefill_noalloc.restype = ctypes.c_int
+    lib.kda_varlen_prefill_noalloc.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_multi.restype = ctypes.c_int
@@ -247,6 +252,23 @@ def kda_varlen_prefill(cfg: Config, cu_seqlens, q, k, v, alpha, b, initial_state
                                  _ptr(o), _ptr(final_state), _ptr(conv_state_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "kda_varlen_prefill")
+    return o, final_state, conv_state_out
+
+
+def kda_varlen_prefill_noalloc(cfg: Config, cu_seqlens, q, k, v, alpha, b, initial_state=None, conv_state_in=None,
+                               *, o, final_state=None, conv_state_out=None, stream=None):
+    """kda_varlen_prefill on the library's fixed per-GPU scratch: no workspace
+    argument and no allocation (o must be passed in).  Batches whose
+    workspace exceeds NOALLOC_SCRATCH_BYTES raise KdaError
+    (KDA_ERR_WORKSPACE_TOO_SMALL).  Returns (o, final_state, conv_state_out)."""
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    st = _lib.kda_varlen_prefill_noalloc(ctypes.byref(cfg.c_struct()), N, q.shape[0], _ptr(cu_seqlens), _ptr(q),
+                                         _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(initial_state),
+                                         _ptr(conv_state_in), _ptr(o), _ptr(final_state), _ptr(conv_state_out),
+                                         _stream(stream))
+    _check(st, "kda_varlen_prefill_noalloc")
     return o, final_state, conv_state_out
 
 

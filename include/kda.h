@@ -185,6 +185,34 @@ kda_status_t kda_varlen_prefill(const kda_config_t *cfg, int32_t N, int32_t tota
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_varlen_prefill without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  The workspace is a fixed array of
+ * KDA_NOALLOC_SCRATCH_BYTES in the library's device memory, one per GPU,
+ * held from the first call on that GPU until the process ends; the call
+ * allocates nothing.  Arguments, layouts and results as for
+ * kda_varlen_prefill.
+ *   - A batch whose workspace (kda_varlen_workspace_bytes) exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES is refused with KDA_ERR_WORKSPACE_TOO_SMALL
+ *     before any device call.  At H = 32, dk = dv = 128, bf16, the chunked
+ *     form needs ~144.5 KB per (64-token chunk, head): up to ~1800 chunk-heads,
+ *     e.g. 3 x 1024 tokens x 32 heads (4096 x 32 does not fit).
+ *   - Every call on one GPU uses that GPU's single array: calls that overlap
+ *     in time on one GPU (different streams, different threads) race and
+ *     must be serialised by the caller.  Nothing from a previous call needs
+ *     clearing: each call writes the scratch bytes it reads.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+kda_status_t kda_varlen_prefill_noalloc(const kda_config_t *cfg, int32_t N, int32_t total_T,
+                                        const int32_t *cu_seqlens,
+                                        const void *q, const void *k, const void *v,
+                                        const void *alpha, const void *b,
+                                        const float *initial_state, const void *conv_state_in,
+                                        void *o, float *final_state, void *conv_state_out,
+                                        void *stream);
+
+/*
  * One decode step: one new token for each of N independent sequences
  * (the fused recurrent form; AliceAI page, section 五).
  *   q, k           [N][H*dk] io_dtype;  v [N][H*dv]
