@@ -521,7 +521,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the 4K prefill, decode, varlen, no-clamp prefill and output-gate measurements")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device-to-device copy (to scale HBM traffic counters)")
+                    help="also run a plain 1 GiB device-to-device copy and a 1 GiB elementwise multiply "
+                         "(to scale HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA core has no cross-GPU path here (asked for --gpus {args.gpus})",
@@ -540,6 +541,8 @@ def main():
         src.fill_(1.0)
         for _ in range(3):
             dst.copy_(src)
+        for _ in range(3):             # and a plain elementwise kernel: 1 GiB read, 1 GiB written
+            torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     B, T = 4, 32768
