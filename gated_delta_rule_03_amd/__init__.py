@@ -42,12 +42,13 @@ FLAG_RAW_GATE = 1 << 2
 FLAG_RAW_BETA = 1 << 3
 FLAG_BETA_X2 = 1 << 4
 
-STAGES = ("chunk_table", "chunk_prep", "chunk_scan", "conv_state", "decode", "output_gate")
+STAGES = ("chunk_table", "chunk_prep", "chunk_scan", "conv_state", "decode", "output_gate", "backward")
 NUM_STAGES = len(STAGES)
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
             "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_decode_multi",
-            "kda_decode_step_gated", "kda_decode_multi_gated", "kda_output_gate", "kda_varlen_prefill_noalloc")
+            "kda_decode_step_gated", "kda_decode_multi_gated", "kda_output_gate", "kda_varlen_prefill_noalloc",
+            "kda_varlen_backward_workspace_bytes", "kda_varlen_backward")
 
 # the fixed scratch behind kda_varlen_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 256 << 20
@@ -101,6 +102,10 @@ def _load_library():
     lib.kda_varlen_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_varlen_prefill_noalloc.restype = ctypes.c_int
     lib.kda_varlen_prefill_noalloc.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_varlen_backward_workspace_bytes.restype = sz
+    lib.kda_varlen_backward_workspace_bytes.argtypes = [cfgp, i32, i32]
+    lib.kda_varlen_backward.restype = ctypes.c_int
+    lib.kda_varlen_backward.argtypes = [cfgp, i32, i32] + [vp] * 23 + [sz, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_multi.restype = ctypes.c_int
@@ -270,6 +275,43 @@ def kda_varlen_prefill_noalloc(cfg: Config, cu_seqlens, q, k, v, alpha, b, initi
                                          _stream(stream))
     _check(st, "kda_varlen_prefill_noalloc")
     return o, final_state, conv_state_out
+
+
+def kda_varlen_backward_workspace_bytes(cfg: Config, N: int, total_T: int) -> int:
+    return int(_lib.kda_varlen_backward_workspace_bytes(ctypes.byref(cfg.c_struct()), N, total_T))
+
+
+def kda_varlen_backward(cfg: Config, cu_seqlens, q, k, v, alpha, b, initial_state=None, conv_state_in=None, *,
+                        d_o, d_final_state=None, want_initial_state=True, want_conv_state=True, workspace=None,
+                        stream=None):
+    """Gradient of a loss through o and the final state of kda_varlen_prefill
+    with respect to every input and parameter.  d_o [total_T, H, dv] (out
+    dtype), d_final_state [N, H, dk, dv] fp32 or None.  Returns a dict of
+    fp32 tensors: dq, dk [total_T, H*dk], dv [total_T, H*dv], dalpha
+    [total_T, H, dk], db [total_T, H], dS0 [N, H, dk, dv] (or None), dconv
+    [N, 3, Ctot] (or None), dw_q, dw_k [H*dk, 4], dw_v [H*dv, 4], ddt_bias
+    [H*dk], dA_log [H]."""
+    N = cu_seqlens.numel() - 1
+    total = q.shape[0]
+    H, dk, dv = cfg.num_heads, cfg.head_k_dim, cfg.head_v_dim
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    dev = q.device
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = {"dq": f(total, H * dk), "dk": f(total, H * dk), "dv": f(total, H * dv), "dalpha": f(total, H, dk),
+         "db": f(total, H), "dS0": f(N, H, dk, dv) if want_initial_state else None,
+         "dconv": f(N, 3, cfg.ctot) if want_conv_state else None, "dw_q": f(H * dk, 4), "dw_k": f(H * dk, 4),
+         "dw_v": f(H * dv, 4), "ddt_bias": f(H * dk), "dA_log": f(H)}
+    nbytes = kda_varlen_backward_workspace_bytes(cfg, N, total)
+    ws = _workspace(nbytes, dev, workspace)
+    st = _lib.kda_varlen_backward(ctypes.byref(cfg.c_struct()), N, total, _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(alpha), _ptr(b), _ptr(initial_state), _ptr(conv_state_in),
+                                  _ptr(d_o), _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                  _ptr(g["dalpha"]), _ptr(g["db"]), _ptr(g["dS0"]), _ptr(g["dconv"]),
+                                  _ptr(g["dw_q"]), _ptr(g["dw_k"]), _ptr(g["dw_v"]), _ptr(g["ddt_bias"]),
+                                  _ptr(g["dA_log"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "kda_varlen_backward")
+    return g
 
 
 def kda_decode_step(cfg: Config, q, k, v, alpha, b, state, conv_state, *, o=None, stream=None):

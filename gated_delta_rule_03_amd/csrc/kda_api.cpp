@@ -162,11 +162,103 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   return KDA_OK;
 }
 
+// The backward's workspace: the chunk table, then per 16-token block and
+// head its record, the block-start state and the block-end adjoint, Delta and
+// its gradient; the conv outputs' gradient per token; the partial parameter
+// gradients per chunk / block.
+struct BwdLayout {
+  size_t cu, chunk0, chunk_seq, desc, recs, Sblk, dSblk, Dblk, dDblk, dy, pdw, pdtb, pAlog, total;
+};
+
+BwdLayout make_bwd_layout(const kda_config_t* cfg, int64_t N, int64_t max_chunks, int64_t total_T) {
+  const int64_t H = cfg->num_heads, D = cfg->head_k_dim;
+  const int64_t mc = max_chunks > 0 ? max_chunks : 1;
+  const int64_t blocks = mc * (kda::kChunk / 16);
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  L.cu = take((N + 1) * sizeof(int32_t));
+  L.chunk0 = take((N + 2) * sizeof(int32_t));
+  L.chunk_seq = take(static_cast<size_t>(mc) * sizeof(int32_t));
+  L.desc = take(static_cast<size_t>(mc) * sizeof(int4));
+  L.recs = take(static_cast<size_t>(blocks) * H * kda::bwd_record_bytes(static_cast<int>(D)));
+  L.Sblk = take(static_cast<size_t>(blocks) * H * D * D * 4);
+  L.dSblk = take(static_cast<size_t>(blocks) * H * D * D * 4);
+  L.Dblk = take(static_cast<size_t>(blocks) * H * 16 * D * 4);
+  L.dDblk = take(static_cast<size_t>(blocks) * H * 16 * D * 4);
+  L.dy = take(static_cast<size_t>(total_T > 0 ? total_T : 1) * 3 * H * D * 4);
+  L.pdw = take(static_cast<size_t>(mc) * 3 * H * D * 4 * 4);
+  L.pdtb = take(static_cast<size_t>(blocks) * H * D * 4);
+  L.pAlog = take(static_cast<size_t>(blocks) * H * 4);
+  L.total = off;
+  return L;
+}
+
+// The backward handles the method as described plus beta x2; the other test
+// hooks and the recurrent form's gates (below -5.4) are not built.
+kda_status_t check_backward(const kda_config_t* cfg) {
+  kda_status_t s = check_config(cfg, true);
+  if (s != KDA_OK) return s;
+  if (cfg->flags & ~static_cast<uint32_t>(KDA_FLAG_BETA_X2)) return KDA_ERR_UNSUPPORTED;
+  if (recurrent_form(cfg)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t kda_version(void) { return 102; }
+int32_t kda_version(void) { return 103; }
+
+size_t kda_varlen_backward_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t total_T) {
+  if (check_backward(cfg) != KDA_OK || N < 0 || total_T < 0) return 0;
+  return make_bwd_layout(cfg, N, chunks_varlen(N, total_T), total_T).total;
+}
+
+kda_status_t kda_varlen_backward(const kda_config_t* cfg, int32_t N, int32_t total_T, const int32_t* cu_seqlens,
+                                 const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                                 const float* initial_state, const void* conv_state_in, const void* d_o,
+                                 const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha, float* db,
+                                 float* d_initial_state, float* d_conv_state_in, float* dw_q, float* dw_k,
+                                 float* dw_v, float* ddt_bias, float* dA_log, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  kda_status_t s = check_backward(cfg);
+  if (s != KDA_OK) return s;
+  if (N < 0 || total_T < 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (N == 0) return KDA_OK;
+  if (!cu_seqlens || !dw_q || !dw_k || !dw_v || !ddt_bias || !dA_log) return KDA_ERR_INVALID_ARGUMENT;
+  if (total_T > 0 && (!q || !k || !v || !alpha || !b || !d_o || !dq || !dk || !dv || !dalpha || !db))
+    return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t mc = chunks_varlen(N, total_T);
+  if (mc * (kda::kChunk / 16) * cfg->num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  const BwdLayout L = make_bwd_layout(cfg, N, mc, total_T);
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < L.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const Params p = make_params(cfg);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* cu_ws = reinterpret_cast<int32_t*>(ws + L.cu);
+  int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
+  int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
+  int4* desc = reinterpret_cast<int4*>(ws + L.desc);
+  ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N};
+  PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, nullptr, nullptr, nullptr};
+  kda::BackwardIO g{d_o, d_final_state, dq, dk, dv, dalpha, db, d_initial_state, d_conv_state_in,
+                    dw_q, dw_k, dw_v, ddt_bias, dA_log};
+  kda::BackwardWS w{reinterpret_cast<uint8_t*>(ws + L.recs), reinterpret_cast<float*>(ws + L.Sblk),
+                    reinterpret_cast<float*>(ws + L.dSblk), reinterpret_cast<float*>(ws + L.Dblk),
+                    reinterpret_cast<float*>(ws + L.dDblk), reinterpret_cast<float*>(ws + L.dy),
+                    reinterpret_cast<float*>(ws + L.pdw), reinterpret_cast<float*>(ws + L.pdtb),
+                    reinterpret_cast<float*>(ws + L.pAlog)};
+  const int imc = static_cast<int>(mc);
+  s = stage(cfg, KDA_STAGE_CHUNK_TABLE, st, [&] {
+    return kda::launch_build_chunks(cu_seqlens, N, 0, cu_ws, chunk0, chunk_seq, desc, imc, p.H, p.D, st);
+  });
+  if (s != KDA_OK) return s;
+  return stage(cfg, KDA_STAGE_BACKWARD, st, [&] {
+    return kda::launch_backward(p, t, io, g, w, N, imc, cfg->io_dtype == KDA_BF16, cfg->out_dtype == KDA_BF16, st);
+  });
+}
 
 const char* kda_status_string(kda_status_t status) {
   switch (status) {

@@ -174,4 +174,39 @@ struct DecodeMultiIO {
 hipError_t launch_decode_multi(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16, bool out_bf16,
                                hipStream_t st);
 
+// The backward pass (gradient of o and of the final state).
+struct BackwardIO {
+  const void* dO;            // [total_T][H][dv] out dtype: gradient of o
+  const float* dS_final;     // [N][H][dk][dv] gradient of the final state, or null
+  float* dq;                 // [total_T][H*dk] gradient of raw q (fp32)
+  float* dk;
+  float* dv;                 // [total_T][H*dv]
+  float* dalpha;             // [total_T][H][dk]
+  float* db;                 // [total_T][H]
+  float* dS_init;            // [N][H][dk][dv] or null
+  float* dconv;              // [N][3][Ctot] or null
+  float* dw_q;               // [H*dk][4]
+  float* dw_k;
+  float* dw_v;               // [H*dv][4]
+  float* ddt_bias;           // [H*dk]
+  float* dA_log;             // [H]
+};
+
+// Workspace of the backward (besides the chunk table).
+struct BackwardWS {
+  uint8_t* recs;             // per (16-token block, head) records
+  float* Sblk;               // state at every block's start   [blocks][H][D][D]
+  float* dSblk;              // adjoint of every block's end state
+  float* Dblk;               // Delta of every block            [blocks][H][16][D]
+  float* dDblk;              // its gradient
+  float* dy;                 // gradient of the conv outputs    [total_T][3][H*D]
+  float* pdw;                // per-chunk conv-weight partials  [chunks][3][H*D][4]
+  float* pdtb;               // per-block dt_bias partials      [blocks][H][D]
+  float* pAlog;              // per-block A_log partials        [blocks][H]
+};
+
+size_t bwd_record_bytes(int D);
+hipError_t launch_backward(const Params& p, const ChunkTable& t, const PrefillIO& io, const BackwardIO& g,
+                           const BackwardWS& ws, int N, int max_chunks, bool io_bf16, bool do_bf16, hipStream_t st);
+
 }  // namespace kda

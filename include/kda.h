@@ -90,7 +90,8 @@ typedef enum kda_stage {
     KDA_STAGE_CONV_STATE = 3,   /* conv history out                                           */
     KDA_STAGE_DECODE = 4,       /* the decode step kernel (also kda_decode_multi)             */
     KDA_STAGE_OUTPUT_GATE = 5,  /* the o_norm + sigmoid output-gate epilogue                  */
-    KDA_NUM_STAGES = 6
+    KDA_STAGE_BACKWARD = 6,     /* the backward pass's kernels (after its chunk table)        */
+    KDA_NUM_STAGES = 7
 } kda_stage_t;
 
 typedef struct kda_config {
@@ -211,6 +212,45 @@ kda_status_t kda_varlen_prefill_noalloc(const kda_config_t *cfg, int32_t N, int3
                                         const float *initial_state, const void *conv_state_in,
                                         void *o, float *final_state, void *conv_state_out,
                                         void *stream);
+
+/*
+ * Backward pass of kda_varlen_prefill: the gradient of a loss through o and
+ * the final state with respect to every input and parameter (the models on
+ * the Ling pages are trained natively with KDA layers; the pages give only
+ * the forward, AliceAI page, section 二, whose reverse-mode derivative this
+ * computes).  The forward is recomputed inside; nothing from a forward call
+ * is needed.  Inputs are those of kda_varlen_prefill (same layouts, dtypes
+ * and cu_seqlens rules) plus
+ *   d_o            [total_T][H][dv] out_dtype: dLoss/do
+ *   d_final_state  [N][H][dk][dv] fp32: dLoss/dfinal_state, or NULL (zero)
+ * Outputs, all fp32 (every element written):
+ *   dq, dk         [total_T][H*dk]   gradients of the raw (pre-conv) q, k
+ *   dv             [total_T][H*dv]
+ *   dalpha         [total_T][H][dk]  (0 where the safe gate clamped g)
+ *   db             [total_T][H]
+ *   d_initial_state [N][H][dk][dv], or NULL if not wanted
+ *   d_conv_state_in [N][3][Ctot] gradient of the incoming conv history
+ *                  (zeros when it was NULL), or NULL if not wanted
+ *   dw_q, dw_k     [H*dk][4], dw_v [H*dv][4], ddt_bias [H*dk], dA_log [H]:
+ *                  summed over all sequences of the batch
+ * Supported: the chunked form's gates (gate_lower_bound >= -5.4) and
+ * flags 0 or KDA_FLAG_BETA_X2; anything else is KDA_ERR_UNSUPPORTED.  The
+ * workspace (kda_varlen_backward_workspace_bytes) holds per 16-token block
+ * and head about 2 dk dv + 6 * 16 dk floats (~170 KB at dk = dv = 128).
+ * Timing stages: KDA_STAGE_CHUNK_TABLE, then KDA_STAGE_BACKWARD.
+ */
+size_t kda_varlen_backward_workspace_bytes(const kda_config_t *cfg, int32_t N, int32_t total_T);
+
+kda_status_t kda_varlen_backward(const kda_config_t *cfg, int32_t N, int32_t total_T,
+                                 const int32_t *cu_seqlens,
+                                 const void *q, const void *k, const void *v,
+                                 const void *alpha, const void *b,
+                                 const float *initial_state, const void *conv_state_in,
+                                 const void *d_o, const float *d_final_state,
+                                 float *dq, float *dk, float *dv, float *dalpha, float *db,
+                                 float *d_initial_state, float *d_conv_state_in,
+                                 float *dw_q, float *dw_k, float *dw_v, float *ddt_bias, float *dA_log,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step: one new token for each of N independent sequences

@@ -1,0 +1,86 @@
+"""GPU parity of the backward pass (kda_varlen_backward) against the fp64
+gradient oracle (oracle/kda_oracle_bwd.c, pinned by finite differences).
+
+Every gradient the call returns is compared element by element: those of the
+raw q, k, v, alpha and b, the initial state, the incoming conv history, the
+conv weights, dt_bias and A_log.  The GPU computes in fp32 from the same
+stored inputs; the bound is max|g - g_ref| <= BOUND x RMS(g_ref) per tensor,
+with BOUND = 1e-4.  Where it comes from: every product is an fp32 sum of at
+most D (<= 128) or 16 terms, good to ~1e-6 relative; the gate's chain carries
+the in-block decay factors e^{+-G}, whose exponents reach 16 x 5.4 = 86 and
+are rounded to fp32 (86 x 2^-24 = 5e-6 relative per factor), and the
+reverse cumulative sums over a block add up to 16 of them.  Measured: at most
+3.6e-5 (d alpha, strongly decaying heads), everything else below 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kda_inputs import BF16, FP32, as_f64, make_problem
+from kda_inputs.torch_io import problem_to_device, to_torch
+from tests.helpers import max_over_rms, rel_fro
+from tests.test_gpu_parity import kda  # noqa: F401  (fixture)
+
+pytestmark = pytest.mark.gpu
+
+BOUND = 1e-4
+NAMES = ("dq", "dk", "dv", "dalpha", "db", "dS0", "dconv", "dw_q", "dw_k", "dw_v", "ddt_bias", "dA_log")
+
+
+def run(kda, p, flags=0, with_dST=True, out=FP32, seed=0):
+    dev = torch.device("cuda:0")
+    out_t = torch.float32 if out == FP32 else torch.bfloat16
+    cfg, t = problem_to_device(p, dev, out_dtype=out_t, flags=flags)
+    r = np.random.default_rng(7000 + seed)
+    dO = r.standard_normal((p.total_T, p.H, p.dv)).astype(np.float32)
+    if out == BF16:
+        from kda_inputs import f32_to_bf16_bits
+        dO = f32_to_bf16_bits(dO)
+    N = len(p.seqlens)
+    dST = r.standard_normal((N, p.H, p.dk, p.dv)).astype(np.float32) if with_dST else None
+    g = kda.kda_varlen_backward(cfg, t["cu_seqlens"], t["q"], t["k"], t["v"], t["alpha"], t["b"],
+                                t["initial_state"], t["conv_state"], d_o=to_torch(dO, out, dev),
+                                d_final_state=None if dST is None else torch.from_numpy(dST).to(dev))
+    torch.cuda.synchronize()
+    ref = oracle.backward(p, as_f64(dO, out), dST, flags=flags)
+    errs = {}
+    for name in NAMES:
+        got = g[name].double().cpu().numpy().reshape(ref[name].shape)
+        assert np.isfinite(got).all(), f"{name} not finite"
+        errs[name] = (max_over_rms(got, ref[name]), rel_fro(got, ref[name]))
+    print(" ".join(f"{n}={e[0]:.2e}" for n, e in errs.items()))
+    for name, (e, _) in errs.items():
+        assert e <= BOUND, f"{name}: max error {e:.3e} x RMS > {BOUND}"
+    return errs
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_backward_fp32(kda, d):
+    p = make_problem(8000 + d, [100, 1, 0, 64, 37], 2, d, d, FP32, state_seqs=[0, 3], conv_state=True)
+    run(kda, p, seed=d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_bf16(kda, d):
+    p = make_problem(8100 + d, [130, 2, 64, 70], 4, d, d, BF16, state_seqs=[0, 2], conv_state=True)
+    run(kda, p, out=BF16, seed=d)
+
+
+def test_backward_beta_x2_without_state_or_history(kda):
+    p = make_problem(8200, [90, 17, 3], 3, 32, 32, FP32, state_seqs=None, conv_state=False)
+    run(kda, p, flags=oracle.FLAG_BETA_X2, with_dST=False, seed=3)
+
+
+def test_backward_4k_every_gradient(kda):
+    """The short prefill workload's shape: B=1, T=4096, H=32, d=128, bf16 inputs
+    and bf16 dO (256 blocks of 16 tokens per head)."""
+    from kda_inputs import workload_prefill_4k
+    p = workload_prefill_4k()
+    run(kda, p, out=BF16, seed=11)
+
+
+def test_backward_strong_decay_hits_the_clamp(kda):
+    p = make_problem(8300, [150, 40], 2, 64, 64, FP32, state_seqs=[0, 1], conv_state=True)
+    p.A_log = np.full_like(p.A_log, 1.5)      # many log-decays clamped at -5
+    run(kda, p, seed=4)
