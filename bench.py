@@ -464,6 +464,44 @@ def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
                          "bytes_per_launch": nbytes}}
 
 
+def bench_backward(kda, torch, ev, dp, steps=5, warmup=1):
+    """The backward pass of the headline prefill (B=4, T=32768, H=32, d=128,
+    bf16 inputs): gradients of every input and parameter for a random bf16 dO
+    and fp32 d(final state), through kda_varlen_backward."""
+    dev = torch.device("cuda:0")
+    B, T = 4, 32768
+    cfg = dp.config(out_dtype=torch.bfloat16)
+    tz = dp.tensors
+    g = torch.Generator(device=dev)
+    g.manual_seed(9_000_001)
+    d_o = torch.randn((B * T, H, D), generator=g, device=dev).to(torch.bfloat16)
+    dST = torch.randn((B, H, D, D), generator=g, device=dev)
+    ws = torch.empty(kda.kda_varlen_backward_workspace_bytes(cfg, B, B * T), dtype=torch.uint8, device=dev)
+    log(f"[bench] backward workspace {ws.numel() / 2**30:.2f} GiB")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return kda.kda_varlen_backward(cfg, tz["cu_seqlens"], tz["q"], tz["k"], tz["v"], tz["alpha"], tz["b"],
+                                       tz["initial_state"], tz["conv_state"], d_o=d_o, d_final_state=dST,
+                                       workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = ev.create(), ev.create()
+    ev.record(e0, stream.cuda_stream)
+    for _ in range(steps):
+        step()
+    ev.record(e1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / steps
+    log(f"[bench] backward: {ms:.2f} ms per call, {B * T / ms * 1e3 / 1e6:.2f} M tokens/s")
+    del ws
+    return {"workload": "kda backward of the chunked prefill B=4 T=32768 H=32 dk=dv=128, bf16 inputs and dO, "
+                        "fp32 gradients of every input and parameter",
+            "ms_per_call": round(ms, 3), "tokens_per_s": round(B * T / ms * 1e3, 1)}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -571,6 +609,7 @@ def main():
         result["varlen"] = bench_varlen(kda, torch, ev)
         result["prefill_no_clamp"] = bench_prefill_no_clamp(kda, torch, ev, dp)
         result["output_gate"] = bench_output_gate(kda, torch, ev)
+        result["backward"] = bench_backward(kda, torch, ev, dp)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dp)
     print(json.dumps(result), flush=True)

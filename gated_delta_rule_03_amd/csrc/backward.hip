@@ -27,6 +27,8 @@
 //   dG = dQ+ Q+ + dK+ K+ - dK- K-   (through the prefix sums)
 //   dGs = dK~ K~                    (through the suffix sums G_C - G)
 //   dg_t = sum_{r >= t} dG_r + sum_{r < t} dGs_r + dG_C
+// where the terms of dG that come from A and Aqk are summed pair by pair over
+// i < t <= r instead (they cancel elsewhere; see bwd_block_grad_kernel).
 // then the preprocess in reverse (L2 norm, SiLU, conv, gate, beta).
 //
 // Kernels, in launch order (all fp32 arithmetic):
@@ -75,22 +77,24 @@ struct BlockSmem {
   float q[kBlk][D];      // q^ (normalised, scaled)
   float k[kBlk][D];      // k^ (normalised)
   float v[kBlk][D];      // v^
-  float G[kBlk][D];      // inclusive in-block prefix sums of g
-  float Gs[kBlk][D];     // exclusive in-block suffix sums of g (G_C - G)
+  float eP[kBlk][D];     // e^{G}, G the inclusive in-block prefix sum of g
+  float eM[kBlk][D];     // e^{-G}
+  float eS[kBlk][D];     // e^{G_C - G}, from the exclusive in-block suffix sum of g
   float beta[kBlk];
   float nq[kBlk], nk[kBlk];   // the L2 norms sqrt(|u|^2 + eps) of q and k
 };
 
 // Conv + SiLU, L2 norm, gate and beta of one block's tokens for head h, into
 // shared memory.  Rows past the block's end are zero, with g = beta = 0.
-template <int D, bool IO_BF16>
+template <int D, bool IO_BF16, int NT>
 __device__ void block_preprocess(const Params& p, const PrefillIO& io, const BlockInfo& b, int h, BlockSmem<D>& s) {
+  static_assert(NT >= 2 * kBlk * 8, "the L2 norms take 8 lanes for each of 32 rows");
   const int tid = threadIdx.x;
   const size_t HD = static_cast<size_t>(p.H) * D;
   const size_t Ctot = 3 * HD;
   const int seq = b.seq;
   const int64_t seq0 = b.tok0 - b.tau0;   // packed index of the sequence's first token
-  for (int task = tid; task < 4 * D; task += kBT) {
+  for (int task = tid; task < 4 * D; task += NT) {
     const int role = task / D, ch = task % D;
     const size_t col = static_cast<size_t>(h) * D + ch;
     if (role < 3) {
@@ -128,11 +132,12 @@ __device__ void block_preprocess(const Params& p, const PrefillIO& io, const Blo
           g[r] = (p.flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound);
         }
         run += g[r];
-        s.G[r][ch] = run;
+        s.eP[r][ch] = expf(run);
+        s.eM[r][ch] = expf(-run);
       }
       float suf = 0.f;
       for (int r = kBlk - 1; r >= 0; --r) {
-        s.Gs[r][ch] = suf;
+        s.eS[r][ch] = expf(suf);
         suf += g[r];
       }
     }
@@ -147,9 +152,9 @@ __device__ void block_preprocess(const Params& p, const PrefillIO& io, const Blo
     s.beta[tid] = be;
   }
   __syncthreads();
-  // L2 norms of q and k: 32 rows, 8 lanes each
-  {
-    const int row = tid / 8, l8 = tid % 8;     // 256 threads: rows 0..15 q, 16..31 k
+  // L2 norms of q and k: 32 rows, 8 lanes each (whole waves: 256 threads)
+  if (tid < 2 * kBlk * 8) {
+    const int row = tid / 8, l8 = tid % 8;     // rows 0..15 q, 16..31 k
     const float* src = row < kBlk ? s.q[row] : s.k[row - kBlk];
     float ss = 0.f;
     for (int c = l8; c < D; c += 8) ss += src[c] * src[c];
@@ -162,7 +167,7 @@ __device__ void block_preprocess(const Params& p, const PrefillIO& io, const Blo
     }
   }
   __syncthreads();
-  for (int e = tid; e < kBlk * D; e += kBT) {
+  for (int e = tid; e < kBlk * D; e += NT) {
     const int r = e / D, c = e % D;
     s.q[r][c] = s.q[r][c] / s.nq[r] * p.scale;
     s.k[r][c] = s.k[r][c] / s.nk[r];
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   const BlockInfo b = block_info(t, blk);
   if (b.ntok <= 0) return;
   const int tid = threadIdx.x;
-  block_preprocess<D, IO_BF16>(p, io, b, h, s);
+  block_preprocess<D, IO_BF16, kBT>(p, io, b, h, s);
   uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
   float* gW = reinterpret_cast<float*>(rec + R.W);
   float* gU = reinterpret_cast<float*>(rec + R.U);
@@ -219,11 +224,10 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   // K-, Q+, K~ and e^{G_C}
   for (int e = tid; e < kBlk * D; e += kBT) {
     const int r = e / D, c = e % D;
-    const float G = s.G[r][c];
-    sKm[r][c] = s.k[r][c] * expf(-G);
-    gQp[e] = s.q[r][c] * expf(G);
-    gKt[e] = s.k[r][c] * expf(s.Gs[r][c]);
-    if (r == 0) geGC[c] = expf(s.G[kBlk - 1][c]);
+    sKm[r][c] = s.k[r][c] * s.eM[r][c];
+    gQp[e] = s.q[r][c] * s.eP[r][c];
+    gKt[e] = s.k[r][c] * s.eS[r][c];
+    if (r == 0) geGC[c] = s.eP[kBlk - 1][c];
   }
   __syncthreads();
   // A (strictly lower) and Aqk (lower with the diagonal): one entry each per thread
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
     float a = 0.f, aq = 0.f;
     if (i <= r) {
       for (int c = 0; c < D; ++c) {
-        const float eg = expf(s.G[r][c]);
+        const float eg = s.eP[r][c];
         const float km = sKm[i][c];
         aq += s.q[r][c] * eg * km;
         if (i < r) a += s.k[r][c] * eg * km;
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
     float w = 0.f, u = 0.f;
     for (int m = 0; m <= r; ++m) {
       const float tb = sT[r][m] * s.beta[m];
-      w += tb * s.k[m][c] * expf(s.G[m][c]);
+      w += tb * s.k[m][c] * s.eP[m][c];
       u += tb * s.v[m][c];
     }
     gW[e] = w;
@@ -272,15 +276,20 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
 // ---------------------------------------------------------------- state scan
 // One workgroup per (sequence, head, value tile of VT columns): the state
 // slice in registers, a thread holding column j = tid % VT of rows
-// tid / VT + m * (256 / VT).
+// tid / VT + m * (256 / VT).  A sequence's blocks are consecutive (block
+// index = 4 x its first chunk + its position); each block's operands are
+// loaded into registers one block ahead and moved to shared memory at the
+// top of the next step, so their latency hides behind a step's arithmetic.
 template <int D, int VT>
 __global__ __launch_bounds__(kBT) void bwd_state_scan_kernel(Params p, ChunkTable t, const float* S_init,
                                                               const uint8_t* recs, float* Sblk, float* Dblk) {
   constexpr BwdRecord R = bwd_record(D);
   constexpr int RG = kBT / VT;          // row groups
   constexpr int RPT = D / RG;           // rows per thread
+  constexpr int TE = (kBlk * D + kBT - 1) / kBT;    // tile elements per thread
+  constexpr int UE = (kBlk * VT + kBT - 1) / kBT;   // U elements per thread
   static_assert(D % RG == 0, "rows split evenly");
-  __shared__ float sW[kBlk][D], sKt[kBlk][D], seG[D];
+  __shared__ float sW[kBlk][D], sKt[kBlk][D], seG[D], sU[kBlk][VT];
   __shared__ float red[RG][kBlk][VT];
   __shared__ float sDel[kBlk][VT];
   const int ntile = D / VT;
@@ -294,60 +303,77 @@ __global__ __launch_bounds__(kBT) void bwd_state_scan_kernel(Params p, ChunkTabl
     const int r = rg + m * RG;
     S[m] = S_init ? S_init[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + j] : 0.f;
   }
-  const int c_begin = t.chunk0[n], c_end = t.chunk0[n + 1];
-  for (int c = c_begin; c < c_end; ++c) {
-    for (int sub = 0; sub < kBlocksPerChunk; ++sub) {
-      const int blk = c * kBlocksPerChunk + sub;
-      const BlockInfo b = block_info(t, blk);
-      if (b.ntok <= 0) break;
-      const size_t bh = static_cast<size_t>(blk) * p.H + h;
-      const uint8_t* rec = recs + bh * R.bytes;
-      const float* gW = reinterpret_cast<const float*>(rec + R.W);
-      const float* gU = reinterpret_cast<const float*>(rec + R.U);
-      const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
-      const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
-      for (int e = tid; e < kBlk * D; e += kBT) {
-        sW[e / D][e % D] = gW[e];
-        sKt[e / D][e % D] = gKt[e];
-      }
-      for (int e = tid; e < D; e += kBT) seG[e] = geG[e];
-      // the state at the block's start
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rg + m * RG;
-        Sblk[bh * SZ + static_cast<size_t>(r) * D + j0 + j] = S[m];
-      }
-      __syncthreads();
-      // Delta = U - W S
-      float acc[kBlk];
-      for (int q = 0; q < kBlk; ++q) acc[q] = 0.f;
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rg + m * RG;
-        for (int q = 0; q < kBlk; ++q) acc[q] += sW[q][r] * S[m];
-      }
-      for (int q = 0; q < kBlk; ++q) red[rg][q][j] = acc[q];
-      __syncthreads();
-      for (int e = tid; e < kBlk * VT; e += kBT) {
-        const int q = e / VT, jj = e % VT;
-        float sum = 0.f;
-        for (int g2 = 0; g2 < RG; ++g2) sum += red[g2][q][jj];
-        const float del = gU[q * D + j0 + jj] - sum;
-        sDel[q][jj] = del;
-        Dblk[bh * kBlk * D + static_cast<size_t>(q) * D + j0 + jj] = del;
-      }
-      __syncthreads();
-      // S <- e^{G_C} S + K~^T Delta
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rg + m * RG;
-        float v = seG[r] * S[m];
-        for (int q = 0; q < kBlk; ++q) v += sKt[q][r] * sDel[q][j];
-        S[m] = v;
-      }
-      __syncthreads();
+  const int L = t.cu[n + 1] - t.cu[n];
+  const int nb = (L + kBlk - 1) / kBlk;
+  const int blk0 = t.chunk0[n] * kBlocksPerChunk;
+  float pW[TE], pK[TE], pU[UE], pE = 0.f;
+  auto fetch = [&](int blk) {
+    const uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
+    const float* gW = reinterpret_cast<const float*>(rec + R.W);
+    const float* gU = reinterpret_cast<const float*>(rec + R.U);
+    const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
+    const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
+    for (int m = 0; m < TE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * D) { pW[m] = gW[e]; pK[m] = gKt[e]; }
     }
+    for (int m = 0; m < UE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * VT) pU[m] = gU[(e / VT) * D + j0 + e % VT];
+    }
+    if (tid < D) pE = geG[tid];
+  };
+  if (nb > 0) fetch(blk0);
+  for (int jb = 0; jb < nb; ++jb) {
+    const int blk = blk0 + jb;
+    const size_t bh = static_cast<size_t>(blk) * p.H + h;
+    for (int m = 0; m < TE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * D) { sW[e / D][e % D] = pW[m]; sKt[e / D][e % D] = pK[m]; }
+    }
+    for (int m = 0; m < UE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * VT) sU[e / VT][e % VT] = pU[m];
+    }
+    if (tid < D) seG[tid] = pE;
+    // the state at the block's start
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      Sblk[bh * SZ + static_cast<size_t>(r) * D + j0 + j] = S[m];
+    }
+    __syncthreads();
+    if (jb + 1 < nb) fetch(blk + 1);
+    // Delta = U - W S
+    float acc[kBlk];
+    for (int q = 0; q < kBlk; ++q) acc[q] = 0.f;
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      for (int q = 0; q < kBlk; ++q) acc[q] += sW[q][r] * S[m];
+    }
+    for (int q = 0; q < kBlk; ++q) red[rg][q][j] = acc[q];
+    __syncthreads();
+    for (int e = tid; e < kBlk * VT; e += kBT) {
+      const int q = e / VT, jj = e % VT;
+      float sum = 0.f;
+      for (int g2 = 0; g2 < RG; ++g2) sum += red[g2][q][jj];
+      const float del = sU[q][jj] - sum;
+      sDel[q][jj] = del;
+      Dblk[bh * kBlk * D + static_cast<size_t>(q) * D + j0 + jj] = del;
+    }
+    __syncthreads();
+    // S <- e^{G_C} S + K~^T Delta
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      float v = seG[r] * S[m];
+      for (int q = 0; q < kBlk; ++q) v += sKt[q][r] * sDel[q][j];
+      S[m] = v;
+    }
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- adjoint scan
+// The state scan's layout, blocks in reverse, operands one block ahead.
 template <int D, int VT, bool DO_BF16>
 __global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTable t, const uint8_t* recs,
                                                                 const void* dO, const float* dS_final, float* dSblk,
@@ -355,6 +381,9 @@ __global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTa
   constexpr BwdRecord R = bwd_record(D);
   constexpr int RG = kBT / VT;
   constexpr int RPT = D / RG;
+  constexpr int TE = (kBlk * D + kBT - 1) / kBT;
+  constexpr int OE = (kBlk * VT + kBT - 1) / kBT;
+  constexpr int AE = (kBlk * kBlk + kBT - 1) / kBT;
   __shared__ float sW[kBlk][D], sKt[kBlk][D], sQp[kBlk][D], seG[D];
   __shared__ float sAqk[kBlk][kBlk];
   __shared__ float sdO[kBlk][VT];
@@ -372,63 +401,85 @@ __global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTa
     const int r = rg + m * RG;
     dS[m] = dS_final ? dS_final[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + j] : 0.f;
   }
-  const int c_begin = t.chunk0[n], c_end = t.chunk0[n + 1];
-  for (int c = c_end - 1; c >= c_begin; --c) {
-    for (int sub = kBlocksPerChunk - 1; sub >= 0; --sub) {
-      const int blk = c * kBlocksPerChunk + sub;
-      const BlockInfo b = block_info(t, blk);
-      if (b.ntok <= 0) continue;
-      const size_t bh = static_cast<size_t>(blk) * p.H + h;
-      const uint8_t* rec = recs + bh * R.bytes;
-      const float* gW = reinterpret_cast<const float*>(rec + R.W);
-      const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
-      const float* gQp = reinterpret_cast<const float*>(rec + R.Qp);
-      const float* gAqk = reinterpret_cast<const float*>(rec + R.Aqk);
-      const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
-      for (int e = tid; e < kBlk * D; e += kBT) {
-        sW[e / D][e % D] = gW[e];
-        sKt[e / D][e % D] = gKt[e];
-        sQp[e / D][e % D] = gQp[e];
-      }
-      for (int e = tid; e < D; e += kBT) seG[e] = geG[e];
-      for (int e = tid; e < kBlk * kBlk; e += kBT) sAqk[e / kBlk][e % kBlk] = gAqk[e];
-      for (int e = tid; e < kBlk * VT; e += kBT) {
-        const int q = e / VT, jj = e % VT;
-        sdO[q][jj] = q < b.ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(b.tok0 + q) * p.H + h) * D + j0 + jj) : 0.f;
-      }
-      // the adjoint of the block's end state
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rg + m * RG;
-        dSblk[bh * SZ + static_cast<size_t>(r) * D + j0 + j] = dS[m];
-      }
-      __syncthreads();
-      // dDelta = Aqk^T dO + K~ dS_C
-      float acc[kBlk];
-      for (int q = 0; q < kBlk; ++q) acc[q] = 0.f;
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rg + m * RG;
-        for (int q = 0; q < kBlk; ++q) acc[q] += sKt[q][r] * dS[m];
-      }
-      for (int q = 0; q < kBlk; ++q) red[rg][q][j] = acc[q];
-      __syncthreads();
-      for (int e = tid; e < kBlk * VT; e += kBT) {
-        const int q = e / VT, jj = e % VT;
-        float sum = 0.f;
-        for (int g2 = 0; g2 < RG; ++g2) sum += red[g2][q][jj];
-        for (int r2 = q; r2 < kBlk; ++r2) sum += sAqk[r2][q] * sdO[r2][jj];
-        sdDel[q][jj] = sum;
-        dDblk[bh * kBlk * D + static_cast<size_t>(q) * D + j0 + jj] = sum;
-      }
-      __syncthreads();
-      // dS0 = Q+^T dO + e^{G_C} dS_C - W^T dDelta
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rg + m * RG;
-        float v = seG[r] * dS[m];
-        for (int q = 0; q < kBlk; ++q) v += sQp[q][r] * sdO[q][j] - sW[q][r] * sdDel[q][j];
-        dS[m] = v;
-      }
-      __syncthreads();
+  const int L = t.cu[n + 1] - t.cu[n];
+  const int nb = (L + kBlk - 1) / kBlk;
+  const int blk0 = t.chunk0[n] * kBlocksPerChunk;
+  const int64_t seq0 = t.cu[n];
+  float pW[TE], pK[TE], pQ[TE], pO[OE], pA[AE], pE = 0.f;
+  auto fetch = [&](int jb) {
+    const int blk = blk0 + jb;
+    const int ntok = min(kBlk, L - jb * kBlk);
+    const uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
+    const float* gW = reinterpret_cast<const float*>(rec + R.W);
+    const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
+    const float* gQp = reinterpret_cast<const float*>(rec + R.Qp);
+    const float* gAqk = reinterpret_cast<const float*>(rec + R.Aqk);
+    const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
+    for (int m = 0; m < TE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * D) { pW[m] = gW[e]; pK[m] = gKt[e]; pQ[m] = gQp[e]; }
     }
+    for (int m = 0; m < AE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * kBlk) pA[m] = gAqk[e];
+    }
+    for (int m = 0; m < OE; ++m) {
+      const int e = tid + m * kBT;
+      const int q = e / VT, jj = e % VT;
+      if (e < kBlk * VT)
+        pO[m] = q < ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + q) * p.H + h) * D + j0 + jj) : 0.f;
+    }
+    if (tid < D) pE = geG[tid];
+  };
+  if (nb > 0) fetch(nb - 1);
+  for (int jb = nb - 1; jb >= 0; --jb) {
+    const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
+    for (int m = 0; m < TE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * D) { sW[e / D][e % D] = pW[m]; sKt[e / D][e % D] = pK[m]; sQp[e / D][e % D] = pQ[m]; }
+    }
+    for (int m = 0; m < AE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * kBlk) sAqk[e / kBlk][e % kBlk] = pA[m];
+    }
+    for (int m = 0; m < OE; ++m) {
+      const int e = tid + m * kBT;
+      if (e < kBlk * VT) sdO[e / VT][e % VT] = pO[m];
+    }
+    if (tid < D) seG[tid] = pE;
+    // the adjoint of the block's end state
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      dSblk[bh * SZ + static_cast<size_t>(r) * D + j0 + j] = dS[m];
+    }
+    __syncthreads();
+    if (jb > 0) fetch(jb - 1);
+    // dDelta = Aqk^T dO + K~ dS_C
+    float acc[kBlk];
+    for (int q = 0; q < kBlk; ++q) acc[q] = 0.f;
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      for (int q = 0; q < kBlk; ++q) acc[q] += sKt[q][r] * dS[m];
+    }
+    for (int q = 0; q < kBlk; ++q) red[rg][q][j] = acc[q];
+    __syncthreads();
+    for (int e = tid; e < kBlk * VT; e += kBT) {
+      const int q = e / VT, jj = e % VT;
+      float sum = 0.f;
+      for (int g2 = 0; g2 < RG; ++g2) sum += red[g2][q][jj];
+      for (int r2 = q; r2 < kBlk; ++r2) sum += sAqk[r2][q] * sdO[r2][jj];
+      sdDel[q][jj] = sum;
+      dDblk[bh * kBlk * D + static_cast<size_t>(q) * D + j0 + jj] = sum;
+    }
+    __syncthreads();
+    // dS0 = Q+^T dO + e^{G_C} dS_C - W^T dDelta
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      float v = seG[r] * dS[m];
+      for (int q = 0; q < kBlk; ++q) v += sQp[q][r] * sdO[q][j] - sW[q][r] * sdDel[q][j];
+      dS[m] = v;
+    }
+    __syncthreads();
   }
   if (dS_init) {
     for (int m = 0; m < RPT; ++m) {
@@ -437,7 +488,7 @@ __global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTa
     }
   }
   // an empty sequence passes its conv history through: no gradient reaches it
-  if (dconv && tile == 0 && c_end == c_begin) {
+  if (dconv && tile == 0 && nb == 0) {
     for (int e = tid; e < 3 * D; e += kBT) {
       const int role = e / D, ch = e % D;
       for (int m = 0; m < 3; ++m)
@@ -447,12 +498,18 @@ __global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTa
 }
 
 // ---------------------------------------------------------------- block gradients
+// Threads of the block-gradient kernel: its shared memory (~134 KB at d = 128)
+// allows one workgroup per compute unit, so it takes two waves per SIMD.
+template <int D>
+constexpr int grad_threads() { return D >= 32 ? 512 : 256; }
+
 template <int D, bool IO_BF16, bool DO_BF16>
-__global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTable t, PrefillIO io, const uint8_t* recs,
+__global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Params p, ChunkTable t, PrefillIO io, const uint8_t* recs,
                                                               const float* Sblk, const float* dSblk, const float* Dblk,
                                                               const float* dDblk, const void* dO, float* dy,
                                                               float* dalpha, float* db, float* pdtb, float* pAlog) {
   constexpr BwdRecord R = bwd_record(D);
+  constexpr int NT = grad_threads<D>();
   constexpr int SC = 16;                  // state columns staged at a time
   __shared__ BlockSmem<D> s;
   __shared__ float sDel[kBlk][D], sdDel[kBlk][D], sdO[kBlk][D];
@@ -460,7 +517,12 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   __shared__ float sX[kBlk][D];           // dW, then dXw
   __shared__ float sT[kBlk][kBlk], sAun[kBlk][kBlk], sdA[kBlk][kBlk], sdAqk[kBlk][kBlk];
   __shared__ float sdbeta[kBlk], sdGC[D];
-  __shared__ float sS0[D][SC + 1], sdSC[D][SC + 1];
+  __shared__ float sStage[2 * D * (SC + 1)];     // S0 / dS_C column slabs, then W and U
+  float (*sS0)[SC + 1] = reinterpret_cast<float (*)[SC + 1]>(sStage);
+  float (*sdSC)[SC + 1] = reinterpret_cast<float (*)[SC + 1]>(sStage + D * (SC + 1));
+  float (*sWt)[D] = reinterpret_cast<float (*)[D]>(sStage);
+  float (*sUt)[D] = reinterpret_cast<float (*)[D]>(sStage + kBlk * D);
+  static_assert(2 * kBlk * D <= 2 * D * (SC + 1), "W and U fit where the slabs were");
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
   const int blk = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   const bool live_chunk = blk / kBlocksPerChunk < t.chunk0[t.N];
@@ -469,11 +531,11 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   const size_t HD = static_cast<size_t>(p.H) * D;
   float* pd = pdtb + (static_cast<size_t>(blk) * p.H + h) * D;
   if (b.ntok <= 0) {          // an empty block adds nothing to the parameter sums
-    for (int e = tid; e < D; e += kBT) pd[e] = 0.f;
+    for (int e = tid; e < D; e += NT) pd[e] = 0.f;
     if (tid == 0) pAlog[static_cast<size_t>(blk) * p.H + h] = 0.f;
     return;
   }
-  block_preprocess<D, IO_BF16>(p, io, b, h, s);
+  block_preprocess<D, IO_BF16, NT>(p, io, b, h, s);
   const size_t bh = static_cast<size_t>(blk) * p.H + h;
   const uint8_t* rec = recs + bh * R.bytes;
   const float* gW = reinterpret_cast<const float*>(rec + R.W);
@@ -482,25 +544,25 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
   const float* S0 = Sblk + bh * D * D;
   const float* dSC = dSblk + bh * D * D;
-  for (int e = tid; e < kBlk * D; e += kBT) {
+  for (int e = tid; e < kBlk * D; e += NT) {
     const int r = e / D, c = e % D;
     sDel[r][c] = Dblk[bh * kBlk * D + e];
     sdDel[r][c] = dDblk[bh * kBlk * D + e];
     sdO[r][c] = r < b.ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(b.tok0 + r) * p.H + h) * D + c) : 0.f;
   }
-  for (int e = tid; e < kBlk * kBlk; e += kBT) sT[e / kBlk][e % kBlk] = gT[e];
+  for (int e = tid; e < kBlk * kBlk; e += NT) sT[e / kBlk][e % kBlk] = gT[e];
   __syncthreads();
 
   // ---- products with S0 and dS_C, staged SC state columns at a time:
   //   dQ+ = dO S0^T, dW = -dDelta S0^T, dK~ = Delta dS_C^T, dG_C = e^{G_C} rowsum(dS_C * S0)
   {
-    constexpr int RPT = kBlk * D / kBT;   // outputs per thread: channel c, rows s0 .. s0 + RPT - 1
+    constexpr int RPT = kBlk * D / NT;   // outputs per thread: channel c, rows s0 .. s0 + RPT - 1
     const int c = tid % D, s0 = (tid / D) * RPT;
     float aQ[RPT], aW[RPT], aK[RPT];
     for (int m = 0; m < RPT; ++m) { aQ[m] = 0.f; aW[m] = 0.f; aK[m] = 0.f; }
     float gc = 0.f;
     for (int j0 = 0; j0 < D; j0 += SC) {
-      for (int e = tid; e < D * SC; e += kBT) {
+      for (int e = tid; e < D * SC; e += NT) {
         const int r = e / SC, jj = e % SC;
         sS0[r][jj] = S0[static_cast<size_t>(r) * D + j0 + jj];
         sdSC[r][jj] = dSC[static_cast<size_t>(r) * D + j0 + jj];
@@ -527,7 +589,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   __syncthreads();
   // ---- dXw = T^T dW (in place through registers), dXu = T^T dDelta (into sdKm as scratch for now: no)
   {
-    constexpr int RPT = kBlk * D / kBT;
+    constexpr int RPT = kBlk * D / NT;
     const int c = tid % D, s0 = (tid / D) * RPT;
     float xw[RPT], xu[RPT];
     for (int m = 0; m < RPT; ++m) {
@@ -548,13 +610,18 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   }
   __syncthreads();
   // ---- dA = -strict_lower(dXw W^T + dXu U^T);  A_un = K+ K-^T;  dAqk = lower(dO Delta^T)
-  {
+  for (int e = tid; e < kBlk * D; e += NT) {
+    sWt[e / D][e % D] = gW[e];
+    sUt[e / D][e % D] = gU[e];
+  }
+  __syncthreads();
+  if (tid < kBlk * kBlk) {
     const int r = tid / kBlk, i = tid % kBlk;
     float da = 0.f, aun = 0.f, daq = 0.f;
     if (i < r) {
       for (int c = 0; c < D; ++c) {
-        da -= sX[r][c] * gW[i * D + c] + sdKm[r][c] * gU[i * D + c];
-        aun += s.k[r][c] * s.k[i][c] * expf(s.G[r][c] - s.G[i][c]);
+        da -= sX[r][c] * sWt[i][c] + sdKm[r][c] * sUt[i][c];
+        aun += s.k[r][c] * s.eP[r][c] * (s.k[i][c] * s.eM[i][c]);
       }
     }
     if (i <= r)
@@ -568,24 +635,27 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   if (tid < kBlk) {
     const int r = tid;
     float d = 0.f;
-    for (int c = 0; c < D; ++c) d += sX[r][c] * s.k[r][c] * expf(s.G[r][c]) + sdKm[r][c] * s.v[r][c];
+    for (int c = 0; c < D; ++c) d += sX[r][c] * s.k[r][c] * s.eP[r][c] + sdKm[r][c] * s.v[r][c];
     for (int i = 0; i < r; ++i) d += sdA[r][i] * sAun[r][i];
     sdbeta[r] = d;
   }
   {
-    constexpr int RPT = kBlk * D / kBT;
+    constexpr int RPT = kBlk * D / NT;
     const int c = tid % D, s0 = (tid / D) * RPT;
-    float dKp[RPT], dKm[RPT], dQp[RPT], dV[RPT];
+    float dKp[RPT], dKm[RPT], dQp[RPT], dV[RPT], gnp[RPT];
     for (int m = 0; m < RPT; ++m) {
       const int r = s0 + m;
       const float be = s.beta[r];
       float kp = be * sX[r][c];                 // Diag(beta) dXw
       float km = 0.f, qp = sdQp[r][c];
-      for (int i = 0; i < r; ++i) kp += be * sdA[r][i] * s.k[i][c] * expf(-s.G[i][c]);        // (beta dA) K-
+      // the decay's gradient through the single-token terms, dO S0^T on Q+ and
+      // beta dXw on K+ (the pair terms of A and Aqk are summed separately)
+      gnp[m] = qp * s.q[r][c] * s.eP[r][c] + kp * s.k[r][c] * s.eP[r][c];
+      for (int i = 0; i < r; ++i) kp += be * sdA[r][i] * s.k[i][c] * s.eM[i][c];            // (beta dA) K-
       for (int r2 = r + 1; r2 < kBlk; ++r2)
-        km += s.beta[r2] * sdA[r2][r] * s.k[r2][c] * expf(s.G[r2][c]);                        // (beta dA)^T K+
-      for (int i = 0; i <= r; ++i) qp += sdAqk[r][i] * s.k[i][c] * expf(-s.G[i][c]);          // dAqk K-
-      for (int r2 = r; r2 < kBlk; ++r2) km += sdAqk[r2][r] * s.q[r2][c] * expf(s.G[r2][c]);  // dAqk^T Q+
+        km += s.beta[r2] * sdA[r2][r] * s.k[r2][c] * s.eP[r2][c];                            // (beta dA)^T K+
+      for (int i = 0; i <= r; ++i) qp += sdAqk[r][i] * s.k[i][c] * s.eM[i][c];              // dAqk K-
+      for (int r2 = r; r2 < kBlk; ++r2) km += sdAqk[r2][r] * s.q[r2][c] * s.eP[r2][c];      // dAqk^T Q+
       dKp[m] = kp;
       dKm[m] = km;
       dQp[m] = qp;
@@ -598,23 +668,40 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
       sdKm[r][c] = dKm[m];
       sdQp[r][c] = dQp[m];
       sX[r][c] = dV[m];                         // sX now holds dV
+      sDel[r][c] = gnp[m];                      // Delta is no longer needed
     }
   }
   __syncthreads();
-  // ---- chain to q^, k^ (into sdQp, sdKp) and the gate (dg into sdKm), per channel
+  // ---- chain to q^, k^ (into sdQp, sdKp) and the gate (dg into sdKm), per channel.
+  // A pair (r, i < r) of A or Aqk enters the decays through e^{G_r - G_i}:
+  // +T_ri on G_r and -T_ri on G_i, with T_ri = (beta_r dA[r][i] k_r
+  // + dAqk[r][i] q_r) k_i e^{G_r - G_i}.  Summed into dg_t = sum_{r >= t} dG_r
+  // the two cancel unless i < t <= r, so the pairs are added directly over
+  // that rectangle (row by row, prefix sums over i): nothing is subtracted,
+  // and no rounding residue of two large canceling sums is left over.
   if (tid < D) {
     const int c = tid;
-    float dG[kBlk], dGs[kBlk];
+    float dG[kBlk], dGs[kBlk], P[kBlk];
     for (int r = 0; r < kBlk; ++r) {
-      const float G = s.G[r][c], eP = expf(G), eM = expf(-G), eS = expf(s.Gs[r][c]);
-      const float q = s.q[r][c], k = s.k[r][c];
+      const float eP = s.eP[r][c], eM = s.eM[r][c], eS = s.eS[r][c];
+      const float k = s.k[r][c];
       const float dqp = sdQp[r][c], dkp = sdKp[r][c], dkm = sdKm[r][c], dkt = sdKt[r][c];
-      dG[r] = dqp * q * eP + dkp * k * eP - dkm * k * eM;
+      dG[r] = sDel[r][c];
       dGs[r] = dkt * k * eS;
+      P[r] = 0.f;
       sdQp[r][c] = dqp * eP;                          // d q^
       sdKp[r][c] = dkp * eP + dkm * eM + dkt * eS;    // d k^
     }
-    // dg_t = sum_{r >= t} dG_r + sum_{r < t} dGs_r + dG_C, for the block's tokens
+    for (int r = 1; r < kBlk; ++r) {
+      const float ar = s.beta[r] * s.k[r][c] * s.eP[r][c], br = s.q[r][c] * s.eP[r][c];
+      float rp = 0.f;
+      for (int t2 = 1; t2 <= r; ++t2) {
+        const int i = t2 - 1;
+        rp += (sdA[r][i] * ar + sdAqk[r][i] * br) * (s.k[i][c] * s.eM[i][c]);
+        P[t2] += rp;
+      }
+    }
+    // dg_t = sum_{r >= t} dG_r + sum_{r < t} dGs_r + dG_C + P_t, for the block's tokens
     const float gc = sdGC[c];
     float suffix = 0.f;
     for (int r = kBlk - 1; r >= 0; --r) {
@@ -623,7 +710,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
     }
     float prefix = 0.f;
     for (int r = 0; r < kBlk; ++r) {
-      sdKm[r][c] = r < b.ntok ? dG[r] + prefix + gc : 0.f;   // dg
+      sdKm[r][c] = r < b.ntok ? dG[r] + prefix + gc + P[r] : 0.f;   // dg
       prefix += dGs[r];
     }
   }
@@ -660,13 +747,13 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
       pd[c] = dtb_part;
     }
     // d A_log: sum over the block's channels (waves 0 and 1 hold them for D = 128)
-    __shared__ float sAl[kBT / kWave];
+    __shared__ float sAl[NT / kWave];
     const float wsum = group_sum<kWave>(alog_part);
     if (tid % kWave == 0) sAl[tid / kWave] = wsum;
     __syncthreads();
     if (tid == 0) {
       float tot = 0.f;
-      for (int w = 0; w < kBT / kWave; ++w) tot += sAl[w];
+      for (int w = 0; w < NT / kWave; ++w) tot += sAl[w];
       pAlog[bh] = tot;
     }
   }
@@ -680,7 +767,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   }
   // L2 norm (q with its scale, k): du = (s / n) (dq^ - q^ (q^ . dq^) / s^2)
   __shared__ float sDot[2][kBlk];
-  {
+  if (tid < 2 * kBlk * 8) {
     const int row = tid / 8, l8 = tid % 8;
     const bool isq = row < kBlk;
     const int r = isq ? row : row - kBlk;
@@ -693,7 +780,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_grad_kernel(Params p, ChunkTabl
   }
   __syncthreads();
   // SiLU: dy = du sigmoid(y) (1 + y (1 - sigmoid(y))), with y recomputed from the raw window
-  for (int task = tid; task < 3 * D; task += kBT) {
+  for (int task = tid; task < 3 * D; task += NT) {
     const int role = task / D, ch = task % D;
     const size_t col = static_cast<size_t>(h) * D + ch;
     const void* xin = role == 0 ? io.q : (role == 1 ? io.k : io.v);
@@ -761,21 +848,33 @@ __global__ __launch_bounds__(3 * D) void bwd_conv_kernel(Params p, ChunkTable t,
     if (io.conv_in) return ld<IO_BF16>(io.conv_in, (static_cast<size_t>(seq) * 3 + (3 + tau)) * 3 * HD + role * HD + col);
     return 0.f;
   };
+  // the chunk's window, loaded before any arithmetic: x at positions
+  // tau0 - 3 .. tau0 + 63 and dy at tau0 .. tau0 + 66 (zeros outside)
+  constexpr int WN = kChunk + 3;
+  float xs[WN], dys[WN];
+#pragma unroll
+  for (int m = 0; m < WN; ++m) {
+    xs[m] = (m - 3 < cnt) ? xat(tau0 - 3 + m) : 0.f;
+    dys[m] = dyat(tau0 + m);
+  }
   float aw[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < cnt; ++r) {
-    const int tau = tau0 + r;
-    float g = 0.f;
-    for (int j = 0; j < 4; ++j) g += wj[j] * dyat(tau + 3 - j);
-    dx[static_cast<size_t>(seq0 + tau) * HD + col] = g;
-    const float dyt = dyat(tau);
-    for (int j = 0; j < 4; ++j) aw[j] += dyt * xat(tau - 3 + j);
+#pragma unroll
+  for (int r = 0; r < kChunk; ++r) {
+    if (r < cnt) {
+      float g = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g += wj[j] * dys[r + 3 - j];
+      dx[static_cast<size_t>(seq0 + tau0 + r) * HD + col] = g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) aw[j] += dys[r] * xs[r + j];
+    }
   }
   for (int j = 0; j < 4; ++j) pw[j] = aw[j];
   if (tau0 == 0 && dconv) {
-    // history slot m holds position m - 3
+    // history slot m holds position m - 3: dx_{m-3} = sum_j w[j] dy_{m-j}
     for (int m = 0; m < 3; ++m) {
       float g = 0.f;
-      for (int j = 0; j < 4; ++j) g += wj[j] * dyat(m - 3 + 3 - j);
+      for (int j = 0; j <= m; ++j) g += wj[j] * dys[m - j];
       dconv[(static_cast<size_t>(seq) * 3 + m) * 3 * HD + role * HD + col] = g;
     }
   }
@@ -831,7 +930,7 @@ hipError_t launch_backward_d(const Params& p, const ChunkTable& t, const Prefill
   bwd_adjoint_scan_kernel<D, VT, DO_BF16><<<nscan, kBT, 0, st>>>(p, t, ws.recs, g.dO, g.dS_final, ws.dSblk, ws.dDblk,
                                                                  g.dS_init, g.dconv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_block_grad_kernel<D, IO_BF16, DO_BF16><<<nblk, kBT, 0, st>>>(p, t, io, ws.recs, ws.Sblk, ws.dSblk, ws.Dblk,
+  bwd_block_grad_kernel<D, IO_BF16, DO_BF16><<<nblk, grad_threads<D>(), 0, st>>>(p, t, io, ws.recs, ws.Sblk, ws.dSblk, ws.Dblk,
                                                                    ws.dDblk, g.dO, ws.dy, g.dalpha, g.db, ws.pdtb,
                                                                    ws.pAlog);
   if ((e = hipGetLastError()) != hipSuccess) return e;

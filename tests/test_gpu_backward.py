@@ -4,13 +4,18 @@ gradient oracle (oracle/kda_oracle_bwd.c, pinned by finite differences).
 Every gradient the call returns is compared element by element: those of the
 raw q, k, v, alpha and b, the initial state, the incoming conv history, the
 conv weights, dt_bias and A_log.  The GPU computes in fp32 from the same
-stored inputs; the bound is max|g - g_ref| <= BOUND x RMS(g_ref) per tensor,
-with BOUND = 1e-4.  Where it comes from: every product is an fp32 sum of at
-most D (<= 128) or 16 terms, good to ~1e-6 relative; the gate's chain carries
-the in-block decay factors e^{+-G}, whose exponents reach 16 x 5.4 = 86 and
-are rounded to fp32 (86 x 2^-24 = 5e-6 relative per factor), and the
-reverse cumulative sums over a block add up to 16 of them.  Measured: at most
-3.6e-5 (d alpha, strongly decaying heads), everything else below 1e-5.
+stored inputs.  The gradients are heavy-tailed (at the 4K workload's
+distributions max|g|/RMS(g) reaches 118 for d alpha, 65 for dk), so the bound
+is elementwise, in an absolute part and a relative part:
+    |g - g_ref| <= EPS * (RMS(g_ref) + |g_ref|),   EPS = 5e-5.
+Where EPS comes from: every product is an fp32 sum of at most D (<= 128) or
+16 terms (~1e-6 relative), and the gate's chain carries the in-block decay
+factors e^{+-G}, whose exponents reach 16 x 5.4 = 86 and are rounded to fp32
+(86 x 2^-24 = 5e-6 relative per factor).  The decay terms of the pairs of A
+and Aqk are summed without cancellation (only over the token range each pair
+reaches), which keeps d alpha at the level of the other gradients.
+Measured on the GPU: at most 1.4e-5 (d alpha, the 4K workload's 131072
+token-heads), most gradients below 5e-6.
 """
 import numpy as np
 import pytest
@@ -19,12 +24,12 @@ import torch
 import oracle
 from kda_inputs import BF16, FP32, as_f64, make_problem
 from kda_inputs.torch_io import problem_to_device, to_torch
-from tests.helpers import max_over_rms, rel_fro
+from tests.helpers import max_over_rms
 from tests.test_gpu_parity import kda  # noqa: F401  (fixture)
 
 pytestmark = pytest.mark.gpu
 
-BOUND = 1e-4
+EPS = 5e-5
 NAMES = ("dq", "dk", "dv", "dalpha", "db", "dS0", "dconv", "dw_q", "dw_k", "dw_v", "ddt_bias", "dA_log")
 
 
@@ -47,11 +52,14 @@ def run(kda, p, flags=0, with_dST=True, out=FP32, seed=0):
     errs = {}
     for name in NAMES:
         got = g[name].double().cpu().numpy().reshape(ref[name].shape)
+        r_ = ref[name]
         assert np.isfinite(got).all(), f"{name} not finite"
-        errs[name] = (max_over_rms(got, ref[name]), rel_fro(got, ref[name]))
-    print(" ".join(f"{n}={e[0]:.2e}" for n, e in errs.items()))
-    for name, (e, _) in errs.items():
-        assert e <= BOUND, f"{name}: max error {e:.3e} x RMS > {BOUND}"
+        rms = float(np.sqrt(np.mean(r_ ** 2)))
+        scaled = np.abs(got - r_) / (rms + np.abs(r_))
+        errs[name] = (max_over_rms(got, r_), float(np.max(scaled)))
+    print(" ".join(f"{n}={e[0]:.1e}/{e[1]:.1e}" for n, e in errs.items()))
+    for name, (_, e) in errs.items():
+        assert e <= EPS, f"{name}: |g - g_ref| / (RMS + |g_ref|) reaches {e:.3e} > {EPS}"
     return errs
 
 
