@@ -44,6 +44,7 @@
 //   bwd_param_reduce  partial parameter gradients summed in block order
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "mfma.h"
 
 namespace kda {
 
@@ -72,14 +73,17 @@ __device__ __forceinline__ BlockInfo block_info(const ChunkTable& t, int blk) {
 }
 
 // Shared-memory image of one block's preprocessed inputs (one head).
+// Rows are padded by one float: matrix-core operand reads take a column
+// across 16 rows, which then fall in 16 different banks.
 template <int D>
 struct BlockSmem {
-  float q[kBlk][D];      // q^ (normalised, scaled)
-  float k[kBlk][D];      // k^ (normalised)
-  float v[kBlk][D];      // v^
-  float eP[kBlk][D];     // e^{G}, G the inclusive in-block prefix sum of g
-  float eM[kBlk][D];     // e^{-G}
-  float eS[kBlk][D];     // e^{G_C - G}, from the exclusive in-block suffix sum of g
+  static constexpr int LD = D + 1;
+  float q[kBlk][LD];     // q^ (normalised, scaled)
+  float k[kBlk][LD];     // k^ (normalised)
+  float v[kBlk][LD];     // v^
+  float eP[kBlk][LD];    // e^{G}, G the inclusive in-block prefix sum of g
+  float eM[kBlk][LD];    // e^{-G}
+  float eS[kBlk][LD];    // e^{G_C - G}, from the exclusive in-block suffix sum of g
   float beta[kBlk];
   float nq[kBlk], nk[kBlk];   // the L2 norms sqrt(|u|^2 + eps) of q and k
 };
@@ -118,7 +122,7 @@ __device__ void block_preprocess(const Params& p, const PrefillIO& io, const Blo
           u = siluf_(w0 * win[0] + w1 * win[1] + w2 * win[2] + w3 * xt);
           win[0] = win[1]; win[1] = win[2]; win[2] = xt;
         }
-        dst[r * D + ch] = u;
+        dst[r * BlockSmem<D>::LD + ch] = u;
       }
     } else {
       const float a_exp = expf(p.A_log[h]);
@@ -203,7 +207,7 @@ template <int D, bool IO_BF16>
 __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTable t, PrefillIO io, uint8_t* recs) {
   constexpr BwdRecord R = bwd_record(D);
   __shared__ BlockSmem<D> s;
-  __shared__ float sKm[kBlk][D];       // K e^{-G}
+  __shared__ float sKm[kBlk][D + 1];   // K e^{-G}
   __shared__ float sA[kBlk][kBlk];     // A, then T
   __shared__ float sT[kBlk][kBlk];
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
@@ -230,20 +234,23 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
     if (r == 0) geGC[c] = s.eP[kBlk - 1][c];
   }
   __syncthreads();
-  // A (strictly lower) and Aqk (lower with the diagonal): one entry each per thread
-  {
-    const int r = tid / kBlk, i = tid % kBlk;
-    float a = 0.f, aq = 0.f;
-    if (i <= r) {
-      for (int c = 0; c < D; ++c) {
-        const float eg = s.eP[r][c];
-        const float km = sKm[i][c];
-        aq += s.q[r][c] * eg * km;
-        if (i < r) a += s.k[r][c] * eg * km;
-      }
+  // A (strictly lower, wave 0) and Aqk (lower with the diagonal, wave 1) on the
+  // fp32 matrix cores: K+ K-^T and Q+ K-^T over K = D (lane layout as in
+  // bwd_block_grad_kernel)
+  const int wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g4 = lane / 16;
+  if (wave < 2) {
+    f32x4 acc = zero4();
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const int k = k0 + g4;
+      const float a = (wave == 0 ? s.k[l16][k] : s.q[l16][k]) * s.eP[l16][k];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sKm[l16][k], acc, 0, 0, 0);
     }
-    sA[r][i] = s.beta[r] * a;
-    gAqk[tid] = aq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      if (wave == 0) sA[r][l16] = l16 < r ? s.beta[r] * acc[i] : 0.f;
+      else gAqk[r * kBlk + l16] = l16 <= r ? acc[i] : 0.f;
+    }
   }
   __syncthreads();
   // T = (I + A)^-1 by forward substitution, lane i owns column i
@@ -259,17 +266,23 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   }
   __syncthreads();
   for (int e = tid; e < kBlk * kBlk; e += kBT) gT[e] = sT[e / kBlk][e % kBlk];
-  // W = T Diag(beta) K+,  U = T Diag(beta) V
-  for (int e = tid; e < kBlk * D; e += kBT) {
-    const int r = e / D, c = e % D;
-    float w = 0.f, u = 0.f;
-    for (int m = 0; m <= r; ++m) {
-      const float tb = sT[r][m] * s.beta[m];
-      w += tb * s.k[m][c] * s.eP[m][c];
-      u += tb * s.v[m][c];
+  // W = T Diag(beta) K+,  U = T Diag(beta) V (K = 16), 16 channels per wave pass
+  for (int c0 = wave * 16; c0 < D; c0 += (kBT / kWave) * 16) {
+    const int c = c0 + l16;
+    f32x4 w = zero4(), u = zero4();
+#pragma unroll
+    for (int st = 0; st < kBlk / 4; ++st) {
+      const int k = 4 * st + g4;
+      const float a = sT[l16][k] * s.beta[k];
+      w = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s.k[k][c] * s.eP[k][c], w, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s.v[k][c], u, 0, 0, 0);
     }
-    gW[e] = w;
-    gU[e] = u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      gW[r * D + c] = w[i];
+      gU[r * D + c] = u[i];
+    }
   }
 }
 
@@ -510,19 +523,13 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
                                                               float* dalpha, float* db, float* pdtb, float* pAlog) {
   constexpr BwdRecord R = bwd_record(D);
   constexpr int NT = grad_threads<D>();
-  constexpr int SC = 16;                  // state columns staged at a time
   __shared__ BlockSmem<D> s;
-  __shared__ float sDel[kBlk][D], sdDel[kBlk][D], sdO[kBlk][D];
-  __shared__ float sdQp[kBlk][D], sdKp[kBlk][D], sdKm[kBlk][D], sdKt[kBlk][D];
-  __shared__ float sX[kBlk][D];           // dW, then dXw
+  __shared__ float sDel[kBlk][D + 1], sdDel[kBlk][D + 1], sdO[kBlk][D + 1];   // padded: matrix-core A reads
+  __shared__ float sdQp[kBlk][D + 1], sdKp[kBlk][D + 1], sdKm[kBlk][D + 1], sdKt[kBlk][D + 1];
+  __shared__ float sX[kBlk][D + 1];       // dW, then dXw, then dV
   __shared__ float sT[kBlk][kBlk], sAun[kBlk][kBlk], sdA[kBlk][kBlk], sdAqk[kBlk][kBlk];
   __shared__ float sdbeta[kBlk], sdGC[D];
-  __shared__ float sStage[2 * D * (SC + 1)];     // S0 / dS_C column slabs, then W and U
-  float (*sS0)[SC + 1] = reinterpret_cast<float (*)[SC + 1]>(sStage);
-  float (*sdSC)[SC + 1] = reinterpret_cast<float (*)[SC + 1]>(sStage + D * (SC + 1));
-  float (*sWt)[D] = reinterpret_cast<float (*)[D]>(sStage);
-  float (*sUt)[D] = reinterpret_cast<float (*)[D]>(sStage + kBlk * D);
-  static_assert(2 * kBlk * D <= 2 * D * (SC + 1), "W and U fit where the slabs were");
+  __shared__ float sWt[kBlk][D + 1], sUt[kBlk][D + 1];  // W and U
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
   const int blk = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   const bool live_chunk = blk / kBlocksPerChunk < t.chunk0[t.N];
@@ -553,82 +560,106 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   for (int e = tid; e < kBlk * kBlk; e += NT) sT[e / kBlk][e % kBlk] = gT[e];
   __syncthreads();
 
-  // ---- products with S0 and dS_C, staged SC state columns at a time:
-  //   dQ+ = dO S0^T, dW = -dDelta S0^T, dK~ = Delta dS_C^T, dG_C = e^{G_C} rowsum(dS_C * S0)
+  // ---- products with S0 and dS_C on the fp32 matrix cores (v_mfma_f32_16x16x4_f32):
+  //   dQ+ = dO S0^T, dW = -dDelta S0^T, dK~ = Delta dS_C^T  (16 x D each) and
+  //   dG_C = e^{G_C} rowsum(dS_C * S0).
+  // Wave w owns output channels 16w .. 16w + 15.  Step s of lane l covers state
+  // column KS * (l / 16) + s (KS = D / 4), so each lane reads two contiguous
+  // runs of KS floats, its pieces of one row of S0 and of dS_C.
   {
-    constexpr int RPT = kBlk * D / NT;   // outputs per thread: channel c, rows s0 .. s0 + RPT - 1
-    const int c = tid % D, s0 = (tid / D) * RPT;
-    float aQ[RPT], aW[RPT], aK[RPT];
-    for (int m = 0; m < RPT; ++m) { aQ[m] = 0.f; aW[m] = 0.f; aK[m] = 0.f; }
-    float gc = 0.f;
-    for (int j0 = 0; j0 < D; j0 += SC) {
-      for (int e = tid; e < D * SC; e += NT) {
-        const int r = e / SC, jj = e % SC;
-        sS0[r][jj] = S0[static_cast<size_t>(r) * D + j0 + jj];
-        sdSC[r][jj] = dSC[static_cast<size_t>(r) * D + j0 + jj];
+    constexpr int KS = D / 4;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int l16 = lane % 16, g = lane / 16;
+    if (wave < D / 16) {
+      const int c = wave * 16 + l16;
+      float sv[KS], dsv[KS];
+      const float* s0row = S0 + static_cast<size_t>(c) * D + g * KS;
+      const float* dsrow = dSC + static_cast<size_t>(c) * D + g * KS;
+#pragma unroll
+      for (int q = 0; q < KS; q += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(s0row + q);
+        const float4 d4 = *reinterpret_cast<const float4*>(dsrow + q);
+        sv[q] = a.x; sv[q + 1] = a.y; sv[q + 2] = a.z; sv[q + 3] = a.w;
+        dsv[q] = d4.x; dsv[q + 1] = d4.y; dsv[q + 2] = d4.z; dsv[q + 3] = d4.w;
       }
-      __syncthreads();
-      for (int jj = 0; jj < SC; ++jj) {
-        const float s0v = sS0[c][jj], dsv = sdSC[c][jj];
-        if (tid < D) gc += s0v * dsv;
-        for (int m = 0; m < RPT; ++m) {
-          aQ[m] += sdO[s0 + m][j0 + jj] * s0v;
-          aW[m] -= sdDel[s0 + m][j0 + jj] * s0v;
-          aK[m] += sDel[s0 + m][j0 + jj] * dsv;
-        }
+      float gc = 0.f;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) gc += sv[q] * dsv[q];
+      gc += __shfl_xor(gc, 16);
+      gc += __shfl_xor(gc, 32);
+      f32x4 aQ = zero4(), aW = zero4(), aK = zero4();
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        const int j = g * KS + q;
+        aQ = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[l16][j], sv[q], aQ, 0, 0, 0);
+        aW = __builtin_amdgcn_mfma_f32_16x16x4f32(sdDel[l16][j], sv[q], aW, 0, 0, 0);
+        aK = __builtin_amdgcn_mfma_f32_16x16x4f32(sDel[l16][j], dsv[q], aK, 0, 0, 0);
       }
-      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        sdQp[r][c] = aQ[i];
+        sX[r][c] = -aW[i];
+        sdKt[r][c] = aK[i];
+      }
+      if (g == 0) sdGC[c] = geG[c] * gc;
     }
-    for (int m = 0; m < RPT; ++m) {
-      sdQp[s0 + m][c] = aQ[m];
-      sX[s0 + m][c] = aW[m];
-      sdKt[s0 + m][c] = aK[m];
-    }
-    if (tid < D) sdGC[c] = geG[c] * gc;
   }
   __syncthreads();
-  // ---- dXw = T^T dW (in place through registers), dXu = T^T dDelta (into sdKm as scratch for now: no)
+  // ---- the 16 x 16 and 16 x D products of the block on the fp32 matrix cores
+  // (v_mfma_f32_16x16x4_f32: lane l gives A[l % 16][k] and B[k][l % 16] with k
+  // the step's K index 4 s + l / 16, and holds C[4 (l / 16) + i][l % 16]).
+  const int wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g4 = lane / 16;
+  // dXw = T^T dW, dXu = T^T dDelta (K = 16); wave w: channels 16w .. 16w + 15
   {
-    constexpr int RPT = kBlk * D / NT;
-    const int c = tid % D, s0 = (tid / D) * RPT;
-    float xw[RPT], xu[RPT];
-    for (int m = 0; m < RPT; ++m) {
-      float aw = 0.f, au = 0.f;
-      const int mm = s0 + m;
-      for (int r = mm; r < kBlk; ++r) {
-        aw += sT[r][mm] * sX[r][c];
-        au += sT[r][mm] * sdDel[r][c];
+    f32x4 xw = zero4(), xu = zero4();
+    const int c = wave * 16 + l16;
+    if (wave < D / 16) {
+#pragma unroll
+      for (int st = 0; st < kBlk / 4; ++st) {
+        const int k = 4 * st + g4;
+        const float a = sT[k][l16];            // T^T[m][k] = T[k][m]
+        xw = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sX[k][c], xw, 0, 0, 0);
+        xu = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sdDel[k][c], xu, 0, 0, 0);
       }
-      xw[m] = aw;
-      xu[m] = au;
     }
     __syncthreads();
-    for (int m = 0; m < RPT; ++m) {
-      sX[s0 + m][c] = xw[m];
-      sdKm[s0 + m][c] = xu[m];    // dXu parked in sdKm until dV is formed
+    if (wave < D / 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sX[4 * g4 + i][c] = xw[i];
+        sdKm[4 * g4 + i][c] = xu[i];          // dXu parked in sdKm until dV is formed
+      }
     }
   }
-  __syncthreads();
-  // ---- dA = -strict_lower(dXw W^T + dXu U^T);  A_un = K+ K-^T;  dAqk = lower(dO Delta^T)
   for (int e = tid; e < kBlk * D; e += NT) {
     sWt[e / D][e % D] = gW[e];
     sUt[e / D][e % D] = gU[e];
   }
   __syncthreads();
-  if (tid < kBlk * kBlk) {
-    const int r = tid / kBlk, i = tid % kBlk;
-    float da = 0.f, aun = 0.f, daq = 0.f;
-    if (i < r) {
-      for (int c = 0; c < D; ++c) {
-        da -= sX[r][c] * sWt[i][c] + sdKm[r][c] * sUt[i][c];
-        aun += s.k[r][c] * s.eP[r][c] * (s.k[i][c] * s.eM[i][c]);
+  // dA = -strict_lower(dXw W^T + dXu U^T) (wave 0), A_un = strict_lower(K+ K-^T)
+  // (wave 1), dAqk = lower(dO Delta^T) (wave 2): 16 x 16 each over K = D
+  if (wave < 3) {
+    f32x4 acc = zero4();
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const int k = k0 + g4;
+      if (wave == 0) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[l16][k], sWt[l16][k], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdKm[l16][k], sUt[l16][k], acc, 0, 0, 0);
+      } else if (wave == 1) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s.k[l16][k] * s.eP[l16][k], s.k[l16][k] * s.eM[l16][k], acc,
+                                                   0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[l16][k], sDel[l16][k], acc, 0, 0, 0);
       }
     }
-    if (i <= r)
-      for (int c = 0; c < D; ++c) daq += sdO[r][c] * sDel[i][c];
-    sdA[r][i] = da;
-    sAun[r][i] = aun;
-    sdAqk[r][i] = daq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      if (wave == 0) sdA[r][l16] = l16 < r ? -acc[i] : 0.f;
+      else if (wave == 1) sAun[r][l16] = l16 < r ? acc[i] : 0.f;
+      else sdAqk[r][l16] = l16 <= r ? acc[i] : 0.f;
+    }
   }
   __syncthreads();
   // ---- dbeta; dV; dK+ and dK- from X and A; dQ+ and dK- from Aqk
@@ -640,35 +671,48 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     sdbeta[r] = d;
   }
   {
-    constexpr int RPT = kBlk * D / NT;
-    const int c = tid % D, s0 = (tid / D) * RPT;
-    float dKp[RPT], dKm[RPT], dQp[RPT], dV[RPT], gnp[RPT];
-    for (int m = 0; m < RPT; ++m) {
-      const int r = s0 + m;
-      const float be = s.beta[r];
-      float kp = be * sX[r][c];                 // Diag(beta) dXw
-      float km = 0.f, qp = sdQp[r][c];
-      // the decay's gradient through the single-token terms, dO S0^T on Q+ and
-      // beta dXw on K+ (the pair terms of A and Aqk are summed separately)
-      gnp[m] = qp * s.q[r][c] * s.eP[r][c] + kp * s.k[r][c] * s.eP[r][c];
-      for (int i = 0; i < r; ++i) kp += be * sdA[r][i] * s.k[i][c] * s.eM[i][c];            // (beta dA) K-
-      for (int r2 = r + 1; r2 < kBlk; ++r2)
-        km += s.beta[r2] * sdA[r2][r] * s.k[r2][c] * s.eP[r2][c];                            // (beta dA)^T K+
-      for (int i = 0; i <= r; ++i) qp += sdAqk[r][i] * s.k[i][c] * s.eM[i][c];              // dAqk K-
-      for (int r2 = r; r2 < kBlk; ++r2) km += sdAqk[r2][r] * s.q[r2][c] * s.eP[r2][c];      // dAqk^T Q+
-      dKp[m] = kp;
-      dKm[m] = km;
-      dQp[m] = qp;
-      dV[m] = be * sdKm[r][c];
+    // (beta dA) K-,  (beta dA)^T K+ + dAqk^T Q+,  dAqk K-  (K = 16)
+    f32x4 kpM = zero4(), kmM = zero4(), qpM = zero4();
+    const int c = wave * 16 + l16;
+    if (wave < D / 16) {
+#pragma unroll
+      for (int st = 0; st < kBlk / 4; ++st) {
+        const int k = 4 * st + g4;
+        const float kmi = s.k[k][c] * s.eM[k][c], kpi = s.k[k][c] * s.eP[k][c], qpi = s.q[k][c] * s.eP[k][c];
+        kpM = __builtin_amdgcn_mfma_f32_16x16x4f32(s.beta[l16] * sdA[l16][k], kmi, kpM, 0, 0, 0);
+        kmM = __builtin_amdgcn_mfma_f32_16x16x4f32(s.beta[k] * sdA[k][l16], kpi, kmM, 0, 0, 0);
+        kmM = __builtin_amdgcn_mfma_f32_16x16x4f32(sdAqk[k][l16], qpi, kmM, 0, 0, 0);
+        qpM = __builtin_amdgcn_mfma_f32_16x16x4f32(sdAqk[l16][k], kmi, qpM, 0, 0, 0);
+      }
+    }
+    float dKp[4], dKm[4], dQp[4], dV[4], gnp[4];
+    if (wave < D / 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
+        const float be = s.beta[r];
+        const float xw = be * sX[r][c];         // Diag(beta) dXw
+        const float q0 = sdQp[r][c];            // dO S0^T
+        // the decay's gradient through the single-token terms (dO S0^T on Q+,
+        // beta dXw on K+); the pair terms of A and Aqk are summed separately
+        gnp[i] = (q0 * s.q[r][c] + xw * s.k[r][c]) * s.eP[r][c];
+        dKp[i] = xw + kpM[i];
+        dKm[i] = kmM[i];
+        dQp[i] = q0 + qpM[i];
+        dV[i] = be * sdKm[r][c];
+      }
     }
     __syncthreads();
-    for (int m = 0; m < RPT; ++m) {
-      const int r = s0 + m;
-      sdKp[r][c] = dKp[m];
-      sdKm[r][c] = dKm[m];
-      sdQp[r][c] = dQp[m];
-      sX[r][c] = dV[m];                         // sX now holds dV
-      sDel[r][c] = gnp[m];                      // Delta is no longer needed
+    if (wave < D / 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
+        sdKp[r][c] = dKp[i];
+        sdKm[r][c] = dKm[i];
+        sdQp[r][c] = dQp[i];
+        sX[r][c] = dV[i];                       // sX now holds dV
+        sDel[r][c] = gnp[i];                    // Delta is no longer needed
+      }
     }
   }
   __syncthreads();
