@@ -16,6 +16,7 @@ import oracle
 import tests.test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
+BWD = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle_bwd.c")   # linked unchanged
 
 MUTANTS = {
     "decay_by_value_axis": ("S[(size_t)i * dv + j] *= e;", "S[(size_t)i * dv + j] *= exp(gt[j % dk]);"),
@@ -94,7 +95,7 @@ def test_pins_catch_mutant(tmp_path, monkeypatch, restore_oracle, name):
     mut = tmp_path / "mut.c"
     mut.write_text(src.replace(old, new))
     lib = tmp_path / "libmut.so"
-    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-std=c11", "-o", str(lib), str(mut),
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-std=c11", "-o", str(lib), str(mut), BWD,
                            "-lm", "-lpthread"])
     monkeypatch.setattr(oracle, "build", lambda force=False: str(lib))
     oracle._lib = None
