@@ -267,3 +267,30 @@ def test_gated_decode_validation(kda):
     assert dm(2, 65, p, p, 1e-6) == kda.KDA_ERR_UNSUPPORTED
     assert dm(0, 3, None, None, 1e-6) == kda.KDA_OK
     assert c.untouched()
+
+
+def test_backward_validation(kda):
+    """The backward refuses what it does not handle (the recurrent form's
+    gates, test hooks other than beta x2) and checks its pointers and
+    workspace before any launch."""
+    lib = kda.library()
+    c = Canary(1 << 12)
+    p = c.ptr
+    bw = lambda cfg_, N, T, ptrs, ws_bytes=1 << 30: lib.kda_varlen_backward(
+        ctypes.byref(cfg_), N, T, *ptrs, p, ws_bytes, None)
+    full = [p] * 22                            # cu_seqlens .. dA_log; the workspace is added by bw
+    cfg, _ = make_cfg(kda)
+    assert bw(make_cfg(kda, gate_lower_bound=float("-inf"))[0], 2, 16, full) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(make_cfg(kda, flags=kda.FLAG_RAW_GATE)[0], 2, 16, full) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(make_cfg(kda, flags=kda.FLAG_SKIP_CONV)[0], 2, 16, full) == kda.KDA_ERR_UNSUPPORTED
+    assert bw(cfg, -1, 16, full) == kda.KDA_ERR_INVALID_ARGUMENT
+    for missing in (0, 1, 8, 10, 17, 21):      # cu_seqlens, q, d_o, dq, dw_q, dA_log
+        ptrs = list(full)
+        ptrs[missing] = None
+        assert bw(cfg, 2, 16, ptrs) == kda.KDA_ERR_INVALID_ARGUMENT, missing
+    assert bw(cfg, 2, 16, full, ws_bytes=100) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bw(cfg, 0, 0, [None] * 22) == kda.KDA_OK
+    assert lib.kda_varlen_backward_workspace_bytes(ctypes.byref(cfg), 2, 16) > 0
+    assert lib.kda_varlen_backward_workspace_bytes(
+        ctypes.byref(make_cfg(kda, flags=kda.FLAG_RAW_BETA)[0]), 2, 16) == 0
+    assert c.untouched()

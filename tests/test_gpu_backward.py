@@ -92,3 +92,20 @@ def test_backward_strong_decay_hits_the_clamp(kda):
     p = make_problem(8300, [150, 40], 2, 64, 64, FP32, state_seqs=[0, 1], conv_state=True)
     p.A_log = np.full_like(p.A_log, 1.5)      # many log-decays clamped at -5
     run(kda, p, seed=4)
+
+
+def test_backward_many_short_sequences(kda):
+    """1100 packed sequences of 0..5 tokens: more than one pass of the chunk
+    table's scan, empty sequences (their state gradient passes through and
+    their history takes none), and sequences shorter than the conv history."""
+    lens = np.random.default_rng(1100).integers(0, 6, size=1100).tolist()
+    p = make_problem(8400, lens, 2, 16, 16, FP32, state_seqs=list(range(0, 1100, 3)), state_std=0.3,
+                     conv_state=True)
+    run(kda, p, seed=5)
+
+
+def test_backward_histories_and_tails(kda):
+    """Sequences of 1, 2, 3 and 17 tokens behind a 64-token one (every tap of
+    the incoming history reached, partial 16-token blocks), bf16."""
+    p = make_problem(8500, [64, 1, 2, 3, 17], 3, 32, 32, BF16, state_seqs=[0, 2, 4], conv_state=True)
+    run(kda, p, out=BF16, seed=6)
