@@ -41,7 +41,8 @@
 //                     d alpha, d b and per-block partial parameter gradients
 //   bwd_conv          per (64-token chunk, head): the conv's reverse: d raw
 //                     q, k, v, the conv history's gradient, per-chunk d conv w
-//   bwd_param_reduce  partial parameter gradients summed in block order
+//   bwd_param_partial, bwd_param_final
+//                     partial parameter gradients summed in two fixed-order passes
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "mfma.h"
@@ -53,6 +54,7 @@ namespace {
 constexpr int kBlk = 16;             // tokens per block
 constexpr int kBT = 256;             // threads of the per-block and scan kernels
 constexpr int kBlocksPerChunk = kChunk / kBlk;
+constexpr int kReduceParts = 64;     // row ranges of the parameter sums' first pass
 
 // A block of the packed batch: block index = chunk * 4 + sub.
 struct BlockInfo {
@@ -88,58 +90,93 @@ struct BlockSmem {
   float nq[kBlk], nk[kBlk];   // the L2 norms sqrt(|u|^2 + eps) of q and k
 };
 
-// Conv + SiLU, L2 norm, gate and beta of one block's tokens for head h, into
-// shared memory.  Rows past the block's end are zero, with g = beta = 0.
+// The raw inputs of one thread's preprocess tasks, loaded together before any
+// of them is used.  Task m of thread tid is tid + m NT: tasks 0 .. 3D - 1 are
+// (q | k | v, channel), holding the three inputs before the block (the conv
+// history, or zeros at a sequence start without one) and the block's 16
+// (zeros past its end); tasks 3D .. 4D - 1 are the gate's channels, holding
+// the block's alphas.
+template <int D, int NT>
+struct BlockRaw {
+  static constexpr int kTasks = (4 * D + NT - 1) / NT;
+  float x[kTasks][3 + kBlk];
+  float w[kTasks][4];    // conv taps (q | k | v tasks); dt_bias in w[m][0] (gate tasks)
+  float bb;              // b of token tid (tid < kBlk)
+};
+
 template <int D, bool IO_BF16, int NT>
-__device__ void block_preprocess(const Params& p, const PrefillIO& io, const BlockInfo& b, int h, BlockSmem<D>& s) {
-  static_assert(NT >= 2 * kBlk * 8, "the L2 norms take 8 lanes for each of 32 rows");
+__device__ __forceinline__ void block_load_raw(const Params& p, const PrefillIO& io, const BlockInfo& b, int h,
+                                               BlockRaw<D, NT>& raw) {
   const int tid = threadIdx.x;
   const size_t HD = static_cast<size_t>(p.H) * D;
   const size_t Ctot = 3 * HD;
-  const int seq = b.seq;
   const int64_t seq0 = b.tok0 - b.tau0;   // packed index of the sequence's first token
-  for (int task = tid; task < 4 * D; task += NT) {
+#pragma unroll
+  for (int m = 0; m < BlockRaw<D, NT>::kTasks; ++m) {
+    const int task = tid + m * NT;
     const int role = task / D, ch = task % D;
     const size_t col = static_cast<size_t>(h) * D + ch;
     if (role < 3) {
       const void* xin = role == 0 ? io.q : (role == 1 ? io.k : io.v);
       const void* w = role == 0 ? p.wq : (role == 1 ? p.wk : p.wv);
-      const float w0 = ld<IO_BF16>(w, col * 4), w1 = ld<IO_BF16>(w, col * 4 + 1);
-      const float w2 = ld<IO_BF16>(w, col * 4 + 2), w3 = ld<IO_BF16>(w, col * 4 + 3);
-      float win[3];
 #pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int tau = b.tau0 - 3 + m;
-        if (tau >= 0) win[m] = ld<IO_BF16>(xin, static_cast<size_t>(seq0 + tau) * HD + col);
-        else if (io.conv_in) win[m] = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(seq) * 3 + (3 + tau)) * Ctot + role * HD + col);
-        else win[m] = 0.f;
+      for (int j = 0; j < 4; ++j) raw.w[m][j] = ld<IO_BF16>(w, col * 4 + j);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int tau = b.tau0 - 3 + i;
+        float x = 0.f;
+        if (tau >= 0) x = ld<IO_BF16>(xin, static_cast<size_t>(seq0 + tau) * HD + col);
+        else if (io.conv_in) x = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(b.seq) * 3 + (3 + tau)) * Ctot + role * HD + col);
+        raw.x[m][i] = x;
       }
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r)
+        raw.x[m][3 + r] = r < b.ntok ? ld<IO_BF16>(xin, static_cast<size_t>(b.tok0 + r) * HD + col) : 0.f;
+    } else if (role == 3) {
+      raw.w[m][0] = p.dt_bias[col];
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r)
+        raw.x[m][3 + r] = r < b.ntok ? ld<IO_BF16>(io.alpha, static_cast<size_t>(b.tok0 + r) * HD + col) : 0.f;
+    }
+  }
+  raw.bb = tid < b.ntok ? ld<IO_BF16>(io.b, static_cast<size_t>(b.tok0 + tid) * p.H + h) : 0.f;
+}
+
+// Conv + SiLU, L2 norm, gate and beta of one block's tokens for head h, from
+// the loaded raw inputs into shared memory.  Rows past the block's end are
+// zero, with g = beta = 0.
+template <int D, int NT>
+__device__ __forceinline__ void block_preprocess(const Params& p, const BlockInfo& b, int h, const BlockRaw<D, NT>& raw,
+                                 BlockSmem<D>& s) {
+  static_assert(NT >= 2 * kBlk * 8, "the L2 norms take 8 lanes for each of 32 rows");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < BlockRaw<D, NT>::kTasks; ++m) {
+    const int task = tid + m * NT;
+    const int role = task / D, ch = task % D;
+    if (role < 3) {
+      const float w0 = raw.w[m][0], w1 = raw.w[m][1], w2 = raw.w[m][2], w3 = raw.w[m][3];
       float* dst = role == 0 ? &s.q[0][0] : (role == 1 ? &s.k[0][0] : &s.v[0][0]);
+#pragma unroll
       for (int r = 0; r < kBlk; ++r) {
-        float u = 0.f;
-        if (r < b.ntok) {
-          const float xt = ld<IO_BF16>(xin, static_cast<size_t>(b.tok0 + r) * HD + col);
-          u = siluf_(w0 * win[0] + w1 * win[1] + w2 * win[2] + w3 * xt);
-          win[0] = win[1]; win[1] = win[2]; win[2] = xt;
-        }
-        dst[r * BlockSmem<D>::LD + ch] = u;
+        const float y = w0 * raw.x[m][r] + w1 * raw.x[m][r + 1] + w2 * raw.x[m][r + 2] + w3 * raw.x[m][r + 3];
+        dst[r * BlockSmem<D>::LD + ch] = r < b.ntok ? siluf_(y) : 0.f;
       }
-    } else {
+    } else if (role == 3) {
       const float a_exp = expf(p.A_log[h]);
-      const float dtb = p.dt_bias[col];
+      const float dtb = raw.w[m][0];
       float run = 0.f;
       float g[kBlk];
+#pragma unroll
       for (int r = 0; r < kBlk; ++r) {
-        g[r] = 0.f;
-        if (r < b.ntok) {
-          const float al = ld<IO_BF16>(io.alpha, static_cast<size_t>(b.tok0 + r) * HD + col);
-          g[r] = (p.flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound);
-        }
+        const float al = raw.x[m][3 + r];
+        g[r] = r < b.ntok ? ((p.flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound)) : 0.f;
         run += g[r];
         s.eP[r][ch] = expf(run);
         s.eM[r][ch] = expf(-run);
       }
       float suf = 0.f;
+#pragma unroll
       for (int r = kBlk - 1; r >= 0; --r) {
         s.eS[r][ch] = expf(suf);
         suf += g[r];
@@ -149,8 +186,7 @@ __device__ void block_preprocess(const Params& p, const PrefillIO& io, const Blo
   if (tid < kBlk) {
     float be = 0.f;
     if (tid < b.ntok) {
-      const float bb = ld<IO_BF16>(io.b, static_cast<size_t>(b.tok0 + tid) * p.H + h);
-      be = sigmoidf_(bb);
+      be = sigmoidf_(raw.bb);
       if (p.flags & KDA_FLAG_BETA_X2) be *= 2.0f;
     }
     s.beta[tid] = be;
@@ -201,6 +237,7 @@ __host__ __device__ constexpr BwdRecord bwd_record(int D) {
 }
 
 size_t bwd_record_bytes(int D) { return bwd_record(D).bytes; }
+int bwd_reduce_parts() { return kReduceParts; }
 
 // ---------------------------------------------------------------- block prep
 template <int D, bool IO_BF16>
@@ -216,7 +253,11 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   const BlockInfo b = block_info(t, blk);
   if (b.ntok <= 0) return;
   const int tid = threadIdx.x;
-  block_preprocess<D, IO_BF16, kBT>(p, io, b, h, s);
+  {
+    BlockRaw<D, kBT> raw;
+    block_load_raw<D, IO_BF16, kBT>(p, io, b, h, raw);
+    block_preprocess<D, kBT>(p, b, h, raw, s);
+  }
   uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
   float* gW = reinterpret_cast<float*>(rec + R.W);
   float* gU = reinterpret_cast<float*>(rec + R.U);
@@ -239,17 +280,22 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   // bwd_block_grad_kernel)
   const int wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g4 = lane / 16;
   if (wave < 2) {
-    f32x4 acc = zero4();
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int k = k0 + g4;
-      const float a = (wave == 0 ? s.k[l16][k] : s.q[l16][k]) * s.eP[l16][k];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sKm[l16][k], acc, 0, 0, 0);
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};   // four independent chains
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = k0 + 4 * j + g4;
+        const float a = (wave == 0 ? s.k[l16][k] : s.q[l16][k]) * s.eP[l16][k];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sKm[l16][k], acc[j], 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g4 + i;
-      if (wave == 0) sA[r][l16] = l16 < r ? s.beta[r] * acc[i] : 0.f;
-      else gAqk[r * kBlk + l16] = l16 <= r ? acc[i] : 0.f;
+      const float v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      if (wave == 0) sA[r][l16] = l16 < r ? s.beta[r] * v : 0.f;
+      else gAqk[r * kBlk + l16] = l16 <= r ? v : 0.f;
     }
   }
   __syncthreads();
@@ -286,139 +332,155 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   }
 }
 
-// ---------------------------------------------------------------- state scan
-// One workgroup per (sequence, head, value tile of VT columns): the state
-// slice in registers, a thread holding column j = tid % VT of rows
-// tid / VT + m * (256 / VT).  A sequence's blocks are consecutive (block
-// index = 4 x its first chunk + its position); each block's operands are
-// loaded into registers one block ahead and moved to shared memory at the
-// top of the next step, so their latency hides behind a step's arithmetic.
-template <int D, int VT>
-__global__ __launch_bounds__(kBT) void bwd_state_scan_kernel(Params p, ChunkTable t, const float* S_init,
-                                                              const uint8_t* recs, float* Sblk, float* Dblk) {
+// ---------------------------------------------------------------- the two scans
+// One wave per (sequence, head, 16-column value tile).  The state slice (or
+// its adjoint) S[0..D) x [j0, j0 + 16) lives in fp32 matrix-core
+// accumulators: row tile t (rows 16t .. 16t + 15) in acc[t], lane l holding
+// rows 16t + 4 (l / 16) + i (i < 4) of column j0 + l % 16.  A product that
+// contracts over the state's rows then takes its B operand straight from the
+// accumulators: step (t, i) of v_mfma_f32_16x16x4_f32 covers rows
+// 16t + 4g + i for the four lane groups g.  A sequence's blocks are
+// consecutive (block index = 4 x its first chunk + its position), and each
+// block's operands are loaded into registers one block ahead.
+// Workgroups are numbered so that all tiles of one (sequence, head) share an
+// XCD (workgroups are dealt to the 8 XCDs round robin) and read its records
+// through one L2.
+constexpr int kScanTile = 16;
+
+__device__ __forceinline__ bool scan_coords(int nh_total, int ntile, int& nh, int& tile) {
+  const int bid = static_cast<int>(blockIdx.x);
+  const int lo = bid % 8, rest = bid / 8;
+  tile = rest % ntile;
+  nh = (rest / ntile) * 8 + lo;
+  return nh < nh_total;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave) void bwd_state_scan_kernel(Params p, ChunkTable t, const float* S_init,
+                                                                const uint8_t* recs, float* Sblk, float* Dblk) {
   constexpr BwdRecord R = bwd_record(D);
-  constexpr int RG = kBT / VT;          // row groups
-  constexpr int RPT = D / RG;           // rows per thread
-  constexpr int TE = (kBlk * D + kBT - 1) / kBT;    // tile elements per thread
-  constexpr int UE = (kBlk * VT + kBT - 1) / kBT;   // U elements per thread
-  static_assert(D % RG == 0, "rows split evenly");
-  __shared__ float sW[kBlk][D], sKt[kBlk][D], seG[D], sU[kBlk][VT];
-  __shared__ float red[RG][kBlk][VT];
-  __shared__ float sDel[kBlk][VT];
-  const int ntile = D / VT;
-  const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(ntile));
-  const int nh = static_cast<int>(blockIdx.x / static_cast<unsigned>(ntile));
+  constexpr int NT16 = D / 16;              // row tiles of the state
+  constexpr int PF = kBlk * D / kWave;      // W / K~ elements per lane
+  __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], seG[D];
+  __shared__ float sDel[kBlk][kScanTile + 1];
+  int nh, tile;
+  if (!scan_coords(t.N * p.H, D / kScanTile, nh, tile)) return;
   const int h = nh % p.H, n = nh / p.H;
-  const int tid = threadIdx.x, j = tid % VT, rg = tid / VT, j0 = tile * VT;
+  const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16, j0 = tile * kScanTile;
   const size_t SZ = static_cast<size_t>(D) * D;
-  float S[RPT];
-  for (int m = 0; m < RPT; ++m) {
-    const int r = rg + m * RG;
-    S[m] = S_init ? S_init[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + j] : 0.f;
-  }
+  f32x4 acc[NT16];
+#pragma unroll
+  for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * t16 + 4 * g + i;
+      acc[t16][i] = S_init ? S_init[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + l16]
+                           : 0.f;
+    }
   const int L = t.cu[n + 1] - t.cu[n];
   const int nb = (L + kBlk - 1) / kBlk;
   const int blk0 = t.chunk0[n] * kBlocksPerChunk;
-  float pW[TE], pK[TE], pU[UE], pE = 0.f;
+  float pW[PF], pK[PF], pU[4], pE[(D + kWave - 1) / kWave];
   auto fetch = [&](int blk) {
     const uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
     const float* gW = reinterpret_cast<const float*>(rec + R.W);
     const float* gU = reinterpret_cast<const float*>(rec + R.U);
     const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
     const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
-    for (int m = 0; m < TE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * D) { pW[m] = gW[e]; pK[m] = gKt[e]; }
-    }
-    for (int m = 0; m < UE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * VT) pU[m] = gU[(e / VT) * D + j0 + e % VT];
-    }
-    if (tid < D) pE = geG[tid];
+#pragma unroll
+    for (int m = 0; m < PF; ++m) { pW[m] = gW[lane + m * kWave]; pK[m] = gKt[lane + m * kWave]; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pU[i] = gU[(4 * g + i) * D + j0 + l16];
+#pragma unroll
+    for (int m = 0; m < (D + kWave - 1) / kWave; ++m)
+      if (lane + m * kWave < D) pE[m] = geG[lane + m * kWave];
   };
   if (nb > 0) fetch(blk0);
   for (int jb = 0; jb < nb; ++jb) {
     const int blk = blk0 + jb;
     const size_t bh = static_cast<size_t>(blk) * p.H + h;
-    for (int m = 0; m < TE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * D) { sW[e / D][e % D] = pW[m]; sKt[e / D][e % D] = pK[m]; }
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+      const int e = lane + m * kWave;
+      sW[e / D][e % D] = pW[m];
+      sKt[e / D][e % D] = pK[m];
     }
-    for (int m = 0; m < UE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * VT) sU[e / VT][e % VT] = pU[m];
-    }
-    if (tid < D) seG[tid] = pE;
+#pragma unroll
+    for (int m = 0; m < (D + kWave - 1) / kWave; ++m)
+      if (lane + m * kWave < D) seG[lane + m * kWave] = pE[m];
+    float U[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) U[i] = pU[i];
     // the state at the block's start
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      Sblk[bh * SZ + static_cast<size_t>(r) * D + j0 + j] = S[m];
-    }
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Sblk[bh * SZ + static_cast<size_t>(16 * t16 + 4 * g + i) * D + j0 + l16] = acc[t16][i];
     __syncthreads();
     if (jb + 1 < nb) fetch(blk + 1);
-    // Delta = U - W S
-    float acc[kBlk];
-    for (int q = 0; q < kBlk; ++q) acc[q] = 0.f;
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      for (int q = 0; q < kBlk; ++q) acc[q] += sW[q][r] * S[m];
-    }
-    for (int q = 0; q < kBlk; ++q) red[rg][q][j] = acc[q];
-    __syncthreads();
-    for (int e = tid; e < kBlk * VT; e += kBT) {
-      const int q = e / VT, jj = e % VT;
-      float sum = 0.f;
-      for (int g2 = 0; g2 < RG; ++g2) sum += red[g2][q][jj];
-      const float del = sU[q][jj] - sum;
-      sDel[q][jj] = del;
-      Dblk[bh * kBlk * D + static_cast<size_t>(q) * D + j0 + jj] = del;
+    // Delta = U - W S  (contracting the state's rows; four accumulators by i)
+    f32x4 d4[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d4[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(sW[l16][16 * t16 + 4 * g + i], acc[t16][i], d4[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float del = U[i] - ((d4[0][i] + d4[1][i]) + (d4[2][i] + d4[3][i]));
+      sDel[4 * g + i][l16] = del;
+      Dblk[bh * kBlk * D + static_cast<size_t>(4 * g + i) * D + j0 + l16] = del;
     }
     __syncthreads();
-    // S <- e^{G_C} S + K~^T Delta
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      float v = seG[r] * S[m];
-      for (int q = 0; q < kBlk; ++q) v += sKt[q][r] * sDel[q][j];
-      S[m] = v;
+    // S <- e^{G_C} S + K~^T Delta  (K = the block's 16 rows)
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t16][i] *= seG[16 * t16 + 4 * g + i];
+#pragma unroll
+      for (int st = 0; st < kBlk / 4; ++st) {
+        const int k = 4 * st + g;
+        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKt[k][16 * t16 + l16], sDel[k][l16], acc[t16], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
 }
 
-// ---------------------------------------------------------------- adjoint scan
-// The state scan's layout, blocks in reverse, operands one block ahead.
-template <int D, int VT, bool DO_BF16>
-__global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTable t, const uint8_t* recs,
-                                                                const void* dO, const float* dS_final, float* dSblk,
-                                                                float* dDblk, float* dS_init, float* dconv) {
+// The state scan's layout, blocks in reverse:
+//   dDelta = Aqk^T dO + K~ dS_C,   dS0 = Q+^T dO + e^{G_C} dS_C - W^T dDelta
+template <int D, bool DO_BF16>
+__global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, ChunkTable t, const uint8_t* recs,
+                                                                  const void* dO, const float* dS_final,
+                                                                  float* dSblk, float* dDblk, float* dS_init,
+                                                                  float* dconv) {
   constexpr BwdRecord R = bwd_record(D);
-  constexpr int RG = kBT / VT;
-  constexpr int RPT = D / RG;
-  constexpr int TE = (kBlk * D + kBT - 1) / kBT;
-  constexpr int OE = (kBlk * VT + kBT - 1) / kBT;
-  constexpr int AE = (kBlk * kBlk + kBT - 1) / kBT;
-  __shared__ float sW[kBlk][D], sKt[kBlk][D], sQp[kBlk][D], seG[D];
-  __shared__ float sAqk[kBlk][kBlk];
-  __shared__ float sdO[kBlk][VT];
-  __shared__ float red[RG][kBlk][VT];
-  __shared__ float sdDel[kBlk][VT];
-  const int ntile = D / VT;
-  const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(ntile));
-  const int nh = static_cast<int>(blockIdx.x / static_cast<unsigned>(ntile));
+  constexpr int NT16 = D / 16;
+  constexpr int PF = kBlk * D / kWave;
+  constexpr int PE = (D + kWave - 1) / kWave;
+  __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], sQp[kBlk][D + 1], seG[D];
+  __shared__ float sAqk[kBlk][kBlk + 1], sdO[kBlk][kScanTile + 1], sdDel[kBlk][kScanTile + 1];
+  int nh, tile;
+  if (!scan_coords(t.N * p.H, D / kScanTile, nh, tile)) return;
   const int h = nh % p.H, n = nh / p.H;
-  const int tid = threadIdx.x, j = tid % VT, rg = tid / VT, j0 = tile * VT;
+  const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16, j0 = tile * kScanTile;
   const size_t SZ = static_cast<size_t>(D) * D;
   const size_t HD = static_cast<size_t>(p.H) * D;
-  float dS[RPT];
-  for (int m = 0; m < RPT; ++m) {
-    const int r = rg + m * RG;
-    dS[m] = dS_final ? dS_final[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + j] : 0.f;
-  }
+  f32x4 acc[NT16];
+#pragma unroll
+  for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * t16 + 4 * g + i;
+      acc[t16][i] = dS_final ? dS_final[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + l16]
+                             : 0.f;
+    }
   const int L = t.cu[n + 1] - t.cu[n];
   const int nb = (L + kBlk - 1) / kBlk;
   const int blk0 = t.chunk0[n] * kBlocksPerChunk;
   const int64_t seq0 = t.cu[n];
-  float pW[TE], pK[TE], pQ[TE], pO[OE], pA[AE], pE = 0.f;
+  float pW[PF], pK[PF], pQ[PF], pA[4], pO[4], pE[PE];
   auto fetch = [&](int jb) {
     const int blk = blk0 + jb;
     const int ntok = min(kBlk, L - jb * kBlk);
@@ -428,81 +490,94 @@ __global__ __launch_bounds__(kBT) void bwd_adjoint_scan_kernel(Params p, ChunkTa
     const float* gQp = reinterpret_cast<const float*>(rec + R.Qp);
     const float* gAqk = reinterpret_cast<const float*>(rec + R.Aqk);
     const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
-    for (int m = 0; m < TE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * D) { pW[m] = gW[e]; pK[m] = gKt[e]; pQ[m] = gQp[e]; }
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+      pW[m] = gW[lane + m * kWave];
+      pK[m] = gKt[lane + m * kWave];
+      pQ[m] = gQp[lane + m * kWave];
     }
-    for (int m = 0; m < AE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * kBlk) pA[m] = gAqk[e];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      pA[m] = gAqk[lane + m * kWave];
+      const int q = (lane + m * kWave) / kScanTile, jj = (lane + m * kWave) % kScanTile;
+      pO[m] = q < ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + q) * p.H + h) * D + j0 + jj) : 0.f;
     }
-    for (int m = 0; m < OE; ++m) {
-      const int e = tid + m * kBT;
-      const int q = e / VT, jj = e % VT;
-      if (e < kBlk * VT)
-        pO[m] = q < ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + q) * p.H + h) * D + j0 + jj) : 0.f;
-    }
-    if (tid < D) pE = geG[tid];
+#pragma unroll
+    for (int m = 0; m < PE; ++m)
+      if (lane + m * kWave < D) pE[m] = geG[lane + m * kWave];
   };
   if (nb > 0) fetch(nb - 1);
   for (int jb = nb - 1; jb >= 0; --jb) {
     const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
-    for (int m = 0; m < TE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * D) { sW[e / D][e % D] = pW[m]; sKt[e / D][e % D] = pK[m]; sQp[e / D][e % D] = pQ[m]; }
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+      const int e = lane + m * kWave;
+      sW[e / D][e % D] = pW[m];
+      sKt[e / D][e % D] = pK[m];
+      sQp[e / D][e % D] = pQ[m];
     }
-    for (int m = 0; m < AE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * kBlk) sAqk[e / kBlk][e % kBlk] = pA[m];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + m * kWave;
+      sAqk[e / kBlk][e % kBlk] = pA[m];
+      sdO[e / kScanTile][e % kScanTile] = pO[m];
     }
-    for (int m = 0; m < OE; ++m) {
-      const int e = tid + m * kBT;
-      if (e < kBlk * VT) sdO[e / VT][e % VT] = pO[m];
-    }
-    if (tid < D) seG[tid] = pE;
+#pragma unroll
+    for (int m = 0; m < PE; ++m)
+      if (lane + m * kWave < D) seG[lane + m * kWave] = pE[m];
     // the adjoint of the block's end state
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      dSblk[bh * SZ + static_cast<size_t>(r) * D + j0 + j] = dS[m];
-    }
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dSblk[bh * SZ + static_cast<size_t>(16 * t16 + 4 * g + i) * D + j0 + l16] = acc[t16][i];
     __syncthreads();
     if (jb > 0) fetch(jb - 1);
-    // dDelta = Aqk^T dO + K~ dS_C
-    float acc[kBlk];
-    for (int q = 0; q < kBlk; ++q) acc[q] = 0.f;
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      for (int q = 0; q < kBlk; ++q) acc[q] += sKt[q][r] * dS[m];
+    // dDelta = K~ dS_C (contracting the state's rows) + Aqk^T dO
+    f32x4 d4[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d4[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKt[l16][16 * t16 + 4 * g + i], acc[t16][i], d4[i], 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < kBlk / 4; ++st) {
+      const int k = 4 * st + g;
+      d4[st] = __builtin_amdgcn_mfma_f32_16x16x4f32(sAqk[k][l16], sdO[k][l16], d4[st], 0, 0, 0);
     }
-    for (int q = 0; q < kBlk; ++q) red[rg][q][j] = acc[q];
-    __syncthreads();
-    for (int e = tid; e < kBlk * VT; e += kBT) {
-      const int q = e / VT, jj = e % VT;
-      float sum = 0.f;
-      for (int g2 = 0; g2 < RG; ++g2) sum += red[g2][q][jj];
-      for (int r2 = q; r2 < kBlk; ++r2) sum += sAqk[r2][q] * sdO[r2][jj];
-      sdDel[q][jj] = sum;
-      dDblk[bh * kBlk * D + static_cast<size_t>(q) * D + j0 + jj] = sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float dd = (d4[0][i] + d4[1][i]) + (d4[2][i] + d4[3][i]);
+      sdDel[4 * g + i][l16] = dd;
+      dDblk[bh * kBlk * D + static_cast<size_t>(4 * g + i) * D + j0 + l16] = dd;
     }
     __syncthreads();
-    // dS0 = Q+^T dO + e^{G_C} dS_C - W^T dDelta
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      float v = seG[r] * dS[m];
-      for (int q = 0; q < kBlk; ++q) v += sQp[q][r] * sdO[q][j] - sW[q][r] * sdDel[q][j];
-      dS[m] = v;
+    // dS0 = e^{G_C} dS_C + Q+^T dO - W^T dDelta
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t16][i] *= seG[16 * t16 + 4 * g + i];
+#pragma unroll
+      for (int st = 0; st < kBlk / 4; ++st) {
+        const int k = 4 * st + g;
+        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQp[k][16 * t16 + l16], sdO[k][l16], acc[t16], 0, 0, 0);
+        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(-sW[k][16 * t16 + l16], sdDel[k][l16], acc[t16], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
   if (dS_init) {
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rg + m * RG;
-      dS_init[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + j] = dS[m];
-    }
+#pragma unroll
+    for (int t16 = 0; t16 < NT16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * t16 + 4 * g + i;
+        dS_init[(static_cast<size_t>(n) * p.H + h) * SZ + static_cast<size_t>(r) * D + j0 + l16] = acc[t16][i];
+      }
   }
   // an empty sequence passes its conv history through: no gradient reaches it
   if (dconv && tile == 0 && nb == 0) {
-    for (int e = tid; e < 3 * D; e += kBT) {
+    for (int e = lane; e < 3 * D; e += kWave) {
       const int role = e / D, ch = e % D;
       for (int m = 0; m < 3; ++m)
         dconv[(static_cast<size_t>(n) * 3 + m) * 3 * HD + role * HD + static_cast<size_t>(h) * D + ch] = 0.f;
@@ -523,6 +598,9 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
                                                               float* dalpha, float* db, float* pdtb, float* pAlog) {
   constexpr BwdRecord R = bwd_record(D);
   constexpr int NT = grad_threads<D>();
+  constexpr int EL = (kBlk * D + NT - 1) / NT;   // block-tile elements per thread
+  constexpr int KS = D / 4;                      // S0 / dS_C columns per lane of the matrix-core waves
+  using Raw = BlockRaw<D, NT>;
   __shared__ BlockSmem<D> s;
   __shared__ float sDel[kBlk][D + 1], sdDel[kBlk][D + 1], sdO[kBlk][D + 1];   // padded: matrix-core A reads
   __shared__ float sdQp[kBlk][D + 1], sdKp[kBlk][D + 1], sdKm[kBlk][D + 1], sdKt[kBlk][D + 1];
@@ -542,74 +620,97 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     if (tid == 0) pAlog[static_cast<size_t>(blk) * p.H + h] = 0.f;
     return;
   }
-  block_preprocess<D, IO_BF16, NT>(p, io, b, h, s);
   const size_t bh = static_cast<size_t>(blk) * p.H + h;
   const uint8_t* rec = recs + bh * R.bytes;
   const float* gW = reinterpret_cast<const float*>(rec + R.W);
   const float* gU = reinterpret_cast<const float*>(rec + R.U);
   const float* gT = reinterpret_cast<const float*>(rec + R.T);
   const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
-  const float* S0 = Sblk + bh * D * D;
-  const float* dSC = dSblk + bh * D * D;
-  for (int e = tid; e < kBlk * D; e += NT) {
-    const int r = e / D, c = e % D;
-    sDel[r][c] = Dblk[bh * kBlk * D + e];
-    sdDel[r][c] = dDblk[bh * kBlk * D + e];
-    sdO[r][c] = r < b.ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(b.tok0 + r) * p.H + h) * D + c) : 0.f;
+  const int wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g4 = lane / 16;
+
+  // ---- every load of the block goes out here, before any arithmetic: the
+  // raw inputs (kept for the reverse of the conv and the gate at the end),
+  // then the scans' outputs and the record, whose latency the preprocess hides
+  Raw raw;
+  block_load_raw<D, IO_BF16, NT>(p, io, b, h, raw);
+  float lDel[EL], ldDel[EL], ldO[EL], lW[EL], lU[EL];
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = tid + m * NT;
+    if (e < kBlk * D) {
+      const int r = e / D, c = e % D;
+      lDel[m] = Dblk[bh * kBlk * D + e];
+      ldDel[m] = dDblk[bh * kBlk * D + e];
+      ldO[m] = r < b.ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(b.tok0 + r) * p.H + h) * D + c) : 0.f;
+      lW[m] = gW[e];
+      lU[m] = gU[e];
+    }
   }
-  for (int e = tid; e < kBlk * kBlk; e += NT) sT[e / kBlk][e % kBlk] = gT[e];
+  const float lT = tid < kBlk * kBlk ? gT[tid] : 0.f;
+  // rows of S0 and dS_C for the matrix-core products: wave w owns output
+  // channels 16w .. 16w + 15, lane l the contiguous state columns
+  // KS (l / 16) .. KS (l / 16) + KS - 1 of row 16w + l % 16
+  float sv[KS], dsv[KS], lgeG = 0.f;
+  if (wave < D / 16) {
+    const int c = wave * 16 + l16;
+    const float* s0row = Sblk + bh * D * D + static_cast<size_t>(c) * D + g4 * KS;
+    const float* dsrow = dSblk + bh * D * D + static_cast<size_t>(c) * D + g4 * KS;
+#pragma unroll
+    for (int q = 0; q < KS; q += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(s0row + q);
+      const float4 d4 = *reinterpret_cast<const float4*>(dsrow + q);
+      sv[q] = a.x; sv[q + 1] = a.y; sv[q + 2] = a.z; sv[q + 3] = a.w;
+      dsv[q] = d4.x; dsv[q + 1] = d4.y; dsv[q + 2] = d4.z; dsv[q + 3] = d4.w;
+    }
+    lgeG = geG[c];
+  }
+  block_preprocess<D, NT>(p, b, h, raw, s);
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = tid + m * NT;
+    if (e < kBlk * D) {
+      const int r = e / D, c = e % D;
+      sDel[r][c] = lDel[m];
+      sdDel[r][c] = ldDel[m];
+      sdO[r][c] = ldO[m];
+    }
+  }
+  if (tid < kBlk * kBlk) sT[tid / kBlk][tid % kBlk] = lT;
   __syncthreads();
 
   // ---- products with S0 and dS_C on the fp32 matrix cores (v_mfma_f32_16x16x4_f32):
   //   dQ+ = dO S0^T, dW = -dDelta S0^T, dK~ = Delta dS_C^T  (16 x D each) and
   //   dG_C = e^{G_C} rowsum(dS_C * S0).
-  // Wave w owns output channels 16w .. 16w + 15.  Step s of lane l covers state
-  // column KS * (l / 16) + s (KS = D / 4), so each lane reads two contiguous
-  // runs of KS floats, its pieces of one row of S0 and of dS_C.
-  {
-    constexpr int KS = D / 4;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int l16 = lane % 16, g = lane / 16;
-    if (wave < D / 16) {
-      const int c = wave * 16 + l16;
-      float sv[KS], dsv[KS];
-      const float* s0row = S0 + static_cast<size_t>(c) * D + g * KS;
-      const float* dsrow = dSC + static_cast<size_t>(c) * D + g * KS;
+  // Step s of lane l covers state column KS (l / 16) + s, the lane's own row
+  // pieces loaded above.
+  if (wave < D / 16) {
+    const int c = wave * 16 + l16;
+    float gc = 0.f;
 #pragma unroll
-      for (int q = 0; q < KS; q += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(s0row + q);
-        const float4 d4 = *reinterpret_cast<const float4*>(dsrow + q);
-        sv[q] = a.x; sv[q + 1] = a.y; sv[q + 2] = a.z; sv[q + 3] = a.w;
-        dsv[q] = d4.x; dsv[q + 1] = d4.y; dsv[q + 2] = d4.z; dsv[q + 3] = d4.w;
-      }
-      float gc = 0.f;
+    for (int q = 0; q < KS; ++q) gc += sv[q] * dsv[q];
+    gc += __shfl_xor(gc, 16);
+    gc += __shfl_xor(gc, 32);
+    f32x4 aQ = zero4(), aW = zero4(), aK = zero4();
 #pragma unroll
-      for (int q = 0; q < KS; ++q) gc += sv[q] * dsv[q];
-      gc += __shfl_xor(gc, 16);
-      gc += __shfl_xor(gc, 32);
-      f32x4 aQ = zero4(), aW = zero4(), aK = zero4();
-#pragma unroll
-      for (int q = 0; q < KS; ++q) {
-        const int j = g * KS + q;
-        aQ = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[l16][j], sv[q], aQ, 0, 0, 0);
-        aW = __builtin_amdgcn_mfma_f32_16x16x4f32(sdDel[l16][j], sv[q], aW, 0, 0, 0);
-        aK = __builtin_amdgcn_mfma_f32_16x16x4f32(sDel[l16][j], dsv[q], aK, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        sdQp[r][c] = aQ[i];
-        sX[r][c] = -aW[i];
-        sdKt[r][c] = aK[i];
-      }
-      if (g == 0) sdGC[c] = geG[c] * gc;
+    for (int q = 0; q < KS; ++q) {
+      const int j = g4 * KS + q;
+      aQ = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[l16][j], sv[q], aQ, 0, 0, 0);
+      aW = __builtin_amdgcn_mfma_f32_16x16x4f32(sdDel[l16][j], sv[q], aW, 0, 0, 0);
+      aK = __builtin_amdgcn_mfma_f32_16x16x4f32(sDel[l16][j], dsv[q], aK, 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i;
+      sdQp[r][c] = aQ[i];
+      sX[r][c] = -aW[i];
+      sdKt[r][c] = aK[i];
+    }
+    if (g4 == 0) sdGC[c] = lgeG * gc;
   }
   __syncthreads();
   // ---- the 16 x 16 and 16 x D products of the block on the fp32 matrix cores
   // (v_mfma_f32_16x16x4_f32: lane l gives A[l % 16][k] and B[k][l % 16] with k
   // the step's K index 4 s + l / 16, and holds C[4 (l / 16) + i][l % 16]).
-  const int wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g4 = lane / 16;
   // dXw = T^T dW, dXu = T^T dDelta (K = 16); wave w: channels 16w .. 16w + 15
   {
     f32x4 xw = zero4(), xu = zero4();
@@ -632,43 +733,57 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
       }
     }
   }
-  for (int e = tid; e < kBlk * D; e += NT) {
-    sWt[e / D][e % D] = gW[e];
-    sUt[e / D][e % D] = gU[e];
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = tid + m * NT;
+    if (e < kBlk * D) {
+      sWt[e / D][e % D] = lW[m];
+      sUt[e / D][e % D] = lU[m];
+    }
   }
   __syncthreads();
   // dA = -strict_lower(dXw W^T + dXu U^T) (wave 0), A_un = strict_lower(K+ K-^T)
-  // (wave 1), dAqk = lower(dO Delta^T) (wave 2): 16 x 16 each over K = D
+  // (wave 1), dAqk = lower(dO Delta^T) (wave 2): 16 x 16 each over K = D, in
+  // four independent accumulators
   if (wave < 3) {
-    f32x4 acc = zero4();
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int k = k0 + g4;
-      if (wave == 0) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[l16][k], sWt[l16][k], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdKm[l16][k], sUt[l16][k], acc, 0, 0, 0);
-      } else if (wave == 1) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s.k[l16][k] * s.eP[l16][k], s.k[l16][k] * s.eM[l16][k], acc,
-                                                   0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[l16][k], sDel[l16][k], acc, 0, 0, 0);
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = k0 + 4 * j + g4;
+        if (wave == 0) {
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[l16][k], sWt[l16][k], acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sdKm[l16][k], sUt[l16][k], acc[j], 0, 0, 0);
+        } else if (wave == 1) {
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(s.k[l16][k] * s.eP[l16][k], s.k[l16][k] * s.eM[l16][k],
+                                                        acc[j], 0, 0, 0);
+        } else {
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sdO[l16][k], sDel[l16][k], acc[j], 0, 0, 0);
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g4 + i;
-      if (wave == 0) sdA[r][l16] = l16 < r ? -acc[i] : 0.f;
-      else if (wave == 1) sAun[r][l16] = l16 < r ? acc[i] : 0.f;
-      else sdAqk[r][l16] = l16 <= r ? acc[i] : 0.f;
+      const float v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      if (wave == 0) sdA[r][l16] = l16 < r ? -v : 0.f;
+      else if (wave == 1) sAun[r][l16] = l16 < r ? v : 0.f;
+      else sdAqk[r][l16] = l16 <= r ? v : 0.f;
     }
   }
   __syncthreads();
-  // ---- dbeta; dV; dK+ and dK- from X and A; dQ+ and dK- from Aqk
-  if (tid < kBlk) {
-    const int r = tid;
+  // ---- dbeta (all threads: NT / 16 lanes per row, a shuffle sum); dV; dK+
+  // and dK- from X and A; dQ+ and dK- from Aqk
+  {
+    constexpr int TPR = NT / kBlk;      // lanes per row (a power of two, at most 64)
+    const int r = tid / TPR, lr = tid % TPR;
     float d = 0.f;
-    for (int c = 0; c < D; ++c) d += sX[r][c] * s.k[r][c] * s.eP[r][c] + sdKm[r][c] * s.v[r][c];
-    for (int i = 0; i < r; ++i) d += sdA[r][i] * sAun[r][i];
-    sdbeta[r] = d;
+    for (int c = lr; c < D; c += TPR) d += sX[r][c] * s.k[r][c] * s.eP[r][c] + sdKm[r][c] * s.v[r][c];
+    for (int i = lr; i < r; i += TPR) d += sdA[r][i] * sAun[r][i];
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o /= 2) d += __shfl_xor(d, o, TPR);
+    if (lr == 0) sdbeta[r] = d;
   }
   {
     // (beta dA) K-,  (beta dA)^T K+ + dAqk^T Q+,  dAqk K-  (K = 16)
@@ -759,18 +874,24 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     }
   }
   __syncthreads();
-  // ---- the preprocess in reverse
+  // ---- the preprocess in reverse, on the threads whose registers hold the
+  // raw inputs of the same (tensor, channel) task
   // gate: d alpha, and the block's partial sums for d dt_bias and d A_log
   {
     const float a_exp = expf(p.A_log[h]);
     float alog_part = 0.f;
-    if (tid < D) {
-      const int c = tid;
+#pragma unroll
+    for (int m = 0; m < Raw::kTasks; ++m) {
+      const int task = tid + m * NT;
+      if (task < 3 * D || task >= 4 * D) continue;
+      const int c = task - 3 * D;
       const size_t col = static_cast<size_t>(h) * D + c;
-      const float dtb = p.dt_bias[col];
+      const float dtb = raw.w[m][0];
       float dtb_part = 0.f;
-      for (int r = 0; r < b.ntok; ++r) {
-        const float al = ld<IO_BF16>(io.alpha, static_cast<size_t>(b.tok0 + r) * HD + col);
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) {
+        if (r >= b.ntok) continue;
+        const float al = raw.x[m][3 + r];
         const float dg = sdKm[r][c];
         float da;
         if (p.flags & KDA_FLAG_RAW_GATE) {
@@ -790,7 +911,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
       }
       pd[c] = dtb_part;
     }
-    // d A_log: sum over the block's channels (waves 0 and 1 hold them for D = 128)
+    // d A_log: sum over the block's channels
     __shared__ float sAl[NT / kWave];
     const float wsum = group_sum<kWave>(alog_part);
     if (tid % kWave == 0) sAl[tid / kWave] = wsum;
@@ -803,8 +924,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   }
   // beta
   if (tid < b.ntok) {
-    const float bb = ld<IO_BF16>(io.b, static_cast<size_t>(b.tok0 + tid) * p.H + h);
-    const float sg = sigmoidf_(bb);
+    const float sg = sigmoidf_(raw.bb);
     float dbv = sdbeta[tid] * sg * (1.f - sg);
     if (p.flags & KDA_FLAG_BETA_X2) dbv *= 2.f;
     db[static_cast<size_t>(b.tok0 + tid) * p.H + h] = dbv;
@@ -823,26 +943,18 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     if (l8 == 0) sDot[isq ? 0 : 1][r] = dot;
   }
   __syncthreads();
-  // SiLU: dy = du sigmoid(y) (1 + y (1 - sigmoid(y))), with y recomputed from the raw window
-  for (int task = tid; task < 3 * D; task += NT) {
+  // SiLU: dy = du sigmoid(y) (1 + y (1 - sigmoid(y))), with y recomputed from the raw inputs
+#pragma unroll
+  for (int m = 0; m < Raw::kTasks; ++m) {
+    const int task = tid + m * NT;
+    if (task >= 3 * D) continue;
     const int role = task / D, ch = task % D;
     const size_t col = static_cast<size_t>(h) * D + ch;
-    const void* xin = role == 0 ? io.q : (role == 1 ? io.k : io.v);
-    const void* w = role == 0 ? p.wq : (role == 1 ? p.wk : p.wv);
-    const float w0 = ld<IO_BF16>(w, col * 4), w1 = ld<IO_BF16>(w, col * 4 + 1);
-    const float w2 = ld<IO_BF16>(w, col * 4 + 2), w3 = ld<IO_BF16>(w, col * 4 + 3);
-    const int64_t seq0 = b.tok0 - b.tau0;
-    float win[3];
-    for (int m = 0; m < 3; ++m) {
-      const int tau = b.tau0 - 3 + m;
-      if (tau >= 0) win[m] = ld<IO_BF16>(xin, static_cast<size_t>(seq0 + tau) * HD + col);
-      else if (io.conv_in) win[m] = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(b.seq) * 3 + (3 + tau)) * 3 * HD + role * HD + col);
-      else win[m] = 0.f;
-    }
-    for (int r = 0; r < b.ntok; ++r) {
-      const float xt = ld<IO_BF16>(xin, static_cast<size_t>(b.tok0 + r) * HD + col);
-      const float y = w0 * win[0] + w1 * win[1] + w2 * win[2] + w3 * xt;
-      win[0] = win[1]; win[1] = win[2]; win[2] = xt;
+    const float w0 = raw.w[m][0], w1 = raw.w[m][1], w2 = raw.w[m][2], w3 = raw.w[m][3];
+#pragma unroll
+    for (int r = 0; r < kBlk; ++r) {
+      if (r >= b.ntok) continue;
+      const float y = w0 * raw.x[m][r] + w1 * raw.x[m][r + 1] + w2 * raw.x[m][r + 2] + w3 * raw.x[m][r + 3];
       float du;
       if (role == 0) {
         const float sc = p.scale, n = s.nq[r];
@@ -863,11 +975,15 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
 // One workgroup per (64-token chunk, head); a thread per (q/k/v, channel)
 // walks the chunk's tokens: dx_t = sum_j w[j] dy_{t+3-j} over tokens of the
 // same sequence, the history's gradient for the sequence's first chunk, and
-// the chunk's partial d w[j] = sum_t dy_t x_{t-3+j}.
+// the chunk's partial d w[j] = sum_t dy_t x_{t-3+j}.  The tokens go in four
+// steps of 16, each step's loads issued before the previous step's
+// arithmetic; addresses are clamped into the sequence and the zeros outside
+// it selected afterwards, so a step's loads go out back to back.
 template <int D, bool IO_BF16>
 __global__ __launch_bounds__(3 * D) void bwd_conv_kernel(Params p, ChunkTable t, PrefillIO io, const float* dy,
                                                           float* dq, float* dk, float* dv, float* dconv,
                                                           float* pdw) {
+  constexpr int SB = 16;                   // tokens per step
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
   const int c = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   const int tid = threadIdx.x, role = tid / D, ch = tid % D;
@@ -882,97 +998,154 @@ __global__ __launch_bounds__(3 * D) void bwd_conv_kernel(Params p, ChunkTable t,
   const void* xin = role == 0 ? io.q : (role == 1 ? io.k : io.v);
   const void* w = role == 0 ? p.wq : (role == 1 ? p.wk : p.wv);
   float* dx = role == 0 ? dq : (role == 1 ? dk : dv);
+  const float* dyc = dy + static_cast<size_t>(seq0) * 3 * HD + role * HD + col;   // dy at sequence position 0
+  const size_t xcol = static_cast<size_t>(seq0) * HD + col;                       // x at sequence position 0
   float wj[4];
+#pragma unroll
   for (int j = 0; j < 4; ++j) wj[j] = ld<IO_BF16>(w, col * 4 + j);
-  auto dyat = [&](int tau) {   // dy of sequence position tau, 0 outside the sequence
-    return (tau >= 0 && tau < L) ? dy[static_cast<size_t>(seq0 + tau) * 3 * HD + role * HD + col] : 0.f;
-  };
-  auto xat = [&](int tau) {    // raw input at sequence position tau (the history before 0)
-    if (tau >= 0) return ld<IO_BF16>(xin, static_cast<size_t>(seq0 + tau) * HD + col);
-    if (io.conv_in) return ld<IO_BF16>(io.conv_in, (static_cast<size_t>(seq) * 3 + (3 + tau)) * 3 * HD + role * HD + col);
-    return 0.f;
-  };
-  // the chunk's window, loaded before any arithmetic: x at positions
-  // tau0 - 3 .. tau0 + 63 and dy at tau0 .. tau0 + 66 (zeros outside)
-  constexpr int WN = kChunk + 3;
-  float xs[WN], dys[WN];
+  // the window before the first step: x at positions tau0 - 3 .. tau0 - 1 (the
+  // sequence's inputs, or at its start the conv history, zeros without one),
+  // dy at tau0 .. tau0 + 2
+  const bool hist = tau0 == 0;
+  const bool from_hist = hist && io.conv_in != nullptr;
+  const void* xsrc = from_hist ? io.conv_in : xin;   // one load from whichever holds the row
+  float xw[3], dyw[3];
 #pragma unroll
-  for (int m = 0; m < WN; ++m) {
-    xs[m] = (m - 3 < cnt) ? xat(tau0 - 3 + m) : 0.f;
-    dys[m] = dyat(tau0 + m);
+  for (int m = 0; m < 3; ++m) {
+    const size_t xi = xcol + static_cast<size_t>(hist ? 0 : tau0 - 3 + m) * HD;
+    const size_t hi = (static_cast<size_t>(seq) * 3 + m) * 3 * HD + role * HD + col;
+    xw[m] = ld<IO_BF16>(xsrc, from_hist ? hi : xi);
+    dyw[m] = dyc[static_cast<size_t>(min(tau0 + m, L - 1)) * 3 * HD];
   }
-  float aw[4] = {0.f, 0.f, 0.f, 0.f};
+  // step k's operands: x at tau0 + 16k .. + 15, dy at tau0 + 16k + 3 .. + 18
+  float xn[SB], dyn[SB];
+  auto fetch = [&](int k) {
 #pragma unroll
-  for (int r = 0; r < kChunk; ++r) {
-    if (r < cnt) {
-      float g = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) g += wj[j] * dys[r + 3 - j];
-      dx[static_cast<size_t>(seq0 + tau0 + r) * HD + col] = g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) aw[j] += dys[r] * xs[r + j];
+    for (int i = 0; i < SB; ++i) {
+      xn[i] = ld<IO_BF16>(xin, xcol + static_cast<size_t>(tau0 + min(SB * k + i, cnt - 1)) * HD);
+      dyn[i] = dyc[static_cast<size_t>(min(tau0 + SB * k + 3 + i, L - 1)) * 3 * HD];
     }
+  };
+  fetch(0);
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    if (hist && !from_hist) xw[m] = 0.f;
+    if (tau0 + m >= L) dyw[m] = 0.f;
   }
-  for (int j = 0; j < 4; ++j) pw[j] = aw[j];
-  if (tau0 == 0 && dconv) {
-    // history slot m holds position m - 3: dx_{m-3} = sum_j w[j] dy_{m-j}
+  // history slot m holds position m - 3: dx_{m-3} = sum_j w[j] dy_{m-j}
+  if (hist && dconv) {
+#pragma unroll
     for (int m = 0; m < 3; ++m) {
       float g = 0.f;
-      for (int j = 0; j <= m; ++j) g += wj[j] * dys[m - j];
+#pragma unroll
+      for (int j = 0; j <= m; ++j) g += wj[j] * dyw[m - j];
       dconv[(static_cast<size_t>(seq) * 3 + m) * 3 * HD + role * HD + col] = g;
     }
   }
+  float aw[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kChunk / SB; ++k) {
+    if (SB * k >= cnt) break;   // uniform over the workgroup
+    float xx[SB + 3], dd[SB + 3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) { xx[m] = xw[m]; dd[m] = dyw[m]; }
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      xx[3 + i] = SB * k + i < cnt ? xn[i] : 0.f;
+      dd[3 + i] = tau0 + SB * k + 3 + i < L ? dyn[i] : 0.f;
+    }
+    if (k + 1 < kChunk / SB) fetch(k + 1);
+#pragma unroll
+    for (int r = 0; r < SB; ++r) {
+      if (SB * k + r < cnt) {
+        float g = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g += wj[j] * dd[r + 3 - j];
+        dx[xcol + static_cast<size_t>(tau0 + SB * k + r) * HD] = g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) aw[j] += dd[r] * xx[r + j];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) { xw[m] = xx[SB + m]; dyw[m] = dd[SB + m]; }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pw[j] = aw[j];
 }
 
 // ---------------------------------------------------------------- parameter sums
-// One thread per parameter gradient element, summing the partials of every
-// chunk (conv weights) or block (dt_bias, A_log) in order.
-__global__ void bwd_param_reduce_kernel(int H, int D, ChunkTable t, const float* pdw, const float* pdtb,
-                                        const float* pAlog, float* dw_q, float* dw_k, float* dw_v, float* ddt_bias,
-                                        float* dA_log) {
-  const int64_t HD = static_cast<int64_t>(H) * D;
-  const int64_t n_w = 3 * HD * 4, n_dtb = HD, n_al = H;
+// The partial parameter gradients (per chunk for the conv weights, per block
+// for dt_bias and A_log) are summed in two deterministic passes: the rows are
+// cut into kReduceParts contiguous ranges, each range summed by four threads
+// per element (rows interleaved) and their sums added in a fixed order; then
+// the ranges' sums are added in range order.  Element e runs over the conv
+// weights' partials [0, n_w), dt_bias's [n_w, n_w + HD) and A_log's after.
+struct ParamSums {
+  const float* pdw;
+  const float* pdtb;
+  const float* pAlog;
+  int64_t n_w, n_dtb, n_al;
+  const int* nchunks;        // the chunk table's count of chunks (on the device)
+  __device__ int64_t total() const { return n_w + n_dtb + n_al; }
+  // the partial of element e in row r, and the element's number of rows
+  // (chunks for the conv weights, 16-token blocks for the others)
+  __device__ int rows(int64_t e) const { return *nchunks * (e < n_w ? 1 : kBlocksPerChunk); }
+  __device__ float at(int64_t e, int r) const {
+    if (e < n_w) return pdw[static_cast<size_t>(r) * n_w + e];
+    if (e < n_w + n_dtb) return pdtb[static_cast<size_t>(r) * n_dtb + (e - n_w)];
+    return pAlog[static_cast<size_t>(r) * n_al + (e - n_w - n_dtb)];
+  }
+};
+
+__global__ __launch_bounds__(256) void bwd_param_partial_kernel(ParamSums ps, float* stage) {
+  __shared__ float red[4][64];
+  const int tid = threadIdx.x, el = tid % 64, sub = tid / 64;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 64 + el;
+  const int part = static_cast<int>(blockIdx.y);
+  float acc = 0.f;
+  if (e < ps.total()) {
+    const int rows = ps.rows(e);
+    const int lo = static_cast<int>(static_cast<int64_t>(rows) * part / kReduceParts);
+    const int hi = static_cast<int>(static_cast<int64_t>(rows) * (part + 1) / kReduceParts);
+    for (int r = lo + sub; r < hi; r += 4) acc += ps.at(e, r);
+  }
+  red[sub][el] = acc;
+  __syncthreads();
+  if (sub == 0 && e < ps.total())
+    stage[static_cast<size_t>(part) * ps.total() + e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
+}
+
+__global__ void bwd_param_final_kernel(ParamSums ps, const float* stage, float* dw_q, float* dw_k, float* dw_v,
+                                       float* ddt_bias, float* dA_log) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int nchunks = t.chunk0[t.N];
-  const int nblocks = nchunks * kBlocksPerChunk;
-  if (e < n_w) {
-    float acc = 0.f;
-    for (int c = 0; c < nchunks; ++c) acc += pdw[static_cast<size_t>(c) * n_w + e];
-    const int64_t role = e / (HD * 4), rest = e % (HD * 4);
-    float* dst = role == 0 ? dw_q : (role == 1 ? dw_k : dw_v);
-    dst[rest] = acc;
-  } else if (e < n_w + n_dtb) {
-    const int64_t i = e - n_w;
-    float acc = 0.f;
-    for (int bk = 0; bk < nblocks; ++bk) acc += pdtb[static_cast<size_t>(bk) * HD + i];
-    ddt_bias[i] = acc;
-  } else if (e < n_w + n_dtb + n_al) {
-    const int64_t i = e - n_w - n_dtb;
-    float acc = 0.f;
-    for (int bk = 0; bk < nblocks; ++bk) acc += pAlog[static_cast<size_t>(bk) * H + i];
-    dA_log[i] = acc;
+  if (e >= ps.total()) return;
+  float acc = 0.f;
+  for (int part = 0; part < kReduceParts; ++part) acc += stage[static_cast<size_t>(part) * ps.total() + e];
+  if (e < ps.n_w) {
+    const int64_t per = ps.n_w / 3, role = e / per, rest = e % per;
+    (role == 0 ? dw_q : (role == 1 ? dw_k : dw_v))[rest] = acc;
+  } else if (e < ps.n_w + ps.n_dtb) {
+    ddt_bias[e - ps.n_w] = acc;
+  } else {
+    dA_log[e - ps.n_w - ps.n_dtb] = acc;
   }
 }
 
 // ---------------------------------------------------------------- launchers
 namespace {
 
-template <int D>
-constexpr int scan_tile() { return D >= 32 ? 32 : D; }
-
 template <int D, bool IO_BF16, bool DO_BF16>
 hipError_t launch_backward_d(const Params& p, const ChunkTable& t, const PrefillIO& io, const BackwardIO& g,
                              const BackwardWS& ws, int N, int max_chunks, hipStream_t st) {
-  constexpr int VT = scan_tile<D>();
   const unsigned nblk = static_cast<unsigned>(max_chunks) * kBlocksPerChunk * static_cast<unsigned>(p.H);
   bwd_block_prep_kernel<D, IO_BF16><<<nblk, kBT, 0, st>>>(p, t, io, ws.recs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned nscan = static_cast<unsigned>(N) * p.H * (D / VT);
-  bwd_state_scan_kernel<D, VT><<<nscan, kBT, 0, st>>>(p, t, io.S0, ws.recs, ws.Sblk, ws.Dblk);
+  const unsigned nh8 = (static_cast<unsigned>(N) * p.H + 7) / 8 * 8;   // (sequence, head) pairs, padded to 8 XCDs
+  const unsigned nscan = nh8 * (D / kScanTile);
+  bwd_state_scan_kernel<D><<<nscan, kWave, 0, st>>>(p, t, io.S0, ws.recs, ws.Sblk, ws.Dblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_adjoint_scan_kernel<D, VT, DO_BF16><<<nscan, kBT, 0, st>>>(p, t, ws.recs, g.dO, g.dS_final, ws.dSblk, ws.dDblk,
-                                                                 g.dS_init, g.dconv);
+  bwd_adjoint_scan_kernel<D, DO_BF16><<<nscan, kWave, 0, st>>>(p, t, ws.recs, g.dO, g.dS_final, ws.dSblk, ws.dDblk,
+                                                               g.dS_init, g.dconv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_block_grad_kernel<D, IO_BF16, DO_BF16><<<nblk, grad_threads<D>(), 0, st>>>(p, t, io, ws.recs, ws.Sblk, ws.dSblk, ws.Dblk,
                                                                    ws.dDblk, g.dO, ws.dy, g.dalpha, g.db, ws.pdtb,
@@ -981,9 +1154,13 @@ hipError_t launch_backward_d(const Params& p, const ChunkTable& t, const Prefill
   bwd_conv_kernel<D, IO_BF16><<<static_cast<unsigned>(max_chunks) * p.H, 3 * D, 0, st>>>(p, t, io, ws.dy, g.dq, g.dk,
                                                                                        g.dv, g.dconv, ws.pdw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t n_out = static_cast<int64_t>(p.H) * D * (3 * 4 + 1) + p.H;
-  bwd_param_reduce_kernel<<<static_cast<unsigned>((n_out + 255) / 256), 256, 0, st>>>(
-      p.H, D, t, ws.pdw, ws.pdtb, ws.pAlog, g.dw_q, g.dw_k, g.dw_v, g.ddt_bias, g.dA_log);
+  ParamSums ps{ws.pdw, ws.pdtb, ws.pAlog, 3 * static_cast<int64_t>(p.H) * D * 4, static_cast<int64_t>(p.H) * D,
+               p.H, t.chunk0 + t.N};
+  const int64_t n_out = ps.n_w + ps.n_dtb + ps.n_al;
+  bwd_param_partial_kernel<<<dim3(static_cast<unsigned>((n_out + 63) / 64), kReduceParts), 256, 0, st>>>(ps, ws.pstage);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_param_final_kernel<<<static_cast<unsigned>((n_out + 255) / 256), 256, 0, st>>>(ps, ws.pstage, g.dw_q, g.dw_k,
+                                                                                     g.dw_v, g.ddt_bias, g.dA_log);
   return hipGetLastError();
 }
 

@@ -165,9 +165,9 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
 // The backward's workspace: the chunk table, then per 16-token block and
 // head its record, the block-start state and the block-end adjoint, Delta and
 // its gradient; the conv outputs' gradient per token; the partial parameter
-// gradients per chunk / block.
+// gradients per chunk / block and their first-pass sums.
 struct BwdLayout {
-  size_t cu, chunk0, chunk_seq, desc, recs, Sblk, dSblk, Dblk, dDblk, dy, pdw, pdtb, pAlog, total;
+  size_t cu, chunk0, chunk_seq, desc, recs, Sblk, dSblk, Dblk, dDblk, dy, pdw, pdtb, pAlog, pstage, total;
 };
 
 BwdLayout make_bwd_layout(const kda_config_t* cfg, int64_t N, int64_t max_chunks, int64_t total_T) {
@@ -190,6 +190,7 @@ BwdLayout make_bwd_layout(const kda_config_t* cfg, int64_t N, int64_t max_chunks
   L.pdw = take(static_cast<size_t>(mc) * 3 * H * D * 4 * 4);
   L.pdtb = take(static_cast<size_t>(blocks) * H * D * 4);
   L.pAlog = take(static_cast<size_t>(blocks) * H * 4);
+  L.pstage = take(static_cast<size_t>(kda::bwd_reduce_parts()) * (H * D * (3 * 4 + 1) + H) * 4);
   L.total = off;
   return L;
 }
@@ -249,7 +250,7 @@ kda_status_t kda_varlen_backward(const kda_config_t* cfg, int32_t N, int32_t tot
                     reinterpret_cast<float*>(ws + L.dSblk), reinterpret_cast<float*>(ws + L.Dblk),
                     reinterpret_cast<float*>(ws + L.dDblk), reinterpret_cast<float*>(ws + L.dy),
                     reinterpret_cast<float*>(ws + L.pdw), reinterpret_cast<float*>(ws + L.pdtb),
-                    reinterpret_cast<float*>(ws + L.pAlog)};
+                    reinterpret_cast<float*>(ws + L.pAlog), reinterpret_cast<float*>(ws + L.pstage)};
   const int imc = static_cast<int>(mc);
   s = stage(cfg, KDA_STAGE_CHUNK_TABLE, st, [&] {
     return kda::launch_build_chunks(cu_seqlens, N, 0, cu_ws, chunk0, chunk_seq, desc, imc, p.H, p.D, st);

@@ -203,7 +203,10 @@ struct BackwardWS {
   float* pdw;                // per-chunk conv-weight partials  [chunks][3][H*D][4]
   float* pdtb;               // per-block dt_bias partials      [blocks][H][D]
   float* pAlog;              // per-block A_log partials        [blocks][H]
+  float* pstage;             // first-pass sums of the partials [bwd_reduce_parts()][3*H*D*4 + H*D + H]
 };
+
+int bwd_reduce_parts();
 
 size_t bwd_record_bytes(int D);
 hipError_t launch_backward(const Params& p, const ChunkTable& t, const PrefillIO& io, const BackwardIO& g,
