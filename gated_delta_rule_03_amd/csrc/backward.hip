@@ -333,40 +333,54 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
 }
 
 // ---------------------------------------------------------------- the two scans
-// One wave per (sequence, head, 16-column value tile).  The state slice (or
-// its adjoint) S[0..D) x [j0, j0 + 16) lives in fp32 matrix-core
-// accumulators: row tile t (rows 16t .. 16t + 15) in acc[t], lane l holding
-// rows 16t + 4 (l / 16) + i (i < 4) of column j0 + l % 16.  A product that
-// contracts over the state's rows then takes its B operand straight from the
-// accumulators: step (t, i) of v_mfma_f32_16x16x4_f32 covers rows
-// 16t + 4g + i for the four lane groups g.  A sequence's blocks are
-// consecutive (block index = 4 x its first chunk + its position), and each
-// block's operands are loaded into registers one block ahead.
-// Workgroups are numbered so that all tiles of one (sequence, head) share an
-// XCD (workgroups are dealt to the 8 XCDs round robin) and read its records
-// through one L2.
+// A workgroup per (sequence, head, TW consecutive 16-column value tiles), a
+// wave per tile.  The state slice (or its adjoint) S[0..D) x [j0, j0 + 16) of
+// a wave lives in fp32 matrix-core accumulators: row tile t (rows 16t ..
+// 16t + 15) in acc[t], lane l holding rows 16t + 4 (l / 16) + i (i < 4) of
+// column j0 + l % 16.  A product that contracts over the state's rows then
+// takes its B operand straight from the accumulators: step (t, i) of
+// v_mfma_f32_16x16x4_f32 covers rows 16t + 4g + i for the four lane groups g.
+// A sequence's blocks are consecutive (block index = 4 x its first chunk +
+// its position).  The block operands the waves share (W, K~, Q+, Aqk,
+// e^{G_C}) are loaded once per workgroup, into registers two blocks ahead
+// (two alternating sets), and moved to shared memory at the step that uses
+// them.  Workgroups are numbered so that those of one (sequence, head) share
+// an XCD (workgroups are dealt to the 8 XCDs round robin) and read its
+// records through one L2.
 constexpr int kScanTile = 16;
 
-__device__ __forceinline__ bool scan_coords(int nh_total, int ntile, int& nh, int& tile) {
+template <int D>
+constexpr int scan_waves() { return D / kScanTile >= 4 ? 4 : D / kScanTile; }
+
+__device__ __forceinline__ bool scan_coords(int nh_total, int ngroups, int& nh, int& grp) {
   const int bid = static_cast<int>(blockIdx.x);
   const int lo = bid % 8, rest = bid / 8;
-  tile = rest % ntile;
-  nh = (rest / ntile) * 8 + lo;
+  grp = rest % ngroups;
+  nh = (rest / ngroups) * 8 + lo;
   return nh < nh_total;
 }
 
 template <int D>
-__global__ __launch_bounds__(kWave) void bwd_state_scan_kernel(Params p, ChunkTable t, const float* S_init,
-                                                                const uint8_t* recs, float* Sblk, float* Dblk) {
+__global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_state_scan_kernel(Params p, ChunkTable t,
+                                                                                const float* S_init,
+                                                                                const uint8_t* recs, float* Sblk,
+                                                                                float* Dblk) {
   constexpr BwdRecord R = bwd_record(D);
-  constexpr int NT16 = D / 16;              // row tiles of the state
-  constexpr int PF = kBlk * D / kWave;      // W / K~ elements per lane
-  __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], seG[D];
-  __shared__ float sDel[kBlk][kScanTile + 1];
-  int nh, tile;
-  if (!scan_coords(t.N * p.H, D / kScanTile, nh, tile)) return;
+  constexpr int TW = scan_waves<D>();
+  constexpr int NTH = kWave * TW;
+  constexpr int NT16 = D / 16;               // row tiles of the state
+  constexpr int CW = kScanTile * TW;         // value columns of the workgroup
+  constexpr int PF = kBlk * D / NTH;         // W / K~ elements per thread
+  constexpr int PU = kBlk * CW / NTH;        // U elements per thread
+  constexpr int PE = (D + NTH - 1) / NTH;    // e^{G_C} elements per thread
+  struct Ops { float w[PF], k[PF], u[PU], e[PE]; };
+  __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], seG[D], sU[kBlk][CW + 1];
+  __shared__ float sDel[TW][kBlk][kScanTile + 1];
+  int nh, grp;
+  if (!scan_coords(t.N * p.H, D / CW, nh, grp)) return;
   const int h = nh % p.H, n = nh / p.H;
-  const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16, j0 = tile * kScanTile;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g = lane / 16;
+  const int c0 = grp * CW, jw = wave * kScanTile, j0 = c0 + jw;
   const size_t SZ = static_cast<size_t>(D) * D;
   f32x4 acc[NT16];
 #pragma unroll
@@ -380,45 +394,47 @@ __global__ __launch_bounds__(kWave) void bwd_state_scan_kernel(Params p, ChunkTa
   const int L = t.cu[n + 1] - t.cu[n];
   const int nb = (L + kBlk - 1) / kBlk;
   const int blk0 = t.chunk0[n] * kBlocksPerChunk;
-  float pW[PF], pK[PF], pU[4], pE[(D + kWave - 1) / kWave];
-  auto fetch = [&](int blk) {
-    const uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
+  auto fetch = [&](Ops& o, int jb) {
+    const uint8_t* rec = recs + (static_cast<size_t>(blk0 + jb) * p.H + h) * R.bytes;
     const float* gW = reinterpret_cast<const float*>(rec + R.W);
     const float* gU = reinterpret_cast<const float*>(rec + R.U);
     const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
     const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
 #pragma unroll
-    for (int m = 0; m < PF; ++m) { pW[m] = gW[lane + m * kWave]; pK[m] = gKt[lane + m * kWave]; }
+    for (int m = 0; m < PF; ++m) { o.w[m] = gW[tid + m * NTH]; o.k[m] = gKt[tid + m * NTH]; }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pU[i] = gU[(4 * g + i) * D + j0 + l16];
-#pragma unroll
-    for (int m = 0; m < (D + kWave - 1) / kWave; ++m)
-      if (lane + m * kWave < D) pE[m] = geG[lane + m * kWave];
-  };
-  if (nb > 0) fetch(blk0);
-  for (int jb = 0; jb < nb; ++jb) {
-    const int blk = blk0 + jb;
-    const size_t bh = static_cast<size_t>(blk) * p.H + h;
-#pragma unroll
-    for (int m = 0; m < PF; ++m) {
-      const int e = lane + m * kWave;
-      sW[e / D][e % D] = pW[m];
-      sKt[e / D][e % D] = pK[m];
+    for (int m = 0; m < PU; ++m) {
+      const int e = tid + m * NTH;
+      o.u[m] = gU[(e / CW) * D + c0 + e % CW];
     }
 #pragma unroll
-    for (int m = 0; m < (D + kWave - 1) / kWave; ++m)
-      if (lane + m * kWave < D) seG[lane + m * kWave] = pE[m];
-    float U[4];
+    for (int m = 0; m < PE; ++m)
+      if (tid + m * NTH < D) o.e[m] = geG[tid + m * NTH];
+  };
+  auto to_shared = [&](const Ops& o) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) U[i] = pU[i];
-    // the state at the block's start
+    for (int m = 0; m < PF; ++m) {
+      const int e = tid + m * NTH;
+      sW[e / D][e % D] = o.w[m];
+      sKt[e / D][e % D] = o.k[m];
+    }
+#pragma unroll
+    for (int m = 0; m < PU; ++m) {
+      const int e = tid + m * NTH;
+      sU[e / CW][e % CW] = o.u[m];
+    }
+#pragma unroll
+    for (int m = 0; m < PE; ++m)
+      if (tid + m * NTH < D) seG[tid + m * NTH] = o.e[m];
+  };
+  // one block: its operands are in shared memory; Sblk <- S, Delta, S update
+  auto step = [&](int jb) {
+    const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
 #pragma unroll
     for (int t16 = 0; t16 < NT16; ++t16)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         Sblk[bh * SZ + static_cast<size_t>(16 * t16 + 4 * g + i) * D + j0 + l16] = acc[t16][i];
-    __syncthreads();
-    if (jb + 1 < nb) fetch(blk + 1);
     // Delta = U - W S  (contracting the state's rows; four accumulators by i)
     f32x4 d4[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -428,12 +444,12 @@ __global__ __launch_bounds__(kWave) void bwd_state_scan_kernel(Params p, ChunkTa
         d4[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(sW[l16][16 * t16 + 4 * g + i], acc[t16][i], d4[i], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float del = U[i] - ((d4[0][i] + d4[1][i]) + (d4[2][i] + d4[3][i]));
-      sDel[4 * g + i][l16] = del;
+      const float del = sU[4 * g + i][jw + l16] - ((d4[0][i] + d4[1][i]) + (d4[2][i] + d4[3][i]));
+      sDel[wave][4 * g + i][l16] = del;
       Dblk[bh * kBlk * D + static_cast<size_t>(4 * g + i) * D + j0 + l16] = del;
     }
-    __syncthreads();
-    // S <- e^{G_C} S + K~^T Delta  (K = the block's 16 rows)
+    // S <- e^{G_C} S + K~^T Delta  (K = the block's 16 rows; sDel is this
+    // wave's own: the wave's LDS operations complete in order)
 #pragma unroll
     for (int t16 = 0; t16 < NT16; ++t16) {
 #pragma unroll
@@ -441,30 +457,56 @@ __global__ __launch_bounds__(kWave) void bwd_state_scan_kernel(Params p, ChunkTa
 #pragma unroll
       for (int st = 0; st < kBlk / 4; ++st) {
         const int k = 4 * st + g;
-        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKt[k][16 * t16 + l16], sDel[k][l16], acc[t16], 0, 0, 0);
+        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(sKt[k][16 * t16 + l16], sDel[wave][k][l16], acc[t16], 0, 0,
+                                                        0);
       }
     }
+  };
+  Ops A, B;
+  if (nb > 0) fetch(A, 0);
+  if (nb > 1) fetch(B, 1);
+  for (int jb = 0; jb < nb; jb += 2) {
+    to_shared(A);
     __syncthreads();
+    if (jb + 2 < nb) fetch(A, jb + 2);
+    step(jb);
+    __syncthreads();
+    if (jb + 1 < nb) {
+      to_shared(B);
+      __syncthreads();
+      if (jb + 3 < nb) fetch(B, jb + 3);
+      step(jb + 1);
+      __syncthreads();
+    }
   }
 }
 
 // The state scan's layout, blocks in reverse:
 //   dDelta = Aqk^T dO + K~ dS_C,   dS0 = Q+^T dO + e^{G_C} dS_C - W^T dDelta
 template <int D, bool DO_BF16>
-__global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, ChunkTable t, const uint8_t* recs,
-                                                                  const void* dO, const float* dS_final,
-                                                                  float* dSblk, float* dDblk, float* dS_init,
-                                                                  float* dconv) {
+__global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_adjoint_scan_kernel(Params p, ChunkTable t,
+                                                                                  const uint8_t* recs,
+                                                                                  const void* dO,
+                                                                                  const float* dS_final,
+                                                                                  float* dSblk, float* dDblk,
+                                                                                  float* dS_init, float* dconv) {
   constexpr BwdRecord R = bwd_record(D);
+  constexpr int TW = scan_waves<D>();
+  constexpr int NTH = kWave * TW;
   constexpr int NT16 = D / 16;
-  constexpr int PF = kBlk * D / kWave;
-  constexpr int PE = (D + kWave - 1) / kWave;
+  constexpr int CW = kScanTile * TW;
+  constexpr int PF = kBlk * D / NTH;
+  constexpr int PA = (kBlk * kBlk + NTH - 1) / NTH;   // Aqk elements per thread
+  constexpr int PE = (D + NTH - 1) / NTH;
+  struct Ops { float w[PF], k[PF], q[PF], a[PA], o[4], e[PE]; };
   __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], sQp[kBlk][D + 1], seG[D];
-  __shared__ float sAqk[kBlk][kBlk + 1], sdO[kBlk][kScanTile + 1], sdDel[kBlk][kScanTile + 1];
-  int nh, tile;
-  if (!scan_coords(t.N * p.H, D / kScanTile, nh, tile)) return;
+  __shared__ float sAqk[kBlk][kBlk + 1];
+  __shared__ float sdO[TW][kBlk][kScanTile + 1], sdDel[TW][kBlk][kScanTile + 1];
+  int nh, grp;
+  if (!scan_coords(t.N * p.H, D / CW, nh, grp)) return;
   const int h = nh % p.H, n = nh / p.H;
-  const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16, j0 = tile * kScanTile;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g = lane / 16;
+  const int c0 = grp * CW, j0 = c0 + wave * kScanTile;
   const size_t SZ = static_cast<size_t>(D) * D;
   const size_t HD = static_cast<size_t>(p.H) * D;
   f32x4 acc[NT16];
@@ -480,11 +522,9 @@ __global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, Chunk
   const int nb = (L + kBlk - 1) / kBlk;
   const int blk0 = t.chunk0[n] * kBlocksPerChunk;
   const int64_t seq0 = t.cu[n];
-  float pW[PF], pK[PF], pQ[PF], pA[4], pO[4], pE[PE];
-  auto fetch = [&](int jb) {
-    const int blk = blk0 + jb;
+  auto fetch = [&](Ops& o, int jb) {
     const int ntok = min(kBlk, L - jb * kBlk);
-    const uint8_t* rec = recs + (static_cast<size_t>(blk) * p.H + h) * R.bytes;
+    const uint8_t* rec = recs + (static_cast<size_t>(blk0 + jb) * p.H + h) * R.bytes;
     const float* gW = reinterpret_cast<const float*>(rec + R.W);
     const float* gKt = reinterpret_cast<const float*>(rec + R.Kt);
     const float* gQp = reinterpret_cast<const float*>(rec + R.Qp);
@@ -492,47 +532,52 @@ __global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, Chunk
     const float* geG = reinterpret_cast<const float*>(rec + R.eGC);
 #pragma unroll
     for (int m = 0; m < PF; ++m) {
-      pW[m] = gW[lane + m * kWave];
-      pK[m] = gKt[lane + m * kWave];
-      pQ[m] = gQp[lane + m * kWave];
+      o.w[m] = gW[tid + m * NTH];
+      o.k[m] = gKt[tid + m * NTH];
+      o.q[m] = gQp[tid + m * NTH];
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      pA[m] = gAqk[lane + m * kWave];
+    for (int m = 0; m < PA; ++m)
+      if (tid + m * NTH < kBlk * kBlk) o.a[m] = gAqk[tid + m * NTH];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {      // this wave's 16 x 16 tile of dO
       const int q = (lane + m * kWave) / kScanTile, jj = (lane + m * kWave) % kScanTile;
-      pO[m] = q < ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + q) * p.H + h) * D + j0 + jj) : 0.f;
+      o.o[m] = q < ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + q) * p.H + h) * D + j0 + jj) : 0.f;
     }
 #pragma unroll
     for (int m = 0; m < PE; ++m)
-      if (lane + m * kWave < D) pE[m] = geG[lane + m * kWave];
+      if (tid + m * NTH < D) o.e[m] = geG[tid + m * NTH];
   };
-  if (nb > 0) fetch(nb - 1);
-  for (int jb = nb - 1; jb >= 0; --jb) {
-    const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
+  auto to_shared = [&](const Ops& o) {
 #pragma unroll
     for (int m = 0; m < PF; ++m) {
-      const int e = lane + m * kWave;
-      sW[e / D][e % D] = pW[m];
-      sKt[e / D][e % D] = pK[m];
-      sQp[e / D][e % D] = pQ[m];
+      const int e = tid + m * NTH;
+      sW[e / D][e % D] = o.w[m];
+      sKt[e / D][e % D] = o.k[m];
+      sQp[e / D][e % D] = o.q[m];
+    }
+#pragma unroll
+    for (int m = 0; m < PA; ++m) {
+      const int e = tid + m * NTH;
+      if (e < kBlk * kBlk) sAqk[e / kBlk][e % kBlk] = o.a[m];
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = lane + m * kWave;
-      sAqk[e / kBlk][e % kBlk] = pA[m];
-      sdO[e / kScanTile][e % kScanTile] = pO[m];
+      sdO[wave][e / kScanTile][e % kScanTile] = o.o[m];
     }
 #pragma unroll
     for (int m = 0; m < PE; ++m)
-      if (lane + m * kWave < D) seG[lane + m * kWave] = pE[m];
+      if (tid + m * NTH < D) seG[tid + m * NTH] = o.e[m];
+  };
+  auto step = [&](int jb) {
+    const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
     // the adjoint of the block's end state
 #pragma unroll
     for (int t16 = 0; t16 < NT16; ++t16)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         dSblk[bh * SZ + static_cast<size_t>(16 * t16 + 4 * g + i) * D + j0 + l16] = acc[t16][i];
-    __syncthreads();
-    if (jb > 0) fetch(jb - 1);
     // dDelta = K~ dS_C (contracting the state's rows) + Aqk^T dO
     f32x4 d4[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -543,16 +588,15 @@ __global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, Chunk
 #pragma unroll
     for (int st = 0; st < kBlk / 4; ++st) {
       const int k = 4 * st + g;
-      d4[st] = __builtin_amdgcn_mfma_f32_16x16x4f32(sAqk[k][l16], sdO[k][l16], d4[st], 0, 0, 0);
+      d4[st] = __builtin_amdgcn_mfma_f32_16x16x4f32(sAqk[k][l16], sdO[wave][k][l16], d4[st], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float dd = (d4[0][i] + d4[1][i]) + (d4[2][i] + d4[3][i]);
-      sdDel[4 * g + i][l16] = dd;
+      sdDel[wave][4 * g + i][l16] = dd;
       dDblk[bh * kBlk * D + static_cast<size_t>(4 * g + i) * D + j0 + l16] = dd;
     }
-    __syncthreads();
-    // dS0 = e^{G_C} dS_C + Q+^T dO - W^T dDelta
+    // dS0 = e^{G_C} dS_C + Q+^T dO - W^T dDelta  (sdDel is this wave's own)
 #pragma unroll
     for (int t16 = 0; t16 < NT16; ++t16) {
 #pragma unroll
@@ -560,11 +604,29 @@ __global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, Chunk
 #pragma unroll
       for (int st = 0; st < kBlk / 4; ++st) {
         const int k = 4 * st + g;
-        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQp[k][16 * t16 + l16], sdO[k][l16], acc[t16], 0, 0, 0);
-        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(-sW[k][16 * t16 + l16], sdDel[k][l16], acc[t16], 0, 0, 0);
+        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQp[k][16 * t16 + l16], sdO[wave][k][l16], acc[t16], 0, 0, 0);
+        acc[t16] = __builtin_amdgcn_mfma_f32_16x16x4f32(-sW[k][16 * t16 + l16], sdDel[wave][k][l16], acc[t16], 0, 0,
+                                                        0);
       }
     }
+  };
+  Ops A, B;
+  if (nb > 0) fetch(A, nb - 1);
+  if (nb > 1) fetch(B, nb - 2);
+  for (int i = 0; i < nb; i += 2) {
+    const int jb = nb - 1 - i;
+    to_shared(A);
     __syncthreads();
+    if (jb - 2 >= 0) fetch(A, jb - 2);
+    step(jb);
+    __syncthreads();
+    if (jb - 1 >= 0) {
+      to_shared(B);
+      __syncthreads();
+      if (jb - 3 >= 0) fetch(B, jb - 3);
+      step(jb - 1);
+      __syncthreads();
+    }
   }
   if (dS_init) {
 #pragma unroll
@@ -576,8 +638,8 @@ __global__ __launch_bounds__(kWave) void bwd_adjoint_scan_kernel(Params p, Chunk
       }
   }
   // an empty sequence passes its conv history through: no gradient reaches it
-  if (dconv && tile == 0 && nb == 0) {
-    for (int e = lane; e < 3 * D; e += kWave) {
+  if (dconv && grp == 0 && nb == 0) {
+    for (int e = tid; e < 3 * D; e += NTH) {
       const int role = e / D, ch = e % D;
       for (int m = 0; m < 3; ++m)
         dconv[(static_cast<size_t>(n) * 3 + m) * 3 * HD + role * HD + static_cast<size_t>(h) * D + ch] = 0.f;
@@ -1141,11 +1203,12 @@ hipError_t launch_backward_d(const Params& p, const ChunkTable& t, const Prefill
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned nh8 = (static_cast<unsigned>(N) * p.H + 7) / 8 * 8;   // (sequence, head) pairs, padded to 8 XCDs
-  const unsigned nscan = nh8 * (D / kScanTile);
-  bwd_state_scan_kernel<D><<<nscan, kWave, 0, st>>>(p, t, io.S0, ws.recs, ws.Sblk, ws.Dblk);
+  constexpr int TW = scan_waves<D>();
+  const unsigned nscan = nh8 * (D / (kScanTile * TW));
+  bwd_state_scan_kernel<D><<<nscan, kWave * TW, 0, st>>>(p, t, io.S0, ws.recs, ws.Sblk, ws.Dblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_adjoint_scan_kernel<D, DO_BF16><<<nscan, kWave, 0, st>>>(p, t, ws.recs, g.dO, g.dS_final, ws.dSblk, ws.dDblk,
-                                                               g.dS_init, g.dconv);
+  bwd_adjoint_scan_kernel<D, DO_BF16><<<nscan, kWave * TW, 0, st>>>(p, t, ws.recs, g.dO, g.dS_final, ws.dSblk,
+                                                                    ws.dDblk, g.dS_init, g.dconv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_block_grad_kernel<D, IO_BF16, DO_BF16><<<nblk, grad_threads<D>(), 0, st>>>(p, t, io, ws.recs, ws.Sblk, ws.dSblk, ws.Dblk,
                                                                    ws.dDblk, g.dO, ws.dy, g.dalpha, g.db, ws.pdtb,

@@ -24,8 +24,9 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // Eight waves per (sequence, head): a 64 KB in-place tile streams measurably
 // faster with 512 threads than with 256 (more bytes in flight per workgroup).
 constexpr int kDecodeThreads = 512;
-// Tokens whose inputs the multi-token decode stages at once.
-constexpr int kMultiGroup = 8;
+// Threads of the multi-token decode, and the tokens whose inputs it stages at once.
+constexpr int kMultiThreads = 256;
+constexpr int kMultiGroup = 4;
 
 // With GATED the output row goes through the layer's epilogue before it is
 // stored (y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), AliceAI page,
@@ -197,27 +198,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
 
 // K tokens per sequence (multi-token decode, speculative verify and commit),
 // the state and conv history found in pools through a slot per sequence.
-// The state is read once; the per-token steps are those of decode_kernel,
-// with the conv window of each channel kept in its thread's registers.  The
-// state after the first `commit` tokens goes back to the pool (none for 0),
-// and so does the conv history after them; every token's output is written.
-// GATED: every token's output row goes through the epilogue, as in
+// The state is read once; the per-token steps are those of decode_kernel.
+// The state after the first `commit` tokens goes back to the pool (none for
+// 0), and so does the conv history after them; every token's output is
+// written.  GATED: every token's output row goes through the epilogue, as in
 // decode_kernel.
+// Four waves per (sequence, head), each thread holding 16 state rows of one
+// float4 column (at dk = 128): the state is most of a thread's registers, and
+// three states fit on a compute unit at once (eight-wave workgroups fit two,
+// their other registers costing as much as the state).  Tokens go in groups:
+// the conv, SiLU and norms of a group's tokens do not depend on the state and
+// are computed for the whole group first, so each token's serial part is the
+// pass over the state, one reduction and the update (two barriers).  The
+// conv windows of the 3 dk channels live in shared memory.
 template <int D, bool IO_BF16, bool OUT_BF16, bool GATED>
-__global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
-  constexpr int NT = kDecodeThreads;
+__global__ __launch_bounds__(kMultiThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
+  constexpr int NT = kMultiThreads;
+  constexpr int NW = NT / kWave;
   constexpr int C4 = D / 4;
   constexpr int RPP = NT / C4;
   constexpr int RPT = (D + RPP - 1) / RPP;
   constexpr int KG = kMultiGroup;
-  static_assert(3 * D <= NT && D <= NT, "one conv channel and one gate channel per thread");
-  __shared__ float x_s[KG][3 * D];   // raw q | k | v of a group of tokens
+  constexpr int NC = 3 * D;                        // conv channels
+  constexpr int CPT = (NC + NT - 1) / NT;          // ... per thread
+  static_assert(D <= NT, "one gate channel per thread");
+  __shared__ float u_s[KG][NC];      // ... after conv + SiLU
   __shared__ float eg_s[KG][D];      // exp(g) of the group's tokens
   __shared__ float b_s[KG];          // beta of the group's tokens
-  __shared__ float u_s[3 * D];
+  __shared__ float nrm_s[KG][3];     // |u_q|^2, |u_k|^2, u_q . u_k
+  __shared__ float win_s[3][NC];     // each channel's last three raw inputs
+  __shared__ float kwin_s[3][NC];    // ... after the committed tokens
   __shared__ float red[2][RPP][D];
   __shared__ float d_s[D];
-  __shared__ float scal[4];
   constexpr int OW = (D + kWave - 1) / kWave;
   __shared__ float osum[OW];
 
@@ -240,47 +253,84 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
     if (r < D) Sv[rr] = __builtin_nontemporal_load(&Sp[static_cast<size_t>(r) * C4 + col4]);
   }
 
-  // this thread's conv channel (q, k or v) and its window of raw inputs
-  const bool conv_lane = tid < 3 * D;
-  const int grp = tid / D, ci = tid % D;
-  const size_t ch = static_cast<size_t>(grp) * HD + static_cast<size_t>(h) * D + ci;
-  const size_t cb = static_cast<size_t>(slot) * 3 * Ctot + ch;
-  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, h0 = 0.f, h1 = 0.f, h2 = 0.f;
-  const void* xsrc = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
-  if (conv_lane) {
-    const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
-    if (!(flags & KDA_FLAG_SKIP_CONV)) {
-      const size_t wi = (static_cast<size_t>(h) * D + ci) * 4;
-      w0 = ld<IO_BF16>(w, wi); w1 = ld<IO_BF16>(w, wi + 1); w2 = ld<IO_BF16>(w, wi + 2); w3 = ld<IO_BF16>(w, wi + 3);
+  // the conv taps of this thread's channels and the pooled history
+  float wt[CPT][4];
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int c = tid + m * NT;
+    wt[m][0] = wt[m][1] = wt[m][2] = wt[m][3] = 0.f;
+    if (c < NC) {
+      const int grp = c / D, ci = c % D;
+      const size_t ch = static_cast<size_t>(grp) * HD + static_cast<size_t>(h) * D + ci;
+      const size_t cb = static_cast<size_t>(slot) * 3 * Ctot + ch;
+      if (!(flags & KDA_FLAG_SKIP_CONV)) {
+        const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
+        const size_t wi = (static_cast<size_t>(h) * D + ci) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[m][j] = ld<IO_BF16>(w, wi + j);
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const float hv = ld<IO_BF16>(io.conv_pool, cb + j * Ctot);
+        win_s[j][c] = hv;
+        kwin_s[j][c] = hv;
+      }
     }
-    h0 = ld<IO_BF16>(io.conv_pool, cb);
-    h1 = ld<IO_BF16>(io.conv_pool, cb + Ctot);
-    h2 = ld<IO_BF16>(io.conv_pool, cb + 2 * Ctot);
   }
-  float k0 = h0, k1 = h1, k2 = h2;   // the window after the committed tokens
   const float a_exp = expf(p.A_log[h]);
   const float dtb = tid < D ? p.dt_bias[h * D + tid] : 0.f;
   float onw = 0.f;
   if constexpr (GATED) onw = tid < D ? io.onw[tid] : 0.f;
+  const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
 
   for (int t0 = 0; t0 < K; t0 += KG) {
     // the group's raw inputs, gates and betas, all loads issued together (the
-    // first group's right behind the state loads); the token loop below then
-    // touches global memory only to store outputs
+    // first group's right behind the state loads)
     const int kg = min(KG, K - t0);
     {
-      float xr[KG], ar[KG];
+      float xr[KG][CPT], ar[KG];
       float br = 0.f;
 #pragma unroll
       for (int j = 0; j < KG; ++j) {
         const size_t tok = static_cast<size_t>(n) * K + t0 + min(j, kg - 1);
-        xr[j] = conv_lane ? ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci) : 0.f;
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) {
+          const int c = tid + m * NT;
+          const int grp = c / D, ci = c % D;
+          const void* xsrc = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
+          xr[j][m] = c < NC ? ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci) : 0.f;
+        }
         ar[j] = tid < D ? ld<IO_BF16>(io.alpha, tok * HD + static_cast<size_t>(h) * D + tid) : 0.f;
       }
       if (tid < kg) br = ld<IO_BF16>(io.b, (static_cast<size_t>(n) * K + t0 + tid) * H + h);
+      // conv + SiLU of the group's tokens, channel by channel (the window in
+      // registers for the group, back in shared memory after it)
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int c = tid + m * NT;
+        if (c < NC) {
+          float h0 = win_s[0][c], h1 = win_s[1][c], h2 = win_s[2][c];
+#pragma unroll
+          for (int j = 0; j < KG; ++j) {
+            if (j < kg) {
+              const float xt = xr[j][m];
+              u_s[j][c] = (flags & KDA_FLAG_SKIP_CONV)
+                              ? xt : siluf_(wt[m][0] * h0 + wt[m][1] * h1 + wt[m][2] * h2 + wt[m][3] * xt);
+              h0 = h1; h1 = h2; h2 = xt;
+              if (t0 + j + 1 == commit) {
+                kwin_s[0][c] = h0;
+                kwin_s[1][c] = h1;
+                kwin_s[2][c] = h2;
+              }
+            }
+          }
+          win_s[0][c] = h0;
+          win_s[1][c] = h1;
+          win_s[2][c] = h2;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < KG; ++j) {
-        if (conv_lane) x_s[j][tid] = xr[j];
         if (tid < D) {
           const float g = (flags & KDA_FLAG_RAW_GATE) ? ar[j] : gate_value(ar[j], dtb, a_exp, p.lower_bound);
           eg_s[j][tid] = expf(g);
@@ -293,35 +343,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
       }
     }
     __syncthreads();
+    // |u_q|^2, |u_k|^2 and u_q . u_k of every token of the group, a wave per task
+    {
+      const int wv = tid / kWave, lane = tid % kWave;
+      for (int task = wv; task < 3 * kg; task += NW) {
+        const int j = task / 3, ty = task % 3;
+        float sum = 0.0f;
+        for (int i = lane; i < D; i += kWave) {
+          const float a = u_s[j][(ty == 1 ? D : 0) + i];
+          const float b2 = u_s[j][(ty == 0 ? 0 : D) + i];
+          sum += a * b2;
+        }
+        sum = group_sum<kWave>(sum);
+        if (lane == 0) nrm_s[j][ty] = sum;
+      }
+    }
+    __syncthreads();
 
     for (int j = 0; j < kg; ++j) {
       const int t = t0 + j;
       const size_t tok = static_cast<size_t>(n) * K + t;
-      if (conv_lane) {
-        const float xt = x_s[j][tid];
-        u_s[tid] = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h0 + w1 * h1 + w2 * h2 + w3 * xt);
-        h0 = h1; h1 = h2; h2 = xt;
-        if (t + 1 == commit) { k0 = h0; k1 = h1; k2 = h2; }
-      }
-      __syncthreads();
-      {
-        const int wv = tid / kWave, lane = tid % kWave;
-        if (wv < 3) {
-          float sum = 0.0f;
-          for (int i = lane; i < D; i += kWave) {
-            const float a = u_s[(wv == 1 ? D : 0) + i];
-            const float b2 = u_s[(wv == 0 ? 0 : D) + i];
-            sum += a * b2;
-          }
-          sum = group_sum<kWave>(sum);
-          if (lane == 0) scal[wv == 2 ? 3 : wv] = sum;
-        }
-      }
-      __syncthreads();
-      const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
-      const float iq = norm ? 1.0f / sqrtf(scal[0] + p.eps) : 1.0f;
-      const float ik = norm ? 1.0f / sqrtf(scal[1] + p.eps) : 1.0f;
-      const float qs = iq * p.scale, ks = ik, beta = b_s[j], qk = scal[3] * iq * ik * p.scale;
+      const float iq = norm ? 1.0f / sqrtf(nrm_s[j][0] + p.eps) : 1.0f;
+      const float ik = norm ? 1.0f / sqrtf(nrm_s[j][1] + p.eps) : 1.0f;
+      const float qs = iq * p.scale, ks = ik, beta = b_s[j], qk = nrm_s[j][2] * iq * ik * p.scale;
 
       float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -330,7 +374,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
         if (r < D) {
           const float e = eg_s[j][r];
           Sv[rr].x *= e; Sv[rr].y *= e; Sv[rr].z *= e; Sv[rr].w *= e;
-          const float kr = u_s[D + r] * ks, qr = u_s[r] * qs;
+          const float kr = u_s[j][D + r] * ks, qr = u_s[j][r] * qs;
           pk[0] += kr * Sv[rr].x; pk[1] += kr * Sv[rr].y; pk[2] += kr * Sv[rr].z; pk[3] += kr * Sv[rr].w;
           pq[0] += qr * Sv[rr].x; pq[1] += qr * Sv[rr].y; pq[2] += qr * Sv[rr].z; pq[3] += qr * Sv[rr].w;
         }
@@ -345,14 +389,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
       if constexpr (GATED) {
         if (tid < D) gsig = sigmoidf_(ld<IO_BF16>(io.gate, tok * HD + static_cast<size_t>(h) * D + tid));
       }
-      __syncthreads();
+      __syncthreads();   // red is complete; d_s and osum are free (read before the last barrier)
       float o_c = 0.f;
       if (tid < D) {
         const int c = tid;
         float pp = 0.f, rq = 0.f;
-#pragma unroll 8
+#pragma unroll
         for (int g2 = 0; g2 < RPP; ++g2) { pp += red[0][g2][c]; rq += red[1][g2][c]; }
-        const float delta = beta * (u_s[2 * D + c] - pp);
+        const float delta = beta * (u_s[j][2 * D + c] - pp);
         d_s[c] = delta;
         o_c = rq + qk * delta;
         if constexpr (!GATED) st<OUT_BF16>(io.o, tok * HD + static_cast<size_t>(h) * D + c, o_c);
@@ -363,7 +407,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
           if ((tid % kWave) == 0) osum[tid / kWave] = ss;
         }
       }
-      __syncthreads();
+      __syncthreads();   // d_s and osum are complete; red is free
       if constexpr (GATED) {
         if (tid < D) {
           float ss = 0.f;
@@ -378,25 +422,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(Params p, 
       for (int rr = 0; rr < RPT; ++rr) {
         const int r = rg + rr * RPP;
         if (r < D) {
-          const float kr = u_s[D + r] * ks;
+          const float kr = u_s[j][D + r] * ks;
           Sv[rr].x += kr * d0; Sv[rr].y += kr * d1; Sv[rr].z += kr * d2; Sv[rr].w += kr * d3;
           if (t + 1 == commit) __builtin_nontemporal_store(Sv[rr], &Sp[static_cast<size_t>(r) * C4 + col4]);
         }
       }
-      __syncthreads();   // u_s, d_s, scal, osum are rewritten by the next token, x_s / eg_s by the next group
     }
+    __syncthreads();   // u_s, eg_s, b_s, nrm_s, d_s and osum are rewritten by the next group
   }
-  if (conv_lane && commit > 0) {
-    st<IO_BF16>(io.conv_pool, cb, k0);
-    st<IO_BF16>(io.conv_pool, cb + Ctot, k1);
-    st<IO_BF16>(io.conv_pool, cb + 2 * Ctot, k2);
+  if (commit > 0) {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int c = tid + m * NT;
+      if (c < NC) {
+        const int grp = c / D, ci = c % D;
+        const size_t cb = static_cast<size_t>(slot) * 3 * Ctot + static_cast<size_t>(grp) * HD +
+                          static_cast<size_t>(h) * D + ci;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) st<IO_BF16>(io.conv_pool, cb + j * Ctot, kwin_s[j][c]);
+      }
+    }
   }
 }
 
 template <int D, bool GATED>
 static hipError_t launch_decode_multi_g(const Params& p, const DecodeMultiIO& io, int N, int K, bool io_bf16,
                                         bool out_bf16, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kDecodeThreads);
+  const dim3 grid(static_cast<unsigned>(N) * p.H), block(kMultiThreads);
   if (io_bf16 && out_bf16) decode_multi_kernel<D, true, true, GATED><<<grid, block, 0, st>>>(p, io, K);
   else if (io_bf16) decode_multi_kernel<D, true, false, GATED><<<grid, block, 0, st>>>(p, io, K);
   else if (out_bf16) decode_multi_kernel<D, false, true, GATED><<<grid, block, 0, st>>>(p, io, K);
