@@ -104,6 +104,11 @@ struct BlockRaw {
   float bb;              // b of token tid (tid < kBlk)
 };
 
+// Every load goes out unconditionally and outside any branch, from an
+// address clamped into the sequence (the block's last token stands in for
+// rows past its end; a valid row for a missing history row, or for the
+// window of a gate task), and the zeros are selected after the loads: a load
+// under a condition is compiled as a branch that waits for it.
 template <int D, bool IO_BF16, int NT>
 __device__ __forceinline__ void block_load_raw(const Params& p, const PrefillIO& io, const BlockInfo& b, int h,
                                                BlockRaw<D, NT>& raw) {
@@ -111,35 +116,42 @@ __device__ __forceinline__ void block_load_raw(const Params& p, const PrefillIO&
   const size_t HD = static_cast<size_t>(p.H) * D;
   const size_t Ctot = 3 * HD;
   const int64_t seq0 = b.tok0 - b.tau0;   // packed index of the sequence's first token
+  const int last = b.ntok - 1;
+  const bool have_hist = io.conv_in != nullptr;
 #pragma unroll
   for (int m = 0; m < BlockRaw<D, NT>::kTasks; ++m) {
     const int task = tid + m * NT;
     const int role = task / D, ch = task % D;
+    const int rq = min(role, 2);                 // the q | k | v tensor the window reads
     const size_t col = static_cast<size_t>(h) * D + ch;
-    if (role < 3) {
-      const void* xin = role == 0 ? io.q : (role == 1 ? io.k : io.v);
-      const void* w = role == 0 ? p.wq : (role == 1 ? p.wk : p.wv);
+    const void* xin = rq == 0 ? io.q : (rq == 1 ? io.k : io.v);
+    const void* tok_src = role == 3 ? io.alpha : xin;     // the block's 16 rows: inputs or alpha
+    const void* w = rq == 0 ? p.wq : (rq == 1 ? p.wk : p.wv);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) raw.w[m][j] = ld<IO_BF16>(w, col * 4 + j);
+    for (int j = 0; j < 4; ++j) raw.w[m][j] = ld<IO_BF16>(w, col * 4 + j);
+    const float dtb = p.dt_bias[col];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int tau = b.tau0 - 3 + i;
-        float x = 0.f;
-        if (tau >= 0) x = ld<IO_BF16>(xin, static_cast<size_t>(seq0 + tau) * HD + col);
-        else if (io.conv_in) x = ld<IO_BF16>(io.conv_in, (static_cast<size_t>(b.seq) * 3 + (3 + tau)) * Ctot + role * HD + col);
-        raw.x[m][i] = x;
-      }
-#pragma unroll
-      for (int r = 0; r < kBlk; ++r)
-        raw.x[m][3 + r] = r < b.ntok ? ld<IO_BF16>(xin, static_cast<size_t>(b.tok0 + r) * HD + col) : 0.f;
-    } else if (role == 3) {
-      raw.w[m][0] = p.dt_bias[col];
-#pragma unroll
-      for (int r = 0; r < kBlk; ++r)
-        raw.x[m][3 + r] = r < b.ntok ? ld<IO_BF16>(io.alpha, static_cast<size_t>(b.tok0 + r) * HD + col) : 0.f;
+    for (int i = 0; i < 3; ++i) {
+      const int tau = b.tau0 - 3 + i;
+      const bool hist = tau < 0 && have_hist;
+      const void* src = hist ? io.conv_in : xin;
+      const size_t idx = hist ? (static_cast<size_t>(b.seq) * 3 + (3 + tau)) * Ctot + rq * HD + col
+                              : static_cast<size_t>(seq0 + max(tau, 0)) * HD + col;
+      raw.x[m][i] = ld<IO_BF16>(src, idx);
     }
+#pragma unroll
+    for (int r = 0; r < kBlk; ++r)
+      raw.x[m][3 + r] = ld<IO_BF16>(tok_src, static_cast<size_t>(b.tok0 + min(r, last)) * HD + col);
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (b.tau0 - 3 + i < 0 && !have_hist) raw.x[m][i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < kBlk; ++r)
+      if (r > last) raw.x[m][3 + r] = 0.f;
+    if (role == 3) raw.w[m][0] = dtb;
   }
-  raw.bb = tid < b.ntok ? ld<IO_BF16>(io.b, static_cast<size_t>(b.tok0 + tid) * p.H + h) : 0.f;
+  raw.bb = ld<IO_BF16>(io.b, static_cast<size_t>(b.tok0 + min(tid % kBlk, last)) * p.H + h);
+  if (tid >= b.ntok) raw.bb = 0.f;
 }
 
 // Conv + SiLU, L2 norm, gate and beta of one block's tokens for head h, from
@@ -540,10 +552,13 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_adjoint_scan_kern
     for (int m = 0; m < PA; ++m)
       if (tid + m * NTH < kBlk * kBlk) o.a[m] = gAqk[tid + m * NTH];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {      // this wave's 16 x 16 tile of dO
+    for (int m = 0; m < 4; ++m) {      // this wave's 16 x 16 tile of dO (rows past the end: zeros)
       const int q = (lane + m * kWave) / kScanTile, jj = (lane + m * kWave) % kScanTile;
-      o.o[m] = q < ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + q) * p.H + h) * D + j0 + jj) : 0.f;
+      o.o[m] = ld<DO_BF16>(dO, (static_cast<size_t>(seq0 + jb * kBlk + min(q, ntok - 1)) * p.H + h) * D + j0 + jj);
     }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if ((lane + m * kWave) / kScanTile >= ntok) o.o[m] = 0.f;
 #pragma unroll
     for (int m = 0; m < PE; ++m)
       if (tid + m * NTH < D) o.e[m] = geG[tid + m * NTH];
@@ -703,17 +718,20 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
       const int r = e / D, c = e % D;
       lDel[m] = Dblk[bh * kBlk * D + e];
       ldDel[m] = dDblk[bh * kBlk * D + e];
-      ldO[m] = r < b.ntok ? ld<DO_BF16>(dO, (static_cast<size_t>(b.tok0 + r) * p.H + h) * D + c) : 0.f;
+      ldO[m] = ld<DO_BF16>(dO, (static_cast<size_t>(b.tok0 + min(r, b.ntok - 1)) * p.H + h) * D + c);
       lW[m] = gW[e];
       lU[m] = gU[e];
     }
   }
-  const float lT = tid < kBlk * kBlk ? gT[tid] : 0.f;
+#pragma unroll
+  for (int m = 0; m < EL; ++m)
+    if ((tid + m * NT) / D >= b.ntok) ldO[m] = 0.f;
+  const float lT = gT[tid % (kBlk * kBlk)];
   // rows of S0 and dS_C for the matrix-core products: wave w owns output
   // channels 16w .. 16w + 15, lane l the contiguous state columns
   // KS (l / 16) .. KS (l / 16) + KS - 1 of row 16w + l % 16
   float sv[KS], dsv[KS], lgeG = 0.f;
-  if (wave < D / 16) {
+  if (D / 16 >= NT / kWave || wave < D / 16) {   // (every wave at d = 128: no branch)
     const int c = wave * 16 + l16;
     const float* s0row = Sblk + bh * D * D + static_cast<size_t>(c) * D + g4 * KS;
     const float* dsrow = dSblk + bh * D * D + static_cast<size_t>(c) * D + g4 * KS;
