@@ -26,7 +26,7 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int kDecodeThreads = 512;
 // Threads of the multi-token decode, and the tokens whose inputs it stages at once.
 constexpr int kMultiThreads = 256;
-constexpr int kMultiGroup = 4;
+constexpr int kMultiGroup = 2;
 
 // With GATED the output row goes through the layer's epilogue before it is
 // stored (y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), AliceAI page,
@@ -53,7 +53,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
   const size_t Ctot = static_cast<size_t>(3) * H * D;
   const uint32_t flags = p.flags;
 
-  // ---- the state tile is requested first: its latency overlaps the preprocess
+  // ---- the small inputs are requested first, all unconditionally (a load
+  // under a condition compiles to a branch that waits for it), then the state
+  // tile.  The memory counter drains in issue order, so waiting for the small
+  // inputs leaves the state's loads in flight behind the preprocess.
+  static_assert(3 * D <= NT, "one conv channel per thread");
+  const int cc = min(tid, 3 * D - 1);     // this thread's conv channel (threads past 3D: a valid one, unused)
+  const int grp = cc / D, ci = cc % D;
+  const size_t ch = static_cast<size_t>(grp) * H * D + static_cast<size_t>(h) * D + ci;
+  const void* xsrc = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
+  const void* wsrc = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
+  const size_t cb = static_cast<size_t>(n) * 3 * Ctot + ch;
+  const size_t wi = (static_cast<size_t>(h) * D + ci) * 4;
+  const float xt = ld<IO_BF16>(xsrc, static_cast<size_t>(n) * H * D + static_cast<size_t>(h) * D + ci);
+  const float h0 = ld<IO_BF16>(io.conv_state, cb);
+  const float h1 = ld<IO_BF16>(io.conv_state, cb + Ctot);
+  const float h2 = ld<IO_BF16>(io.conv_state, cb + 2 * Ctot);
+  const float w0 = ld<IO_BF16>(wsrc, wi), w1 = ld<IO_BF16>(wsrc, wi + 1);
+  const float w2 = ld<IO_BF16>(wsrc, wi + 2), w3 = ld<IO_BF16>(wsrc, wi + 3);
+  const int gi = tid % D;                 // this thread's gate / output channel
+  const float al = ld<IO_BF16>(io.alpha, (static_cast<size_t>(n) * H + h) * D + gi);
+  const float dtb = p.dt_bias[h * D + gi];
+  const float bb = ld<IO_BF16>(io.b, static_cast<size_t>(n) * H + h);
+  float graw = 0.f, onw = 0.f;            // epilogue operands of this thread's output column
+  if constexpr (GATED) {
+    graw = ld<IO_BF16>(io.gate, (static_cast<size_t>(n) * H + h) * D + gi);
+    onw = io.onw[gi];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const int col4 = tid % C4, rg = tid / C4;
   const size_t base = (static_cast<size_t>(n) * H + h) * D * D;
   f32x4v* Sp = reinterpret_cast<f32x4v*>(io.state + base);
@@ -63,48 +90,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(Params p, Decode
     const int r = rg + rr * RPP;
     if (r < D) Sv[rr] = __builtin_nontemporal_load(&Sp[static_cast<size_t>(r) * C4 + col4]);
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- preprocess: conv + SiLU for the 3D channels of this head; shift history
-  for (int c = tid; c < 3 * D; c += NT) {
-    const int grp = c / D, i = c % D;
-    const size_t ch = static_cast<size_t>(grp) * H * D + static_cast<size_t>(h) * D + i;
-    const void* x = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
-    const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
-    const float xt = ld<IO_BF16>(x, static_cast<size_t>(n) * H * D + static_cast<size_t>(h) * D + i);
-    const size_t cb = static_cast<size_t>(n) * 3 * Ctot + ch;
-    const float h0 = ld<IO_BF16>(io.conv_state, cb);
-    const float h1 = ld<IO_BF16>(io.conv_state, cb + Ctot);
-    const float h2 = ld<IO_BF16>(io.conv_state, cb + 2 * Ctot);
-    float u;
-    if (flags & KDA_FLAG_SKIP_CONV) {
-      u = xt;
-    } else {
-      const size_t wi = (static_cast<size_t>(h) * D + i) * 4;
-      const float y = ld<IO_BF16>(w, wi) * h0 + ld<IO_BF16>(w, wi + 1) * h1 + ld<IO_BF16>(w, wi + 2) * h2 +
-                      ld<IO_BF16>(w, wi + 3) * xt;
-      u = siluf_(y);
-    }
+  if (tid < 3 * D) {
+    u_s[tid] = (flags & KDA_FLAG_SKIP_CONV) ? xt : siluf_(w0 * h0 + w1 * h1 + w2 * h2 + w3 * xt);
     st<IO_BF16>(io.conv_state, cb, h1);
     st<IO_BF16>(io.conv_state, cb + Ctot, h2);
     st<IO_BF16>(io.conv_state, cb + 2 * Ctot, xt);
-    u_s[c] = u;
   }
   const float a_exp = expf(p.A_log[h]);
-  for (int i = tid; i < D; i += NT) {
-    const float al = ld<IO_BF16>(io.alpha, (static_cast<size_t>(n) * H + h) * D + i);
-    const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, p.dt_bias[h * D + i], a_exp, p.lower_bound);
-    e_s[i] = expf(g);
+  if (tid < D) {
+    const float g = (flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound);
+    e_s[tid] = expf(g);
   }
-  // epilogue operands of this thread's output column
-  float gsig = 0.f, onw = 0.f;
-  if constexpr (GATED) {
-    if (tid < D) {
-      gsig = sigmoidf_(ld<IO_BF16>(io.gate, (static_cast<size_t>(n) * H + h) * D + tid));
-      onw = io.onw[tid];
-    }
-  }
+  float gsig = 0.f;
+  if constexpr (GATED) gsig = sigmoidf_(graw);
   if (tid == 0) {
-    const float bb = ld<IO_BF16>(io.b, static_cast<size_t>(n) * H + h);
     float be = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
     if (flags & KDA_FLAG_BETA_X2) be *= 2.0f;
     scal[2] = be;
@@ -245,6 +247,46 @@ void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
   const uint32_t flags = p.flags;
 
   const int col4 = tid % C4, rg = tid / C4;
+  // The small inputs go out first, all unconditionally (a load under a
+  // condition compiles to a branch that waits for it; lanes without a channel
+  // read a valid one and ignore it): the conv taps, the pooled history and the
+  // first group's inputs.  Then the state tile: the memory counter drains in
+  // issue order, so the first group's preprocess runs while it arrives.
+  float wt[CPT][4], hist[CPT][3];
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) {
+    const int c = min(tid + m * NT, NC - 1);
+    const int grp = c / D, ci = c % D;
+    const size_t cb = static_cast<size_t>(slot) * 3 * Ctot + static_cast<size_t>(grp) * HD +
+                      static_cast<size_t>(h) * D + ci;
+    const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
+    const size_t wi = (static_cast<size_t>(h) * D + ci) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wt[m][j] = ld<IO_BF16>(w, wi + j);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) hist[m][j] = ld<IO_BF16>(io.conv_pool, cb + j * Ctot);
+  }
+  const float dtb = p.dt_bias[h * D + tid % D];
+  float onw = 0.f;
+  if constexpr (GATED) onw = io.onw[tid % D];
+  float xr[KG][CPT], ar[KG], br;           // a group's raw inputs, alphas and this lane's beta input
+  auto load_group = [&](int t0, int kg) {
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const size_t tok = static_cast<size_t>(n) * K + t0 + min(j, kg - 1);
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const int c = min(tid + m * NT, NC - 1);
+        const int grp = c / D, ci = c % D;
+        const void* xsrc = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
+        xr[j][m] = ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci);
+      }
+      ar[j] = ld<IO_BF16>(io.alpha, tok * HD + static_cast<size_t>(h) * D + tid % D);
+    }
+    br = ld<IO_BF16>(io.b, (static_cast<size_t>(n) * K + t0 + min(tid, kg - 1)) * H + h);
+  };
+  if (K > 0) load_group(0, min(KG, K));
+  __builtin_amdgcn_sched_barrier(0);
   f32x4v* Sp = reinterpret_cast<f32x4v*>(io.state_pool + (static_cast<size_t>(slot) * H + h) * D * D);
   f32x4v Sv[RPT];
 #pragma unroll
@@ -252,57 +294,25 @@ void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
     const int r = rg + rr * RPP;
     if (r < D) Sv[rr] = __builtin_nontemporal_load(&Sp[static_cast<size_t>(r) * C4 + col4]);
   }
-
-  // the conv taps of this thread's channels and the pooled history
-  float wt[CPT][4];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
     const int c = tid + m * NT;
-    wt[m][0] = wt[m][1] = wt[m][2] = wt[m][3] = 0.f;
     if (c < NC) {
-      const int grp = c / D, ci = c % D;
-      const size_t ch = static_cast<size_t>(grp) * HD + static_cast<size_t>(h) * D + ci;
-      const size_t cb = static_cast<size_t>(slot) * 3 * Ctot + ch;
-      if (!(flags & KDA_FLAG_SKIP_CONV)) {
-        const void* w = grp == 0 ? p.wq : (grp == 1 ? p.wk : p.wv);
-        const size_t wi = (static_cast<size_t>(h) * D + ci) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wt[m][j] = ld<IO_BF16>(w, wi + j);
-      }
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        const float hv = ld<IO_BF16>(io.conv_pool, cb + j * Ctot);
-        win_s[j][c] = hv;
-        kwin_s[j][c] = hv;
+        win_s[j][c] = hist[m][j];
+        kwin_s[j][c] = hist[m][j];
       }
     }
   }
   const float a_exp = expf(p.A_log[h]);
-  const float dtb = tid < D ? p.dt_bias[h * D + tid] : 0.f;
-  float onw = 0.f;
-  if constexpr (GATED) onw = tid < D ? io.onw[tid] : 0.f;
   const bool norm = !(flags & KDA_FLAG_SKIP_L2NORM);
 
   for (int t0 = 0; t0 < K; t0 += KG) {
-    // the group's raw inputs, gates and betas, all loads issued together (the
-    // first group's right behind the state loads)
     const int kg = min(KG, K - t0);
+    if (t0 > 0) load_group(t0, kg);
     {
-      float xr[KG][CPT], ar[KG];
-      float br = 0.f;
-#pragma unroll
-      for (int j = 0; j < KG; ++j) {
-        const size_t tok = static_cast<size_t>(n) * K + t0 + min(j, kg - 1);
-#pragma unroll
-        for (int m = 0; m < CPT; ++m) {
-          const int c = tid + m * NT;
-          const int grp = c / D, ci = c % D;
-          const void* xsrc = grp == 0 ? io.q : (grp == 1 ? io.k : io.v);
-          xr[j][m] = c < NC ? ld<IO_BF16>(xsrc, tok * HD + static_cast<size_t>(h) * D + ci) : 0.f;
-        }
-        ar[j] = tid < D ? ld<IO_BF16>(io.alpha, tok * HD + static_cast<size_t>(h) * D + tid) : 0.f;
-      }
-      if (tid < kg) br = ld<IO_BF16>(io.b, (static_cast<size_t>(n) * K + t0 + tid) * H + h);
       // conv + SiLU of the group's tokens, channel by channel (the window in
       // registers for the group, back in shared memory after it)
 #pragma unroll
@@ -366,6 +376,8 @@ void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
       const float iq = norm ? 1.0f / sqrtf(nrm_s[j][0] + p.eps) : 1.0f;
       const float ik = norm ? 1.0f / sqrtf(nrm_s[j][1] + p.eps) : 1.0f;
       const float qs = iq * p.scale, ks = ik, beta = b_s[j], qk = nrm_s[j][2] * iq * ik * p.scale;
+      float graw = 0.f;   // the epilogue's gate of this token (every lane loads a valid one)
+      if constexpr (GATED) graw = ld<IO_BF16>(io.gate, tok * HD + static_cast<size_t>(h) * D + tid % D);
 
       float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -384,12 +396,9 @@ void decode_multi_kernel(Params p, DecodeMultiIO io, int K) {
         red[0][rg][col4 * 4 + jj] = pk[jj];
         red[1][rg][col4 * 4 + jj] = pq[jj];
       }
-      // the epilogue's gate of this token, loaded before the barrier
-      float gsig = 0.f;
-      if constexpr (GATED) {
-        if (tid < D) gsig = sigmoidf_(ld<IO_BF16>(io.gate, tok * HD + static_cast<size_t>(h) * D + tid));
-      }
       __syncthreads();   // red is complete; d_s and osum are free (read before the last barrier)
+      float gsig = 0.f;
+      if constexpr (GATED) gsig = sigmoidf_(graw);
       float o_c = 0.f;
       if (tid < D) {
         const int c = tid;
