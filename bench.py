@@ -429,6 +429,46 @@ def bench_prefill_no_clamp(kda, torch, ev, dp, steps=5, warmup=2):
                          "lane_ops_per_launch": lane_ops}}
 
 
+def bench_prefill_slabs(kda, torch, ev, dp, slabs=(8192, 2048), steps=10, warmup=2):
+    """The 32K prefill with a workspace for slabs of S positions per sequence
+    instead of one pass (the chunked form run window after window, the state
+    carried between them; results bit-identical to one pass)."""
+    dev = torch.device("cuda:0")
+    B, T = 4, 32768
+    cfg = dp.config(out_dtype=torch.bfloat16)
+    tz = dp.tensors
+    q, k, v = (tz[n].view(B, T, -1) for n in ("q", "k", "v"))
+    alpha, b = tz["alpha"].view(B, T, H, D), tz["b"].view(B, T, H)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"workload": "kda chunked prefill B=4 T=32768 H=32 dk=dv=128, bf16, workspace for slabs of S positions",
+           "one_pass_workspace_gib": round(kda.kda_prefill_workspace_bytes(cfg, B, T) / 2**30, 2), "slabs": {}}
+    for slab in slabs:
+        ws = torch.empty(kda.kda_prefill_slab_workspace_bytes(cfg, B, slab), dtype=torch.uint8, device=dev)
+
+        def step():
+            kda.kda_prefill(cfg, q, k, v, alpha, b, tz["initial_state"], tz["conv_state"], o=o, final_state=S_out,
+                            workspace=ws, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        e0, e1 = ev.create(), ev.create()
+        torch.cuda.synchronize()
+        ev.record(e0, stream.cuda_stream)
+        for _ in range(steps):
+            step()
+        ev.record(e1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = ev.ms(e0, e1) / steps
+        gib = ws.numel() / 2**30
+        log(f"[bench] prefill in slabs of {slab}: {ms:.3f} ms/step, workspace {gib:.2f} GiB")
+        out["slabs"][str(slab)] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(B * T / ms * 1e3, 1),
+                                   "workspace_gib": round(gib, 3)}
+        del ws
+    return out
+
+
 def bench_output_gate(kda, torch, ev, steps=20, warmup=3):
     """The o_norm x sigmoid-gate epilogue on the 32K prefill's output shape
     (4 x 32768 tokens x 32 heads x 128, bf16 o and gate), in place."""
@@ -608,6 +648,7 @@ def main():
         result["decode_multi"] = bench_decode_multi(kda, torch, ev)
         result["varlen"] = bench_varlen(kda, torch, ev)
         result["prefill_no_clamp"] = bench_prefill_no_clamp(kda, torch, ev, dp)
+        result["prefill_slabs"] = bench_prefill_slabs(kda, torch, ev, dp)
         result["output_gate"] = bench_output_gate(kda, torch, ev)
         result["backward"] = bench_backward(kda, torch, ev, dp)
     if not args.no_cpu_baseline:

@@ -12,7 +12,7 @@ Entry points (same names as the C ABI):
   kda_decode_multi(cfg, q, ..., state_pool, conv_pool, slots=, n_commit=)
   kda_decode_step_gated / kda_decode_multi_gated   the same, output epilogue fused
   kda_output_gate(cfg, o, gate, o_norm_weight)     the output epilogue alone
-  kda_prefill_workspace_bytes / kda_varlen_workspace_bytes
+  kda_prefill_workspace_bytes / kda_varlen_workspace_bytes / kda_prefill_slab_workspace_bytes
 """
 from __future__ import annotations
 
@@ -48,7 +48,7 @@ NUM_STAGES = len(STAGES)
 EXPORTED = ("kda_version", "kda_status_string", "kda_prefill_workspace_bytes", "kda_prefill",
             "kda_varlen_workspace_bytes", "kda_varlen_prefill", "kda_decode_step", "kda_decode_multi",
             "kda_decode_step_gated", "kda_decode_multi_gated", "kda_output_gate", "kda_varlen_prefill_noalloc",
-            "kda_varlen_backward_workspace_bytes", "kda_varlen_backward")
+            "kda_varlen_backward_workspace_bytes", "kda_varlen_backward", "kda_prefill_slab_workspace_bytes")
 
 # the fixed scratch behind kda_varlen_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 256 << 20
@@ -96,6 +96,8 @@ def _load_library():
     lib.kda_prefill_workspace_bytes.argtypes = [cfgp, i32, i32]
     lib.kda_varlen_workspace_bytes.restype = sz
     lib.kda_varlen_workspace_bytes.argtypes = [cfgp, i32, i32]
+    lib.kda_prefill_slab_workspace_bytes.restype = sz
+    lib.kda_prefill_slab_workspace_bytes.argtypes = [cfgp, i32, i32]
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_varlen_prefill.restype = ctypes.c_int
@@ -214,6 +216,13 @@ def kda_prefill_workspace_bytes(cfg: Config, B: int, T: int) -> int:
 
 def kda_varlen_workspace_bytes(cfg: Config, N: int, total_T: int) -> int:
     return int(_lib.kda_varlen_workspace_bytes(ctypes.byref(cfg.c_struct()), N, total_T))
+
+
+def kda_prefill_slab_workspace_bytes(cfg: Config, N: int, slab_tokens: int) -> int:
+    """Workspace for the chunked prefill of N sequences run in slabs of
+    slab_tokens positions; passing a workspace of this size (smaller than
+    the one-pass size) to kda_prefill / kda_varlen_prefill runs them in slabs."""
+    return int(_lib.kda_prefill_slab_workspace_bytes(ctypes.byref(cfg.c_struct()), N, slab_tokens))
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Params p, Chun
   if (c >= t.chunk0[t.N]) return;
   const int H = p.H;
   const int s = t.chunk_seq[c];
-  const int tau0 = (c - t.chunk0[s]) * kChunk;
+  const int tau0 = t.s0 + (c - t.chunk0[s]) * kChunk;
   const int64_t tok0 = static_cast<int64_t>(t.cu[s]) + tau0;
   const int len = min(kChunk, t.cu[s + 1] - static_cast<int>(tok0));
   const int tid = threadIdx.x;

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   }
 
   auto chunk_step = [&](int c, OpsA<D, DVT, NP>& A, OpsB<D, DVT, NP>& B) {
-    const int tau = (c - c_first) * kChunk;
+    const int tau = t.s0 + (c - c_first) * kChunk;   // the chunk's position in the sequence
     const int len = min(kChunk, seq_len - tau);
 
     // ---- W S and Q+ S for this wave's 16 token rows.  The S^T pieces of
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(512) void chunk_scan_split_kernel(Params p, ChunkTa
     }
     __syncthreads();
     for (int c = c_first; c < c_end; ++c) {
-      const int tau = (c - c_first) * kChunk;
+      const int tau = t.s0 + (c - c_first) * kChunk;   // the chunk's position in the sequence
       const int len = min(kChunk, seq_len - tau);
       f32x4 accQ[CJ];
 #pragma unroll

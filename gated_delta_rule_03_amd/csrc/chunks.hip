@@ -4,7 +4,9 @@
 // lengths) into a chunk table without any host synchronisation: chunk0[s] is
 // the first 64-token chunk of sequence s (an exclusive scan of ceil(len/64)),
 // chunk0[N] the number of chunks, chunk_seq[c] the sequence owning chunk c and
-// desc[c] where chunk c lies.
+// desc[c] where chunk c lies.  A table may cover a window of positions
+// [s0, s0 + span) of every sequence (the prefill run in slabs); its chunks
+// keep their positions in the whole sequence.
 // Chunks never straddle two sequences; the last chunk of a sequence may be
 // partial.  Grids of the chunk kernels are sized by a host upper bound and
 // blocks past chunk0[N] exit.
@@ -30,13 +32,14 @@ namespace kda {
 __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __restrict__ cu_in, int32_t N,
                                                             int32_t T_uniform, int32_t* __restrict__ cu_ws,
                                                             int32_t* __restrict__ chunk0, int32_t long_tiles,
-                                                            int32_t ncu) {
+                                                            int32_t ncu, int32_t s0, int32_t span) {
   __shared__ int32_t scan[1024];
   __shared__ int32_t carry_s, max_s, long_s;
   const int tid = threadIdx.x;
-  auto chunks_of = [&](int s) {
+  auto chunks_of = [&](int s) {   // chunks of the sequence's positions [s0, s0 + span)
     const int len = cu_in ? (cu_in[s + 1] - cu_in[s]) : T_uniform;
-    return (len + kChunk - 1) / kChunk;
+    const int in = min(max(len - s0, 0), span);
+    return (in + kChunk - 1) / kChunk;
   };
   for (int s = tid; s <= N; s += 1024) cu_ws[s] = cu_in ? cu_in[s] : s * T_uniform;
   if (tid == 0) {
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __res
 __global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __restrict__ chunk0,
                                                              const int32_t* __restrict__ cu, int32_t N,
                                                              int32_t* __restrict__ chunk_seq, int4* __restrict__ desc,
-                                                             int32_t max_chunks) {
+                                                             int32_t max_chunks, int32_t s0) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= max_chunks || c >= chunk0[N]) return;
   int lo = 0, hi = N - 1;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void fill_chunk_seq_kernel(const int32_t* __re
     if (chunk0[mid] <= c) lo = mid; else hi = mid - 1;
   }
   chunk_seq[c] = lo;
-  const int tau0 = (c - chunk0[lo]) * kChunk;
+  const int tau0 = s0 + (c - chunk0[lo]) * kChunk;
   const int tok0 = cu[lo] + tau0;
   desc[c] = make_int4(lo, tau0, min(kChunk, cu[lo + 1] - tok0), tok0);
 }
@@ -118,15 +121,15 @@ hipError_t device_cus(int* ncu) {
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws, int32_t* chunk0,
                                int32_t* chunk_seq, int4* desc, int32_t max_chunks, int32_t H, int32_t D,
-                               hipStream_t st) {
+                               hipStream_t st, int32_t s0, int32_t span) {
   int ncu = 0;
   hipError_t e0 = device_cus(&ncu);
   if (e0 != hipSuccess) return e0;
   const int long_tiles = H * (D >= 64 ? D / 64 : 1);
-  build_chunks_kernel<<<1, 1024, 0, st>>>(cu_in, N, T_uniform, cu_ws, chunk0, long_tiles, ncu);
+  build_chunks_kernel<<<1, 1024, 0, st>>>(cu_in, N, T_uniform, cu_ws, chunk0, long_tiles, ncu, s0, span);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_chunks <= 0) return e;
-  fill_chunk_seq_kernel<<<(max_chunks + 255) / 256, 256, 0, st>>>(chunk0, cu_ws, N, chunk_seq, desc, max_chunks);
+  fill_chunk_seq_kernel<<<(max_chunks + 255) / 256, 256, 0, st>>>(chunk0, cu_ws, N, chunk_seq, desc, max_chunks, s0);
   return hipGetLastError();
 }
 

@@ -123,7 +123,7 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
   int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
   int4* desc = reinterpret_cast<int4*>(ws + L.desc);
-  ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N};
+  ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N, 0};
   uint8_t* records = reinterpret_cast<uint8_t*>(ws + L.records);
   const bool io_bf16 = cfg->io_dtype == KDA_BF16;
   const bool out_bf16 = cfg->out_dtype == KDA_BF16;
@@ -158,6 +158,76 @@ kda_status_t run_prefill(const kda_config_t* cfg, int32_t N, int64_t total_T, in
   if (io.conv_out) {
     s = stage(cfg, KDA_STAGE_CONV_STATE, st, [&] { return kda::launch_conv_state_out(p, t, io, io_bf16, st); });
     if (s != KDA_OK) return s;
+  }
+  return KDA_OK;
+}
+
+// The chunked prefill in slabs, for a workspace smaller than a whole pass
+// needs: windows of `slab` positions (a multiple of 64) of every sequence,
+// one after the other, each a chunk table, a prep and a scan over the
+// window's chunks, with the state carried from window to window in place
+// (in the caller's final state, or in a buffer of the workspace).  The
+// result is bit-identical to one pass: the scan's state at a chunk boundary
+// is the same fp32 value whether it stays in registers or goes to memory.
+struct SlabLayout {
+  Layout L;
+  size_t state, total;
+};
+
+SlabLayout make_slab_layout(const kda_config_t* cfg, int64_t N, int64_t slab) {
+  SlabLayout S{};
+  S.L = make_layout(cfg, N, N * (slab / kda::kChunk), 0);
+  S.state = S.L.total;
+  S.total = align_up(S.state + static_cast<size_t>(N) * cfg->num_heads * cfg->head_k_dim * cfg->head_v_dim * 4);
+  return S;
+}
+
+// The longest slab (a multiple of 64 tokens, at most `cap`) whose workspace
+// fits in `bytes`, or 0.
+int64_t slab_for(const kda_config_t* cfg, int64_t N, size_t bytes, int64_t cap) {
+  if (N <= 0 || make_slab_layout(cfg, N, kda::kChunk).total > bytes) return 0;
+  int64_t lo = 1, hi = (cap + kda::kChunk - 1) / kda::kChunk;   // in chunks
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (make_slab_layout(cfg, N, mid * kda::kChunk).total <= bytes) lo = mid; else hi = mid - 1;
+  }
+  return lo * kda::kChunk;
+}
+
+kda_status_t run_prefill_slabs(const kda_config_t* cfg, int32_t N, int64_t total_T, const int32_t* cu_in,
+                               int32_t T_uniform, const PrefillIO& io, void* workspace, int64_t slab,
+                               hipStream_t st) {
+  const Params p = make_params(cfg);
+  const SlabLayout S = make_slab_layout(cfg, N, slab);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* cu_ws = reinterpret_cast<int32_t*>(ws + S.L.cu);
+  int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + S.L.chunk0);
+  int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + S.L.chunk_seq);
+  int4* desc = reinterpret_cast<int4*>(ws + S.L.desc);
+  uint8_t* records = reinterpret_cast<uint8_t*>(ws + S.L.records);
+  float* state = io.S_out ? io.S_out : reinterpret_cast<float*>(ws + S.state);
+  const bool io_bf16 = cfg->io_dtype == KDA_BF16;
+  const bool out_bf16 = cfg->out_dtype == KDA_BF16;
+  const int mc = static_cast<int>(static_cast<int64_t>(N) * (slab / kda::kChunk));
+  // the longest a sequence can be: the batch's length, or all its tokens
+  const int64_t longest = cu_in ? total_T : T_uniform;
+  const int64_t nslabs = longest > 0 ? (longest + slab - 1) / slab : 1;   // (one pass writes the states of an empty batch)
+  for (int64_t k = 0; k < nslabs; ++k) {
+    const int32_t s0 = static_cast<int32_t>(k * slab);
+    PrefillIO sio = io;
+    sio.S0 = k == 0 ? io.S0 : state;
+    sio.S_out = state;
+    sio.conv_out = nullptr;
+    ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N, s0};
+    hipError_t e = kda::launch_build_chunks(cu_in, N, T_uniform, cu_ws, chunk0, chunk_seq, desc, mc, p.H, p.D, st,
+                                            s0, static_cast<int32_t>(slab));
+    if (e == hipSuccess) e = kda::launch_chunk_prep(p, t, sio, records, mc, io_bf16, st);
+    if (e == hipSuccess) e = kda::launch_chunk_scan(p, t, sio, records, io_bf16, out_bf16, cu_in != nullptr, st);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+  }
+  if (io.conv_out) {   // (the table's sequence offsets are the whole batch's)
+    const ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N, 0};
+    return stage(cfg, KDA_STAGE_CONV_STATE, st, [&] { return kda::launch_conv_state_out(p, t, io, io_bf16, st); });
   }
   return KDA_OK;
 }
@@ -209,7 +279,7 @@ kda_status_t check_backward(const kda_config_t* cfg) {
 
 extern "C" {
 
-int32_t kda_version(void) { return 103; }
+int32_t kda_version(void) { return 104; }
 
 size_t kda_varlen_backward_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t total_T) {
   if (check_backward(cfg) != KDA_OK || N < 0 || total_T < 0) return 0;
@@ -242,7 +312,7 @@ kda_status_t kda_varlen_backward(const kda_config_t* cfg, int32_t N, int32_t tot
   int32_t* chunk0 = reinterpret_cast<int32_t*>(ws + L.chunk0);
   int32_t* chunk_seq = reinterpret_cast<int32_t*>(ws + L.chunk_seq);
   int4* desc = reinterpret_cast<int4*>(ws + L.desc);
-  ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N};
+  ChunkTable t{cu_ws, chunk0, chunk_seq, desc, N, 0};
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, nullptr, nullptr, nullptr};
   kda::BackwardIO g{d_o, d_final_state, dq, dk, dv, dalpha, db, d_initial_state, d_conv_state_in,
                     dw_q, dw_k, dw_v, ddt_bias, dA_log};
@@ -284,6 +354,13 @@ size_t kda_varlen_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t to
   return make_layout(cfg, N, chunks_varlen(N, total_T), total_T).total;
 }
 
+size_t kda_prefill_slab_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t slab_tokens) {
+  if (check_config(cfg, true) != KDA_OK || N < 1 || slab_tokens < 1 || recurrent_form(cfg)) return 0;
+  const int64_t slab = (static_cast<int64_t>(slab_tokens) + kda::kChunk - 1) / kda::kChunk * kda::kChunk;
+  if (static_cast<int64_t>(N) * (slab / kda::kChunk) > INT32_MAX) return 0;
+  return make_slab_layout(cfg, N, slab).total;
+}
+
 kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const void* q, const void* k, const void* v,
                          const void* alpha, const void* b, const float* initial_state, const void* conv_state_in,
                          void* o, float* final_state, void* conv_state_out, void* workspace, size_t workspace_bytes,
@@ -297,8 +374,13 @@ kda_status_t kda_prefill(const kda_config_t* cfg, int32_t B, int32_t T, const vo
   const int64_t mc = chunks_uniform(B, T);
   const size_t need = make_layout(cfg, B, mc, static_cast<int64_t>(B) * T).total;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};
+  if (workspace_bytes < need) {   // the chunked form runs in slabs of T, if one of 64 tokens fits
+    const int64_t slab = recurrent_form(cfg) ? 0 : slab_for(cfg, B, workspace_bytes, T);
+    if (slab <= 0) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    return run_prefill_slabs(cfg, B, static_cast<int64_t>(B) * T, nullptr, T, io, workspace, slab,
+                             static_cast<hipStream_t>(stream));
+  }
   return run_prefill(cfg, B, static_cast<int64_t>(B) * T, mc, nullptr, T, io, workspace,
                      static_cast<hipStream_t>(stream));
 }
@@ -317,8 +399,12 @@ kda_status_t kda_varlen_prefill(const kda_config_t* cfg, int32_t N, int32_t tota
   if (mc > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   const size_t need = make_layout(cfg, N, mc, total_T).total;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   PrefillIO io{q, k, v, alpha, b, initial_state, conv_state_in, o, final_state, conv_state_out};
+  if (workspace_bytes < need) {   // the chunked form runs in slabs, if one of 64 tokens per sequence fits
+    const int64_t slab = recurrent_form(cfg) ? 0 : slab_for(cfg, N, workspace_bytes, total_T);
+    if (slab <= 0) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    return run_prefill_slabs(cfg, N, total_T, cu_seqlens, 0, io, workspace, slab, static_cast<hipStream_t>(stream));
+  }
   return run_prefill(cfg, N, total_T, mc, cu_seqlens, 0, io, workspace, static_cast<hipStream_t>(stream));
 }
 

@@ -88,6 +88,8 @@ struct ChunkTable {
   const int32_t* chunk_seq;  // [max_chunks] sequence of each chunk
   const int4* desc;          // [max_chunks] (sequence, first token in it, tokens, first packed token)
   int32_t N;
+  int32_t s0;                // the table covers positions [s0, s0 + span) of every sequence (0 and
+                             // the whole sequence unless the prefill runs in slabs); a multiple of 64
 };
 
 struct PrefillIO {
@@ -105,7 +107,7 @@ struct PrefillIO {
 
 hipError_t launch_build_chunks(const int32_t* cu_in, int32_t N, int32_t T_uniform, int32_t* cu_ws,
                                int32_t* chunk0, int32_t* chunk_seq, int4* desc, int32_t max_chunks, int32_t H,
-                               int32_t D, hipStream_t st);
+                               int32_t D, hipStream_t st, int32_t s0 = 0, int32_t span = INT32_MAX);
 // Compute units of the current device (queried on every call).
 hipError_t device_cus(int* ncu);
 hipError_t launch_chunk_prep(const Params& p, const ChunkTable& t, const PrefillIO& io, uint8_t* records,

@@ -44,17 +44,24 @@ extern "C" kda_status_t kda_varlen_prefill_noalloc(const kda_config_t* cfg, int3
                                                    const float* initial_state, const void* conv_state_in, void* o,
                                                    float* final_state, void* conv_state_out, void* stream) {
   // sizes before any device call: a batch whose workspace exceeds the
-  // scratch is refused; an invalid configuration or size (query answer 0)
-  // and the empty batch take the ordinary entry point's checks and answer
+  // scratch runs in slabs (chunked form), and is refused when not even a
+  // slab of 64 tokens per sequence fits; an invalid configuration or size
+  // (query answer 0) and the empty batch take the ordinary entry point's
+  // checks and answer
   const size_t need = kda_varlen_workspace_bytes(cfg, N, total_T);
   if (need == 0 || N == 0)
     return kda_varlen_prefill(cfg, N, total_T, cu_seqlens, q, k, v, alpha, b, initial_state, conv_state_in, o,
                               final_state, conv_state_out, nullptr, 0, stream);
-  if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) {
+    const size_t slab_need = kda_prefill_slab_workspace_bytes(cfg, N, 64);
+    if (slab_need == 0 || slab_need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  }
   void* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess) return KDA_ERR_HIP;
   // every kernel of the prefill writes the scratch bytes it later reads (the
-  // chunk table, then the records), so nothing needs clearing between calls
+  // chunk table, then the records; in slabs also the carried state, written
+  // by the first slab before any later one reads it), so nothing needs
+  // clearing between calls
   return kda_varlen_prefill(cfg, N, total_T, cu_seqlens, q, k, v, alpha, b, initial_state, conv_state_in, o,
                             final_state, conv_state_out, ws, KDA_NOALLOC_SCRATCH_BYTES, stream);
 }

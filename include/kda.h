@@ -147,7 +147,16 @@ size_t kda_prefill_workspace_bytes(const kda_config_t *cfg, int32_t B, int32_t T
  *   o              [B][T][H][dv] out_dtype (required)
  *   final_state    [B][H][dk][dv] fp32, or NULL; may alias initial_state
  *   conv_state_out [B][3][Ctot] io_dtype, or NULL; may alias conv_state_in
- *   workspace      device scratch of at least kda_prefill_workspace_bytes()
+ *   workspace      device scratch of kda_prefill_workspace_bytes() for one pass
+ *                  over the whole batch.  A smaller workspace runs the chunked
+ *                  form (gate lower bound >= -5.4) in slabs: windows of the
+ *                  longest multiple of 64 positions of every sequence whose
+ *                  kda_prefill_slab_workspace_bytes() fits, one after the
+ *                  other, with the state carried between them.  The results
+ *                  are bit-identical to one pass.  KDA_ERR_WORKSPACE_TOO_SMALL
+ *                  when not even a 64-token slab fits, or for the recurrent
+ *                  form (bound below -5.4).  The per-stage timing events
+ *                  (stage_events) are not recorded in slabs.
  * No other aliasing is allowed.
  */
 kda_status_t kda_prefill(const kda_config_t *cfg, int32_t B, int32_t T,
@@ -164,6 +173,18 @@ kda_status_t kda_prefill(const kda_config_t *cfg, int32_t B, int32_t T,
 size_t kda_varlen_workspace_bytes(const kda_config_t *cfg, int32_t N, int32_t total_T);
 
 /*
+ * Workspace size in bytes for the chunked prefill (kda_prefill with B = N, or
+ * kda_varlen_prefill) run in slabs of slab_tokens positions per sequence
+ * (rounded up to a multiple of 64): the chunk table and records of one slab
+ * plus a carried state of [N][H][dk][dv] fp32.  It depends on neither T nor
+ * total_T, which bounds the workspace of long prefills (4 x 32768 tokens at
+ * H = 32, d = 128: 9.0 GiB in one pass, 2.3 GiB in slabs of 8192).  Returns 0
+ * for an invalid configuration, N < 1, slab_tokens < 1 or a gate lower bound
+ * below -5.4 (the recurrent form, which has no slabs).
+ */
+size_t kda_prefill_slab_workspace_bytes(const kda_config_t *cfg, int32_t N, int32_t slab_tokens);
+
+/*
  * Chunked prefill of N sequences packed back to back (varlen).
  *   cu_seqlens     [N+1] int32, DEVICE; cu[0] = 0, cu[N] = total_T,
  *                  nondecreasing (zero-length sequences allowed).  The
@@ -175,7 +196,10 @@ size_t kda_varlen_workspace_bytes(const kda_config_t *cfg, int32_t N, int32_t to
  *   o              [total_T][H][dv]
  *   final_state    [N][H][dk][dv] or NULL;  conv_state_out [N][3][Ctot] or NULL
  * State and conv history restart at each sequence; chunks never straddle two
- * sequences.  Aliasing rules as for kda_prefill.
+ * sequences.  Aliasing rules, and slabs for a smaller workspace, as for
+ * kda_prefill (a slab is a window of positions of every sequence; the host
+ * does not know the longest sequence, so it runs ceil(total_T / slab) of
+ * them, the later ones empty for short sequences).
  */
 kda_status_t kda_varlen_prefill(const kda_config_t *cfg, int32_t N, int32_t total_T,
                                 const int32_t *cu_seqlens,
@@ -194,10 +218,14 @@ kda_status_t kda_varlen_prefill(const kda_config_t *cfg, int32_t N, int32_t tota
  * allocates nothing.  Arguments, layouts and results as for
  * kda_varlen_prefill.
  *   - A batch whose workspace (kda_varlen_workspace_bytes) exceeds
- *     KDA_NOALLOC_SCRATCH_BYTES is refused with KDA_ERR_WORKSPACE_TOO_SMALL
- *     before any device call.  At H = 32, dk = dv = 128, bf16, the chunked
- *     form needs ~144.5 KB per (64-token chunk, head): up to ~1800 chunk-heads,
- *     e.g. 3 x 1024 tokens x 32 heads (4096 x 32 does not fit).
+ *     KDA_NOALLOC_SCRATCH_BYTES runs in slabs (as kda_varlen_prefill does
+ *     with a small workspace); it is refused with KDA_ERR_WORKSPACE_TOO_SMALL,
+ *     before any device call, when not even one slab of 64 tokens fits
+ *     (kda_prefill_slab_workspace_bytes(cfg, N, 64) above the scratch: at
+ *     H = 32, dk = dv = 128, bf16, 6.5 MB per sequence, a chunk's records for
+ *     every head and the carried state, so N up to 39) or for the recurrent
+ *     form.  One pass fits up to ~1800 (64-token chunk,
+ *     head) pairs, e.g. 3 x 1024 tokens x 32 heads.
  *   - Every call on one GPU uses that GPU's single array: calls that overlap
  *     in time on one GPU (different streams, different threads) race and
  *     must be serialised by the caller.  Nothing from a previous call needs

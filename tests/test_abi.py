@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(kda):
 
 
 def test_version_and_status_strings(kda):
-    assert kda.version() == 103
+    assert kda.version() == 104
     for code, name in ((0, "KDA_OK"), (1, "KDA_ERR_INVALID_ARGUMENT"), (2, "KDA_ERR_UNSUPPORTED"),
                        (3, "KDA_ERR_WORKSPACE_TOO_SMALL"), (4, "KDA_ERR_HIP")):
         assert kda.status_string(code) == name
@@ -141,6 +141,29 @@ def test_workspace_query_grows_with_size(kda):
     c = lib.kda_varlen_workspace_bytes(ctypes.byref(cfg), 2, 128)
     assert 0 < a < b <= c
     assert a % 256 == 0
+
+
+def test_slab_workspace_query(kda):
+    """The workspace of the chunked prefill in slabs: one slab's chunk table
+    and records plus the carried state, independent of the batch's length;
+    a workspace below one 64-token slab is refused before any launch."""
+    cfg, _ = make_cfg(kda, H=32, dk=128, dv=128)
+    lib = kda.library()
+    q = lambda N, S: lib.kda_prefill_slab_workspace_bytes(ctypes.byref(cfg), N, S)
+    assert q(1, 1) == q(1, 64) > 0 and q(1, 65) == q(1, 128) > q(1, 64)
+    assert q(4, 8192) > q(2, 8192) > q(1, 8192) and q(4, 8192) % 256 == 0
+    # the carried state [N][H][dk][dv] fp32 and N x S / 64 chunk records
+    assert q(4, 8192) > 4 * 32 * 128 * 128 * 4 + 4 * 128 * 32 * 140 * 1024
+    assert q(4, 8192) < lib.kda_prefill_workspace_bytes(ctypes.byref(cfg), 4, 32768) / 3
+    assert q(0, 64) == 0 and q(1, 0) == 0
+    cfg_rec, _ = make_cfg(kda, H=32, dk=128, dv=128, gate_lower_bound=float("-inf"))
+    assert lib.kda_prefill_slab_workspace_bytes(ctypes.byref(cfg_rec), 1, 64) == 0   # no slabs for the recurrent form
+    # below one slab: refused, nothing touched
+    small, _ = make_cfg(kda)
+    one = lib.kda_prefill_slab_workspace_bytes(ctypes.byref(small), 1, 64)
+    assert 0 < one < lib.kda_prefill_workspace_bytes(ctypes.byref(small), 1, 4096)
+    st, bufs = call_prefill(kda, small, B=1, T=4096, ws_bytes=one - 1)
+    assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL and all(b.untouched() for b in bufs.values())
 
 
 def test_workspace_of_the_recurrent_form(kda):

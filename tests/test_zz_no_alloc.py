@@ -3,8 +3,9 @@ library's fixed per-GPU scratch, for callers that cannot allocate) against
 kda_varlen_prefill with a caller workspace.  Both run the same kernels on the
 same inputs, so o, the final state and the conv history must agree bit for
 bit.  Two calls in a row, the second on a smaller batch (the scratch keeps the
-first call's bytes), then a batch whose workspace exceeds the scratch, which
-must be refused before anything runs.
+first call's bytes); a batch whose one-pass workspace exceeds the scratch,
+which runs in slabs; and one where not even a slab fits, which must be
+refused before anything runs.
 """
 import numpy as np
 import pytest
@@ -59,14 +60,24 @@ def test_noalloc_recurrent_form(kda):
     run_both(kda, p, gate_lower_bound=float("-inf"))
 
 
-def test_noalloc_refuses_batches_beyond_the_scratch(kda):
+def test_noalloc_runs_batches_beyond_the_scratch_in_slabs(kda):
+    """A batch whose one-pass workspace exceeds the scratch runs in slabs of
+    positions, bit-identical to the one-pass call with a workspace."""
+    p = make_problem(4900, [20000, 9000, 0, 77], 4, 128, 128, BF16, state_seqs=[0, 1], conv_state=True)
+    cfg, _ = problem_to_device(p, torch.device("cuda:0"))
+    assert kda.kda_varlen_workspace_bytes(cfg, 4, p.total_T) > kda.NOALLOC_SCRATCH_BYTES
+    run_both(kda, p)
+
+
+def test_noalloc_refuses_batches_beyond_one_slab(kda):
+    """Refused before anything runs when not even a 64-token slab fits: 40
+    sequences at H = 32, d = 128 need 6.5 MB each."""
     dev = torch.device("cuda:0")
     p = make_problem(4800, [64], 32, 128, 128, BF16)
     cfg, t = problem_to_device(p, dev)
-    total = 4 * 4096
-    need = kda.kda_varlen_workspace_bytes(cfg, 1, total)
-    assert need > kda.NOALLOC_SCRATCH_BYTES
-    cu = torch.tensor([0, total], dtype=torch.int32, device=dev)
+    N, total = 40, 40 * 64
+    assert kda.kda_prefill_slab_workspace_bytes(cfg, N, 64) > kda.NOALLOC_SCRATCH_BYTES
+    cu = torch.arange(0, total + 1, 64, dtype=torch.int32, device=dev)
     q = torch.zeros((total, 32 * 128), dtype=torch.bfloat16, device=dev)
     b = torch.zeros((total, 32), dtype=torch.bfloat16, device=dev)
     o = torch.full((total, 32, 128), 7.0, device=dev)
