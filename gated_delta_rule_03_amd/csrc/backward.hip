@@ -685,6 +685,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   __shared__ float sT[kBlk][kBlk], sAun[kBlk][kBlk], sdA[kBlk][kBlk], sdAqk[kBlk][kBlk];
   __shared__ float sdbeta[kBlk], sdGC[D];
   __shared__ float sWt[kBlk][D + 1], sUt[kBlk][D + 1];  // W and U
+  __shared__ float sPart[NT / kWave][kBlk][kBlk];        // the waves' partial 16 x 16 products
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
   const int blk = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   const bool live_chunk = blk / kBlocksPerChunk < t.chunk0[t.N];
@@ -822,20 +823,28 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     }
   }
   __syncthreads();
-  // dA = -strict_lower(dXw W^T + dXu U^T) (wave 0), A_un = strict_lower(K+ K-^T)
-  // (wave 1), dAqk = lower(dO Delta^T) (wave 2): 16 x 16 each over K = D, in
-  // four independent accumulators
-  if (wave < 3) {
+  // dA = -strict_lower(dXw W^T + dXu U^T), A_un = strict_lower(K+ K-^T) and
+  // dAqk = lower(dO Delta^T): 16 x 16 each over K = D, the channel range split
+  // over the waves (dA, two products a step, on half of them; A_un and dAqk on
+  // a quarter each), four independent accumulators per wave, then the waves'
+  // partial sums added in a fixed order
+  {
+    constexpr int NW = NT / kWave;
+    constexpr int nA = NW / 2, nU = NW / 4;              // waves per product (nQ = nU)
+    const int prod = wave < nA ? 0 : (wave < nA + nU ? 1 : 2);
+    const int part = prod == 0 ? wave : (prod == 1 ? wave - nA : wave - nA - nU);
+    const int KW = prod == 0 ? D / nA : D / nU;          // channels of this wave
+    const int kbeg = part * KW;
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-    for (int k0 = 0; k0 < D; k0 += 16) {
+    for (int st0 = 0; st0 < KW / 4; st0 += 4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int k = k0 + 4 * j + g4;
-        if (wave == 0) {
+        if (st0 + j >= KW / 4) break;
+        const int k = kbeg + 4 * (st0 + j) + g4;
+        if (prod == 0) {
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[l16][k], sWt[l16][k], acc[j], 0, 0, 0);
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sdKm[l16][k], sUt[l16][k], acc[j], 0, 0, 0);
-        } else if (wave == 1) {
+        } else if (prod == 1) {
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(s.k[l16][k] * s.eP[l16][k], s.k[l16][k] * s.eM[l16][k],
                                                         acc[j], 0, 0, 0);
         } else {
@@ -844,12 +853,17 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      const float v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
-      if (wave == 0) sdA[r][l16] = l16 < r ? -v : 0.f;
-      else if (wave == 1) sAun[r][l16] = l16 < r ? v : 0.f;
-      else sdAqk[r][l16] = l16 <= r ? v : 0.f;
+    for (int i = 0; i < 4; ++i)
+      sPart[wave][4 * g4 + i][l16] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+    __syncthreads();
+    for (int e = tid; e < 3 * kBlk * kBlk; e += NT) {
+      const int pr = e / (kBlk * kBlk), r = (e / kBlk) % kBlk, i = e % kBlk;
+      const int w0 = pr == 0 ? 0 : (pr == 1 ? nA : nA + nU), nw = pr == 0 ? nA : nU;
+      float v = 0.f;
+      for (int w = 0; w < nw; ++w) v += sPart[w0 + w][r][i];
+      if (pr == 0) sdA[r][i] = i < r ? -v : 0.f;
+      else if (pr == 1) sAun[r][i] = i < r ? v : 0.f;
+      else sdAqk[r][i] = i <= r ? v : 0.f;
     }
   }
   __syncthreads();
@@ -918,39 +932,69 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   // the two cancel unless i < t <= r, so the pairs are added directly over
   // that rectangle (row by row, prefix sums over i): nothing is subtracted,
   // and no rounding residue of two large canceling sums is left over.
-  if (tid < D) {
-    const int c = tid;
-    float dG[kBlk], dGs[kBlk], P[kBlk];
-    for (int r = 0; r < kBlk; ++r) {
-      const float eP = s.eP[r][c], eM = s.eM[r][c], eS = s.eS[r][c];
-      const float k = s.k[r][c];
-      const float dqp = sdQp[r][c], dkp = sdKp[r][c], dkm = sdKm[r][c], dkt = sdKt[r][c];
-      dG[r] = sDel[r][c];
-      dGs[r] = dkt * k * eS;
-      P[r] = 0.f;
-      sdQp[r][c] = dqp * eP;                          // d q^
-      sdKp[r][c] = dkp * eP + dkm * eM + dkt * eS;    // d k^
-    }
-    for (int r = 1; r < kBlk; ++r) {
-      const float ar = s.beta[r] * s.k[r][c] * s.eP[r][c], br = s.q[r][c] * s.eP[r][c];
-      float rp = 0.f;
-      for (int t2 = 1; t2 <= r; ++t2) {
-        const int i = t2 - 1;
-        rp += (sdA[r][i] * ar + sdAqk[r][i] * br) * (s.k[i][c] * s.eM[i][c]);
-        P[t2] += rp;
+  // Four parts per channel (waves at d = 128), part p taking rows p, p + 4, ...:
+  // the elementwise terms, then the pair terms of its rows into a partial P,
+  // which meet in shared memory (buffers no longer needed: W, U, dDelta, dO)
+  // and are added in part order by the channel's first thread.
+  {
+    constexpr int PT = NT / D >= 4 ? 4 : NT / D;
+    static_assert(kBlk % PT == 0, "rows split evenly over the parts");
+    const int c = tid % D, part = tid / D;
+    float (*pp)[D + 1] = part == 0 ? sWt : (part == 1 ? sUt : (part == 2 ? sdDel : sdO));
+    if (part < PT) {
+      float P[kBlk];
+#pragma unroll
+      for (int t2 = 0; t2 < kBlk; ++t2) P[t2] = 0.f;
+#pragma unroll
+      for (int j = 0; j < kBlk / PT; ++j) {
+        const int r = part + PT * j;
+        const float eP = s.eP[r][c], eM = s.eM[r][c], eS = s.eS[r][c];
+        const float k = s.k[r][c];
+        const float dqp = sdQp[r][c], dkp = sdKp[r][c], dkm = sdKm[r][c], dkt = sdKt[r][c];
+        sdQp[r][c] = dqp * eP;                          // d q^
+        sdKp[r][c] = dkp * eP + dkm * eM + dkt * eS;    // d k^
+        sdKt[r][c] = dkt * k * eS;                      // dGs, in place of dK~
       }
+#pragma unroll
+      for (int j = 0; j < kBlk / PT; ++j) {
+        const int r = part + PT * j;
+        const float ar = s.beta[r] * s.k[r][c] * s.eP[r][c], br = s.q[r][c] * s.eP[r][c];
+        float rp = 0.f;
+#pragma unroll
+        for (int t2 = 1; t2 < kBlk; ++t2) {
+          if (t2 <= r) {
+            const int i = t2 - 1;
+            rp += (sdA[r][i] * ar + sdAqk[r][i] * br) * (s.k[i][c] * s.eM[i][c]);
+            P[t2] += rp;
+          }
+        }
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < kBlk; ++t2) pp[t2][c] = P[t2];
     }
+    __syncthreads();
     // dg_t = sum_{r >= t} dG_r + sum_{r < t} dGs_r + dG_C + P_t, for the block's tokens
-    const float gc = sdGC[c];
-    float suffix = 0.f;
-    for (int r = kBlk - 1; r >= 0; --r) {
-      suffix += dG[r];
-      dG[r] = suffix;
-    }
-    float prefix = 0.f;
-    for (int r = 0; r < kBlk; ++r) {
-      sdKm[r][c] = r < b.ntok ? dG[r] + prefix + gc + P[r] : 0.f;   // dg
-      prefix += dGs[r];
+    if (tid < D) {
+      float dG[kBlk];
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) dG[r] = sDel[r][c];
+      float suffix = 0.f;
+#pragma unroll
+      for (int r = kBlk - 1; r >= 0; --r) {
+        suffix += dG[r];
+        dG[r] = suffix;
+      }
+      const float gc = sdGC[c];
+      float prefix = 0.f;
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) {
+        float Pr = sWt[r][c];
+        if (PT > 1) Pr += sUt[r][c];
+        if (PT > 2) Pr += sdDel[r][c];
+        if (PT > 3) Pr += sdO[r][c];
+        sdKm[r][c] = r < b.ntok ? dG[r] + prefix + gc + Pr : 0.f;   // dg
+        prefix += sdKt[r][c];
+      }
     }
   }
   __syncthreads();
