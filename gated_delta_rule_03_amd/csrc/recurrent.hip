@@ -76,21 +76,24 @@ __global__ __launch_bounds__(4 * D) void token_prep_kernel(Params p, ChunkTable 
     const void* xin = role == 0 ? qin : (role == 1 ? kin : vin);
     const void* w = role == 0 ? p.wq : (role == 1 ? p.wk : p.wv);
     const bool raw = flags & KDA_FLAG_SKIP_CONV;
-    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f;
-    if (!raw) {
-      w0 = ld<IO_BF16>(w, col * 4);
-      w1 = ld<IO_BF16>(w, col * 4 + 1);
-      w2 = ld<IO_BF16>(w, col * 4 + 2);
-      w3 = ld<IO_BF16>(w, col * 4 + 3);
-    }
+    // every load goes out unconditionally (a load under a condition compiles
+    // to a branch that waits for it), the unused values replaced afterwards
+    float w0 = ld<IO_BF16>(w, col * 4), w1 = ld<IO_BF16>(w, col * 4 + 1);
+    float w2 = ld<IO_BF16>(w, col * 4 + 2), w3 = ld<IO_BF16>(w, col * 4 + 3);
     float hm[3];
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
       const int tau = tau0 - 3 + m;
-      if (tau >= 0) hm[m] = ld<IO_BF16>(xin, static_cast<size_t>(tok0 - tau0 + tau) * HD + col);
-      else if (conv_in) hm[m] = ld<IO_BF16>(conv_in, (static_cast<size_t>(s) * 3 + (3 + tau)) * Ctot + role * HD + col);
-      else hm[m] = 0.f;
+      const bool hist = tau < 0 && conv_in != nullptr;
+      const void* src = hist ? conv_in : xin;
+      const size_t idx = hist ? (static_cast<size_t>(s) * 3 + (3 + tau)) * Ctot + role * HD + col
+                              : static_cast<size_t>(tok0 - tau0 + max(tau, 0)) * HD + col;
+      hm[m] = ld<IO_BF16>(src, idx);
     }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      if (tau0 - 3 + m < 0 && conv_in == nullptr) hm[m] = 0.f;
+    if (raw) { w0 = 0.f; w1 = 0.f; w2 = 0.f; w3 = 1.f; }
     float x[kChunk];
 #pragma unroll
     for (int r = 0; r < kChunk; ++r)   // rows past the chunk's end re-read its last row
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(4 * D) void token_prep_kernel(Params p, ChunkTable 
       if (r < len) rbase[static_cast<size_t>(r) * RF + 2 * D + ch] = expf(g);
     }
   }
+  const float bb = ld<IO_BF16>(bin, static_cast<size_t>(tok0 + min(tid, len - 1)) * H + h);
   if (tid < len) {
-    const float bb = ld<IO_BF16>(bin, static_cast<size_t>(tok0 + tid) * H + h);
     float be = (flags & KDA_FLAG_RAW_BETA) ? bb : sigmoidf_(bb);
     if (flags & KDA_FLAG_BETA_X2) be *= 2.0f;
     float* rr = rbase + static_cast<size_t>(tid) * RF + 4 * D;
