@@ -251,6 +251,57 @@ __host__ __device__ constexpr BwdRecord bwd_record(int D) {
 size_t bwd_record_bytes(int D) { return bwd_record(D).bytes; }
 int bwd_reduce_parts() { return kReduceParts; }
 
+namespace {
+
+// The block states (S0 of every block, the adjoint dS_C at every block end)
+// are stored in the order the block-gradient kernel's lanes read them.  Its
+// wave w owns state rows 16w .. 16w + 15 and lane l reads KS = D / 4
+// consecutive columns KS (l / 16) .. of row 16w + l % 16 as KS / 4 float4s;
+// element (c, j) therefore sits at
+//   ((c / 16 * (KS / 4) + (j % KS) / 4) * 64 + (j / KS) * 16 + c % 16) * 4 + j % 4,
+// so that each of the reader's 16-byte wave loads covers 1 KB of contiguous
+// memory (in row order a load touches 64 cache lines for 16 bytes each).
+template <int D>
+__device__ __forceinline__ size_t state_index(int c, int j) {
+  constexpr int KS = D / 4;
+  return static_cast<size_t>(((c / 16 * (KS / 4) + (j % KS) / 4) * 64 + (j / KS) * 16 + c % 16) * 4 + j % 4);
+}
+
+
+// A scan wave's state slice (columns j0 .. j0 + 15, accumulator layout) to
+// memory in state_index order.  At d >= 64 the slice is 32 runs of 256
+// contiguous bytes there (one per row tile and 4-column group); it is laid
+// out in that order in the wave's shared-memory area first, then leaves in
+// 16-byte stores covering 1 KB each.  Smaller d store element by element.
+constexpr int kRun = 68;
+
+template <int D>
+__device__ __forceinline__ void store_state(float* dst, const f32x4 (&acc)[D / 16], float* stg, int j0, int lane) {
+  constexpr int KS = D / 4;
+  const int l16 = lane % 16, g = lane / 16;
+  if constexpr (D >= 64) {
+    // stg[(t16 * 4 + m) * kRun + r16 * 4 + e]: row 16 t16 + r16, column
+    // j0 + 4 m + e (runs padded to 68 floats against bank conflicts)
+#pragma unroll
+    for (int t16 = 0; t16 < D / 16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stg[(t16 * 4 + l16 / 4) * kRun + (4 * g + i) * 4 + l16 % 4] = acc[t16][i];
+    const int m0 = (j0 % KS) / 4, g4 = j0 / KS;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {      // 4 runs of 256 B per 16-byte wave store
+      const int run = k * 4 + lane / 16, t16 = run / 4, m = run % 4;
+      const float4 v = *reinterpret_cast<const float4*>(&stg[run * kRun + (lane % 16) * 4]);
+      *reinterpret_cast<float4*>(&dst[((t16 * (KS / 4) + m0 + m) * 64 + g4 * 16 + lane % 16) * 4]) = v;
+    }
+  } else {
+#pragma unroll
+    for (int t16 = 0; t16 < D / 16; ++t16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[state_index<D>(16 * t16 + 4 * g + i, j0 + l16)] = acc[t16][i];
+  }
+}
+}  // namespace
+
 // ---------------------------------------------------------------- block prep
 template <int D, bool IO_BF16>
 __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTable t, PrefillIO io, uint8_t* recs) {
@@ -388,6 +439,7 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_state_scan_kernel
   struct Ops { float w[PF], k[PF], u[PU], e[PE]; };
   __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], seG[D], sU[kBlk][CW + 1];
   __shared__ float sDel[TW][kBlk][kScanTile + 1];
+  __shared__ __align__(16) float sStg[TW][D >= 64 ? D / 4 * kRun : 4];   // staged state stores
   int nh, grp;
   if (!scan_coords(t.N * p.H, D / CW, nh, grp)) return;
   const int h = nh % p.H, n = nh / p.H;
@@ -442,11 +494,7 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_state_scan_kernel
   // one block: its operands are in shared memory; Sblk <- S, Delta, S update
   auto step = [&](int jb) {
     const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
-#pragma unroll
-    for (int t16 = 0; t16 < NT16; ++t16)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Sblk[bh * SZ + static_cast<size_t>(16 * t16 + 4 * g + i) * D + j0 + l16] = acc[t16][i];
+    store_state<D>(Sblk + bh * SZ, acc, &sStg[wave][0], j0, lane);
     // Delta = U - W S  (contracting the state's rows; four accumulators by i)
     f32x4 d4[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -514,6 +562,7 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_adjoint_scan_kern
   __shared__ float sW[kBlk][D + 1], sKt[kBlk][D + 1], sQp[kBlk][D + 1], seG[D];
   __shared__ float sAqk[kBlk][kBlk + 1];
   __shared__ float sdO[TW][kBlk][kScanTile + 1], sdDel[TW][kBlk][kScanTile + 1];
+  __shared__ __align__(16) float sStg[TW][D >= 64 ? D / 4 * kRun : 4];   // staged state stores
   int nh, grp;
   if (!scan_coords(t.N * p.H, D / CW, nh, grp)) return;
   const int h = nh % p.H, n = nh / p.H;
@@ -588,11 +637,7 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_adjoint_scan_kern
   auto step = [&](int jb) {
     const size_t bh = static_cast<size_t>(blk0 + jb) * p.H + h;
     // the adjoint of the block's end state
-#pragma unroll
-    for (int t16 = 0; t16 < NT16; ++t16)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dSblk[bh * SZ + static_cast<size_t>(16 * t16 + 4 * g + i) * D + j0 + l16] = acc[t16][i];
+    store_state<D>(dSblk + bh * SZ, acc, &sStg[wave][0], j0, lane);
     // dDelta = K~ dS_C (contracting the state's rows) + Aqk^T dO
     f32x4 d4[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -730,16 +775,18 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   const float lT = gT[tid % (kBlk * kBlk)];
   // rows of S0 and dS_C for the matrix-core products: wave w owns output
   // channels 16w .. 16w + 15, lane l the contiguous state columns
-  // KS (l / 16) .. KS (l / 16) + KS - 1 of row 16w + l % 16
+  // KS (l / 16) .. KS (l / 16) + KS - 1 of row 16w + l % 16 (stored in that
+  // order: state_index)
   float sv[KS], dsv[KS], lgeG = 0.f;
   if (D / 16 >= NT / kWave || wave < D / 16) {   // (every wave at d = 128: no branch)
     const int c = wave * 16 + l16;
-    const float* s0row = Sblk + bh * D * D + static_cast<size_t>(c) * D + g4 * KS;
-    const float* dsrow = dSblk + bh * D * D + static_cast<size_t>(c) * D + g4 * KS;
+    const size_t base = bh * D * D + (static_cast<size_t>(wave) * (KS / 4) * 64 + lane) * 4;
+    const float* s0row = Sblk + base;
+    const float* dsrow = dSblk + base;
 #pragma unroll
     for (int q = 0; q < KS; q += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(s0row + q);
-      const float4 d4 = *reinterpret_cast<const float4*>(dsrow + q);
+      const float4 a = *reinterpret_cast<const float4*>(s0row + q * 64);
+      const float4 d4 = *reinterpret_cast<const float4*>(dsrow + q * 64);
       sv[q] = a.x; sv[q + 1] = a.y; sv[q + 2] = a.z; sv[q + 3] = a.w;
       dsv[q] = d4.x; dsv[q + 1] = d4.y; dsv[q + 2] = d4.z; dsv[q + 3] = d4.w;
     }
