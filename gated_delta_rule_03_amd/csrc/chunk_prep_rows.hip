@@ -304,9 +304,12 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
   // the wait for them counts only the memory operations of one iteration.
   Raw nxt;
   ChunkPos cur_pos{}, nxt_pos{};
-  uint4 a_cur[KSW];
+  // the gate of this lane's row and channels for the chunk about to run,
+  // computed during the previous chunk's phase 5 (its VALU has room there;
+  // phase 1 is VALU-bound), from alpha loaded in that chunk's phase 3
+  float g_cur[CPL];
 #pragma unroll
-  for (int ks = 0; ks < KSW; ++ks) a_cur[ks] = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < CPL; ++j) g_cur[j] = 0.f;
   uint32_t b_cur = 0u;
   // the descriptor of the chunk after the next (a uniform index: a scalar
   // load, one chunk ahead of its use)
@@ -325,15 +328,30 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
             (nxt.zero >> j) & 1u ? make_uint4(0u, 0u, 0u, 0u) : nxt.x[j];
     }
     uint32_t bw = nxt.b;
+    asm volatile("" : "+v"(bw));   // arrived before the next load goes out
+    b_cur = bw;
+  };
+  // gate (computed for every lane, then selected) of the chunk at cp, from
+  // nx's alpha; rows past the chunk's end get 0
+  auto gate_of = [&](const Raw& nx, const ChunkPos& cp, const LaneCoords& L, const float* dtb) {
+    const bool live = L.r < cp.len;
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
-      uint32_t aw[4] = {nxt.a[ks].x, nxt.a[ks].y, nxt.a[ks].z, nxt.a[ks].w};
+      const int c0 = CW * L.cq + 32 * ks + 8 * L.q4;
+      const uint32_t aw[4] = {nx.a[ks].x, nx.a[ks].y, nx.a[ks].z, nx.a[ks].w};
+      const float4 d0 = *reinterpret_cast<const float4*>(&dtb[c0]);
+      const float4 d1 = *reinterpret_cast<const float4*>(&dtb[c0 + 4]);
+      const float dt[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      float al[8], gc[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(aw[i]));   // arrived before the next load goes out
-      a_cur[ks] = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+      for (int i = 0; i < 8; ++i) {
+        al[i] = (i & 1) ? __uint_as_float(aw[i / 2] & 0xffff0000u) : __uint_as_float(aw[i / 2] << 16);
+        gc[i] = gate_value(al[i], dt[i], a_exp, p.lower_bound);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g_cur[8 * ks + i] = live ? (raw_gate ? al[i] : gc[i]) : 0.f;
     }
-    asm volatile("" : "+v"(bw));
-    b_cur = bw;
+    pin(g_cur);   // computed here, not sunk past the next barrier
   };
   if (grp < total) {
     cur_pos = chunk_pos(scalar_load_desc(t.desc, grp));
@@ -341,6 +359,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     load_gate_inputs(nxt, cur_pos, coords(tid));
     desc_ahead = scalar_load_desc(t.desc, min(grp + G, total - 1));
     stage(coords(tid));
+    __syncthreads();   // dt_bias is in shared memory
+    gate_of(nxt, cur_pos, coords(tid), sDtb);
   }
 
   for (int c = grp; c < total; c += G) {
@@ -420,24 +440,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
         compiler_fence();
       }
     }
-    // the gate likewise: computed for every lane, then selected
 #pragma unroll
-    for (int ks = 0; ks < KSW; ++ks) {
-      const int c0 = CW * cq + 32 * ks + 8 * q4;
-      const uint32_t aw[4] = {a_cur[ks].x, a_cur[ks].y, a_cur[ks].z, a_cur[ks].w};
-      const float4 d0 = *reinterpret_cast<const float4*>(&dtb[c0]);
-      const float4 d1 = *reinterpret_cast<const float4*>(&dtb[c0 + 4]);
-      const float dt[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-      float al[8], gc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        al[i] = (i & 1) ? __uint_as_float(aw[i / 2] & 0xffff0000u) : __uint_as_float(aw[i / 2] << 16);
-        gc[i] = gate_value(al[i], dt[i], a_exp, p.lower_bound);
-      }
-      pin(gc);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) gv[8 * ks + i] = live ? (raw_gate ? al[i] : gc[i]) : 0.f;
-    }
+    for (int j = 0; j < CPL; ++j) gv[j] = g_cur[j];
     pin(qv);
     pin(kv);
     pin(gv);
@@ -986,8 +990,9 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 
     // ---- 5. per wave, on its own column blocks of X^T:
     //      X = T [beta K+ | beta V] (bf16 pieces, k steps up to the diagonal),
-    //      then W and U^T out
+    //      then W and U^T out; the next chunk's gate on the side
     {
+      gate_of(nxt, nxt_pos, L, dtb);
 #pragma unroll
       for (int bi = 0; bi < CBPW; ++bi) {
         const int cb = w + bi * NW;
