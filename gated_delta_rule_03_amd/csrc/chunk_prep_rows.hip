@@ -304,12 +304,13 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
   // the wait for them counts only the memory operations of one iteration.
   Raw nxt;
   ChunkPos cur_pos{}, nxt_pos{};
-  // the gate of this lane's row and channels for the chunk about to run,
+  // the in-block decay sums (prefix sums of the gate over the lane's 16-row
+  // block) of this lane's row and channels for the chunk about to run,
   // computed during the previous chunk's phase 5 (its VALU has room there;
   // phase 1 is VALU-bound), from alpha loaded in that chunk's phase 3
-  float g_cur[CPL];
+  float g_cur[CPL], e_cur[CPL];   // and e^{P_r}
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) g_cur[j] = 0.f;
+  for (int j = 0; j < CPL; ++j) g_cur[j] = e_cur[j] = 0.f;
   uint32_t b_cur = 0u;
   // the descriptor of the chunk after the next (a uniform index: a scalar
   // load, one chunk ahead of its use)
@@ -351,7 +352,13 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 #pragma unroll
       for (int i = 0; i < 8; ++i) g_cur[8 * ks + i] = live ? (raw_gate ? al[i] : gc[i]) : 0.f;
     }
+    // in-block decay sums P_r (through token r): DPP scans over the 16 lanes
+    // (token rows) of each row of the wave
+    row_prefix(g_cur);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) e_cur[j] = exp_fast(g_cur[j]);
     pin(g_cur);   // computed here, not sunk past the next barrier
+    pin(e_cur);
   };
   if (grp < total) {
     cur_pos = chunk_pos(scalar_load_desc(t.desc, grp));
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
 
     // ---- 1. conv + SiLU of this lane's row (q, k; v follows in phase 4b),
     //      gate, beta
-    float qv[CPL], kv[CPL], gv[CPL];
+    float qv[CPL], kv[CPL];
 #pragma unroll
     for (int tens = 0; tens < 2; ++tens) {
 #pragma unroll
@@ -440,11 +447,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
         compiler_fence();
       }
     }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) gv[j] = g_cur[j];
     pin(qv);
     pin(kv);
-    pin(gv);
     float beta = 0.f;
     if (live) {
       const float bb = bf16_to_f32(static_cast<uint16_t>(b_cur));
@@ -473,10 +477,10 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     // pieces' resolution
     float P[CPL], eP[CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) P[j] = gv[j];
-    row_prefix(P);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) eP[j] = exp_fast(P[j]);
+    for (int j = 0; j < CPL; ++j) {
+      P[j] = g_cur[j];
+      eP[j] = e_cur[j];
+    }
     pin(P);
     pin(eP);
     if (ln == 15) {
