@@ -1046,7 +1046,41 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   }
   __syncthreads();
   // ---- the preprocess in reverse, on the threads whose registers hold the
-  // raw inputs of the same (tensor, channel) task
+  // raw inputs of the same (tensor, channel) task.  The gate's tasks, v's
+  // SiLU and the L2 norms' dot products need nothing from one another and go
+  // in one phase (different threads); the SiLU of q and k follows, after the
+  // dot products are in shared memory.
+  __shared__ float sAl[NT / kWave];
+  __shared__ float sDot[2][kBlk];
+  // SiLU: dy = du sigmoid(y) (1 + y (1 - sigmoid(y))), with y recomputed from
+  // the raw inputs; roles 0 and 1 (q, k) through the L2 norm's reverse
+  auto silu_reverse = [&](bool qk) {
+#pragma unroll
+    for (int m = 0; m < Raw::kTasks; ++m) {
+      const int task = tid + m * NT;
+      if (task >= 3 * D || (task < 2 * D) != qk) continue;
+      const int role = task / D, ch = task % D;
+      const size_t col = static_cast<size_t>(h) * D + ch;
+      const float w0 = raw.w[m][0], w1 = raw.w[m][1], w2 = raw.w[m][2], w3 = raw.w[m][3];
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) {
+        if (r >= b.ntok) continue;
+        const float y = w0 * raw.x[m][r] + w1 * raw.x[m][r + 1] + w2 * raw.x[m][r + 2] + w3 * raw.x[m][r + 3];
+        float du;
+        if (role == 0) {
+          const float sc = p.scale, n = s.nq[r];
+          du = sc / n * (sdQp[r][ch] - s.q[r][ch] * sDot[0][r] / (sc * sc));
+        } else if (role == 1) {
+          const float n = s.nk[r];
+          du = (sdKp[r][ch] - s.k[r][ch] * sDot[1][r]) / n;
+        } else {
+          du = sX[r][ch];            // dV
+        }
+        const float sg = sigmoidf_(y);
+        dy[static_cast<size_t>(b.tok0 + r) * 3 * HD + role * HD + col] = du * sg * (1.f + y * (1.f - sg));
+      }
+    }
+  };
   // gate: d alpha, and the block's partial sums for d dt_bias and d A_log
   {
     const float a_exp = expf(p.A_log[h]);
@@ -1082,16 +1116,9 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
       }
       pd[c] = dtb_part;
     }
-    // d A_log: sum over the block's channels
-    __shared__ float sAl[NT / kWave];
+    // d A_log: the waves' sums, added after the barrier below
     const float wsum = group_sum<kWave>(alog_part);
     if (tid % kWave == 0) sAl[tid / kWave] = wsum;
-    __syncthreads();
-    if (tid == 0) {
-      float tot = 0.f;
-      for (int w = 0; w < NT / kWave; ++w) tot += sAl[w];
-      pAlog[bh] = tot;
-    }
   }
   // beta
   if (tid < b.ntok) {
@@ -1101,7 +1128,6 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     db[static_cast<size_t>(b.tok0 + tid) * p.H + h] = dbv;
   }
   // L2 norm (q with its scale, k): du = (s / n) (dq^ - q^ (q^ . dq^) / s^2)
-  __shared__ float sDot[2][kBlk];
   if (tid < 2 * kBlk * 8) {
     const int row = tid / 8, l8 = tid % 8;
     const bool isq = row < kBlk;
@@ -1113,33 +1139,14 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     dot += __shfl_xor(dot, 4, 8);
     if (l8 == 0) sDot[isq ? 0 : 1][r] = dot;
   }
+  silu_reverse(false);   // v
   __syncthreads();
-  // SiLU: dy = du sigmoid(y) (1 + y (1 - sigmoid(y))), with y recomputed from the raw inputs
-#pragma unroll
-  for (int m = 0; m < Raw::kTasks; ++m) {
-    const int task = tid + m * NT;
-    if (task >= 3 * D) continue;
-    const int role = task / D, ch = task % D;
-    const size_t col = static_cast<size_t>(h) * D + ch;
-    const float w0 = raw.w[m][0], w1 = raw.w[m][1], w2 = raw.w[m][2], w3 = raw.w[m][3];
-#pragma unroll
-    for (int r = 0; r < kBlk; ++r) {
-      if (r >= b.ntok) continue;
-      const float y = w0 * raw.x[m][r] + w1 * raw.x[m][r + 1] + w2 * raw.x[m][r + 2] + w3 * raw.x[m][r + 3];
-      float du;
-      if (role == 0) {
-        const float sc = p.scale, n = s.nq[r];
-        du = sc / n * (sdQp[r][ch] - s.q[r][ch] * sDot[0][r] / (sc * sc));
-      } else if (role == 1) {
-        const float n = s.nk[r];
-        du = (sdKp[r][ch] - s.k[r][ch] * sDot[1][r]) / n;
-      } else {
-        du = sX[r][ch];            // dV
-      }
-      const float sg = sigmoidf_(y);
-      dy[static_cast<size_t>(b.tok0 + r) * 3 * HD + role * HD + col] = du * sg * (1.f + y * (1.f - sg));
-    }
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < NT / kWave; ++w) tot += sAl[w];
+    pAlog[bh] = tot;
   }
+  silu_reverse(true);    // q, k
 }
 
 // ---------------------------------------------------------------- conv reverse
