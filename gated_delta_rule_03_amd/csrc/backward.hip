@@ -87,7 +87,9 @@ struct BlockSmem {
   float eM[kBlk][LD];    // e^{-G}
   float eS[kBlk][LD];    // e^{G_C - G}, from the exclusive in-block suffix sum of g
   float beta[kBlk];
-  float nq[kBlk], nk[kBlk];   // the L2 norms sqrt(|u|^2 + eps) of q and k
+  // per row, with n = sqrt(|u|^2 + eps) the L2 norm: scale / n for q, 1 / n
+  // for k (one division per row; the elementwise steps multiply)
+  float rq[kBlk], rk[kBlk];
 };
 
 // The raw inputs of one thread's preprocess tasks, loaded together before any
@@ -215,14 +217,14 @@ __device__ __forceinline__ void block_preprocess(const Params& p, const BlockInf
     ss += __shfl_xor(ss, 4, 8);
     if (l8 == 0) {
       const float n = sqrtf(ss + p.eps);
-      if (row < kBlk) s.nq[row] = n; else s.nk[row - kBlk] = n;
+      if (row < kBlk) s.rq[row] = p.scale / n; else s.rk[row - kBlk] = 1.f / n;
     }
   }
   __syncthreads();
   for (int e = tid; e < kBlk * D; e += NT) {
     const int r = e / D, c = e % D;
-    s.q[r][c] = s.q[r][c] / s.nq[r] * p.scale;
-    s.k[r][c] = s.k[r][c] / s.nk[r];
+    s.q[r][c] *= s.rq[r];
+    s.k[r][c] *= s.rk[r];
   }
   __syncthreads();
 }
@@ -1068,11 +1070,9 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
         const float y = w0 * raw.x[m][r] + w1 * raw.x[m][r + 1] + w2 * raw.x[m][r + 2] + w3 * raw.x[m][r + 3];
         float du;
         if (role == 0) {
-          const float sc = p.scale, n = s.nq[r];
-          du = sc / n * (sdQp[r][ch] - s.q[r][ch] * sDot[0][r] / (sc * sc));
+          du = s.rq[r] * (sdQp[r][ch] - s.q[r][ch] * sDot[0][r]);
         } else if (role == 1) {
-          const float n = s.nk[r];
-          du = (sdKp[r][ch] - s.k[r][ch] * sDot[1][r]) / n;
+          du = s.rk[r] * (sdKp[r][ch] - s.k[r][ch] * sDot[1][r]);
         } else {
           du = sX[r][ch];            // dV
         }
@@ -1127,7 +1127,8 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     if (p.flags & KDA_FLAG_BETA_X2) dbv *= 2.f;
     db[static_cast<size_t>(b.tok0 + tid) * p.H + h] = dbv;
   }
-  // L2 norm (q with its scale, k): du = (s / n) (dq^ - q^ (q^ . dq^) / s^2)
+  // L2 norm (q with its scale, k): du = (s / n) (dq^ - q^ (q^ . dq^) / s^2);
+  // sDot holds (q^ . dq^) / s^2 and k^ . dk^
   if (tid < 2 * kBlk * 8) {
     const int row = tid / 8, l8 = tid % 8;
     const bool isq = row < kBlk;
@@ -1137,7 +1138,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
     dot += __shfl_xor(dot, 1, 8);
     dot += __shfl_xor(dot, 2, 8);
     dot += __shfl_xor(dot, 4, 8);
-    if (l8 == 0) sDot[isq ? 0 : 1][r] = dot;
+    if (l8 == 0) sDot[isq ? 0 : 1][r] = isq ? dot / (p.scale * p.scale) : dot;
   }
   silu_reverse(false);   // v
   __syncthreads();
