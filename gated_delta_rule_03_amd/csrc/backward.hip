@@ -186,13 +186,13 @@ __device__ __forceinline__ void block_preprocess(const Params& p, const BlockInf
         const float al = raw.x[m][3 + r];
         g[r] = r < b.ntok ? ((p.flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound)) : 0.f;
         run += g[r];
-        s.eP[r][ch] = expf(run);
-        s.eM[r][ch] = expf(-run);
+        s.eP[r][ch] = exp_precise(run);   // ~2 ulp, half the instructions of expf
+        s.eM[r][ch] = exp_precise(-run);
       }
       float suf = 0.f;
 #pragma unroll
       for (int r = kBlk - 1; r >= 0; --r) {
-        s.eS[r][ch] = expf(suf);
+        s.eS[r][ch] = exp_precise(suf);
         suf += g[r];
       }
     }
