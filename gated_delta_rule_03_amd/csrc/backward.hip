@@ -186,13 +186,12 @@ __device__ __forceinline__ void block_preprocess(const Params& p, const BlockInf
         const float al = raw.x[m][3 + r];
         g[r] = r < b.ntok ? ((p.flags & KDA_FLAG_RAW_GATE) ? al : gate_value(al, dtb, a_exp, p.lower_bound)) : 0.f;
         run += g[r];
-        s.eP[r][ch] = exp_precise(run);   // ~2 ulp, half the instructions of expf
-        s.eM[r][ch] = exp_precise(-run);
+        s.eP[r][ch] = run;   // exponentiated below, by every thread
       }
       float suf = 0.f;
 #pragma unroll
       for (int r = kBlk - 1; r >= 0; --r) {
-        s.eS[r][ch] = exp_precise(suf);
+        s.eS[r][ch] = suf;
         suf += g[r];
       }
     }
@@ -221,10 +220,17 @@ __device__ __forceinline__ void block_preprocess(const Params& p, const BlockInf
     }
   }
   __syncthreads();
+  // the normalisation, and the decays' exponentials spread over every thread
+  // (the gate's threads formed their exponents: G_r, and G_C - G_r); the
+  // hardware base-2 exponential with the rounding residual carried, ~2 ulp
   for (int e = tid; e < kBlk * D; e += NT) {
     const int r = e / D, c = e % D;
     s.q[r][c] *= s.rq[r];
     s.k[r][c] *= s.rk[r];
+    const float G = s.eP[r][c];
+    s.eP[r][c] = exp_precise(G);
+    s.eM[r][c] = exp_precise(-G);
+    s.eS[r][c] = exp_precise(s.eS[r][c]);
   }
   __syncthreads();
 }
