@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   constexpr BwdRecord R = bwd_record(D);
   __shared__ BlockSmem<D> s;
   __shared__ float sKm[kBlk][D + 1];   // K e^{-G}
-  __shared__ float sA[kBlk][kBlk];     // A, then T
+  __shared__ float sPart[4][kBlk][kBlk];   // half-channel partial products of A and Aqk
   __shared__ float sT[kBlk][kBlk];
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
   const int blk = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
@@ -346,40 +346,60 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
     if (r == 0) geGC[c] = s.eP[kBlk - 1][c];
   }
   __syncthreads();
-  // A (strictly lower, wave 0) and Aqk (lower with the diagonal, wave 1) on the
-  // fp32 matrix cores: K+ K-^T and Q+ K-^T over K = D (lane layout as in
-  // bwd_block_grad_kernel)
+  // A (strictly lower) and Aqk (lower with the diagonal) on the fp32 matrix
+  // cores: K+ K-^T and Q+ K-^T over K = D, each product on two waves that take
+  // half the channels each, 8 of every 16 (lane layout as in
+  // bwd_block_grad_kernel); the halves meet in shared memory
   const int wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g4 = lane / 16;
-  if (wave < 2) {
+  static_assert(kBT / kWave == 4, "A and Aqk take two waves each");
+  {
+    const int prod = wave >> 1, half = wave & 1;   // prod 0: A, 1: Aqk
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};   // four independent chains
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = k0 + 4 * j + g4;
-        const float a = (wave == 0 ? s.k[l16][k] : s.q[l16][k]) * s.eP[l16][k];
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sKm[l16][k], acc[j], 0, 0, 0);
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int k = k0 + 4 * (2 * half + j2) + g4;
+        const float a = (prod == 0 ? s.k[l16][k] : s.q[l16][k]) * s.eP[l16][k];
+        const int ch = 2 * ((k0 / 16) & 1) + j2;
+        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sKm[l16][k], acc[ch], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i;
-      const float v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
-      if (wave == 0) sA[r][l16] = l16 < r ? s.beta[r] * v : 0.f;
-      else gAqk[r * kBlk + l16] = l16 <= r ? v : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) sPart[wave][4 * g4 + i][l16] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
   }
   __syncthreads();
-  // T = (I + A)^-1 by forward substitution, lane i owns column i
-  if (tid < kBlk) {
-    const int i = tid;
+  if (wave == 0) {
+    // T = (I + A)^-1 by forward substitution, lane i < 16 owns column i.  The
+    // strictly lower A is read into registers first (120 values, the halves
+    // added), so the substitution chain does no shared-memory reads; each
+    // row's sum runs in four partial sums.
+    const int i = lane;
+    float a[kBlk * (kBlk - 1) / 2];
+#pragma unroll
+    for (int r = 1, q = 0; r < kBlk; ++r)
+#pragma unroll
+      for (int m = 0; m < r; ++m, ++q) a[q] = s.beta[r] * (sPart[0][r][m] + sPart[1][r][m]);
     float col[kBlk];
-    for (int r = 0; r < kBlk; ++r) {
-      float v = (r == i) ? 1.f : 0.f;
-      for (int m = 0; m < r; ++m) v -= sA[r][m] * col[m];
+#pragma unroll
+    for (int r = 0, q = 0; r < kBlk; ++r) {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < r; ++m, ++q) ps[m & 3] += a[q] * col[m];
+      const float v = ((r == i) ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
       col[r] = r < i ? 0.f : v;
     }
-    for (int r = 0; r < kBlk; ++r) sT[r][i] = col[r];
+    if (i < kBlk) {
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) sT[r][i] = col[r];
+    }
+  } else if (wave == 1) {
+    // Aqk out (the two halves added; lower with the diagonal)
+#pragma unroll
+    for (int e4 = 0; e4 < kBlk * kBlk / kWave; ++e4) {
+      const int e = lane + e4 * kWave, r = e / kBlk, c = e % kBlk;
+      gAqk[e] = c <= r ? sPart[2][r][c] + sPart[3][r][c] : 0.f;
+    }
   }
   __syncthreads();
   for (int e = tid; e < kBlk * kBlk; e += kBT) gT[e] = sT[e / kBlk][e % kBlk];
