@@ -755,7 +755,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
   __shared__ float sDel[kBlk][D + 1], sdDel[kBlk][D + 1], sdO[kBlk][D + 1];   // padded: matrix-core A reads
   __shared__ float sdQp[kBlk][D + 1], sdKp[kBlk][D + 1], sdKm[kBlk][D + 1], sdKt[kBlk][D + 1];
   __shared__ float sX[kBlk][D + 1];       // dW, then dXw, then dV
-  __shared__ float sT[kBlk][kBlk], sAun[kBlk][kBlk], sdA[kBlk][kBlk], sdAqk[kBlk][kBlk];
+  __shared__ __align__(16) float sT[kBlk][kBlk], sAun[kBlk][kBlk], sdA[kBlk][kBlk], sdAqk[kBlk][kBlk];
   __shared__ float sdbeta[kBlk], sdGC[D];
   __shared__ float sWt[kBlk][D + 1], sUt[kBlk][D + 1];  // W and U
   __shared__ float sPart[NT / kWave][kBlk][kBlk];        // the waves' partial 16 x 16 products
@@ -1030,16 +1030,29 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
         sdKp[r][c] = dkp * eP + dkm * eM + dkt * eS;    // d k^
         sdKt[r][c] = dkt * k * eS;                      // dGs, in place of dK~
       }
+      // K-[i][c] for every column i of the pairs, and each row's dA, dAqk as
+      // 16-byte reads: the loop below then reads nothing from shared memory
+      float km[kBlk - 1];
+#pragma unroll
+      for (int i = 0; i < kBlk - 1; ++i) km[i] = s.k[i][c] * s.eM[i][c];
 #pragma unroll
       for (int j = 0; j < kBlk / PT; ++j) {
         const int r = part + PT * j;
         const float ar = s.beta[r] * s.k[r][c] * s.eP[r][c], br = s.q[r][c] * s.eP[r][c];
+        float da[kBlk], dq[kBlk];
+#pragma unroll
+        for (int q = 0; q < kBlk / 4; ++q) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&sdA[r][4 * q]);
+          const float4 b4 = *reinterpret_cast<const float4*>(&sdAqk[r][4 * q]);
+          da[4 * q] = a4.x; da[4 * q + 1] = a4.y; da[4 * q + 2] = a4.z; da[4 * q + 3] = a4.w;
+          dq[4 * q] = b4.x; dq[4 * q + 1] = b4.y; dq[4 * q + 2] = b4.z; dq[4 * q + 3] = b4.w;
+        }
         float rp = 0.f;
 #pragma unroll
         for (int t2 = 1; t2 < kBlk; ++t2) {
           if (t2 <= r) {
             const int i = t2 - 1;
-            rp += (sdA[r][i] * ar + sdAqk[r][i] * br) * (s.k[i][c] * s.eM[i][c]);
+            rp += (da[i] * ar + dq[i] * br) * km[i];
             P[t2] += rp;
           }
         }
