@@ -1061,27 +1061,37 @@ __global__ __launch_bounds__(grad_threads<D>()) void bwd_block_grad_kernel(Param
       for (int t2 = 0; t2 < kBlk; ++t2) pp[t2][c] = P[t2];
     }
     __syncthreads();
-    // dg_t = sum_{r >= t} dG_r + sum_{r < t} dGs_r + dG_C + P_t, for the block's tokens
-    if (tid < D) {
-      float dG[kBlk];
+    // dg_t = sum_{r >= t} dG_r + sum_{r < t} dGs_r + dG_C + P_t, for the block's
+    // tokens: every part's thread forms the channel's suffix and prefix sums
+    // (all reads first) and writes its own kBlk / PT rows
+    if (part < PT) {
+      float dG[kBlk], pre[kBlk];
 #pragma unroll
-      for (int r = 0; r < kBlk; ++r) dG[r] = sDel[r][c];
-      float suffix = 0.f;
+      for (int r = 0; r < kBlk; ++r) {
+        dG[r] = sDel[r][c];
+        pre[r] = sdKt[r][c];
+      }
+      const float gc = sdGC[c];
+      float suffix = 0.f, prefix = 0.f;
 #pragma unroll
       for (int r = kBlk - 1; r >= 0; --r) {
         suffix += dG[r];
         dG[r] = suffix;
       }
-      const float gc = sdGC[c];
-      float prefix = 0.f;
 #pragma unroll
       for (int r = 0; r < kBlk; ++r) {
+        const float g = pre[r];
+        pre[r] = prefix;
+        prefix += g;
+      }
+#pragma unroll
+      for (int r = 0; r < kBlk; ++r) {
+        if (r / (kBlk / PT) != part) continue;   // (uniform over the wave)
         float Pr = sWt[r][c];
         if (PT > 1) Pr += sUt[r][c];
         if (PT > 2) Pr += sdDel[r][c];
         if (PT > 3) Pr += sdO[r][c];
-        sdKm[r][c] = r < b.ntok ? dG[r] + prefix + gc + Pr : 0.f;   // dg
-        prefix += sdKt[r][c];
+        sdKm[r][c] = r < b.ntok ? dG[r] + pre[r] + gc + Pr : 0.f;   // dg
       }
     }
   }
