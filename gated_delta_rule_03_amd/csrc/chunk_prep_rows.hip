@@ -514,25 +514,39 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     float qP[CPL], kP[CPL];
     SplitN<NP> kcp[KSW];   // k e^{-P} pieces: the B operand of this lane's diagonal block
     // e^{G before block R} and the sum of the later block totals, per channel
+    // (R is uniform over the wave: the branches are scalar; each product and
+    // sum starts from its first term, not from 1 or 0)
     auto before_after = [&](int c0, float (&eb)[8], float (&after)[8]) {
+      auto load8 = [&](const float* row, float (&x)[8]) {
+        const float4 a = *reinterpret_cast<const float4*>(row + c0);
+        const float4 b = *reinterpret_cast<const float4*>(row + c0 + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      };
+      if (R == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        eb[i] = 1.f;
-        after[i] = 0.f;
-      }
+        for (int i = 0; i < 8; ++i) eb[i] = 1.f;
+      } else {
+        load8(sEBt[0], eb);
 #pragma unroll 1
-      for (int J = 0; J < R; ++J) {
-        const float4 e0 = *reinterpret_cast<const float4*>(&sEBt[J][c0]);
-        const float4 e1 = *reinterpret_cast<const float4*>(&sEBt[J][c0 + 4]);
-        eb[0] *= e0.x; eb[1] *= e0.y; eb[2] *= e0.z; eb[3] *= e0.w;
-        eb[4] *= e1.x; eb[5] *= e1.y; eb[6] *= e1.z; eb[7] *= e1.w;
+        for (int J = 1; J < R; ++J) {
+          float e[8];
+          load8(sEBt[J], e);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) eb[i] *= e[i];
+        }
       }
+      if (R == 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) after[i] = 0.f;
+      } else {
+        load8(sBt[3], after);
 #pragma unroll 1
-      for (int J = 3; J > R; --J) {
-        const float4 b0 = *reinterpret_cast<const float4*>(&sBt[J][c0]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&sBt[J][c0 + 4]);
-        after[0] += b0.x; after[1] += b0.y; after[2] += b0.z; after[3] += b0.w;
-        after[4] += b1.x; after[5] += b1.y; after[6] += b1.z; after[7] += b1.w;
+        for (int J = 2; J > R; --J) {
+          float b[8];
+          load8(sBt[J], b);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) after[i] += b[i];
+        }
       }
     };
     {
