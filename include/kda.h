@@ -37,7 +37,9 @@
  *  - All tensor pointers are DEVICE pointers, contiguous, row-major in the
  *    layout given, 16-byte aligned.  The caller owns every buffer; the library
  *    allocates no device memory and keeps no mutable global state, so calls on
- *    different streams are independent.
+ *    different streams are independent.  The one exception is
+ *    kda_varlen_prefill_noalloc, whose fixed per-GPU scratch array is shared
+ *    by all its calls on that GPU (see there).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and is asynchronous: the library never synchronises and never reads
  *    device data on the host.
