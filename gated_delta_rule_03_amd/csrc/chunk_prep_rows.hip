@@ -399,7 +399,8 @@ __global__ __launch_bounds__(64 * 4 * (D / CW), 1) void chunk_prep_rows_kernel(P
     const float* dtb = sDtb + inv;
 
     // ---- 1. conv + SiLU of this lane's row (q, k; v follows in phase 4b),
-    //      gate, beta
+    //      beta, the norms' partial sums; the gate and its in-block sums came
+    //      from the previous chunk's phase 5
     float qv[CPL], kv[CPL];
 #pragma unroll
     for (int tens = 0; tens < 2; ++tens) {
