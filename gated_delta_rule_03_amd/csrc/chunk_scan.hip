@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(Params p, ChunkTable t,
   const int sh = (bx / 8 / NTILE) * 8 + bx % 8;
   if (sh >= n_sh) return;
   if (gate >= 0 && t.chunk0[t.N + 1] != gate) return;
-  const int s = sh / H, h = sh % H;
+  const int s = t.scan_seq(sh / H), h = sh % H;
   const int j0 = tile * DVT;
   const int tid = threadIdx.x, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar branches
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(512) void chunk_scan_split_kernel(Params p, ChunkTa
   const int sh = (bx / 8 / NTILE) * 8 + bx % 8;
   if (sh >= n_sh) return;
   if (gate >= 0 && t.chunk0[t.N + 1] != gate) return;
-  const int s = sh / H, h = sh % H;
+  const int s = t.scan_seq(sh / H), h = sh % H;
   const int j0 = tile * DVT;
   const int tid = threadIdx.x, lane = tid % kWave, ln = lane & 15, q4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __res
                                                             int32_t* __restrict__ chunk0, int32_t long_tiles,
                                                             int32_t ncu, int32_t s0, int32_t span) {
   __shared__ int32_t scan[1024];
-  __shared__ int32_t carry_s, max_s, long_s;
+  __shared__ int32_t carry_s, max_s, long_s, carry_l, carry_o;
   const int tid = threadIdx.x;
   auto chunks_of = [&](int s) {   // chunks of the sequence's positions [s0, s0 + span)
     const int len = cu_in ? (cu_in[s + 1] - cu_in[s]) : T_uniform;
@@ -85,6 +85,38 @@ __global__ __launch_bounds__(1024) void build_chunks_kernel(const int32_t* __res
   if (tid == 0) {
     chunk0[N] = carry_s;
     chunk0[N + 1] = static_cast<int64_t>(long_s) * long_tiles < ncu ? 1 : 0;
+  }
+  // the scan's dispatch order: the long sequences first, then the others,
+  // each in index order (a stable partition; within a block the two counts
+  // travel packed in one prefix sum, 16 bits each, a block holding at most
+  // 1024 sequences).  Workgroups start in launch order, so a long sequence's
+  // serial chain would otherwise wait for the short ones before it.
+  const int n_long_total = cu_in ? long_s : N;
+  int32_t* order = chunk0 + N + 2;
+  if (tid == 0) {
+    carry_l = 0;
+    carry_o = 0;
+  }
+  for (int base = 0; base < N; base += 1024) {
+    const int s = base + tid;
+    const bool lg = s < N && (!cu_in || 2 * chunks_of(s) > mx);
+    const int packed = s < N ? (lg ? 1 : 1 << 16) : 0;
+    __syncthreads();   // the previous block's reads of scan[] and of the carries are done
+    scan[tid] = packed;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int ex = scan[tid] - packed;   // this block's sequences before s, packed
+    if (s < N) order[lg ? carry_l + (ex & 0xffff) : n_long_total + carry_o + (ex >> 16)] = s;
+    __syncthreads();
+    if (tid == 0) {
+      carry_l += scan[1023] & 0xffff;
+      carry_o += scan[1023] >> 16;
+    }
   }
 }
 

@@ -80,7 +80,7 @@ Layout make_layout(const kda_config_t* cfg, int64_t N, int64_t max_chunks, int64
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   L.cu = take((N + 1) * sizeof(int32_t));
-  L.chunk0 = take((N + 2) * sizeof(int32_t));
+  L.chunk0 = take((2 * N + 2) * sizeof(int32_t));   // and the scan's sequence order
   L.chunk_seq = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int32_t));
   L.desc = take(static_cast<size_t>(max_chunks > 0 ? max_chunks : 1) * sizeof(int4));
   if (recurrent_form(cfg))
@@ -248,7 +248,7 @@ BwdLayout make_bwd_layout(const kda_config_t* cfg, int64_t N, int64_t max_chunks
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   L.cu = take((N + 1) * sizeof(int32_t));
-  L.chunk0 = take((N + 2) * sizeof(int32_t));
+  L.chunk0 = take((2 * N + 2) * sizeof(int32_t));   // and the scan's sequence order
   L.chunk_seq = take(static_cast<size_t>(mc) * sizeof(int32_t));
   L.desc = take(static_cast<size_t>(mc) * sizeof(int4));
   L.recs = take(static_cast<size_t>(blocks) * H * kda::bwd_record_bytes(static_cast<int>(D)));

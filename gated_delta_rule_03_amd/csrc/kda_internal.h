@@ -83,13 +83,17 @@ struct Params {
 // Device-side description of a packed batch, built by the chunk-table kernel.
 struct ChunkTable {
   const int32_t* cu;         // [N+1] token offsets
-  const int32_t* chunk0;     // [N+2] first chunk of each sequence; chunk0[N] = total chunks;
-                             // chunk0[N+1] = 1 when the scan takes its narrow value tile
+  const int32_t* chunk0;     // [2N+2] first chunk of each sequence; chunk0[N] = total chunks;
+                             // chunk0[N+1] = 1 when the scan takes its narrow value tile;
+                             // chunk0[N+2+i] = the i-th sequence in the scan's dispatch order
   const int32_t* chunk_seq;  // [max_chunks] sequence of each chunk
   const int4* desc;          // [max_chunks] (sequence, first token in it, tokens, first packed token)
   int32_t N;
   int32_t s0;                // the table covers positions [s0, s0 + span) of every sequence (0 and
                              // the whole sequence unless the prefill runs in slabs); a multiple of 64
+  // The sequence the scan's i-th (sequence, head) group of workgroups runs:
+  // the long sequences first, so that their serial chains start at once.
+  __device__ int32_t scan_seq(int32_t i) const { return chunk0[N + 2 + i]; }
 };
 
 struct PrefillIO {
