@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_state_scan_kernel
   __shared__ __align__(16) float sStg[TW][D >= 64 ? D / 4 * kRun : 4];   // staged state stores
   int nh, grp;
   if (!scan_coords(t.N * p.H, D / CW, nh, grp)) return;
-  const int h = nh % p.H, n = nh / p.H;
+  const int h = nh % p.H, n = t.scan_seq(nh / p.H);   // long sequences first
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g = lane / 16;
   const int c0 = grp * CW, jw = wave * kScanTile, j0 = c0 + jw;
   const size_t SZ = static_cast<size_t>(D) * D;
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kWave * scan_waves<D>()) void bwd_adjoint_scan_kern
   __shared__ __align__(16) float sStg[TW][D >= 64 ? D / 4 * kRun : 4];   // staged state stores
   int nh, grp;
   if (!scan_coords(t.N * p.H, D / CW, nh, grp)) return;
-  const int h = nh % p.H, n = nh / p.H;
+  const int h = nh % p.H, n = t.scan_seq(nh / p.H);   // long sequences first
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, l16 = lane % 16, g = lane / 16;
   const int c0 = grp * CW, j0 = c0 + wave * kScanTile;
   const size_t SZ = static_cast<size_t>(D) * D;
