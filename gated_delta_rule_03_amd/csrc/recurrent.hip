@@ -175,6 +175,7 @@ __global__ __launch_bounds__(4 * D) void token_prep_kernel(Params p, ChunkTable 
 // DVT = NW CG CPL.
 template <int D, int RGW, int NW, int CPL, bool OUT_BF16>
 __global__ __launch_bounds__(kWave * NW) void recurrent_scan_kernel(Params p, const int32_t* __restrict__ cu,
+                                                                 const int32_t* __restrict__ order,
                                                                  int32_t N, const float* __restrict__ recs,
                                                                  int64_t total_T, const float* S0, float* S_out,
                                                                  void* o) {
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(kWave * NW) void recurrent_scan_kernel(Params p, co
   int L = blockIdx.x;
   if (G % 8 == 0) L = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
   const int tile = L % NTILE, nh = L / NTILE;
-  const int n = nh / H, h = nh % H;
+  const int n = order[nh / H], h = nh % H;   // the chunk table's order: long sequences first
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int rg = lane % RGW, cg = lane / RGW;
   const int col0 = tile * DVT + (CG * w + cg) * CPL;
@@ -379,10 +380,10 @@ static hipError_t launch_recurrent_scan_dc(const Params& p, const ChunkTable& t,
   const dim3 grid(static_cast<unsigned>(t.N) * p.H * (D / (NW * (kWave / RGW) * CPL)));
   if (out_bf16)
     recurrent_scan_kernel<D, RGW, NW, CPL, true>
-        <<<grid, kWave * NW, 0, st>>>(p, t.cu, t.N, recs, total_T, io.S0, io.S_out, io.o);
+        <<<grid, kWave * NW, 0, st>>>(p, t.cu, t.chunk0 + t.N + 2, t.N, recs, total_T, io.S0, io.S_out, io.o);
   else
     recurrent_scan_kernel<D, RGW, NW, CPL, false>
-        <<<grid, kWave * NW, 0, st>>>(p, t.cu, t.N, recs, total_T, io.S0, io.S_out, io.o);
+        <<<grid, kWave * NW, 0, st>>>(p, t.cu, t.chunk0 + t.N + 2, t.N, recs, total_T, io.S0, io.S_out, io.o);
   return hipGetLastError();
 }
 
