@@ -279,7 +279,7 @@ kda_status_t check_backward(const kda_config_t* cfg) {
 
 extern "C" {
 
-int32_t kda_version(void) { return 104; }
+int32_t kda_version(void) { return 105; }
 
 size_t kda_varlen_backward_workspace_bytes(const kda_config_t* cfg, int32_t N, int32_t total_T) {
   if (check_backward(cfg) != KDA_OK || N < 0 || total_T < 0) return 0;

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(kda):
 
 
 def test_version_and_status_strings(kda):
-    assert kda.version() == 104
+    assert kda.version() == 105
     for code, name in ((0, "KDA_OK"), (1, "KDA_ERR_INVALID_ARGUMENT"), (2, "KDA_ERR_UNSUPPORTED"),
                        (3, "KDA_ERR_WORKSPACE_TOO_SMALL"), (4, "KDA_ERR_HIP")):
         assert kda.status_string(code) == name
