@@ -312,12 +312,20 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&acc)[D / 1
 
 // ---------------------------------------------------------------- block prep
 template <int D, bool IO_BF16>
-__global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTable t, PrefillIO io, uint8_t* recs) {
+__global__ __launch_bounds__(kBT, 3) void bwd_block_prep_kernel(Params p, ChunkTable t, PrefillIO io, uint8_t* recs) {
   constexpr BwdRecord R = bwd_record(D);
   __shared__ BlockSmem<D> s;
-  __shared__ float sKm[kBlk][D + 1];   // K e^{-G}
-  __shared__ float sPart[4][kBlk][kBlk];   // half-channel partial products of A and Aqk
-  __shared__ float sT[kBlk][kBlk];
+  // The half-channel partial products of A and Aqk, then T.  Where they fit
+  // (d = 128) they go into the area of e^{G_C - G}, which is no longer needed
+  // after the first pass below: shared memory is then the preprocessed block
+  // alone, ~49 KB, and three workgroups fit on a compute unit instead of two
+  // (the launch bound holds the registers to three waves per SIMD's share).
+  constexpr int kPT = 5 * kBlk * kBlk;
+  constexpr bool kAlias = kBlk * (D + 1) >= kPT;
+  __shared__ float sPT_own[kAlias ? 1 : kPT];
+  float* const pt = kAlias ? &s.eS[0][0] : sPT_own;
+  float (*sPart)[kBlk][kBlk] = reinterpret_cast<float (*)[kBlk][kBlk]>(pt);
+  float (*sT)[kBlk] = reinterpret_cast<float (*)[kBlk]>(pt + 4 * kBlk * kBlk);
   const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.H));
   const int blk = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.H));
   if (blk / kBlocksPerChunk >= t.chunk0[t.N]) return;
@@ -337,10 +345,9 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
   float* gT = reinterpret_cast<float*>(rec + R.T);
   float* gAqk = reinterpret_cast<float*>(rec + R.Aqk);
   float* geGC = reinterpret_cast<float*>(rec + R.eGC);
-  // K-, Q+, K~ and e^{G_C}
+  // Q+, K~ and e^{G_C}
   for (int e = tid; e < kBlk * D; e += kBT) {
     const int r = e / D, c = e % D;
-    sKm[r][c] = s.k[r][c] * s.eM[r][c];
     gQp[e] = s.q[r][c] * s.eP[r][c];
     gKt[e] = s.k[r][c] * s.eS[r][c];
     if (r == 0) geGC[c] = s.eP[kBlk - 1][c];
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(kBT) void bwd_block_prep_kernel(Params p, ChunkTabl
         const int k = k0 + 4 * (2 * half + j2) + g4;
         const float a = (prod == 0 ? s.k[l16][k] : s.q[l16][k]) * s.eP[l16][k];
         const int ch = 2 * ((k0 / 16) & 1) + j2;
-        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sKm[l16][k], acc[ch], 0, 0, 0);
+        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s.k[l16][k] * s.eM[l16][k], acc[ch], 0, 0, 0);   // K-
       }
     }
 #pragma unroll
